@@ -1,0 +1,62 @@
+"""The pins are strong enough: each plants one plausible mistake in a copy of the
+oracle's C source (on the CPU, in a temporary directory), rebuilds it, and checks
+that a pin from test_oracle_pins fails. The real oracle is restored afterwards."""
+import os
+import shutil
+import subprocess
+
+import pytest
+
+import oracle
+import oracle.oracle as orc
+from tests import test_oracle_pins as pins
+
+MUTATIONS = [
+    ("ties go to the higher index",
+     "while (b >= 0 && key[order[b]] < key[o])", "while (b >= 0 && key[order[b]] <= key[o])",
+     lambda: pins.test_prune_1d_exhaustive_int8_small_values(2)),
+    ("keeps the smallest magnitudes",
+     "for (int s = 0; s < N; s++) keep[order[s]] = 1;", "for (int s = 0; s < N; s++) keep[order[M - 1 - s]] = 1;",
+     lambda: pins.test_prune_1d_equals_brute_force("f16", 4, (2,), 50, False)),
+    ("tile score drops its last row",
+     "double score = ((s[0] + s[1]) + s[2]) + s[3];", "double score = ((s[0] + s[1]) + s[2]);",
+     lambda: pins.test_prune_tile_equals_brute_force_and_dp("f16", False)),
+    ("tile enumeration skips candidates",
+     "if (col[0] == 2 && col[1] == 2 && col[2] == 2 && col[3] == 2) {",
+     "if (col[0] == 2 && col[1] == 2 && col[2] == 2 && col[3] == 2 && p0 <= p3) {",
+     pins.test_exactly_90_transposable_patterns),
+    ("metadata fields written most-significant bit first",
+     "for (int q = 0; q < b; q++) put_bit(mrow, t0 + q, (j >> q) & 1);",
+     "for (int q = 0; q < b; q++) put_bit(mrow, t0 + (b - 1 - q), (j >> q) & 1);",
+     lambda: pins.test_round_trips("f16", 2, 4, "N")),
+    ("fp16 exponent bias off by one",
+     "else v = ldexp((double)(f + 1024), e - 25);", "else v = ldexp((double)(f + 1024), e - 24);",
+     pins.test_f16_decode_all_bit_patterns),
+    ("product reads B transposed",
+     "for (int64_t j = 0; j < n; j++) acc[j] += a * brow[j];", "for (int64_t j = 0; j < n; j++) acc[j] += a * B[j * k + kk];",
+     pins.test_gemm_matches_library_matmul),
+    ("negative zero counted as a non-zero",
+     "return (((const uint16_t*)p)[i] & 0x7FFFu) != 0;", "return ((const uint16_t*)p)[i] != 0;",
+     pins.test_check_counts_injected_violations),
+    ("decompress drops the last kept value of each group",
+     "for (int s = 0; s < N; s++) {\n        int64_t t0 = (g * N + s) * (int64_t)b;\n        int j = 0;\n        for (int q = 0; q < b; q++) j |= get_bit(mrow, t0 + q) << q;\n        copy_elem(",
+     "for (int s = 0; s < N - 1; s++) {\n        int64_t t0 = (g * N + s) * (int64_t)b;\n        int j = 0;\n        for (int q = 0; q < b; q++) j |= get_bit(mrow, t0 + q) << q;\n        copy_elem(",
+     lambda: pins.test_round_trips("bf16", 2, 4, "T")),
+]
+
+
+@pytest.mark.parametrize("name,old,new,pin", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(name, old, new, pin, tmp_path, monkeypatch):
+    src = open(orc._SRC).read()
+    assert src.count(old) == 1, name
+    mutated = tmp_path / "oracle_mut.c"
+    mutated.write_text(src.replace(old, new))
+    so = tmp_path / "liboracle_mut.so"
+    subprocess.check_call(["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC", "-shared",
+                           "-o", str(so), str(mutated), "-lm"])
+    monkeypatch.setattr(orc, "_SRC", str(mutated))
+    monkeypatch.setattr(orc, "_SO", str(so))
+    monkeypatch.setattr(orc, "_lib", None)
+    with pytest.raises(AssertionError):
+        pin()
+    monkeypatch.setattr(orc, "_lib", None)
