@@ -1,0 +1,191 @@
+/*
+ * nmsparse — N:M fine-grained structured-sparse matrix multiply for AMD
+ * Instinct MI355X (gfx950).
+ *
+ *   D = alpha * op(A) * op(B) + beta * C
+ *
+ * A is the sparse operand: in every group of M consecutive elements along the
+ * reduction dimension k of op(A), at most N are non-zero (2:4 is the case the
+ * matrix cores run natively; general N:M with M in {4, 8, 16, 32} runs on the
+ * gather paths). B, C and D are dense.
+ *
+ * The operation, its layouts and the set-up-once / multiply-many workflow
+ * follow the NVIDIA developer blog "Exploiting Ampere structured sparsity with
+ * cuSPARSELt" (the section defining D = alpha*op(A)*op(B) + beta*C with N/T
+ * layouts, the workflow list, and the code example: prune, prune check,
+ * compressed size, compress, matmul). The magnitude top-N rule follows the
+ * apex pull request "[sparse] update support for arbitrary N:M settings
+ * sparse" (extension 1, the greedy per-group mask); the transposable 4x4-tile
+ * mask follows pytorch issue 126420 "backpropagation for sparse
+ * semi-structured" (the maintainer reply on forward and backward needing
+ * 2:4 in both directions).
+ *
+ * Conventions used by every entry point
+ * -------------------------------------
+ *  - Every matrix is row-major. op_a / op_b say whether the stored array is
+ *    used as is (NM_OP_N) or transposed (NM_OP_T):
+ *      op_a = N: A stored m x k (lda >= k);  op_a = T: A stored k x m (lda >= m)
+ *      op_b = N: B stored k x n (ldb >= n);  op_b = T: B stored n x k (ldb >= k)
+ *      C and D: m x n (ldc, ldd >= n).
+ *    (The blog defines N/T on column-major storage; its column-major "TN" is
+ *    byte-for-byte this library's "NT" with D written transposed.)
+ *  - Element types (type_ab, type_cd): (NM_F16, NM_F16), (NM_BF16, NM_BF16)
+ *    with fp32 accumulation; (NM_I8, NM_I32) with exact int32 accumulation
+ *    (the blog's type list; C and D are int32 for the integer path).
+ *  - Leading dimensions are in elements. All device pointers must be 16-byte
+ *    aligned, and every row of a matrix whose row is at least 16 bytes long
+ *    must start on a 16-byte boundary (ld * element size % 16 == 0).
+ *  - Ownership: the caller allocates and owns every device buffer. A plan owns
+ *    host memory only. The library never allocates device memory and never
+ *    synchronises the device: device work is enqueued on the caller's stream
+ *    (`stream` is a hipStream_t passed as void*, NULL = the null stream).
+ *  - Errors: invalid arguments, shapes and alignment are reported before
+ *    anything is enqueued (nothing runs). A failed kernel launch returns
+ *    NM_ERR_HIP. nm_last_error() gives a message for the last failure on the
+ *    calling thread.
+ *
+ * Compressed layout (this library's definition; the blog only says the sparse
+ * matrix is stored as its non-zeros at half size plus "a small amount of
+ * metadata"). For every row r of op(A) and group g (columns gM .. gM+M-1),
+ * the kept in-group offsets i_0 < ... < i_{N-1} are those the 1-D rule below
+ * selects. Then
+ *     values[r * values_ld + g*N + s] = op(A)[r][g*M + i_s]
+ *     bits [(g*N + s)*b, (g*N + s + 1)*b) of row r of meta  = i_s
+ * with b = ceil(log2 M) (2 bits for M = 4, 5 bits for M = 32). Each meta row
+ * is a little-endian bit stream (bit t is bit t%8 of byte t/8) of meta_ld
+ * bytes. values_ld (elements) and meta_ld (bytes) are the row lengths rounded
+ * up to 16 bytes; every padding bit and element is zero. For 2:4 a group is
+ * the nibble i_0 | i_1 << 2, which is also the index format the gfx950 sparse
+ * matrix instructions consume.
+ *
+ * 1-D selection rule: in every group keep the N elements of largest |x|;
+ * among equal magnitudes the lower offset wins (for fp16/bf16 the magnitude
+ * order is the order of the bit pattern with the sign cleared, so +0 and -0
+ * are equal). Exactly N slots are kept per group even when some are zero.
+ */
+#ifndef NMSPARSE_H
+#define NMSPARSE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NM_OK = 0,
+  NM_ERR_INVALID_ARG = 1, /* null pointer, unknown enum, bad N:M, non-integral alpha/beta on the int path */
+  NM_ERR_SHAPE = 2,       /* k % M != 0, tile mode on dims not divisible by 4, ld too small, size overflow */
+  NM_ERR_ALIGN = 3,       /* pointer or leading dimension breaks the 16-byte rule */
+  NM_ERR_UNSUPPORTED = 4, /* valid request this build does not implement (e.g. column-major D) */
+  NM_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
+} nm_status_t;
+
+typedef enum { NM_F16 = 0, NM_BF16 = 1, NM_I8 = 2, NM_I32 = 3 } nm_dtype_t;
+typedef enum { NM_OP_N = 0, NM_OP_T = 1 } nm_op_t;
+typedef enum { NM_ROW_MAJOR = 0 } nm_order_t;
+typedef enum { NM_PRUNE_1D = 0, NM_PRUNE_TILE4X4 = 1 } nm_prune_mode_t;
+
+/* Problem descriptor: the blog's structured / dense / matmul descriptors
+ * folded into one struct. All fields are read by nm_plan_init and copied. */
+typedef struct {
+  int64_t m, n, k;          /* D is m x n; k is the reduction dimension */
+  int32_t nm_n, nm_m;       /* N kept of every M along k of op(A); 1 <= N < M, M in {4, 8, 16, 32} */
+  int32_t op_a, op_b;       /* nm_op_t */
+  int32_t type_ab, type_cd; /* nm_dtype_t pair, see above */
+  int64_t lda, ldb, ldc, ldd;
+  int32_t order_cd;         /* NM_ROW_MAJOR (the only order in this build) */
+  int32_t reserved;         /* must be 0 */
+} nm_problem_t;
+
+typedef struct nm_plan* nm_plan_t;
+
+/* Validate a problem and build a plan (host only, no device call). The plan
+ * fixes shapes, layouts, compressed sizes and the SpMM kernel. On failure
+ * *plan is set to NULL. */
+nm_status_t nm_plan_init(nm_plan_t* plan, const nm_problem_t* problem);
+
+/* Release a plan (host memory only). NULL is accepted. */
+nm_status_t nm_plan_destroy(nm_plan_t plan);
+
+/* Sizes of the compressed form of op(A) (the blog's compressed-size query):
+ * values_bytes = m * values_ld * sizeof(type_ab); meta_bytes = m * meta_ld.
+ * Any output pointer may be NULL. */
+nm_status_t nm_compressed_size(nm_plan_t plan, size_t* values_bytes, size_t* meta_bytes,
+                               int64_t* values_ld_elems, int64_t* meta_ld_bytes);
+
+/* Size of the optional keep mask written by nm_prune: one bit per element of
+ * the stored A (rows x cols as stored), uint32 words, least significant bit
+ * first, each stored row starting a new word: mask_ld_words = ceil(cols/32). */
+nm_status_t nm_mask_size(nm_plan_t plan, size_t* mask_bytes, int64_t* mask_ld_words);
+
+/* Prune the stored A (lda) into dA_pruned (same shape and lda; may equal dA).
+ *  NM_PRUNE_1D:      the 1-D rule above along k of op(A); kept values copied
+ *                    bit for bit, every other element written as +0.
+ *  NM_PRUNE_TILE4X4: requires N:M = 2:4 and both stored dimensions divisible
+ *                    by 4. On every 4x4 tile of the stored matrix keep the
+ *                    pattern with exactly two elements per row and per column
+ *                    (90 candidates) that maximises the kept sum of |x|,
+ *                    summed in fp64 as ((s0 + s1) + s2) + s3 over tile rows;
+ *                    ties go to the first candidate when candidates are
+ *                    ordered lexicographically by their per-row pair index
+ *                    (pairs ordered (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)).
+ *                    The result is 2:4 along both dimensions, so it serves
+ *                    op_a = N (forward) and op_a = T (backward).
+ * d_mask may be NULL; otherwise it receives the keep mask (nm_mask_size). */
+nm_status_t nm_prune(nm_plan_t plan, const void* dA, void* dA_pruned, int32_t mode,
+                     uint32_t* d_mask, void* stream);
+
+/* Conformance check (the blog's prune check, with its flag made a count):
+ * writes to *d_violations (device int32) the number of groups of op(A) that
+ * hold more than N non-zeros (1-D), or the number of 4x4-tile rows plus
+ * tile columns with more than two non-zeros (TILE4X4). 0 means conforming.
+ * -0.0 counts as zero. The count overwrites *d_violations. */
+nm_status_t nm_prune_check(nm_plan_t plan, const void* dA, int32_t mode, int32_t* d_violations,
+                           void* stream);
+
+/* Compress the stored A into (values, meta) in the layout above. The
+ * selection is the 1-D rule, so compress(A) == compress(prune(A)); on an
+ * input that already conforms, the kept slots are its non-zeros plus the
+ * lowest-offset zeros. Padding is written as zero. */
+nm_status_t nm_compress(nm_plan_t plan, const void* dA, void* d_values, void* d_meta, void* stream);
+
+/* Inverse of nm_compress: writes the dense stored A (lda, op_a orientation):
+ * kept values at their offsets, +0 everywhere else. */
+nm_status_t nm_decompress(nm_plan_t plan, const void* d_values, const void* d_meta, void* dA_out,
+                          void* stream);
+
+/* D = alpha * op(A) * op(B) + beta * C with A given as (values, meta).
+ * alpha and beta are host floats (the blog's example passes host floats);
+ * on the int8 path both must be integers. dC may be NULL when *beta == 0 and
+ * may equal dD. fp16/bf16 outputs are alpha*acc + beta*C evaluated in fp32 and
+ * rounded to nearest even. d_workspace must be NULL (no workspace needed). */
+nm_status_t nm_spmm(nm_plan_t plan, const float* alpha, const void* d_values, const void* d_meta,
+                    const void* dB, const float* beta, const void* dC, void* dD, void* d_workspace,
+                    void* stream);
+
+/* Same-shape dense product D = alpha * op(A) * op(B) + beta * C with A dense
+ * (stored with lda and op_a as in the plan). This is the in-library
+ * comparator for the sparse speed-up (the blog's dense-vs-sparse table); it
+ * ignores N:M. */
+nm_status_t nm_dense_gemm(nm_plan_t plan, const float* alpha, const void* dA, const void* dB,
+                          const float* beta, const void* dC, void* dD, void* stream);
+
+/* Name of the SpMM kernel the plan dispatches to (static string). */
+const char* nm_plan_kernel_name(nm_plan_t plan);
+
+/* Static text for a status code. */
+const char* nm_status_string(nm_status_t status);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* nm_last_error(void);
+
+/* Library version as major*10000 + minor*100 + patch. */
+int32_t nm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NMSPARSE_H */

@@ -1,0 +1,265 @@
+// nmsparse C ABI: plan validation, size queries, argument checks and dispatch.
+//
+// The workflow (plan once; prune, check, compress; multiply many times with new
+// B) follows the cuSPARSELt blog's workflow list and code example; here the
+// handle, the descriptors, the algorithm selection and the plan collapse into
+// one host-only plan object. Every check happens before anything is enqueued.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <string>
+
+#include "nm_internal.h"
+
+namespace nm {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+static nm_status_t fail(nm_status_t st, const std::string& msg) {
+  set_error(msg);
+  return st;
+}
+
+static nm_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return NM_OK;
+  return fail(NM_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+static int esize(int dt) { return dt == NM_I8 ? 1 : (dt == NM_I32 ? 4 : 2); }
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Row-start rule: every row of at least 16 bytes starts on a 16-byte boundary.
+static bool ld_ok(int64_t row_elems, int64_t ld, int es) {
+  return row_elems * es < 16 || (ld * es) % 16 == 0;
+}
+
+static const int64_t kMaxElems = (int64_t)1 << 46;
+
+}  // namespace nm
+
+using namespace nm;
+
+extern "C" {
+
+int32_t nm_version(void) { return 10000; }
+
+const char* nm_status_string(nm_status_t s) {
+  switch (s) {
+    case NM_OK: return "NM_OK";
+    case NM_ERR_INVALID_ARG: return "NM_ERR_INVALID_ARG: invalid argument";
+    case NM_ERR_SHAPE: return "NM_ERR_SHAPE: shape or leading dimension not allowed";
+    case NM_ERR_ALIGN: return "NM_ERR_ALIGN: pointer or row start not 16-byte aligned";
+    case NM_ERR_UNSUPPORTED: return "NM_ERR_UNSUPPORTED: not supported by this build";
+    case NM_ERR_HIP: return "NM_ERR_HIP: HIP runtime error";
+  }
+  return "unknown nm_status_t";
+}
+
+const char* nm_last_error(void) { return g_last_error.c_str(); }
+
+nm_status_t nm_plan_init(nm_plan_t* plan, const nm_problem_t* p) {
+  if (!plan) return fail(NM_ERR_INVALID_ARG, "plan is NULL");
+  *plan = nullptr;
+  if (!p) return fail(NM_ERR_INVALID_ARG, "problem is NULL");
+  if (p->m < 0 || p->n < 0 || p->k < 0) return fail(NM_ERR_SHAPE, "m, n, k must be >= 0");
+  if (p->m > kMaxElems || p->n > kMaxElems || p->k > kMaxElems) return fail(NM_ERR_SHAPE, "dimension too large");
+  const int M = p->nm_m, N = p->nm_n;
+  if (!(M == 4 || M == 8 || M == 16 || M == 32)) return fail(NM_ERR_INVALID_ARG, "M must be 4, 8, 16 or 32");
+  if (N < 1 || N >= M) return fail(NM_ERR_INVALID_ARG, "N must satisfy 1 <= N < M");
+  if ((p->op_a != NM_OP_N && p->op_a != NM_OP_T) || (p->op_b != NM_OP_N && p->op_b != NM_OP_T))
+    return fail(NM_ERR_INVALID_ARG, "op_a / op_b must be NM_OP_N or NM_OP_T");
+  const bool pair_ok = (p->type_ab == NM_F16 && p->type_cd == NM_F16) ||
+                       (p->type_ab == NM_BF16 && p->type_cd == NM_BF16) ||
+                       (p->type_ab == NM_I8 && p->type_cd == NM_I32);
+  if (!pair_ok) return fail(NM_ERR_INVALID_ARG, "type pair must be (F16,F16), (BF16,BF16) or (I8,I32)");
+  if (p->order_cd != NM_ROW_MAJOR) return fail(NM_ERR_UNSUPPORTED, "only row-major C/D");
+  if (p->reserved != 0) return fail(NM_ERR_INVALID_ARG, "reserved must be 0");
+  if (p->k % M != 0) return fail(NM_ERR_SHAPE, "k must be a multiple of M");
+  const int ea = esize(p->type_ab), ec = esize(p->type_cd);
+  const int64_t a_rows = p->op_a == NM_OP_N ? p->m : p->k;
+  const int64_t a_cols = p->op_a == NM_OP_N ? p->k : p->m;
+  const int64_t b_rows = p->op_b == NM_OP_N ? p->k : p->n;
+  const int64_t b_cols = p->op_b == NM_OP_N ? p->n : p->k;
+  if (p->lda < (a_cols > 0 ? a_cols : 1) || p->ldb < (b_cols > 0 ? b_cols : 1) ||
+      p->ldc < (p->n > 0 ? p->n : 1) || p->ldd < (p->n > 0 ? p->n : 1))
+    return fail(NM_ERR_SHAPE, "leading dimension smaller than the row length");
+  if (p->lda > kMaxElems || p->ldb > kMaxElems || p->ldc > kMaxElems || p->ldd > kMaxElems)
+    return fail(NM_ERR_SHAPE, "leading dimension too large");
+  if ((double)a_rows * (double)p->lda > (double)kMaxElems || (double)b_rows * (double)p->ldb > (double)kMaxElems ||
+      (double)p->m * (double)p->ldd > (double)kMaxElems || (double)p->m * (double)p->ldc > (double)kMaxElems)
+    return fail(NM_ERR_SHAPE, "matrix too large");
+  if (!ld_ok(a_cols, p->lda, ea) || !ld_ok(b_cols, p->ldb, ea) || !ld_ok(p->n, p->ldc, ec) ||
+      !ld_ok(p->n, p->ldd, ec))
+    return fail(NM_ERR_ALIGN, "rows of 16 bytes or more must start on 16-byte boundaries (ld * elem size % 16)");
+
+  nm_plan* pl = new (std::nothrow) nm_plan();
+  if (!pl) return fail(NM_ERR_INVALID_ARG, "out of host memory");
+  pl->p = *p;
+  pl->esz_ab = ea;
+  pl->esz_cd = ec;
+  pl->a_rows = a_rows;
+  pl->a_cols = a_cols;
+  int b = 0;
+  while ((1 << b) < M) b++;
+  pl->bits = b;
+  const int64_t per16 = 16 / ea;
+  const int64_t nvals = p->k / M * N;
+  pl->vld = (nvals + per16 - 1) / per16 * per16;
+  const int64_t mbytes = (p->k / M * N * b + 7) / 8;
+  pl->mld = (mbytes + 15) / 16 * 16;
+  // kernel choice
+  if (p->n <= 16) pl->kernel = K_SKINNY;
+  else if (N == 2 && M == 4) pl->kernel = K_SMFMAC_24;
+  else pl->kernel = K_GATHER_MFMA;
+  *plan = pl;
+  set_error("");
+  return NM_OK;
+}
+
+nm_status_t nm_plan_destroy(nm_plan_t plan) {
+  delete plan;
+  return NM_OK;
+}
+
+const char* nm_plan_kernel_name(nm_plan_t plan) {
+  if (!plan) return "none";
+  switch (plan->kernel) {
+    case K_SMFMAC_24: return "spmm_smfmac_2of4";
+    case K_GATHER_MFMA: return "spmm_gather_mfma";
+    case K_SKINNY: return "spmm_skinny";
+  }
+  return "none";
+}
+
+nm_status_t nm_compressed_size(nm_plan_t plan, size_t* values_bytes, size_t* meta_bytes, int64_t* values_ld,
+                               int64_t* meta_ld) {
+  if (!plan) return fail(NM_ERR_INVALID_ARG, "plan is NULL");
+  if (values_bytes) *values_bytes = (size_t)(plan->p.m * plan->vld * plan->esz_ab);
+  if (meta_bytes) *meta_bytes = (size_t)(plan->p.m * plan->mld);
+  if (values_ld) *values_ld = plan->vld;
+  if (meta_ld) *meta_ld = plan->mld;
+  return NM_OK;
+}
+
+nm_status_t nm_mask_size(nm_plan_t plan, size_t* mask_bytes, int64_t* mask_ld_words) {
+  if (!plan) return fail(NM_ERR_INVALID_ARG, "plan is NULL");
+  const int64_t w = (plan->a_cols + 31) / 32;
+  if (mask_bytes) *mask_bytes = (size_t)(plan->a_rows * w * 4);
+  if (mask_ld_words) *mask_ld_words = w;
+  return NM_OK;
+}
+
+static nm_status_t check_mode(const nm_plan* plan, int32_t mode) {
+  if (mode != NM_PRUNE_1D && mode != NM_PRUNE_TILE4X4) return fail(NM_ERR_INVALID_ARG, "unknown prune mode");
+  if (mode == NM_PRUNE_TILE4X4) {
+    if (!(plan->p.nm_n == 2 && plan->p.nm_m == 4)) return fail(NM_ERR_INVALID_ARG, "tile mode needs N:M = 2:4");
+    if (plan->a_rows % 4 || plan->a_cols % 4) return fail(NM_ERR_SHAPE, "tile mode needs both stored dims % 4 == 0");
+  }
+  return NM_OK;
+}
+
+nm_status_t nm_prune(nm_plan_t plan, const void* dA, void* dA_pruned, int32_t mode, uint32_t* d_mask, void* stream) {
+  if (!plan) return fail(NM_ERR_INVALID_ARG, "plan is NULL");
+  nm_status_t st = check_mode(plan, mode);
+  if (st != NM_OK) return st;
+  const bool empty = plan->a_rows == 0 || plan->a_cols == 0;
+  if (!empty && (!dA || !dA_pruned)) return fail(NM_ERR_INVALID_ARG, "dA / dA_pruned is NULL");
+  if (!aligned16(dA) || !aligned16(dA_pruned) || !aligned16(d_mask))
+    return fail(NM_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  if (empty) return NM_OK;
+  hipStream_t s = (hipStream_t)stream;
+  if (mode == NM_PRUNE_TILE4X4) return hip_status(launch_prune_tile(*plan, dA, dA_pruned, d_mask, s), "prune (tile)");
+  return hip_status(launch_prune_1d(*plan, dA, dA_pruned, d_mask, s), "prune (1-D)");
+}
+
+nm_status_t nm_prune_check(nm_plan_t plan, const void* dA, int32_t mode, int32_t* d_violations, void* stream) {
+  if (!plan) return fail(NM_ERR_INVALID_ARG, "plan is NULL");
+  nm_status_t st = check_mode(plan, mode);
+  if (st != NM_OK) return st;
+  if (!d_violations) return fail(NM_ERR_INVALID_ARG, "d_violations is NULL");
+  const bool empty = plan->a_rows == 0 || plan->a_cols == 0;
+  if (!empty && !dA) return fail(NM_ERR_INVALID_ARG, "dA is NULL");
+  if (!aligned16(dA)) return fail(NM_ERR_ALIGN, "dA must be 16-byte aligned");
+  if (((uintptr_t)d_violations & 3u) != 0) return fail(NM_ERR_ALIGN, "d_violations must be 4-byte aligned");
+  return hip_status(launch_check(*plan, dA, mode, d_violations, (hipStream_t)stream), "prune check");
+}
+
+nm_status_t nm_compress(nm_plan_t plan, const void* dA, void* d_values, void* d_meta, void* stream) {
+  if (!plan) return fail(NM_ERR_INVALID_ARG, "plan is NULL");
+  const bool empty = plan->p.m == 0 || plan->p.k == 0;
+  if (!empty && (!dA || !d_values || !d_meta)) return fail(NM_ERR_INVALID_ARG, "dA / d_values / d_meta is NULL");
+  if (!aligned16(dA) || !aligned16(d_values) || !aligned16(d_meta))
+    return fail(NM_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  if (empty) return NM_OK;
+  return hip_status(launch_compress(*plan, dA, d_values, d_meta, (hipStream_t)stream), "compress");
+}
+
+nm_status_t nm_decompress(nm_plan_t plan, const void* d_values, const void* d_meta, void* dA_out, void* stream) {
+  if (!plan) return fail(NM_ERR_INVALID_ARG, "plan is NULL");
+  const bool empty = plan->p.m == 0 || plan->p.k == 0;
+  if (!empty && (!dA_out || !d_values || !d_meta)) return fail(NM_ERR_INVALID_ARG, "d_values / d_meta / dA_out is NULL");
+  if (!aligned16(dA_out) || !aligned16(d_values) || !aligned16(d_meta))
+    return fail(NM_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  if (empty) return NM_OK;
+  return hip_status(launch_decompress(*plan, d_values, d_meta, dA_out, (hipStream_t)stream), "decompress");
+}
+
+static nm_status_t check_scalars(const nm_plan* plan, const float* alpha, const float* beta) {
+  if (!alpha || !beta) return fail(NM_ERR_INVALID_ARG, "alpha / beta is NULL");
+  if (!isfinite(*alpha) || !isfinite(*beta)) return fail(NM_ERR_INVALID_ARG, "alpha / beta must be finite");
+  if (plan->p.type_ab == NM_I8) {
+    if (*alpha != floorf(*alpha) || *beta != floorf(*beta) || fabsf(*alpha) > 16777216.0f || fabsf(*beta) > 16777216.0f)
+      return fail(NM_ERR_INVALID_ARG, "int8 path: alpha and beta must be integers of magnitude <= 2^24");
+  }
+  return NM_OK;
+}
+
+static nm_status_t check_product_ptrs(const nm_plan* plan, const void* a0, const void* a1, const void* dB,
+                                      float beta, const void* dC, void* dD) {
+  const bool out_empty = plan->p.m == 0 || plan->p.n == 0;
+  if (!out_empty) {
+    if (!dD) return fail(NM_ERR_INVALID_ARG, "dD is NULL");
+    if (beta != 0.0f && !dC) return fail(NM_ERR_INVALID_ARG, "dC is NULL while beta != 0");
+    if (plan->p.k > 0 && (!a0 || !a1 || !dB)) return fail(NM_ERR_INVALID_ARG, "A / B operand is NULL");
+  }
+  if (!aligned16(a0) || !aligned16(a1) || !aligned16(dB) || !aligned16(dC) || !aligned16(dD))
+    return fail(NM_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  return NM_OK;
+}
+
+nm_status_t nm_spmm(nm_plan_t plan, const float* alpha, const void* d_values, const void* d_meta, const void* dB,
+                    const float* beta, const void* dC, void* dD, void* d_workspace, void* stream) {
+  if (!plan) return fail(NM_ERR_INVALID_ARG, "plan is NULL");
+  nm_status_t st = check_scalars(plan, alpha, beta);
+  if (st != NM_OK) return st;
+  if (d_workspace) return fail(NM_ERR_INVALID_ARG, "d_workspace must be NULL");
+  st = check_product_ptrs(plan, d_values, d_meta, dB, *beta, dC, dD);
+  if (st != NM_OK) return st;
+  if (plan->p.m == 0 || plan->p.n == 0) return NM_OK;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e;
+  switch (plan->kernel) {
+    case K_SMFMAC_24: e = launch_spmm_smfmac(*plan, *alpha, d_values, d_meta, dB, *beta, dC, dD, s); break;
+    case K_GATHER_MFMA: e = launch_spmm_gather(*plan, *alpha, d_values, d_meta, dB, *beta, dC, dD, s); break;
+    default: e = launch_spmm_skinny(*plan, *alpha, d_values, d_meta, dB, *beta, dC, dD, s); break;
+  }
+  return hip_status(e, "spmm");
+}
+
+nm_status_t nm_dense_gemm(nm_plan_t plan, const float* alpha, const void* dA, const void* dB, const float* beta,
+                          const void* dC, void* dD, void* stream) {
+  if (!plan) return fail(NM_ERR_INVALID_ARG, "plan is NULL");
+  nm_status_t st = check_scalars(plan, alpha, beta);
+  if (st != NM_OK) return st;
+  st = check_product_ptrs(plan, dA, dA, dB, *beta, dC, dD);
+  if (st != NM_OK) return st;
+  if (plan->p.m == 0 || plan->p.n == 0) return NM_OK;
+  return hip_status(launch_dense_gemm(*plan, *alpha, dA, dB, *beta, dC, dD, (hipStream_t)stream), "dense gemm");
+}
+
+}  // extern "C"

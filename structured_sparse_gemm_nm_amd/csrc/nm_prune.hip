@@ -1,0 +1,506 @@
+// Prune, prune check, compress and decompress kernels (HBM-bound).
+//
+// What they compute:
+//  - 1-D N:M selection: keep the N largest |x| in every group of M along k of
+//    op(A), ties to the lower offset (apex PR "[sparse] update support for
+//    arbitrary N:M settings sparse", extension 1, greedy per-group top-N).
+//  - Transposable 2:4 on 4x4 tiles: two kept per tile row and per tile column,
+//    chosen to maximise the kept |x| (pytorch issue 126420 "backpropagation for
+//    sparse semi-structured", maintainer reply).
+//  - Prune check: count of non-conforming groups (cuSPARSELt blog, the
+//    prune-check snippet, whose non-zero flag means "does not conform").
+//  - Compress / decompress: kept values plus b-bit in-group offsets (cuSPARSELt
+//    blog, Figure 2 text), in the layout documented in include/nmsparse.h.
+//
+// Design: a block owns a tile of 64 logical rows x 256 logical k of op(A).
+// The tile is copied between HBM and LDS in the *stored* orientation with
+// 16-byte row-contiguous accesses (so op_a = T costs the same as op_a = N);
+// threads then work group by group out of LDS, and results (pruned tile, keep
+// mask, values, metadata bytes) are staged in LDS and written back row-
+// contiguously. Every tile writes the row padding of the compressed buffers
+// when it holds the row's last group.
+#include "nm_internal.h"
+#include "nm_device.h"
+
+namespace nm {
+
+constexpr int TILE_R = 64;    // logical rows per tile
+constexpr int TILE_K = 256;   // logical k per tile
+constexpr int TPB = 256;      // threads per block
+
+struct TileArgs {
+  const uint8_t* a;     // stored dense input (prune, compress)
+  uint8_t* out;         // stored dense output (prune, decompress)
+  uint32_t* mask;       // optional keep mask (prune)
+  uint8_t* vals;        // compressed values (out for compress, in for decompress)
+  uint8_t* meta;        // metadata bytes
+  int64_t m, k;         // logical op(A) dims
+  int64_t lda;          // stored leading dimension (elements)
+  int64_t mask_ld;      // words per stored row of the mask
+  int64_t vld, mld;     // compressed strides (elements, bytes)
+  int N, op_t, bits, vec_ok;
+};
+
+enum TileOp { T_PRUNE = 0, T_COMPRESS = 1, T_DECOMPRESS = 2 };
+
+// Copy a stored sub-block [sr0, sr0+SR) x [sc0, sc0+SC) between HBM and LDS
+// (LDS row stride SC elements). Out-of-matrix elements read as 0 and are not
+// written back.
+template <int ESZ, int SR, int SC>
+__device__ __forceinline__ void tile_in(uint8_t* lds, const uint8_t* g, int64_t sr0, int64_t sc0,
+                                        int64_t rows, int64_t cols, int64_t ld, bool vec_ok) {
+  constexpr int CH = 16 / ESZ;
+  constexpr int CPR = SC / CH;
+  for (int c = threadIdx.x; c < SR * CPR; c += TPB) {
+    const int r = c / CPR, cc = (c % CPR) * CH;
+    const int64_t gr = sr0 + r, gc = sc0 + cc;
+    uint8_t* dst = lds + (size_t)(r * SC + cc) * ESZ;
+    if (vec_ok && gr < rows && gc + CH <= cols) {
+      *(u32x4*)dst = __builtin_nontemporal_load((const u32x4*)(g + (size_t)(gr * ld + gc) * ESZ));
+    } else {
+      for (int e = 0; e < CH; e++) {
+        const bool in = gr < rows && gc + e < cols;
+        if (ESZ == 2) ((uint16_t*)dst)[e] = in ? ((const uint16_t*)g)[gr * ld + gc + e] : (uint16_t)0;
+        else dst[e] = in ? g[gr * ld + gc + e] : (uint8_t)0;
+      }
+    }
+  }
+}
+
+template <int ESZ, int SR, int SC>
+__device__ __forceinline__ void tile_out(uint8_t* g, const uint8_t* lds, int64_t sr0, int64_t sc0,
+                                         int64_t rows, int64_t cols, int64_t ld, bool vec_ok) {
+  constexpr int CH = 16 / ESZ;
+  constexpr int CPR = SC / CH;
+  for (int c = threadIdx.x; c < SR * CPR; c += TPB) {
+    const int r = c / CPR, cc = (c % CPR) * CH;
+    const int64_t gr = sr0 + r, gc = sc0 + cc;
+    if (gr >= rows) continue;
+    const uint8_t* src = lds + (size_t)(r * SC + cc) * ESZ;
+    if (vec_ok && gc + CH <= cols) {
+      __builtin_nontemporal_store(*(const u32x4*)src, (u32x4*)(g + (size_t)(gr * ld + gc) * ESZ));
+    } else {
+      for (int e = 0; e < CH && gc + e < cols; e++) {
+        if (ESZ == 2) ((uint16_t*)g)[gr * ld + gc + e] = ((const uint16_t*)src)[e];
+        else g[gr * ld + gc + e] = src[e];
+      }
+    }
+  }
+}
+
+template <int ESZ>
+__device__ __forceinline__ uint32_t lds_elem(const uint8_t* lds, int idx) {
+  return ESZ == 2 ? (uint32_t)((const uint16_t*)lds)[idx] : (uint32_t)lds[idx];
+}
+template <int ESZ>
+__device__ __forceinline__ void lds_set(uint8_t* lds, int idx, uint32_t v) {
+  if (ESZ == 2) ((uint16_t*)lds)[idx] = (uint16_t)v;
+  else lds[idx] = (uint8_t)v;
+}
+
+// LDS budget (bytes): dense tile + values tile + metadata tile + mask words.
+constexpr int LDS_DENSE = TILE_R * TILE_K * 2;
+constexpr int LDS_VALS = TILE_R * TILE_K * 2;          // N <= M - 1 < M: values never exceed the dense tile
+// Largest metadata bytes per tile row over all (N, M) supported: (TILE_K / M) * N * b / 8 with N = M - 1:
+// M=4: 64*3*2/8 = 48, M=8: 32*7*3/8 = 84, M=16: 16*15*4/8 = 120, M=32: 8*31*5/8 = 155.
+constexpr int META_ROW_BYTES = 160;                     // rounded up to a whole number of words
+constexpr int LDS_META = TILE_R * META_ROW_BYTES;
+constexpr int LDS_MASK = TILE_R * TILE_K / 8;
+
+template <int DT, int ESZ, int M, int OP>
+__global__ void __launch_bounds__(TPB) tile_kernel(TileArgs A) {
+  __shared__ __attribute__((aligned(16))) uint8_t s_dense[LDS_DENSE];
+  __shared__ __attribute__((aligned(16))) uint8_t s_vals[OP == T_PRUNE ? 16 : LDS_VALS];
+  __shared__ __attribute__((aligned(16))) uint32_t s_meta[OP == T_PRUNE ? 4 : LDS_META / 4];
+  __shared__ __attribute__((aligned(16))) uint32_t s_mask[OP == T_PRUNE ? LDS_MASK / 4 : 4];
+
+  constexpr int GPR = TILE_K / M;           // groups per tile row
+  const int N = A.N, b = A.bits;
+  const int64_t i0 = (int64_t)blockIdx.y * TILE_R;
+  const int64_t k0 = (int64_t)blockIdx.x * TILE_K;
+  const bool opT = A.op_t != 0;
+  const int64_t srows = opT ? A.k : A.m, scols = opT ? A.m : A.k;   // stored dims
+  const int64_t sr0 = opT ? k0 : i0, sc0 = opT ? i0 : k0;
+  const int rows_here = (int)min((int64_t)TILE_R, A.m - i0);
+  const int groups_here = (int)(min((int64_t)TILE_K, A.k - k0) / M);
+  const int vals_per_row = groups_here * N;                          // elements
+  const int meta_bits_row = groups_here * N * b;
+  const int meta_bytes_row = (meta_bits_row + 7) / 8;
+  const int meta_words_row = (META_ROW_BYTES) / 4;
+  const bool last_k_tile = k0 + TILE_K >= A.k;
+
+  // ---- stage inputs ----
+  if (OP == T_PRUNE || OP == T_COMPRESS) {
+    if (opT) tile_in<ESZ, TILE_K, TILE_R>(s_dense, A.a, sr0, sc0, srows, scols, A.lda, A.vec_ok);
+    else tile_in<ESZ, TILE_R, TILE_K>(s_dense, A.a, sr0, sc0, srows, scols, A.lda, A.vec_ok);
+  }
+  if (OP == T_PRUNE) {
+    for (int w = threadIdx.x; w < LDS_MASK / 4; w += TPB) s_mask[w] = 0;
+  }
+  if (OP == T_COMPRESS) {
+    for (int w = threadIdx.x; w < LDS_META / 4; w += TPB) s_meta[w] = 0;
+  }
+  if (OP == T_DECOMPRESS) {
+    for (int w = threadIdx.x; w < LDS_DENSE / 16; w += TPB) ((u32x4*)s_dense)[w] = u32x4{0, 0, 0, 0};
+    const int64_t vbase = (k0 / M) * N;                  // first value of this tile in a row
+    const int64_t mbase = (k0 / M) * N * b / 8;          // first metadata byte (byte aligned)
+    for (int e = threadIdx.x; e < TILE_R * vals_per_row; e += TPB) {
+      const int r = e / vals_per_row, c = e % vals_per_row;
+      if (r < rows_here) {
+        const size_t gi = (size_t)((i0 + r) * A.vld + vbase + c);
+        lds_set<ESZ>(s_vals, r * (GPR * N) + c, ESZ == 2 ? (uint32_t)((const uint16_t*)A.vals)[gi] : (uint32_t)A.vals[gi]);
+      }
+    }
+    for (int e = threadIdx.x; e < TILE_R * meta_bytes_row; e += TPB) {
+      const int r = e / meta_bytes_row, c = e % meta_bytes_row;
+      if (r < rows_here) ((uint8_t*)s_meta)[r * META_ROW_BYTES + c] = A.meta[(i0 + r) * A.mld + mbase + c];
+    }
+  }
+  __syncthreads();
+
+  // ---- per-group work out of LDS ----
+  for (int it = threadIdx.x; it < TILE_R * GPR; it += TPB) {
+    int i, g;
+    if (opT) { i = it % TILE_R; g = it / TILE_R; }
+    else { i = it / GPR; g = it % GPR; }
+    if (i >= rows_here || g >= groups_here) continue;
+    // element (i, g*M + j) of the logical tile lives at this LDS index:
+    auto at = [&](int j) { return opT ? (g * M + j) * TILE_R + i : i * TILE_K + g * M + j; };
+    if (OP == T_DECOMPRESS) {
+      const uint8_t* mrow = (const uint8_t*)s_meta + i * META_ROW_BYTES;
+      for (int s = 0; s < N; s++) {
+        const int t0 = (g * N + s) * b;
+        uint32_t w = (uint32_t)mrow[t0 / 8] | ((uint32_t)mrow[t0 / 8 + 1] << 8);
+        const int j = (int)((w >> (t0 % 8)) & ((1u << b) - 1u));
+        lds_set<ESZ>(s_dense, at(j), lds_elem<ESZ>(s_vals, i * (GPR * N) + g * N + s));
+      }
+      continue;
+    }
+    uint32_t mag[M];
+#pragma unroll
+    for (int j = 0; j < M; j++) mag[j] = magkey<DT>(lds_elem<ESZ>(s_dense, at(j)));
+    const uint32_t keep = select_topn<M>(mag, N);
+    if (OP == T_PRUNE) {
+#pragma unroll
+      for (int j = 0; j < M; j++)
+        if (!((keep >> j) & 1u)) lds_set<ESZ>(s_dense, at(j), 0u);
+      if (A.mask) {
+        if (!opT) {
+          // bits (i, g*M .. g*M+M-1) of the stored tile; M divides 32
+          const int bit = g * M;
+          atomicOr(&s_mask[i * (TILE_K / 32) + bit / 32], keep << (bit % 32));
+        } else {
+#pragma unroll
+          for (int j = 0; j < M; j++)
+            if ((keep >> j) & 1u) atomicOr(&s_mask[(g * M + j) * (TILE_R / 32) + i / 32], 1u << (i % 32));
+        }
+      }
+    } else {  // T_COMPRESS
+      int s = 0;
+      uint8_t* vrow = s_vals + (size_t)(i * (GPR * N)) * ESZ;
+      uint32_t* mrow = s_meta + i * meta_words_row;
+#pragma unroll
+      for (int j = 0; j < M; j++) {
+        if (!((keep >> j) & 1u)) continue;
+        lds_set<ESZ>(vrow, g * N + s, lds_elem<ESZ>(s_dense, at(j)));
+        const int t0 = (g * N + s) * b;
+        atomicOr(&mrow[t0 / 32], (uint32_t)j << (t0 % 32));
+        if ((t0 % 32) + b > 32) atomicOr(&mrow[t0 / 32 + 1], (uint32_t)j >> (32 - t0 % 32));
+        s++;
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- write back ----
+  if (OP == T_PRUNE || OP == T_DECOMPRESS) {
+    if (opT) tile_out<ESZ, TILE_K, TILE_R>(A.out, s_dense, sr0, sc0, srows, scols, A.lda, A.vec_ok);
+    else tile_out<ESZ, TILE_R, TILE_K>(A.out, s_dense, sr0, sc0, srows, scols, A.lda, A.vec_ok);
+  }
+  if (OP == T_PRUNE && A.mask) {
+    constexpr int WPR_N = TILE_K / 32, WPR_T = TILE_R / 32;
+    const int SR = opT ? TILE_K : TILE_R, WPR = opT ? WPR_T : WPR_N;
+    for (int e = threadIdx.x; e < SR * WPR; e += TPB) {
+      const int r = e / WPR, w = e % WPR;
+      const int64_t gr = sr0 + r, gw = sc0 / 32 + w;
+      if (gr < srows && gw < A.mask_ld) A.mask[gr * A.mask_ld + gw] = s_mask[e];
+    }
+  }
+  if (OP == T_COMPRESS) {
+    const int64_t vbase = (k0 / M) * N;
+    const int64_t mbase = (k0 / M) * N * b / 8;
+    // values (plus the zero padding of the row after its last group)
+    const int64_t vend = last_k_tile ? A.vld : vbase + vals_per_row;
+    const int vcount = (int)(vend - vbase);
+    for (int e = threadIdx.x; e < rows_here * vcount; e += TPB) {
+      const int r = e / vcount, c = e % vcount;
+      const uint32_t v = c < vals_per_row ? lds_elem<ESZ>(s_vals, r * (GPR * N) + c) : 0u;
+      const size_t gi = (size_t)((i0 + r) * A.vld + vbase + c);
+      if (ESZ == 2) ((uint16_t*)A.vals)[gi] = (uint16_t)v;
+      else A.vals[gi] = (uint8_t)v;
+    }
+    const int64_t mend = last_k_tile ? A.mld : mbase + meta_bytes_row;
+    const int mcount = (int)(mend - mbase);
+    for (int e = threadIdx.x; e < rows_here * mcount; e += TPB) {
+      const int r = e / mcount, c = e % mcount;
+      const uint8_t v = c < meta_bytes_row ? ((const uint8_t*)s_meta)[r * META_ROW_BYTES + c] : (uint8_t)0;
+      A.meta[(i0 + r) * A.mld + mbase + c] = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ 4x4 tiles
+
+// Pair p keeps columns PA[p] and PB[p] of a tile row.
+__device__ constexpr int PA[6] = {0, 0, 0, 1, 1, 2};
+__device__ constexpr int PB[6] = {1, 2, 3, 2, 3, 3};
+
+// Number of (p0, p1, p2, p3) choices with every column chosen twice; p3 is
+// forced by the first three rows (the two columns still at one).
+constexpr int count_tile_patterns() {
+  constexpr int pa[6] = {0, 0, 0, 1, 1, 2}, pb[6] = {1, 2, 3, 2, 3, 3};
+  int n = 0;
+  for (int p0 = 0; p0 < 6; p0++)
+    for (int p1 = 0; p1 < 6; p1++)
+      for (int p2 = 0; p2 < 6; p2++) {
+        int c[4] = {0, 0, 0, 0};
+        c[pa[p0]]++; c[pb[p0]]++; c[pa[p1]]++; c[pb[p1]]++; c[pa[p2]]++; c[pb[p2]]++;
+        int ones = 0, bad = 0;
+        for (int x = 0; x < 4; x++) { ones += c[x] == 1; bad += (c[x] == 0 || c[x] > 2); }
+        n += (!bad && ones == 2);
+      }
+  return n;
+}
+static_assert(count_tile_patterns() == 90, "4x4 tiles with two per row and column: 90 patterns");
+
+template <int DT, int ESZ>
+__device__ __forceinline__ uint32_t load_raw(const uint8_t* p, int64_t idx) {
+  return ESZ == 2 ? (uint32_t)((const uint16_t*)p)[idx] : (uint32_t)p[idx];
+}
+
+// One thread per 4x4 tile of the stored matrix; lanes run along tile columns so
+// each of the four row loads is contiguous across the wave.
+template <int DT, int ESZ>
+__global__ void __launch_bounds__(TPB) tile4_prune_kernel(const uint8_t* a, uint8_t* out, uint32_t* mask,
+                                                          int64_t rows, int64_t cols, int64_t ld,
+                                                          int64_t mask_ld) {
+  const int64_t tj = (int64_t)blockIdx.x * TPB + threadIdx.x;
+  const int64_t ti = blockIdx.y;
+  const bool active = tj < cols / 4;
+  uint32_t raw[4][4];
+  double w[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; r++)
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      raw[r][c] = active ? load_raw<DT, ESZ>(a, (ti * 4 + r) * ld + tj * 4 + c) : 0u;
+      w[r][c] = absval64<DT>(raw[r][c]);
+    }
+  double s[4][6];
+#pragma unroll
+  for (int r = 0; r < 4; r++)
+#pragma unroll
+    for (int p = 0; p < 6; p++) s[r][p] = w[r][PA[p]] + w[r][PB[p]];
+  // scan candidates in order (p0 outermost); replace only on a strictly larger score
+  double best = -1.0;
+  int bp0 = 0, bp1 = 0, bp2 = 0, bp3 = 0;
+#pragma unroll
+  for (int p0 = 0; p0 < 6; p0++)
+#pragma unroll
+    for (int p1 = 0; p1 < 6; p1++)
+#pragma unroll
+      for (int p2 = 0; p2 < 6; p2++) {
+        int c[4] = {0, 0, 0, 0};
+        c[PA[p0]]++; c[PB[p0]]++; c[PA[p1]]++; c[PB[p1]]++; c[PA[p2]]++; c[PB[p2]]++;
+        int ones = 0, bad = 0, lo = -1, hi = -1;
+#pragma unroll
+        for (int x = 0; x < 4; x++) {
+          ones += c[x] == 1; bad += (c[x] == 0 || c[x] > 2);
+          if (c[x] == 1) { if (lo < 0) lo = x; else hi = x; }
+        }
+        if (bad || ones != 2) continue;
+        int p3 = 0;
+#pragma unroll
+        for (int p = 0; p < 6; p++) if (PA[p] == lo && PB[p] == hi) p3 = p;
+        const double score = ((s[0][p0] + s[1][p1]) + s[2][p2]) + s[3][p3];
+        if (score > best) { best = score; bp0 = p0; bp1 = p1; bp2 = p2; bp3 = p3; }
+      }
+  const int bp[4] = {bp0, bp1, bp2, bp3};
+  uint32_t rowbits[4];
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    rowbits[r] = (1u << PA[bp[r]]) | (1u << PB[bp[r]]);
+    if (active) {
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        const uint32_t v = ((rowbits[r] >> c) & 1u) ? raw[r][c] : 0u;
+        const int64_t idx = (ti * 4 + r) * ld + tj * 4 + c;
+        if (ESZ == 2) ((uint16_t*)out)[idx] = (uint16_t)v;
+        else out[idx] = (uint8_t)v;
+      }
+    }
+  }
+  if (mask) {
+    // 8 consecutive tiles share a 32-bit mask word per row: OR them across lanes.
+    const int sub = (int)(tj % 8);
+#pragma unroll
+    for (int r = 0; r < 4; r++) {
+      uint32_t v = active ? (rowbits[r] << (4 * sub)) : 0u;
+      v |= __shfl_xor(v, 1);
+      v |= __shfl_xor(v, 2);
+      v |= __shfl_xor(v, 4);
+      if (active && sub == 0) mask[(ti * 4 + r) * mask_ld + tj / 8] = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ checks
+
+__device__ __forceinline__ void add_count(int32_t* count, int v) {
+  // wave reduction, then one atomic per wave
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  if ((threadIdx.x & 63) == 0 && v) atomicAdd(count, v);
+}
+
+template <int DT, int ESZ>
+__global__ void __launch_bounds__(TPB) check1d_kernel(const uint8_t* a, int64_t m, int64_t k, int64_t lda,
+                                                      int N, int M, int op_t, int32_t* count) {
+  const int64_t groups = k / M;
+  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x;
+  int bad = 0;
+  if (t < m * groups) {
+    int64_t i, g;
+    if (op_t) { i = t % m; g = t / m; }        // lanes along stored columns
+    else { i = t / groups; g = t % groups; }   // lanes along a stored row
+    int nz = 0;
+    for (int j = 0; j < M; j++) {
+      const int64_t idx = op_t ? (g * M + j) * lda + i : i * lda + g * M + j;
+      nz += magkey<DT>(load_raw<DT, ESZ>(a, idx)) != 0u;
+    }
+    bad = nz > N;
+  }
+  add_count(count, bad);
+}
+
+template <int DT, int ESZ>
+__global__ void __launch_bounds__(TPB) check_tile_kernel(const uint8_t* a, int64_t rows, int64_t cols, int64_t ld,
+                                                         int32_t* count) {
+  const int64_t tj = (int64_t)blockIdx.x * TPB + threadIdx.x;
+  const int64_t ti = blockIdx.y;
+  int bad = 0;
+  if (tj < cols / 4) {
+    uint32_t nzm = 0;   // bit r*4+c set when element (r, c) is non-zero
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+#pragma unroll
+      for (int c = 0; c < 4; c++)
+        nzm |= (magkey<DT>(load_raw<DT, ESZ>(a, (ti * 4 + r) * ld + tj * 4 + c)) != 0u ? 1u : 0u) << (r * 4 + c);
+#pragma unroll
+    for (int x = 0; x < 4; x++) {
+      bad += __builtin_popcount((nzm >> (4 * x)) & 0xFu) > 2;
+      bad += __builtin_popcount(nzm & (0x1111u << x)) > 2;
+    }
+  }
+  add_count(count, bad);
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int32_t v) { *p = v; }
+
+// ------------------------------------------------------------------ launchers
+
+static TileArgs make_args(const nm_plan& pl) {
+  TileArgs A{};
+  A.m = pl.p.m; A.k = pl.p.k; A.lda = pl.p.lda;
+  A.N = pl.p.nm_n; A.op_t = pl.p.op_a == NM_OP_T; A.bits = pl.bits;
+  A.vld = pl.vld; A.mld = pl.mld;
+  A.mask_ld = (pl.a_cols + 31) / 32;
+  A.vec_ok = (pl.p.lda * pl.esz_ab) % 16 == 0;
+  return A;
+}
+
+template <int OP, int DT, int ESZ>
+static hipError_t dispatch_tile_m(const nm_plan& pl, const TileArgs& A, hipStream_t s) {
+  const dim3 grid((unsigned)((pl.p.k + TILE_K - 1) / TILE_K), (unsigned)((pl.p.m + TILE_R - 1) / TILE_R));
+  switch (pl.p.nm_m) {
+    case 4: hipLaunchKernelGGL((tile_kernel<DT, ESZ, 4, OP>), grid, dim3(TPB), 0, s, A); break;
+    case 8: hipLaunchKernelGGL((tile_kernel<DT, ESZ, 8, OP>), grid, dim3(TPB), 0, s, A); break;
+    case 16: hipLaunchKernelGGL((tile_kernel<DT, ESZ, 16, OP>), grid, dim3(TPB), 0, s, A); break;
+    case 32: hipLaunchKernelGGL((tile_kernel<DT, ESZ, 32, OP>), grid, dim3(TPB), 0, s, A); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <int OP>
+static hipError_t dispatch_tile(const nm_plan& pl, const TileArgs& A, hipStream_t s) {
+  if (pl.p.m == 0 || pl.p.k == 0) return hipSuccess;
+  switch (pl.p.type_ab) {
+    case NM_F16: return dispatch_tile_m<OP, DT_F16, 2>(pl, A, s);
+    case NM_BF16: return dispatch_tile_m<OP, DT_BF16, 2>(pl, A, s);
+    default: return dispatch_tile_m<OP, DT_I8, 1>(pl, A, s);
+  }
+}
+
+hipError_t launch_prune_1d(const nm_plan& pl, const void* a, void* out, uint32_t* mask, hipStream_t s) {
+  TileArgs A = make_args(pl);
+  A.a = (const uint8_t*)a; A.out = (uint8_t*)out; A.mask = mask;
+  return dispatch_tile<T_PRUNE>(pl, A, s);
+}
+
+hipError_t launch_compress(const nm_plan& pl, const void* a, void* vals, void* meta, hipStream_t s) {
+  TileArgs A = make_args(pl);
+  A.a = (const uint8_t*)a; A.vals = (uint8_t*)vals; A.meta = (uint8_t*)meta;
+  // k == 0 gives zero-length compressed rows: nothing to write.
+  return dispatch_tile<T_COMPRESS>(pl, A, s);
+}
+
+hipError_t launch_decompress(const nm_plan& pl, const void* vals, const void* meta, void* out, hipStream_t s) {
+  TileArgs A = make_args(pl);
+  A.vals = (uint8_t*)vals; A.meta = (uint8_t*)meta; A.out = (uint8_t*)out;
+  return dispatch_tile<T_DECOMPRESS>(pl, A, s);
+}
+
+hipError_t launch_prune_tile(const nm_plan& pl, const void* a, void* out, uint32_t* mask, hipStream_t s) {
+  const int64_t rows = pl.a_rows, cols = pl.a_cols;
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const dim3 grid((unsigned)((cols / 4 + TPB - 1) / TPB), (unsigned)(rows / 4));
+  const int64_t mld = (cols + 31) / 32;
+  const uint8_t* ap = (const uint8_t*)a;
+  uint8_t* op = (uint8_t*)out;
+  switch (pl.p.type_ab) {
+    case NM_F16: hipLaunchKernelGGL((tile4_prune_kernel<DT_F16, 2>), grid, dim3(TPB), 0, s, ap, op, mask, rows, cols, pl.p.lda, mld); break;
+    case NM_BF16: hipLaunchKernelGGL((tile4_prune_kernel<DT_BF16, 2>), grid, dim3(TPB), 0, s, ap, op, mask, rows, cols, pl.p.lda, mld); break;
+    default: hipLaunchKernelGGL((tile4_prune_kernel<DT_I8, 1>), grid, dim3(TPB), 0, s, ap, op, mask, rows, cols, pl.p.lda, mld); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_check(const nm_plan& pl, const void* a, int mode, int32_t* count, hipStream_t s) {
+  hipLaunchKernelGGL(fill_i32_kernel, dim3(1), dim3(1), 0, s, count, 0);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const uint8_t* ap = (const uint8_t*)a;
+  if (mode == NM_PRUNE_TILE4X4) {
+    const int64_t rows = pl.a_rows, cols = pl.a_cols;
+    if (rows == 0 || cols == 0) return hipSuccess;
+    const dim3 grid((unsigned)((cols / 4 + TPB - 1) / TPB), (unsigned)(rows / 4));
+    switch (pl.p.type_ab) {
+      case NM_F16: hipLaunchKernelGGL((check_tile_kernel<DT_F16, 2>), grid, dim3(TPB), 0, s, ap, rows, cols, pl.p.lda, count); break;
+      case NM_BF16: hipLaunchKernelGGL((check_tile_kernel<DT_BF16, 2>), grid, dim3(TPB), 0, s, ap, rows, cols, pl.p.lda, count); break;
+      default: hipLaunchKernelGGL((check_tile_kernel<DT_I8, 1>), grid, dim3(TPB), 0, s, ap, rows, cols, pl.p.lda, count); break;
+    }
+    return hipGetLastError();
+  }
+  const int64_t total = pl.p.m * (pl.p.k / pl.p.nm_m);
+  if (total == 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + TPB - 1) / TPB));
+  const int opt = pl.p.op_a == NM_OP_T;
+  switch (pl.p.type_ab) {
+    case NM_F16: hipLaunchKernelGGL((check1d_kernel<DT_F16, 2>), grid, dim3(TPB), 0, s, ap, pl.p.m, pl.p.k, pl.p.lda, pl.p.nm_n, pl.p.nm_m, opt, count); break;
+    case NM_BF16: hipLaunchKernelGGL((check1d_kernel<DT_BF16, 2>), grid, dim3(TPB), 0, s, ap, pl.p.m, pl.p.k, pl.p.lda, pl.p.nm_n, pl.p.nm_m, opt, count); break;
+    default: hipLaunchKernelGGL((check1d_kernel<DT_I8, 1>), grid, dim3(TPB), 0, s, ap, pl.p.m, pl.p.k, pl.p.lda, pl.p.nm_n, pl.p.nm_m, opt, count); break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace nm

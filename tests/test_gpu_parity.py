@@ -1,0 +1,272 @@
+"""GPU parity: every kernel behind the C ABI against the CPU oracle on seeded
+inputs at sizes the oracle finishes in seconds, spanning several tiles and a
+ragged tail. Masks, pruned matrices, values, metadata (padding included) and
+int32 outputs must be bit-exact; fp16/bf16 outputs must satisfy
+|D - D_ref| <= 1e-2 * (|alpha| (|A| |B|)_ij + |beta| |C_ij|) + 1e-3."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import structured_sparse_gemm_nm_amd as nm
+from structured_sparse_gemm_nm_amd import inputs
+from tests.gpu_helpers import Guarded, dev, host, sync
+
+pytestmark = pytest.mark.gpu
+
+RAW = {"f16": np.uint16, "bf16": np.uint16, "i8": np.int8}
+TRAW = {"f16": torch.int16, "bf16": torch.int16, "i8": torch.int8}
+NM_CASES = [(2, 4), (1, 4), (3, 4), (2, 8), (5, 16), (4, 32), (8, 32)]
+
+
+def rand(dtype, shape, seed, sigma=1.0):
+    if dtype == "i8":
+        return inputs.uniform_int(shape, seed, -127, 127)
+    return inputs.normal(shape, seed, sigma, dtype)
+
+
+def stored(op, rows, cols):
+    return (rows, cols) if op == "N" else (cols, rows)
+
+
+def plan_for(dtype, m, n, k, N, M, op_a="N", op_b="N", **kw):
+    return nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=op_b, dtype=dtype, **kw)
+
+
+# ------------------------------------------------------------------ prune / check / compress
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("N,M", NM_CASES)
+@pytest.mark.parametrize("op", ["N", "T"])
+def test_prune_1d(dtype, N, M, op):
+    m, k = 208, 544
+    a = rand(dtype, stored(op, m, k), 10 + N * M)
+    ref, keep = oracle.prune_1d(a, dtype, N, M, op)
+    plan = plan_for(dtype, m, 8, k, N, M, op_a=op)
+    da = dev(a)
+    out = Guarded(a.shape, TRAW[dtype])
+    mask = Guarded((plan.mask_bytes // 4,), torch.int32)
+    nm.nm_prune(plan, da, out.t, "1d", mask.t)
+    sync()
+    out.check(); mask.check()
+    assert np.array_equal(host(out.t, RAW[dtype]), ref)
+    assert np.array_equal(host(mask.t, np.uint32).reshape(ref.shape[0], -1), oracle.mask_bits(keep))
+    # in place
+    nm.nm_prune(plan, da, da, "1d")
+    sync()
+    assert np.array_equal(host(da, RAW[dtype]), ref)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("shape", [(132, 272), (4, 4), (8, 1040)])
+def test_prune_tile(dtype, shape):
+    a = rand(dtype, shape, 77, 0.02)
+    ref, keep = oracle.prune_tile(a, dtype)
+    plan = plan_for(dtype, shape[0], 16, shape[1], 2, 4)
+    out = Guarded(shape, TRAW[dtype])
+    mask = Guarded((plan.mask_bytes // 4,), torch.int32)
+    nm.nm_prune(plan, dev(a), out.t, "tile", mask.t)
+    sync()
+    out.check(); mask.check()
+    assert np.array_equal(host(out.t, RAW[dtype]), ref)
+    assert np.array_equal(host(mask.t, np.uint32).reshape(shape[0], -1), oracle.mask_bits(keep))
+    # the tile result conforms in both directions; the original does not
+    cnt = torch.zeros(1, dtype=torch.int32, device="cuda")
+    nm.nm_prune_check(plan, out.t, "tile", cnt)
+    sync()
+    assert int(cnt.item()) == 0
+    nm.nm_prune_check(plan, dev(a), "tile", cnt)
+    sync()
+    assert int(cnt.item()) == oracle.check_tile(a, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "i8"])
+@pytest.mark.parametrize("N,M", NM_CASES)
+@pytest.mark.parametrize("op", ["N", "T"])
+def test_check_1d(dtype, N, M, op):
+    m, k = 144, 352
+    a = rand(dtype, stored(op, m, k), 5)
+    a[:: 7] = 0                                           # some rows with no non-zeros at all
+    plan = plan_for(dtype, m, 8, k, N, M, op_a=op)
+    cnt = torch.full((1,), 12345, dtype=torch.int32, device="cuda")
+    nm.nm_prune_check(plan, dev(a), "1d", cnt)
+    sync()
+    assert int(cnt.item()) == oracle.check_1d(a, dtype, N, M, op)
+    p, _ = oracle.prune_1d(a, dtype, N, M, op)
+    nm.nm_prune_check(plan, dev(p), "1d", cnt)
+    sync()
+    assert int(cnt.item()) == 0
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("N,M", NM_CASES + [(31, 32), (7, 8), (15, 16)])
+@pytest.mark.parametrize("op", ["N", "T"])
+def test_compress_decompress(dtype, N, M, op):
+    m, k = 208, 544
+    a = rand(dtype, stored(op, m, k), 20 + N + M)
+    vref, mref = oracle.compress(a, dtype, N, M, op)
+    plan = plan_for(dtype, m, 8, k, N, M, op_a=op)
+    vals = Guarded((m, plan.values_ld), TRAW[dtype])
+    meta = Guarded((m, plan.meta_ld), torch.uint8)
+    nm.nm_compress(plan, dev(a), vals.t, meta.t)
+    sync()
+    vals.check(); meta.check()
+    assert np.array_equal(host(vals.t, RAW[dtype]), vref)
+    assert np.array_equal(host(meta.t, np.uint8), mref)
+    # decompress the oracle's compressed form back to the stored layout
+    dref = oracle.decompress(vref, mref, dtype, m, k, N, M, op)
+    out = Guarded(a.shape, TRAW[dtype])
+    nm.nm_decompress(plan, dev(vref), dev(mref), out.t)
+    sync()
+    out.check()
+    assert np.array_equal(host(out.t, RAW[dtype]), dref)
+
+
+# ------------------------------------------------------------------ products
+
+def ref_product(dtype, ahat_logical, b_logical, alpha, beta, c):
+    if dtype == "i8":
+        return oracle.gemm_i64(ahat_logical, b_logical, int(alpha), int(beta), c), None
+    A = oracle.decode(ahat_logical, dtype)
+    B = oracle.decode(b_logical, dtype)
+    C = oracle.decode(c, dtype) if c is not None else None
+    D = oracle.gemm_f64(A, B, alpha, beta, C)
+    tol = oracle.tolerance(np.abs(A), np.abs(B), alpha, beta, C)
+    return D, tol
+
+
+def assert_close(dtype, got_raw, ref, tol):
+    if dtype == "i8":
+        assert np.array_equal(got_raw.astype(np.int64), ref), np.argwhere(got_raw.astype(np.int64) != ref)[:5]
+        return
+    got = oracle.decode(got_raw, dtype)
+    assert np.isfinite(got).all()
+    err = np.abs(got - ref)
+    bad = err > tol
+    assert not bad.any(), (np.argwhere(bad)[:5], err[bad][:5], tol[bad][:5])
+
+
+def run_spmm(dtype, N, M, m, n, k, op_b, alpha, beta, seed, op_a="N"):
+    a = rand(dtype, stored(op_a, m, k), seed)
+    ahat_stored, _ = oracle.prune_1d(a, dtype, N, M, op_a)
+    ahat = ahat_stored if op_a == "N" else np.ascontiguousarray(ahat_stored.T)
+    vref, mref = oracle.compress(a, dtype, N, M, op_a)
+    b_log = rand(dtype, (k, n), seed + 1)
+    b_st = b_log if op_b == "N" else np.ascontiguousarray(b_log.T)
+    c = None
+    if beta != 0:
+        c = (inputs.uniform_int((m, n), seed + 2, -2**20, 2**20, np.int32) if dtype == "i8"
+             else rand(dtype, (m, n), seed + 2))
+    plan = plan_for(dtype, m, n, k, N, M, op_a=op_a, op_b=op_b)
+    odt = torch.int32 if dtype == "i8" else torch.int16
+    d = Guarded((m, n), odt)
+    nm.nm_spmm(plan, alpha, dev(vref), dev(mref), dev(b_st), beta, dev(c) if c is not None else None, d.t)
+    sync()
+    d.check()
+    ref, tol = ref_product(dtype, ahat, b_log, alpha, beta, c)
+    assert_close(dtype, host(d.t, np.int32 if dtype == "i8" else np.uint16), ref, tol)
+    return plan
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("op_b", ["N", "T"])
+@pytest.mark.parametrize("m,n,k", [(200, 144, 336), (128, 128, 64), (64, 272, 1040), (17, 48, 4)])
+@pytest.mark.parametrize("ab", [(1.0, 0.0), (2.0, -3.0)])
+def test_spmm_2of4(dtype, op_b, m, n, k, ab):
+    alpha, beta = ab
+    if dtype != "i8":
+        alpha, beta = (0.75, -1.25) if beta != 0 else (1.0, 0.0)
+    plan = run_spmm(dtype, 2, 4, m, n, k, op_b, alpha, beta, 1000 + m + n + k)
+    assert plan.kernel_name == "spmm_smfmac_2of4"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_spmm_identity_is_bit_exact(dtype):
+    """B = I: each output is one exact product, so D equals the pruned A bit for bit;
+    with one-hot rows this also pins the instruction's lane and offset mapping."""
+    m, k = 96, 192
+    a = rand(dtype, (m, k), 3)
+    ahat, _ = oracle.prune_1d(a, dtype, 2, 4)
+    v, meta = oracle.compress(a, dtype, 2, 4)
+    one = np.float16(1).view(np.uint16) if dtype == "f16" else np.uint16(0x3F80)
+    eye = np.zeros((k, k), np.uint16)
+    np.fill_diagonal(eye, one)
+    for op_b in ("N", "T"):
+        plan = plan_for(dtype, m, k, k, 2, 4, op_b=op_b)
+        d = torch.empty((m, k), dtype=torch.int16, device="cuda")
+        nm.nm_spmm(plan, 1.0, dev(v), dev(meta), dev(eye), 0.0, None, d)
+        sync()
+        got = host(d, np.uint16).copy()
+        got[(got & 0x7FFF) == 0] = 0                  # -0 and +0 both mean zero here
+        assert np.array_equal(got, ahat)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("N,M", [(1, 4), (3, 4), (2, 8), (5, 16), (4, 32), (8, 32)])
+@pytest.mark.parametrize("op_b", ["N", "T"])
+def test_spmm_gather(dtype, N, M, op_b):
+    alpha, beta = (1.0, 1.0) if dtype == "i8" else (0.5, 0.25)
+    plan = run_spmm(dtype, N, M, 150, 80, 544, op_b, alpha, beta, 2000 + N * M)
+    assert plan.kernel_name == "spmm_gather_mfma"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("N,M", [(2, 4), (4, 32), (8, 32), (3, 8)])
+@pytest.mark.parametrize("n", [1, 3, 8, 16])
+@pytest.mark.parametrize("op_b", ["N", "T"])
+def test_spmm_skinny(dtype, N, M, n, op_b):
+    alpha, beta = (1.0, 0.0) if n != 3 else ((1.0, -2.0) if dtype == "i8" else (1.5, 0.5))
+    plan = run_spmm(dtype, N, M, 100, n, 1088, op_b, alpha, beta, 3000 + n)
+    assert plan.kernel_name == "spmm_skinny"
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("op_a", ["N", "T"])
+@pytest.mark.parametrize("op_b", ["N", "T"])
+@pytest.mark.parametrize("n", [8, 144])
+def test_dense_gemm(dtype, op_a, op_b, n):
+    m, k = 144, 208
+    a_log = rand(dtype, (m, k), 41)
+    a_st = a_log if op_a == "N" else np.ascontiguousarray(a_log.T)
+    b_log = rand(dtype, (k, n), 42)
+    b_st = b_log if op_b == "N" else np.ascontiguousarray(b_log.T)
+    plan = plan_for(dtype, m, n, k, 2, 4, op_a=op_a, op_b=op_b)
+    odt = torch.int32 if dtype == "i8" else torch.int16
+    d = Guarded((m, n), odt)
+    nm.nm_dense_gemm(plan, 1.0, dev(a_st), dev(b_st), 0.0, None, d.t)
+    sync()
+    d.check()
+    ref, tol = ref_product(dtype, a_log, b_log, 1.0, 0.0, None)
+    assert_close(dtype, host(d.t, np.int32 if dtype == "i8" else np.uint16), ref, tol)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "i8"])
+@pytest.mark.parametrize("n", [4, 48])
+def test_k_zero_gives_beta_c(dtype, n):
+    m = 24
+    c = inputs.uniform_int((m, n), 1, -100, 100, np.int32) if dtype == "i8" else rand(dtype, (m, n), 1)
+    plan = plan_for(dtype, m, n, 0, 2, 4)
+    odt = torch.int32 if dtype == "i8" else torch.int16
+    d = torch.empty((m, n), dtype=odt, device="cuda")
+    nm.nm_spmm(plan, 1.0, None, None, None, 2.0 if dtype == "i8" else 0.5, dev(c), d)
+    sync()
+    got = host(d, np.int32 if dtype == "i8" else np.uint16)
+    if dtype == "i8":
+        assert np.array_equal(got, 2 * c)
+    else:
+        assert np.array_equal(oracle.decode(got, dtype), 0.5 * oracle.decode(c, dtype))
+
+
+def test_c_may_alias_d():
+    m, n, k = 64, 64, 128
+    a = rand("f16", (m, k), 8)
+    v, meta = oracle.compress(a, "f16", 2, 4)
+    ahat, _ = oracle.prune_1d(a, "f16", 2, 4)
+    b = rand("f16", (k, n), 9)
+    c = rand("f16", (m, n), 10)
+    plan = plan_for("f16", m, n, k, 2, 4)
+    dc = dev(c)
+    nm.nm_spmm(plan, 1.0, dev(v), dev(meta), dev(b), 1.0, dc, dc)
+    sync()
+    ref, tol = ref_product("f16", ahat, b, 1.0, 1.0, c)
+    assert_close("f16", host(dc, np.uint16), ref, tol)

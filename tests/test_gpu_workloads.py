@@ -1,0 +1,108 @@
+"""Full-size parity on the benchmark's workloads, through the same C-ABI calls
+and launch configuration the benchmark times. Pruned matrices, values and
+metadata are compared bit-exactly in full; the product is compared on sampled
+outputs that the oracle computes one by one (all outputs for the small case)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import structured_sparse_gemm_nm_amd as nm
+from structured_sparse_gemm_nm_amd import inputs
+from tests.gpu_helpers import dev, host, sync
+
+pytestmark = pytest.mark.gpu
+
+RAW = {"f16": np.uint16, "bf16": np.uint16, "i8": np.int8}
+TRAW = {"f16": torch.int16, "bf16": torch.int16, "i8": torch.int8}
+
+
+def sample_points(m, n, count, seed):
+    rng = np.random.default_rng(seed)
+    pi = rng.integers(0, m, count)
+    pj = rng.integers(0, n, count)
+    edge_i = np.array([0, 0, m - 1, m - 1, m // 2])
+    edge_j = np.array([0, n - 1, 0, n - 1, n // 2])
+    return np.concatenate([pi, edge_i]), np.concatenate([pj, edge_j])
+
+
+def check_points(w, ahat_log, b_st, op_b, c, got, pi, pj):
+    dtype = w["dtype"]
+    ui, inv_i = np.unique(pi, return_inverse=True)
+    uj, inv_j = np.unique(pj, return_inverse=True)
+    rows = ahat_log[ui]
+    cols = b_st[uj] if op_b == "T" else np.ascontiguousarray(b_st[:, uj].T)   # (len(uj), k)
+    if dtype == "i8":
+        prod = rows.astype(np.int64) @ cols.astype(np.int64).T                   # exact
+        ref = int(w["alpha"]) * prod[inv_i, inv_j] + (int(w["beta"]) * c[pi, pj].astype(np.int64) if c is not None else 0)
+        assert np.array_equal(got[pi, pj].astype(np.int64), ref)
+        return
+    A = oracle.decode(rows, dtype)
+    B = oracle.decode(cols, dtype)
+    ridx = np.arange(len(ui))[inv_i]
+    cidx = np.arange(len(uj))[inv_j]
+    D = oracle.gemm_f64_points(A, B, ridx, cidx, w["alpha"], 0.0)
+    T = oracle.gemm_f64_points(np.abs(A), np.abs(B), ridx, cidx, abs(w["alpha"]), 0.0)
+    tol = 1e-2 * T + 1e-3
+    g = oracle.decode(got[pi, pj], dtype)
+    err = np.abs(g - D)
+    assert np.isfinite(g).all()
+    assert (err <= tol).all(), (err.max(), np.argmax(err - tol))
+
+
+CASES = [("c1_fp16_256", "N"), ("c2_fc1", "T"), ("c2_fc1", "N"), ("c2_fc2", "T"), ("c2_fc2", "N"),
+         ("c2_proj", "T"), ("c2_proj", "N"), ("c3_fwd", "T"), ("c3_bwd", "T"), ("c4_int8", "N"),
+         ("c4_int8", "T"), ("c5_4of32_n1", "N"), ("c5_4of32_n8", "N"), ("c5_4of32_n4096", "N"),
+         ("c5_8of32_n1", "N"), ("c5_8of32_n8", "N"), ("c5_8of32_n4096", "N")]
+
+
+@pytest.mark.parametrize("name,op_b", CASES, ids=["%s-%s" % c for c in CASES])
+def test_workload(name, op_b):
+    w = inputs.WORKLOADS[name]
+    dtype, N, M, m, n, k = w["dtype"], w["N"], w["M"], w["m"], w["n"], w["k"]
+    op_a = w.get("op_a", "N")
+    print("workload", name, "op_b", op_b, flush=True)
+    a, b, c = inputs.workload_inputs(name, op_b)
+    plan = nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=op_b, dtype=dtype)
+    mode = "tile" if w.get("tile") else "1d"
+    # prune on the GPU, bit-exact against the oracle
+    if mode == "tile":
+        ref_p, _ = oracle.prune_tile(a, dtype)
+    else:
+        ref_p, _ = oracle.prune_1d(a, dtype, N, M, op_a)
+    da = dev(a)
+    dp = torch.empty_like(da)
+    nm.nm_prune(plan, da, dp, mode)
+    cnt = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    nm.nm_prune_check(plan, dp, mode, cnt)
+    sync()
+    assert np.array_equal(host(dp, RAW[dtype]), ref_p)
+    assert int(cnt.item()) == 0
+    # compress the pruned matrix
+    vref, mref = oracle.compress(ref_p, dtype, N, M, op_a)
+    vals, meta = plan.empty_values(), plan.empty_meta()
+    vals = vals.view(TRAW[dtype]) if dtype != "i8" else vals
+    nm.nm_compress(plan, dp, vals, meta)
+    sync()
+    assert np.array_equal(host(vals, RAW[dtype]), vref)
+    assert np.array_equal(host(meta, np.uint8), mref)
+    # decompress back
+    back = torch.empty_like(dp)
+    nm.nm_decompress(plan, vals, meta, back)
+    sync()
+    assert np.array_equal(host(back, RAW[dtype]), ref_p)
+    del back, da
+    # the product
+    db = dev(b)
+    dc = dev(c) if c is not None else None
+    odt = torch.int32 if dtype == "i8" else torch.int16
+    d = torch.empty((m, n), dtype=odt, device="cuda")
+    nm.nm_spmm(plan, w["alpha"], vals, meta, db, w["beta"], dc, d)
+    sync()
+    got = host(d, np.int32 if dtype == "i8" else np.uint16)
+    ahat_log = ref_p if op_a == "N" else np.ascontiguousarray(ref_p.T)
+    if m * n * k <= 256 * 256 * 256:
+        pi, pj = np.divmod(np.arange(m * n), n)
+    else:
+        pi, pj = sample_points(m, n, 3000, 7)
+    check_points(w, ahat_log, b, op_b, c, got, pi, pj)
