@@ -1,0 +1,306 @@
+"""Benchmark: N:M structured-sparse GEMM hot path on one MI355X.
+
+A step is one pass of the whole hot path over the BERT-Large GEMM shapes of
+the cuSPARSELt blog's Table 1 (FC1 4096x1024, FC2 1024x4096, PROJ 1024x1024
+weights; 4096 tokens = batch 32 x seq 128): for each weight, 2:4 prune,
+conformance check, compress, the SpMM against the activations in both
+layouts (NT: tokens x features as stored; NN: its transpose), and decompress.
+Weights are re-sparsified every step, as in runtime-sparsified training where
+the weights change between steps (the blog: compress again when A changes).
+
+value  = dense-equivalent TFLOP/s of the step's SpMMs (2*m*n*k each) over the
+         whole step time (prune/check/compress/decompress included).
+Also reported: the SpMM kernels alone, the same-shape dense MFMA GEMM written
+in this library, the speed-up, the roofline of the dominant kernel (measured
+with HIP events on the launch stream over the timed region), and the CPU
+oracle timed on one step of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+PEAK_TFLOPS = {"f16": 2516.6, "bf16": 2516.6, "i8": 5033.0}   # dense matrix peaks (TFLOP/s, TOP/s)
+
+# workload name -> list of (label, inputs.WORKLOADS key) GEMMs making one step
+WORKLOAD_SETS = {
+    "bert": [("fc1", "c2_fc1"), ("fc2", "c2_fc2"), ("proj", "c2_proj")],
+    "c1": [("c1", "c1_fp16_256")],
+    "c3": [("fwd", "c3_fwd"), ("bwd", "c3_bwd")],
+    "c4": [("int8", "c4_int8")],
+    "c5_4of32": [("n1", "c5_4of32_n1"), ("n8", "c5_4of32_n8"), ("n4096", "c5_4of32_n4096")],
+    "c5_8of32": [("n1", "c5_8of32_n1"), ("n8", "c5_8of32_n8"), ("n4096", "c5_8of32_n4096")],
+}
+WORKLOAD_DESC = {
+    "bert": "BERT-Large GEMMs (FC1 4096x1024, FC2 1024x4096, PROJ 1024x1024 weights, 4096 tokens), fp16 2:4, NT+NN",
+    "c1": "fp16 2:4, A 256x256, B 256x64, NN",
+    "c3": "bf16 transposable 2:4 training pair, W 11008x4096, X 8192x4096, dY 8192x11008, NT",
+    "c4": "int8 2:4, 4096^3, int32 C/D, beta=1, NN+NT",
+    "c5_4of32": "fp16 4:32, A 4096x4096, B 4096 x {1, 8, 4096}, NN",
+    "c5_8of32": "fp16 8:32, A 4096x4096, B 4096 x {1, 8, 4096}, NN",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="bert", choices=sorted(WORKLOAD_SETS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this library's hot path is single-GPU "
+              "(sharding is described in DESIGN.md, not implemented); got --gpus %d" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import structured_sparse_gemm_nm_amd as nm
+    from structured_sparse_gemm_nm_amd import inputs
+
+    torch.cuda.set_device(0)
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+
+    def to_dev(a):
+        a = np.ascontiguousarray(a)
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(a).to(dev)
+
+    # ---------------------------------------------------------------- set-up (not timed)
+    gemms = []
+    for label, wname in WORKLOAD_SETS[args.workload]:
+        w = inputs.WORKLOADS[wname]
+        dtype, N, M, m, n, k = w["dtype"], w["N"], w["M"], w["m"], w["n"], w["k"]
+        op_a = w.get("op_a", "N")
+        layouts = ["T", "N"] if args.workload in ("bert", "c4") else [w.get("op_b", "N")]
+        a, b_first, c = inputs.workload_inputs(wname, layouts[0])
+        bs = {layouts[0]: b_first}
+        for ob in layouts[1:]:
+            bs[ob] = inputs.workload_inputs(wname, ob)[1]
+        mode = "tile" if w.get("tile") else "1d"
+        g = dict(label=label, name=wname, w=w, dtype=dtype, m=m, n=n, k=k, N=N, M=M, mode=mode, op_a=op_a)
+        g["plan"] = nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=layouts[0], dtype=dtype)
+        g["plans"] = {ob: nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=ob, dtype=dtype) for ob in layouts}
+        g["A"] = to_dev(a)
+        g["Ap"] = torch.empty_like(g["A"])
+        g["Ad"] = torch.empty_like(g["A"])
+        g["vals"] = g["plan"].empty_values()
+        g["meta"] = g["plan"].empty_meta()
+        g["cnt"] = torch.zeros(1, dtype=torch.int32, device=dev)
+        g["B"] = {ob: to_dev(bs[ob]) for ob in layouts}
+        g["C"] = to_dev(c) if c is not None else None
+        odt = torch.int32 if dtype == "i8" else torch.float16 if dtype == "f16" else torch.bfloat16
+        g["D"] = {ob: torch.empty((m, n), dtype=odt, device=dev) for ob in layouts}
+        g["layouts"] = layouts
+        g["host"] = dict(a=a, b=bs, c=c)
+        gemms.append(g)
+
+    # events per SpMM launch (measured on the stream the kernels run on)
+    def step(ev=None):
+        for g in gemms:
+            nm.nm_prune(g["plan"], g["A"], g["Ap"], g["mode"])
+            nm.nm_prune_check(g["plan"], g["Ap"], g["mode"], g["cnt"])
+            nm.nm_compress(g["plan"], g["Ap"], g["vals"], g["meta"])
+            for ob in g["layouts"]:
+                if ev is not None:
+                    e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
+                nm.nm_spmm(g["plans"][ob], g["w"]["alpha"], g["vals"], g["meta"], g["B"][ob], g["w"]["beta"],
+                           g["C"], g["D"][ob])
+                if ev is not None:
+                    e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
+                    ev.append((g, ob, e0, e1))
+            nm.nm_decompress(g["plan"], g["vals"], g["meta"], g["Ad"])
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    viol = [int(g["cnt"].item()) for g in gemms]
+    assert all(v == 0 for v in viol), "prune check failed: %s" % viol
+
+    events = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(events)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    def flops_dense_eq(g):
+        return 2.0 * g["m"] * g["n"] * g["k"]
+
+    step_flops = sum(flops_dense_eq(g) * len(g["layouts"]) for g in gemms)
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    # per-launch SpMM durations
+    per = {}
+    for g, ob, e0, e1 in events:
+        key = (g["label"], ob)
+        per.setdefault(key, []).append(e0.elapsed_time(e1))
+    spmm_ms = {k: float(np.mean(v)) for k, v in per.items()}
+    spmm_total_ms = sum(spmm_ms[(g["label"], ob)] for g in gemms for ob in g["layouts"])
+    spmm_only_tflops = step_flops / (spmm_total_ms * 1e-3) / 1e12
+
+    # dominant kernel: the SpMM kernel instantiation (kernel name + layout) with the most time
+    kern = {}
+    for g in gemms:
+        for ob in g["layouts"]:
+            kk = (g["plans"][ob].kernel_name, ob)
+            d = kern.setdefault(kk, dict(ms=0.0, flops=0.0, bytes=0.0, launches=0, dtype=g["dtype"]))
+            d["ms"] += spmm_ms[(g["label"], ob)]
+            d["launches"] += 1
+            keep = g["N"] / g["M"]
+            d["flops"] += 2.0 * g["m"] * g["n"] * g["k"] * keep            # multiply-adds actually required
+            d["bytes"] += spmm_bytes(g)
+    dom_key = max(kern, key=lambda kk: kern[kk]["ms"])
+    dom = kern[dom_key]
+    avg_ms = dom["ms"] / dom["launches"]
+    avg_flops = dom["flops"] / dom["launches"]
+    avg_bytes = dom["bytes"] / dom["launches"]
+    ai = avg_flops / avg_bytes
+    peak_f = PEAK_TFLOPS[dom["dtype"]]
+    ridge = peak_f * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if ai >= ridge:
+        achieved = avg_flops / (avg_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_f, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak_f, 4), "traffic": None}
+    else:
+        achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    roofline["kernel"] = "%s (op_b=%s)" % dom_key
+    roofline["launch_ms"] = round(avg_ms, 5)
+
+    # dense comparator, same shapes, same layouts
+    dense = {}
+    if not args.no_dense:
+        for g in gemms:
+            for ob in g["layouts"]:
+                pl = g["plans"][ob]
+                f = lambda: nm.nm_dense_gemm(pl, g["w"]["alpha"], g["Ap"], g["B"][ob], g["w"]["beta"], g["C"], g["D"][ob])
+                for _ in range(max(2, args.warmup)):
+                    f()
+                e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)
+                reps = max(5, args.steps)
+                e0.record(stream)
+                for _ in range(reps):
+                    f()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                dense[(g["label"], ob)] = e0.elapsed_time(e1) / reps
+    per_gemm = []
+    for g in gemms:
+        for ob in g["layouts"]:
+            key = (g["label"], ob)
+            t_s = spmm_ms[key]
+            row = {"gemm": g["label"], "layout": "N" + ob, "m": g["m"], "n": g["n"], "k": g["k"],
+                   "kernel": g["plans"][ob].kernel_name, "spmm_ms": round(t_s, 5),
+                   "spmm_tflops": round(flops_dense_eq(g) / (t_s * 1e-3) / 1e12, 2)}
+            if key in dense:
+                row["dense_ms"] = round(dense[key], 5)
+                row["dense_tflops"] = round(flops_dense_eq(g) / (dense[key] * 1e-3) / 1e12, 2)
+                row["speedup"] = round(dense[key] / t_s, 3)
+            per_gemm.append(row)
+    speedup = None
+    if dense:
+        speedup = round(sum(dense.values()) / spmm_total_ms, 3)
+
+    # CPU oracle on one step of the same workload
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(gemms)
+
+    dtype = gemms[0]["dtype"]
+    out = {
+        "metric": "dense-equivalent TFLOP/s of 2:4 SpMM (fp16, bf16, int8) + speedup vs dense GEMM",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"f16": "f16", "bf16": "bf16", "i8": "i8"}[dtype],
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_DESC[args.workload], "pattern": "%d:%d" % (gemms[0]["N"], gemms[0]["M"]),
+                   "step": "prune+check+compress+spmm(per layout)+decompress per weight"},
+        "spmm_only_tflops": round(spmm_only_tflops, 2),
+        "speedup_vs_dense": speedup,
+        "per_gemm": per_gemm,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out))
+
+
+def spmm_bytes(g):
+    """Algorithmic HBM bytes of one SpMM launch: compressed values + metadata + B + D (+ C when beta != 0)."""
+    es = 1 if g["dtype"] == "i8" else 2
+    cd = 4 if g["dtype"] == "i8" else 2
+    keep = g["N"] / g["M"]
+    bits = int(np.ceil(np.log2(g["M"])))
+    total = g["m"] * g["k"] * keep * es + g["m"] * (g["k"] // g["M"]) * g["N"] * bits / 8.0
+    total += g["k"] * g["n"] * es + g["m"] * g["n"] * cd
+    if g["w"]["beta"] != 0:
+        total += g["m"] * g["n"] * cd
+    return total
+
+
+CPU_SAMPLE_FLOPS = 2.0e11   # bound on the oracle's product work (about 10-20 s on 8-16 cores)
+
+
+def cpu_baseline(gemms):
+    """The oracle (test infrastructure, untuned) doing one step of the same work on the host cores."""
+    import oracle
+    flops = 0.0
+    total = sum(2.0 * g["m"] * g["n"] * g["k"] * len(g["layouts"]) for g in gemms)
+    frac = min(1.0, CPU_SAMPLE_FLOPS / total)
+    t0 = time.perf_counter()
+    for g in gemms:
+        dtype, N, M = g["dtype"], g["N"], g["M"]
+        a = g["host"]["a"]
+        if g["mode"] == "tile":
+            p, _ = oracle.prune_tile(a, dtype)
+        else:
+            p, _ = oracle.prune_1d(a, dtype, N, M, g["op_a"])
+        oracle.check_1d(p, dtype, N, M, g["op_a"])
+        v, meta = oracle.compress(p, dtype, N, M, g["op_a"])
+        ahat = oracle.decompress(v, meta, dtype, g["m"], g["k"], N, M, g["op_a"])
+        ahat_log = ahat if g["op_a"] == "N" else np.ascontiguousarray(ahat.T)
+        rows = max(1, int(round(g["m"] * frac)))          # the product on the first rows only
+        for ob in g["layouts"]:
+            b = g["host"]["b"][ob]
+            b_log = b if ob == "N" else np.ascontiguousarray(b.T)
+            if dtype == "i8":
+                c = g["host"]["c"][:rows] if g["host"]["c"] is not None else None
+                oracle.gemm_i64(ahat_log[:rows], b_log, int(g["w"]["alpha"]), int(g["w"]["beta"]), c)
+            else:
+                oracle.gemm_f64(oracle.decode(ahat_log[:rows], dtype), oracle.decode(b_log, dtype), g["w"]["alpha"], 0.0)
+            flops += 2.0 * rows * g["n"] * g["k"]
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": "one step of the workload: prune, check, compress, decompress of every weight in full, and "
+                      "the fp64 dense-loop product for every GEMM and layout on the first %.1f%% of the rows "
+                      "(value = product flops done / total time), %.1f s" % (100 * frac, dt)}
+
+
+if __name__ == "__main__":
+    main()

@@ -355,3 +355,11 @@ void or_spmm_compressed_f64(const void* vals, int64_t vals_ld, const uint8_t* me
     free(acc);
   }
 }
+
+/* Number of threads the OpenMP loops above use (reported with CPU timings). */
+#ifdef _OPENMP
+#include <omp.h>
+int or_threads(void) { return omp_get_max_threads(); }
+#else
+int or_threads(void) { return 1; }
+#endif

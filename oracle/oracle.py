@@ -61,6 +61,7 @@ def lib():
         L.or_gemm_f64.argtypes = [P, P, P, P, I64, I64, I64, D, D]
         L.or_gemm_f64_points.argtypes = [P, P, P, P, I64, P, P, I64, D, D]
         L.or_gemm_i64.argtypes = [P, P, P, P, I64, I64, I64, I64, I64]
+        L.or_threads.restype = I; L.or_threads.argtypes = []
         L.or_spmm_compressed_f64.argtypes = [P, I64, P, I64, I, I64, I64, I, I, P, I64, P, P, D, D]
         _lib = L
     return _lib
@@ -92,6 +93,11 @@ def decode(raw, dtype):
     out = np.empty(raw.shape, np.float64)
     lib().or_decode(_ptr(raw), DT[dtype], raw.size, _ptr(out))
     return out
+
+
+def threads():
+    """OpenMP threads the oracle's parallel loops use."""
+    return lib().or_threads()
 
 
 def meta_bits(M):
