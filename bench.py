@@ -37,6 +37,7 @@ WORKLOAD_SETS = {
     "c1": [("c1", "c1_fp16_256")],
     "c3": [("fwd", "c3_fwd"), ("bwd", "c3_bwd")],
     "c4": [("int8", "c4_int8")],
+    "x1": [("fwd", "x1_fwd"), ("bwd", "x1_bwd")],
     "c5_4of32": [("n1", "c5_4of32_n1"), ("n8", "c5_4of32_n8"), ("n4096", "c5_4of32_n4096")],
     "c5_8of32": [("n1", "c5_8of32_n1"), ("n8", "c5_8of32_n8"), ("n4096", "c5_8of32_n4096")],
 }
@@ -45,6 +46,7 @@ WORKLOAD_DESC = {
     "c1": "fp16 2:4, A 256x256, B 256x64, NN",
     "c3": "bf16 transposable 2:4 training pair, W 11008x4096, X 8192x4096, dY 8192x11008, NT",
     "c4": "int8 2:4, 4096^3, int32 C/D, beta=1, NN+NT",
+    "x1": "fp16 transposable 2:4 pair at the training shapes: W 11008x4096, X 8192x4096, dY 8192x11008, NT",
     "c5_4of32": "fp16 4:32, A 4096x4096, B 4096 x {1, 8, 4096}, NN",
     "c5_8of32": "fp16 8:32, A 4096x4096, B 4096 x {1, 8, 4096}, NN",
 }

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnmsparse.so")
-SOURCES = ["nm_api.hip", "nm_prune.hip", "nm_gemm.hip"]
+SOURCES = ["nm_api.hip", "nm_prune.hip", "nm_gemm.hip", "nm_gemm_f16.hip", "nm_gemm_bf16.hip", "nm_gemm_i8.hip"]
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 CLANG = os.path.join(ROCM, "llvm", "bin", "clang++")

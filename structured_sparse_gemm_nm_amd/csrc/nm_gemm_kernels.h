@@ -1,0 +1,1067 @@
+// Matrix-core kernel templates (included by the per-type instantiation files): D = alpha * op(A) * op(B) + beta * C.
+//
+//  - A_SPARSE24: A is 2:4 compressed (values + 2-bit offsets). The gfx950
+//    sparse matrix instructions (v_smfmac_f32_16x16x64_{f16,bf16},
+//    v_smfmac_i32_16x16x128_i8) take the compressed values and the offsets
+//    directly: the offsets select which activations (rows of op(B)) meet each
+//    kept weight, the mechanism the cuSPARSELt blog describes for Figure 2.
+//  - A_DENSE: dense A on the dense MFMA instructions; the same-shape
+//    comparator for the sparse speed-up (the blog's dense/sparse table).
+//  - A_GATHER: general N:M. Each k-step the block expands its compressed rows
+//    into a dense LDS tile (zero fill + scatter of the kept values by their
+//    offsets) and runs the dense MFMA on it. Element-wise N:M gives every row
+//    its own offsets, so there is no shared gather of B rows to exploit.
+//
+// Block tile 128 x 128, four waves in a 2 x 2 grid, 64 x 64 per wave, 16 x 16
+// instruction tiles. One k-step covers 128 bytes of k per row of op(B): 64
+// elements for 16-bit types, 128 for int8. B is staged in LDS column-major
+// ([n][k], k contiguous): op_b = T (n x k as stored) copies 16-byte chunks;
+// op_b = N (k x n) transposes 4 x 8 (or 4 x 16) register blocks on the way in.
+// Global loads for step s+1 are issued before the matrix instructions of
+// step s and written to the other LDS buffer afterwards.
+//
+// Lane layouts used below (checked on gfx950 hardware with one-hot and random
+// operands): for the 16x16 instructions lane l covers row/column (l % 16) and
+// quarter q = l / 16; the accumulator holds D[4q + r][l % 16], r = 0..3.
+//  dense f16/bf16 16x16x32: A and B hold k = 8q .. 8q+7.
+//  dense i8 16x16x64:       A and B hold k = 16q .. 16q+15.
+//  smfmac 16x16x64 (16-bit): A holds compressed values 8q .. 8q+7 (logical k
+//    16q .. 16q+15, four groups), the index word holds their 2-bit offsets as
+//    nibbles i0 | i1 << 2, one per group; B holds k = 8q .. 8q+7 and
+//    32 + 8q .. 32 + 8q + 7.
+//  smfmac 16x16x128 (i8): A holds compressed bytes 16q .. 16q+15 (logical k
+//    32q .. 32q+31), 32 index bits; B holds k = 16q .. 16q+15 and
+//    64 + 16q .. 64 + 16q + 15.
+#pragma once
+#include <stdlib.h>
+#include <string.h>
+
+#include <type_traits>
+
+#include "nm_device.h"
+#include "nm_internal.h"
+
+namespace nm {
+
+constexpr int NTH = 256;              // four waves
+constexpr int KBYTES = 128;           // bytes of k per row of a dense k-step
+constexpr int BSTRIDE = KBYTES + 16;  // LDS row stride of B / dense A tiles (bank spread)
+constexpr int ASTRIDE_SP = 80;        // LDS row stride of 2:4 compressed A: 64 B values + meta + pad
+constexpr int STG_V = 128;            // gather staging: value bytes per row per step (<= 124 used)
+constexpr int STG_M = 96;             // gather staging: metadata bytes per row per step
+
+enum AMode { A_SPARSE24 = 0, A_DENSE = 1, A_GATHER = 2 };
+
+struct GemmArgs {
+  const uint8_t* a;     // dense A (A_DENSE) or compressed values
+  const uint8_t* meta;  // metadata (A_SPARSE24, A_GATHER)
+  const uint8_t* b;
+  const uint8_t* c;
+  uint8_t* d;
+  int64_t m, n, k;
+  int64_t lda;          // dense A leading dim (elements) or values_ld
+  int64_t mld;          // metadata row stride (bytes)
+  int64_t ldb, ldc, ldd;
+  float alpha, beta;
+  int N, M, bits;
+  int a_vec, b_vec;     // 16-byte vector loads allowed on A / B rows
+};
+
+// ---------------------------------------------------------------- operand staging
+
+// One k-step of a "k-major" operand tile (ROWS rows x 128 bytes of k) from a
+// source whose rows are k-contiguous (op_b = T, or dense A with op_a = N):
+// tile row r is src[(r0 + r) * ld + k0 ...]. ROWS/32 chunks of 16 bytes per thread.
+template <int ROWS> struct KChunks { u32x4 v[ROWS / 32]; };
+
+template <int ESZ, int ROWS>
+__device__ __forceinline__ void load_kcontig(KChunks<ROWS>& R, const uint8_t* src, int64_t r0, int64_t rows,
+                                             int64_t ld, int64_t k0, int64_t k, bool vec) {
+  constexpr int EPC = 16 / ESZ;   // elements per chunk
+#pragma unroll
+  for (int i = 0; i < ROWS / 32; i++) {
+    const int id = threadIdx.x + NTH * i;
+    const int r = id / 8, part = id % 8;
+    const int64_t gr = r0 + r, gk = k0 + part * EPC;
+    if (vec && gr < rows && gk + EPC <= k) {
+      R.v[i] = *(const u32x4*)(src + (size_t)(gr * ld + gk) * ESZ);
+    } else {
+      uint8_t tmp[16];
+#pragma unroll
+      for (int e = 0; e < 16; e++) tmp[e] = 0;
+      if (gr < rows) {
+        for (int e = 0; e < EPC; e++)
+          if (gk + e < k) {
+            if (ESZ == 2) ((uint16_t*)tmp)[e] = ((const uint16_t*)src)[gr * ld + gk + e];
+            else tmp[e] = src[gr * ld + gk + e];
+          }
+      }
+      R.v[i] = *(u32x4*)tmp;
+    }
+  }
+}
+
+template <int ROWS>
+__device__ __forceinline__ void store_kcontig(uint8_t* lds, const KChunks<ROWS>& R) {
+#pragma unroll
+  for (int i = 0; i < ROWS / 32; i++) {
+    const int id = threadIdx.x + NTH * i;
+    const int r = id / 8, part = id % 8;
+    *(u32x4*)(lds + r * BSTRIDE + part * 16) = R.v[i];
+  }
+}
+
+// The same tile from a source whose rows run along the tile's rows (op_b = N:
+// B stored k x n; dense A with op_a = T). Each (chunk, k-quad) pair is four
+// consecutive k rows of one 16-byte column chunk, transposed in registers.
+template <int ESZ, int COLS>
+__device__ __forceinline__ void load_mncontig(KChunks<COLS>& R, const uint8_t* src, int64_t c0, int64_t cols,
+                                              int64_t ld, int64_t k0, int64_t k, bool vec) {
+  constexpr int EPC = 16 / ESZ;                 // columns per chunk
+  constexpr int CPR = COLS / EPC;               // chunks per k row
+#pragma unroll
+  for (int j = 0; j < COLS / 128; j++) {
+    const int pid = threadIdx.x + NTH * j;
+    const int cc = pid % CPR, kq = pid / CPR;
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+      const int64_t gk = k0 + kq * 4 + i, gc = c0 + cc * EPC;
+      u32x4 val;
+      if (vec && gk < k && gc + EPC <= cols) {
+        val = *(const u32x4*)(src + (size_t)(gk * ld + gc) * ESZ);
+      } else {
+        uint8_t tmp[16];
+#pragma unroll
+        for (int e = 0; e < 16; e++) tmp[e] = 0;
+        if (gk < k) {
+          for (int e = 0; e < EPC; e++)
+            if (gc + e < cols) {
+              if (ESZ == 2) ((uint16_t*)tmp)[e] = ((const uint16_t*)src)[gk * ld + gc + e];
+              else tmp[e] = src[gk * ld + gc + e];
+            }
+        }
+        val = *(u32x4*)tmp;
+      }
+      R.v[j * 4 + i] = val;
+    }
+  }
+}
+
+template <int ESZ, int COLS>
+__device__ __forceinline__ void store_mncontig(uint8_t* lds, const KChunks<COLS>& R) {
+  constexpr int EPC = 16 / ESZ;
+  constexpr int CPR = COLS / EPC;
+#pragma unroll
+  for (int j = 0; j < COLS / 128; j++) {
+    const int pid = threadIdx.x + NTH * j;
+    const int cc = pid % CPR, kq = pid / CPR;
+    const u32x4* v = &R.v[j * 4];
+    if (ESZ == 2) {
+      // column c of the chunk gets four 16-bit values (k = 4kq .. 4kq+3)
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        const uint32_t w0 = v[0][d], w1 = v[1][d], w2 = v[2][d], w3 = v[3][d];
+        const u32x2 lo = {(w0 & 0xFFFFu) | (w1 << 16), (w2 & 0xFFFFu) | (w3 << 16)};
+        const u32x2 hi = {(w0 >> 16) | (w1 & 0xFFFF0000u), (w2 >> 16) | (w3 & 0xFFFF0000u)};
+        const int col = cc * EPC + 2 * d;
+        *(u32x2*)(lds + col * BSTRIDE + kq * 8) = lo;
+        *(u32x2*)(lds + (col + 1) * BSTRIDE + kq * 8) = hi;
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        const uint32_t w0 = v[0][d], w1 = v[1][d], w2 = v[2][d], w3 = v[3][d];
+#pragma unroll
+        for (int x = 0; x < 4; x++) {
+          const uint32_t val = ((w0 >> (8 * x)) & 0xFFu) | (((w1 >> (8 * x)) & 0xFFu) << 8) |
+                               (((w2 >> (8 * x)) & 0xFFu) << 16) | (((w3 >> (8 * x)) & 0xFFu) << 24);
+          const int col = cc * EPC + 4 * d + x;
+          *(uint32_t*)(lds + col * BSTRIDE + kq * 4) = val;
+        }
+      }
+    }
+  }
+}
+
+// 2:4 compressed A: per row and k-step 64 bytes of values (ROWS/64 chunks per
+// thread) and 8 (16-bit types) or 16 (int8) metadata bytes (thread t loads row t).
+template <int ROWS> struct SpChunks { u32x4 v[ROWS / 64]; u32x4 meta; };
+
+template <int ESZ, int ROWS>
+__device__ __forceinline__ void load_sp24(SpChunks<ROWS>& R, const GemmArgs& A, int64_t r0, int ks) {
+  const int64_t nvals = A.k / 2;                        // compressed elements per row
+  constexpr int EPC = 16 / ESZ;
+  const int64_t v0 = (int64_t)ks * (64 / ESZ);          // first compressed element of this step
+#pragma unroll
+  for (int i = 0; i < ROWS / 64; i++) {
+    const int id = threadIdx.x + NTH * i;
+    const int r = id / 4, part = id % 4;
+    const int64_t gr = r0 + r, gv = v0 + part * EPC;
+    if (gr < A.m && gv + EPC <= nvals) {
+      R.v[i] = *(const u32x4*)(A.a + (size_t)(gr * A.lda + gv) * ESZ);
+    } else {
+      uint8_t tmp[16];
+#pragma unroll
+      for (int e = 0; e < 16; e++) tmp[e] = 0;
+      if (gr < A.m)
+        for (int e = 0; e < EPC; e++)
+          if (gv + e < nvals) {
+            if (ESZ == 2) ((uint16_t*)tmp)[e] = ((const uint16_t*)A.a)[gr * A.lda + gv + e];
+            else tmp[e] = A.a[gr * A.lda + gv + e];
+          }
+      R.v[i] = *(u32x4*)tmp;
+    }
+  }
+  // Metadata bytes [ks*MB, ks*MB + MB) of the row; the row's zero padding
+  // covers a partial last step (its offsets then meet zero values only).
+  constexpr int MB = ESZ == 2 ? 8 : 16;
+  R.meta = u32x4{0, 0, 0, 0};
+  if (threadIdx.x < ROWS) {
+    const int64_t gr = r0 + threadIdx.x;
+    const int64_t off = (int64_t)ks * MB;
+    if (gr < A.m && off + MB <= A.mld) {
+      if (MB == 8) {
+        const u32x2 t = *(const u32x2*)(A.meta + gr * A.mld + off);
+        R.meta = u32x4{t[0], t[1], 0, 0};
+      } else {
+        R.meta = *(const u32x4*)(A.meta + gr * A.mld + off);
+      }
+    }
+  }
+}
+
+template <int ESZ, int ROWS>
+__device__ __forceinline__ void store_sp24(uint8_t* lds, const SpChunks<ROWS>& R) {
+#pragma unroll
+  for (int i = 0; i < ROWS / 64; i++) {
+    const int id = threadIdx.x + NTH * i;
+    const int r = id / 4, part = id % 4;
+    *(u32x4*)(lds + r * ASTRIDE_SP + part * 16) = R.v[i];
+  }
+  if (threadIdx.x < ROWS) {
+    if (ESZ == 2) *(u32x2*)(lds + threadIdx.x * ASTRIDE_SP + 64) = u32x2{R.meta[0], R.meta[1]};
+    else *(u32x4*)(lds + threadIdx.x * ASTRIDE_SP + 64) = R.meta;
+  }
+}
+
+// ---------------------------------------------------------------- general N:M expansion
+
+// Copy the compressed bytes of step ks for the block's rows into LDS staging:
+// values (dword aligned: 128*N/M bytes per step) and the dword-aligned window
+// of metadata covering the step's offset fields.
+template <int ESZ, int ROWS>
+__device__ __forceinline__ void stage_gather(uint8_t* stg, const GemmArgs& A, int64_t r0, int ks) {
+  const int KL = KBYTES / ESZ;                                // logical k per step
+  const int gps = KL / A.M;                                   // groups per step
+  const int vbytes = gps * A.N * ESZ;                         // value bytes per row per step
+  const int64_t row_vbytes = A.lda * ESZ;                     // padded row: zeros after the last value
+  const int64_t bit0 = (int64_t)ks * gps * A.N * A.bits;
+  const int64_t w0 = bit0 / 32;
+  const int64_t row_mwords = (A.mld) / 4;
+  const int nmw = (gps * A.N * A.bits + 31) / 32 + 1;        // words covering the step's fields
+  const int vw = vbytes / 4;
+  for (int e = threadIdx.x; e < ROWS * (vw + nmw); e += NTH) {
+    const int r = e / (vw + nmw), c = e % (vw + nmw);
+    const int64_t gr = r0 + r;
+    uint32_t val = 0;
+    if (c < vw) {
+      const int64_t off = (int64_t)ks * vbytes + c * 4;
+      if (gr < A.m && off + 4 <= row_vbytes) val = *(const uint32_t*)(A.a + gr * A.lda * ESZ + off);
+      *(uint32_t*)(stg + r * STG_V + c * 4) = val;
+    } else {
+      const int64_t w = w0 + (c - vw);
+      if (gr < A.m && w < row_mwords) val = *(const uint32_t*)(A.meta + gr * A.mld + w * 4);
+      *(uint32_t*)(stg + ROWS * STG_V + r * STG_M + (c - vw) * 4) = val;
+    }
+  }
+}
+
+// Zero each (row, group) region of the dense A tile and scatter its kept values.
+template <int ESZ, int ROWS>
+__device__ __forceinline__ void expand_gather(uint8_t* adense, const uint8_t* stg, const GemmArgs& A, int ks) {
+  const int KL = KBYTES / ESZ;
+  const int gps = KL / A.M;
+  const int64_t groups_left = A.k / A.M - (int64_t)ks * gps;
+  const int gvalid = (int)(groups_left < gps ? groups_left : gps);
+  const int bitoff = (int)(((int64_t)ks * gps * A.N * A.bits) % 32);
+  const int gbytes = A.M * ESZ;
+  for (int e = threadIdx.x; e < ROWS * gps; e += NTH) {
+    const int r = e / gps, g = e % gps;
+    uint8_t* dst = adense + r * BSTRIDE + g * gbytes;
+    for (int x = 0; x < gbytes; x += 4) *(uint32_t*)(dst + x) = 0u;
+    if (g >= gvalid) continue;
+    const uint8_t* vrow = stg + r * STG_V;
+    const uint32_t* mrow = (const uint32_t*)(stg + ROWS * STG_V + r * STG_M);
+    for (int s = 0; s < A.N; s++) {
+      const int t = bitoff + (g * A.N + s) * A.bits;
+      const uint64_t w = (uint64_t)mrow[t / 32] | ((uint64_t)mrow[t / 32 + 1] << 32);
+      const int j = (int)((w >> (t % 32)) & ((1u << A.bits) - 1u));
+      if (ESZ == 2) ((uint16_t*)dst)[j] = ((const uint16_t*)vrow)[g * A.N + s];
+      else dst[j] = vrow[g * A.N + s];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- matrix instructions
+
+template <int DT> struct Frag;
+template <> struct Frag<DT_F16> { typedef half8_t ab; typedef _Float16 half16_t __attribute__((ext_vector_type(16))); typedef half16_t b2; };
+template <> struct Frag<DT_BF16> { typedef bf16x8_t ab; typedef __bf16 bf16x16_t __attribute__((ext_vector_type(16))); typedef bf16x16_t b2; };
+template <> struct Frag<DT_I8> { typedef intx4 ab; typedef intx8 b2; };
+template <int DT> struct Acc { typedef floatx16 t; };
+template <> struct Acc<DT_I8> { typedef intx16 t; };
+
+template <int DT>
+__device__ __forceinline__ typename Frag<DT>::b2 concat(const typename Frag<DT>::ab& lo, const typename Frag<DT>::ab& hi) {
+  if constexpr (DT == DT_I8) {
+    return intx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  } else {
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15);
+  }
+}
+
+// 32x32 sparse instruction: 32 (16-bit) or 64 (int8) logical k.
+template <int DT>
+__device__ __forceinline__ typename Acc<DT>::t smfmac32(const typename Frag<DT>::ab& a, const typename Frag<DT>::b2& b,
+                                                      typename Acc<DT>::t c, int idx) {
+  if constexpr (DT == DT_F16) return __builtin_amdgcn_smfmac_f32_32x32x32_f16(a, b, c, idx, 0, 0);
+  else if constexpr (DT == DT_BF16) return __builtin_amdgcn_smfmac_f32_32x32x32_bf16(a, b, c, idx, 0, 0);
+  else return __builtin_amdgcn_smfmac_i32_32x32x64_i8(a, b, c, idx, 0, 0);
+}
+
+// 32x32 dense instruction: 16 (16-bit) or 32 (int8) k.
+template <int DT>
+__device__ __forceinline__ typename Acc<DT>::t mfma32(const typename Frag<DT>::ab& a, const typename Frag<DT>::ab& b,
+                                                    typename Acc<DT>::t c) {
+  if constexpr (DT == DT_F16) return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  else if constexpr (DT == DT_BF16) return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  else return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+// Map the hardware block id to a (row tile, column tile). The dispatcher deals
+// consecutive block ids round-robin to the eight XCDs, each with its own L2;
+// renumbering gives every XCD a contiguous range of logical tiles. Logical ids
+// then walk down a band of GROUP row tiles before moving right, so the blocks
+// resident on one XCD at the same time cover a compact GROUP x (CUs / GROUP)
+// patch and share both A row tiles and B column tiles in that XCD's L2.
+constexpr int NUM_XCD = 8;
+__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
+  constexpr int GROUP = 8;
+  const int64_t nb = gridDim.x;
+  const int64_t hw = blockIdx.x;
+  const int64_t per = nb / NUM_XCD, rem = nb % NUM_XCD;
+  const int64_t x = hw % NUM_XCD, local = hw / NUM_XCD;
+  const int64_t id = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + local;
+  const int64_t per_band = GROUP * tiles_n;
+  const int64_t band = id / per_band;
+  const int64_t first = band * GROUP;
+  const int64_t rows_in_band = (tiles_m - first) < GROUP ? (tiles_m - first) : GROUP;
+  const int64_t in = id % per_band;
+  tm = first + in % rows_in_band;
+  tn = in / rows_in_band;
+}
+
+// ---------------------------------------------------------------- the tiled kernel
+
+// Block tile BM x BN, four waves in a 2 x 2 grid, (BM/2) x (BN/2) per wave of
+// 32 x 32 instruction tiles. Lane l of a 32x32 instruction covers row/column
+// l % 32 and half q = l / 32; its accumulator holds D[8(r/4) + 4q + r%4][l % 32].
+//  smfmac 32x32x32 (16-bit): A = compressed values 8q..8q+7 of the 16 per row
+//   (logical k 16q..16q+15), index = their nibbles (16 bits); B = k 8q..8q+7
+//   and 16+8q..16+8q+7.  int8 32x32x64: A = compressed bytes 16q..16q+15,
+//   index 32 bits; B = k 16q..16q+15 and 32+16q..32+16q+15.
+//  dense 32x32x16 (16-bit) / 32x32x32 (int8): A and B = 16 bytes at 16q.
+template <int DT, int AMODE, int BKC, int AKC, int BM, int BN>
+__global__ void __launch_bounds__(NTH) gemm_kernel(GemmArgs A) {
+  constexpr int ESZ = DT == DT_I8 ? 1 : 2;
+  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  constexpr int LDS_A = AMODE == A_SPARSE24 ? BM * ASTRIDE_SP : BM * BSTRIDE;
+  constexpr int LDS_B = BN * BSTRIDE;
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[AMODE == A_GATHER ? 1 : 2][LDS_A];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][LDS_B];
+  __shared__ __attribute__((aligned(16))) uint8_t s_stg[AMODE == A_GATHER ? BM * (STG_V + STG_M) : 16];
+
+  typedef typename Acc<DT>::t acc_t;
+  typedef typename Frag<DT>::ab ab_t;
+
+  const int64_t tiles_m = (A.m + BM - 1) / BM, tiles_n = (A.n + BN - 1) / BN;
+  int64_t tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int64_t r0 = tm * BM, c0 = tn * BN;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+  const int l32 = lane & 31, q = lane >> 5;
+
+  acc_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; i++)
+#pragma unroll
+    for (int j = 0; j < FN; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0;
+
+  const int64_t KL = KBYTES / ESZ;                  // logical k per step
+  const int ksteps = (int)((A.k + KL - 1) / KL);
+
+  KChunks<BN> rb;
+  KChunks<BM> ra;
+  SpChunks<BM> rs;
+  auto load_step = [&](int ks) {
+    const int64_t k0 = (int64_t)ks * KL;
+    if (BKC) load_kcontig<ESZ, BN>(rb, A.b, c0, A.n, A.ldb, k0, A.k, A.b_vec);
+    else load_mncontig<ESZ, BN>(rb, A.b, c0, A.n, A.ldb, k0, A.k, A.b_vec);
+    if (AMODE == A_DENSE) {
+      if (AKC) load_kcontig<ESZ, BM>(ra, A.a, r0, A.m, A.lda, k0, A.k, A.a_vec);
+      else load_mncontig<ESZ, BM>(ra, A.a, r0, A.m, A.lda, k0, A.k, A.a_vec);
+    }
+    if (AMODE == A_SPARSE24) load_sp24<ESZ, BM>(rs, A, r0, ks);
+  };
+  auto store_step = [&](int buf) {
+    if (BKC) store_kcontig<BN>(s_b[buf], rb);
+    else store_mncontig<ESZ, BN>(s_b[buf], rb);
+    if (AMODE == A_DENSE) {
+      if (AKC) store_kcontig<BM>(s_a[buf], ra);
+      else store_mncontig<ESZ, BM>(s_a[buf], ra);
+    }
+    if (AMODE == A_SPARSE24) store_sp24<ESZ, BM>(s_a[buf], rs);
+  };
+
+  auto compute = [&](const uint8_t* la, const uint8_t* lb) {
+    if constexpr (AMODE == A_SPARSE24) {
+      constexpr int MB = ESZ == 2 ? 8 : 16;           // metadata bytes per row per step
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+        ab_t av[FM];
+        int ai[FM];
+#pragma unroll
+        for (int fm = 0; fm < FM; fm++) {
+          const uint8_t* p = la + (wm0 + fm * 32 + l32) * ASTRIDE_SP;
+          av[fm] = *(const ab_t*)(p + 32 * h + 16 * q);
+          ai[fm] = ESZ == 2 ? (int)*(const uint16_t*)(p + 64 + h * (MB / 2) + 2 * q)
+                            : (int)*(const uint32_t*)(p + 64 + h * (MB / 2) + 4 * q);
+        }
+#pragma unroll
+        for (int fn = 0; fn < FN; fn++) {
+          const uint8_t* p = lb + (wn0 + fn * 32 + l32) * BSTRIDE + 64 * h;
+          const typename Frag<DT>::b2 bv = concat<DT>(*(const ab_t*)(p + 16 * q), *(const ab_t*)(p + 32 + 16 * q));
+#pragma unroll
+          for (int fm = 0; fm < FM; fm++) acc[fm][fn] = smfmac32<DT>(av[fm], bv, acc[fm][fn], ai[fm]);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        ab_t av[FM];
+#pragma unroll
+        for (int fm = 0; fm < FM; fm++) av[fm] = *(const ab_t*)(la + (wm0 + fm * 32 + l32) * BSTRIDE + 32 * i + 16 * q);
+#pragma unroll
+        for (int fn = 0; fn < FN; fn++) {
+          const ab_t bv = *(const ab_t*)(lb + (wn0 + fn * 32 + l32) * BSTRIDE + 32 * i + 16 * q);
+#pragma unroll
+          for (int fm = 0; fm < FM; fm++) acc[fm][fn] = mfma32<DT>(av[fm], bv, acc[fm][fn]);
+        }
+      }
+    }
+  };
+
+  if constexpr (AMODE == A_GATHER) {
+    for (int ks = 0; ks < ksteps; ks++) {
+      load_step(ks);
+      stage_gather<ESZ, BM>(s_stg, A, r0, ks);
+      store_step(0);
+      __syncthreads();
+      expand_gather<ESZ, BM>(s_a[0], s_stg, A, ks);
+      __syncthreads();
+      compute(s_a[0], s_b[0]);
+      __syncthreads();
+    }
+  } else {
+    // Two-deep prefetch: registers hold step s+1 while step s computes; they
+    // go to the idle LDS buffer afterwards and the loads for s+2 start.
+    if (ksteps > 0) {
+      load_step(0);
+      store_step(0);
+    }
+    if (ksteps > 1) load_step(1);
+    __syncthreads();
+    for (int ks = 0; ks < ksteps; ks++) {
+      const int buf = ks & 1;
+      compute(s_a[buf], s_b[buf]);
+      if (ks + 1 < ksteps) store_step(buf ^ 1);
+      if (ks + 2 < ksteps) load_step(ks + 2);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: D = alpha * acc + beta * C ----
+#pragma unroll
+  for (int fm = 0; fm < FM; fm++)
+#pragma unroll
+    for (int fn = 0; fn < FN; fn++) {
+      const int64_t col = c0 + wn0 + fn * 32 + l32;
+      if (col >= A.n) continue;
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int64_t row = r0 + wm0 + fm * 32 + 8 * (r / 4) + 4 * q + (r % 4);
+        if (row >= A.m) continue;
+        if constexpr (DT == DT_I8) {
+          int64_t v = (int64_t)A.alpha * acc[fm][fn][r];
+          if (A.beta != 0.0f) v += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.ldc + col];
+          ((int32_t*)A.d)[row * A.ldd + col] = (int32_t)v;
+        } else {
+          float v = A.alpha * acc[fm][fn][r];
+          if (A.beta != 0.0f) v += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.ldc + col]);
+          ((uint16_t*)A.d)[row * A.ldd + col] = to_bits16<DT>(v);
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------- full-tile kernel
+
+// The same product for problems made of whole tiles (m % BM == 0, n % BN == 0,
+// k a multiple of the k-step, 16-byte rows, every operand below 2 GiB): no
+// bounds checks; each thread keeps 32-bit byte offsets of its chunks from
+// block-uniform bases, advanced by a uniform step offset. Fragments for the
+// next instruction group are read from LDS while the current group's matrix
+// instructions run.
+template <int DT, int AMODE, int BKC, int AKC, int BM, int BN>
+__global__ void __launch_bounds__(NTH) gemm_fast_kernel(GemmArgs A) {
+  constexpr int ESZ = DT == DT_I8 ? 1 : 2;
+  constexpr int EPC = 16 / ESZ;
+  constexpr int KL = KBYTES / ESZ;
+  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
+  constexpr int LDS_A = AMODE == A_SPARSE24 ? BM * ASTRIDE_SP : BM * BSTRIDE;
+  constexpr int LDS_B = BN * BSTRIDE;
+  constexpr int MB = ESZ == 2 ? 8 : 16;           // metadata bytes per row per step
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][LDS_A];
+  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][LDS_B];
+
+  typedef typename Acc<DT>::t acc_t;
+  typedef typename Frag<DT>::ab ab_t;
+  typedef typename Frag<DT>::b2 b2_t;
+
+  const int64_t tiles_m = A.m / BM, tiles_n = A.n / BN;
+  int64_t tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int64_t r0 = tm * BM, c0 = tn * BN;
+  const int t = threadIdx.x;
+  const int lane = t & 63, wave = t >> 6;
+  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
+  const int l32 = lane & 31, q = lane >> 5;
+  const int ksteps = (int)(A.k / KL);
+
+  // ---- per-thread chunk offsets (bytes) ----
+  const uint8_t* bbase = A.b + (size_t)(BKC ? c0 * A.ldb : c0) * ESZ;
+  const uint32_t bstep = BKC ? (uint32_t)KBYTES : (uint32_t)(KL * A.ldb * ESZ);
+  uint32_t boff[BN / 32];
+  if (BKC) {
+#pragma unroll
+    for (int i = 0; i < BN / 32; i++) {
+      const int id = t + NTH * i, r = id / 8, part = id % 8;
+      boff[i] = (uint32_t)((r * A.ldb + part * EPC) * ESZ);
+    }
+  } else {
+    constexpr int CPR = BN / EPC;
+#pragma unroll
+    for (int j = 0; j < BN / 128; j++) {
+      const int pid = t + NTH * j, cc = pid % CPR, kq = pid / CPR;
+#pragma unroll
+      for (int i = 0; i < 4; i++) boff[j * 4 + i] = (uint32_t)(((kq * 4 + i) * A.ldb + cc * EPC) * ESZ);
+    }
+  }
+  const uint8_t* abase;
+  uint32_t astep;
+  uint32_t aoff[AMODE == A_DENSE ? BM / 32 : BM / 64];
+  uint32_t moff = 0;
+  if constexpr (AMODE == A_DENSE) {
+    abase = A.a + (size_t)(AKC ? r0 * A.lda : r0) * ESZ;
+    astep = AKC ? (uint32_t)KBYTES : (uint32_t)(KL * A.lda * ESZ);
+    if (AKC) {
+#pragma unroll
+      for (int i = 0; i < BM / 32; i++) {
+        const int id = t + NTH * i, r = id / 8, part = id % 8;
+        aoff[i] = (uint32_t)((r * A.lda + part * EPC) * ESZ);
+      }
+    } else {
+      constexpr int CPR = BM / EPC;
+#pragma unroll
+      for (int j = 0; j < BM / 128; j++) {
+        const int pid = t + NTH * j, cc = pid % CPR, kq = pid / CPR;
+#pragma unroll
+        for (int i = 0; i < 4; i++) aoff[j * 4 + i] = (uint32_t)(((kq * 4 + i) * A.lda + cc * EPC) * ESZ);
+      }
+    }
+  } else {
+    abase = A.a + (size_t)(r0 * A.lda) * ESZ;
+    astep = 64;
+#pragma unroll
+    for (int i = 0; i < BM / 64; i++) {
+      const int id = t + NTH * i, r = id / 4, part = id % 4;
+      aoff[i] = (uint32_t)((r * A.lda + part * EPC) * ESZ);
+    }
+    moff = (uint32_t)(t * A.mld);
+  }
+  const uint8_t* mbase = A.meta + (size_t)(r0 * A.mld);
+
+  KChunks<BN> rb;
+  KChunks<BM> ra;
+  SpChunks<BM> rs;
+  auto load_step = [&](int ks) {
+    const uint8_t* bp = bbase + (size_t)ks * bstep;
+#pragma unroll
+    for (int i = 0; i < BN / 32; i++) rb.v[i] = *(const u32x4*)(bp + boff[i]);
+    const uint8_t* ap = abase + (size_t)ks * astep;
+    if constexpr (AMODE == A_DENSE) {
+#pragma unroll
+      for (int i = 0; i < BM / 32; i++) ra.v[i] = *(const u32x4*)(ap + aoff[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < BM / 64; i++) rs.v[i] = *(const u32x4*)(ap + aoff[i]);
+      if (t < BM) {
+        const uint8_t* mp = mbase + (size_t)ks * MB + moff;
+        if (MB == 8) {
+          const u32x2 w = *(const u32x2*)mp;
+          rs.meta = u32x4{w[0], w[1], 0, 0};
+        } else {
+          rs.meta = *(const u32x4*)mp;
+        }
+      }
+    }
+  };
+  auto store_step = [&](int buf) {
+    if (BKC) store_kcontig<BN>(s_b[buf], rb);
+    else store_mncontig<ESZ, BN>(s_b[buf], rb);
+    if constexpr (AMODE == A_DENSE) {
+      if (AKC) store_kcontig<BM>(s_a[buf], ra);
+      else store_mncontig<ESZ, BM>(s_a[buf], ra);
+    } else {
+      store_sp24<ESZ, BM>(s_a[buf], rs);
+    }
+  };
+
+  acc_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; i++)
+#pragma unroll
+    for (int j = 0; j < FN; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0;
+
+  // ---- fragments ----
+  struct SpFrag { ab_t a[FM]; int idx[FM]; b2_t b[FN]; };
+  struct DnFrag { ab_t a[FM]; ab_t b[FN]; };
+  auto load_sp = [&](SpFrag& F, const uint8_t* la, const uint8_t* lb, int h) {
+#pragma unroll
+    for (int fm = 0; fm < FM; fm++) {
+      const uint8_t* p = la + (wm0 + fm * 32 + l32) * ASTRIDE_SP;
+      F.a[fm] = *(const ab_t*)(p + 32 * h + 16 * q);
+      F.idx[fm] = ESZ == 2 ? (int)*(const uint16_t*)(p + 64 + h * (MB / 2) + 2 * q)
+                           : (int)*(const uint32_t*)(p + 64 + h * (MB / 2) + 4 * q);
+    }
+#pragma unroll
+    for (int fn = 0; fn < FN; fn++) {
+      const uint8_t* p = lb + (wn0 + fn * 32 + l32) * BSTRIDE + 64 * h;
+      F.b[fn] = concat<DT>(*(const ab_t*)(p + 16 * q), *(const ab_t*)(p + 32 + 16 * q));
+    }
+  };
+  auto mma_sp = [&](const SpFrag& F) {
+#pragma unroll
+    for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+      for (int fm = 0; fm < FM; fm++) acc[fm][fn] = smfmac32<DT>(F.a[fm], F.b[fn], acc[fm][fn], F.idx[fm]);
+  };
+  auto load_dn = [&](DnFrag& F, const uint8_t* la, const uint8_t* lb, int i) {
+#pragma unroll
+    for (int fm = 0; fm < FM; fm++) F.a[fm] = *(const ab_t*)(la + (wm0 + fm * 32 + l32) * BSTRIDE + 32 * i + 16 * q);
+#pragma unroll
+    for (int fn = 0; fn < FN; fn++) F.b[fn] = *(const ab_t*)(lb + (wn0 + fn * 32 + l32) * BSTRIDE + 32 * i + 16 * q);
+  };
+  auto mma_dn = [&](const DnFrag& F) {
+#pragma unroll
+    for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+      for (int fm = 0; fm < FM; fm++) acc[fm][fn] = mfma32<DT>(F.a[fm], F.b[fn], acc[fm][fn]);
+  };
+  auto compute = [&](int buf) {
+    const uint8_t* la = s_a[buf];
+    const uint8_t* lb = s_b[buf];
+    if constexpr (AMODE == A_SPARSE24) {
+      SpFrag F0, F1;
+      load_sp(F0, la, lb, 0);
+      load_sp(F1, la, lb, 1);
+      mma_sp(F0);
+      mma_sp(F1);
+    } else {
+      DnFrag F0, F1;
+      load_dn(F0, la, lb, 0);
+      load_dn(F1, la, lb, 1);
+      mma_dn(F0);
+      load_dn(F0, la, lb, 2);
+      mma_dn(F1);
+      load_dn(F1, la, lb, 3);
+      mma_dn(F0);
+      mma_dn(F1);
+    }
+  };
+
+  load_step(0);
+  store_step(0);
+  if (ksteps > 1) load_step(1);
+  __syncthreads();
+  for (int ks = 0; ks < ksteps; ks++) {
+    const int buf = ks & 1;
+    compute(buf);
+    if (ks + 1 < ksteps) store_step(buf ^ 1);
+    if (ks + 2 < ksteps) load_step(ks + 2);
+    __syncthreads();
+  }
+
+  // ---- epilogue: D = alpha * acc + beta * C ----
+#pragma unroll
+  for (int fm = 0; fm < FM; fm++)
+#pragma unroll
+    for (int fn = 0; fn < FN; fn++) {
+      const int64_t col = c0 + wn0 + fn * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int64_t row = r0 + wm0 + fm * 32 + 8 * (r / 4) + 4 * q + (r % 4);
+        if constexpr (DT == DT_I8) {
+          int64_t v = (int64_t)A.alpha * acc[fm][fn][r];
+          if (A.beta != 0.0f) v += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.ldc + col];
+          ((int32_t*)A.d)[row * A.ldd + col] = (int32_t)v;
+        } else {
+          float v = A.alpha * acc[fm][fn][r];
+          if (A.beta != 0.0f) v += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.ldc + col]);
+          ((uint16_t*)A.d)[row * A.ldd + col] = to_bits16<DT>(v);
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------- LDS-DMA ring kernel (NT)
+
+// For op_b = T (B stored n x k, k contiguous) and operands made of whole tiles:
+// global memory is copied straight into LDS (global_load_lds_dwordx4: lane i
+// of a wave instruction writes 16 bytes at LDS base + 16 i), into a ring of S
+// stages, issued S - 1 k-steps ahead, so no registers stage the copies and
+// several steps of loads are in flight while the matrix instructions run.
+// Because the DMA fixes where each lane's 16 bytes land, the layouts are
+// unpadded and XOR-swizzled instead: each lane fetches the chunk that belongs
+// in its slot, slot = chunk ^ swz(row).
+//   B and dense A rows: 128 bytes = 8 chunks, swz8(r) = (r1 r2 r3) ^ (r0 << 2)
+//     (bits of r), i.e. ((r >> 1) & 7) ^ ((r & 1) << 2).
+//   2:4 values rows: 64 bytes = 4 chunks, swz4(r) = r2 << 1 | (r1 ^ r3).
+//   metadata rows: MB bytes (8 for 16-bit types, 16 for int8), unswizzled.
+// A 16-byte LDS read serves 16 lanes per pass when the LDS presents 64 banks
+// (8 lanes with 32): with these swizzles the rows that fall on the same banks
+// inside either group always read different slots, so one chunk read by 16
+// (or 8) consecutive rows is conflict-free in both cases.
+
+template <int N_>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N_ >= 0 && N_ < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N_ & 0xF) | (0x7 << 4) | (0xF << 8) | ((N_ >> 4) << 14));
+}
+
+// Barrier that orders LDS accesses only (the asm clobber keeps the compiler
+// from moving memory operations across it; the caller waits for its own DMA).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
+__device__ __forceinline__ int swz4(int r) { return (((r >> 2) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1); }
+
+__device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const void*)g, (lds_ptr_t)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* lds_wave_base) {
+  __builtin_amdgcn_global_load_lds((const void*)g, (lds_ptr_t)lds_wave_base, 4, 0, 0);
+}
+
+template <int DT, int AMODE, int BM, int BN, int S, int WGM, int WGN>
+__global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
+  constexpr int NW = WGM * WGN;                          // waves per block
+  constexpr int ESZ = DT == DT_I8 ? 1 : 2;
+  constexpr int KL = KBYTES / ESZ;
+  constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 32, FN = WN / 32;
+  constexpr int MB = ESZ == 2 ? 8 : 16;                  // metadata bytes per row per step
+  constexpr int MDW = MB / 4;
+  constexpr bool SP = AMODE == A_SPARSE24;
+  constexpr int A_VAL = SP ? BM * 64 : BM * 128;         // values (2:4) or dense A rows
+  constexpr int A_META = SP ? BM * MB : 0;
+  constexpr int B_ST = BN * 128;
+  constexpr int STAGE = A_VAL + A_META + B_ST;
+  static_assert(S * STAGE <= 160 * 1024, "LDS ring too large");
+  // DMA wave instructions per stage (64 lanes x 16 or 4 bytes), split evenly over the waves
+  constexpr int TB = BN / 8, TA = SP ? BM / 16 : BM / 8, TMT = SP ? BM * MDW / 64 : 0;
+  static_assert(TB % NW == 0 && TA % NW == 0 && TMT % NW == 0, "DMA split");
+  constexpr int NB = TB / NW, NA = TA / NW, NMT = TMT / NW;
+  constexpr int L = NB + NA + NMT;                       // per wave per stage (same for every wave)
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[S * STAGE];
+
+  typedef typename Acc<DT>::t acc_t;
+  typedef typename Frag<DT>::ab ab_t;
+  typedef typename Frag<DT>::b2 b2_t;
+
+  const int64_t tiles_m = A.m / BM, tiles_n = A.n / BN;
+  int64_t tm, tn;
+  tile_coords(tiles_m, tiles_n, tm, tn);
+  const int64_t r0 = tm * BM, c0 = tn * BN;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: keeps LDS/M0 math scalar
+  const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
+  const int l32 = lane & 31, q = lane >> 5;
+  const int ksteps = (int)(A.k / KL);
+
+  // ---- DMA: block-uniform bases (advanced per step in scalar registers) and
+  // per-lane byte offsets computed once ----
+  const uint8_t* bbase = A.b + (size_t)(c0 * A.ldb) * ESZ;
+  const uint8_t* abase = A.a + (size_t)(r0 * A.lda) * ESZ;
+  const uint8_t* mbase = A.meta + (size_t)(r0 * A.mld);
+  uint32_t ob[NB], oa[NA], om[NMT > 0 ? NMT : 1];
+#pragma unroll
+  for (int j = 0; j < NB; j++) {
+    const int row = 8 * (wave * NB + j) + lane / 8, slot = lane % 8;
+    ob[j] = (uint32_t)(row * A.ldb * ESZ + ((slot ^ swz8(row)) << 4));
+  }
+#pragma unroll
+  for (int j = 0; j < NA; j++) {
+    if (SP) {
+      const int row = 16 * (wave * NA + j) + lane / 4, slot = lane % 4;
+      oa[j] = (uint32_t)(row * A.lda * ESZ + ((slot ^ swz4(row)) << 4));
+    } else {
+      const int row = 8 * (wave * NA + j) + lane / 8, slot = lane % 8;
+      oa[j] = (uint32_t)(row * A.lda * ESZ + ((slot ^ swz8(row)) << 4));
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NMT; j++) {                        // 4-byte pieces, MDW per row
+    const int p = 64 * (wave * NMT + j) + lane;
+    om[j] = (uint32_t)((p / MDW) * A.mld + (p % MDW) * 4);
+  }
+  auto issue = [&](int st) {
+    uint8_t* base = ring + (st % S) * STAGE;
+    const uint8_t* bp = bbase + (size_t)st * KBYTES;
+    const uint8_t* ap = abase + (size_t)st * (SP ? 64 : KBYTES);
+    const uint8_t* mp = mbase + (size_t)st * MB;
+#pragma unroll
+    for (int j = 0; j < NB; j++) dma16(bp + ob[j], base + A_VAL + A_META + (wave * NB + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < NA; j++) dma16(ap + oa[j], base + (wave * NA + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < NMT; j++) dma4(mp + om[j], base + A_VAL + (wave * NMT + j) * 256);
+  };
+
+  acc_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; i++)
+#pragma unroll
+    for (int j = 0; j < FN; j++)
+#pragma unroll
+      for (int r = 0; r < 16; r++) acc[i][j][r] = 0;
+
+  auto bchunk = [&](const uint8_t* lb, int row, int c) -> ab_t {
+    return *(const ab_t*)(lb + row * 128 + ((c ^ swz8(row)) << 4));
+  };
+
+#pragma unroll
+  for (int st = 0; st < S - 1; st++)
+    if (st < ksteps) issue(st);
+  for (int ks = 0; ks < ksteps; ks++) {
+    // this wave's copies for step ks are done once at most the later issued
+    // steps (ks+1 .. ks+S-2, as far as they exist) are still outstanding
+    if (ks + S - 2 < ksteps) wait_vmcnt<L * (S - 2)>();
+    else if (S > 3 && ks + S - 3 < ksteps) wait_vmcnt<L * (S > 3 ? S - 3 : 0)>();
+    else wait_vmcnt<0>();
+    lds_barrier();
+    if (ks + S - 1 < ksteps) issue(ks + S - 1);          // refills the slot read in step ks - 1
+    const uint8_t* st = ring + (ks % S) * STAGE;
+    if constexpr (SP) {
+      // Stream: per half-step, A fragments once, then B column tiles one by
+      // one; the next group's LDS reads are issued before the current group's
+      // matrix instructions.
+      const uint8_t* la = st;
+      const uint8_t* lm = st + A_VAL;
+      const uint8_t* lb = st + A_VAL + A_META;
+      ab_t av[2][FM];
+      int iv[2][FM];
+      b2_t bv[2];
+      auto load_a = [&](int h) {
+#pragma unroll
+        for (int fm = 0; fm < FM; fm++) {
+          const int row = wm0 + fm * 32 + l32;
+          const int c = 2 * h + q;
+          av[h][fm] = *(const ab_t*)(la + row * 64 + ((c ^ swz4(row)) << 4));
+          iv[h][fm] = ESZ == 2 ? (int)*(const uint16_t*)(lm + row * MB + h * (MB / 2) + 2 * q)
+                               : (int)*(const uint32_t*)(lm + row * MB + h * (MB / 2) + 4 * q);
+        }
+      };
+      auto load_b = [&](int slot, int h, int fn) {
+        const int row = wn0 + fn * 32 + l32;
+        bv[slot] = concat<DT>(bchunk(lb, row, 4 * h + q), bchunk(lb, row, 4 * h + 2 + q));
+      };
+      load_a(0);
+      load_b(0, 0, 0);
+#pragma unroll
+      for (int h = 0; h < 2; h++) {
+#pragma unroll
+        for (int fn = 0; fn < FN; fn++) {
+          const int g = h * FN + fn;                     // group index: B fragment slot g % 2
+          __builtin_amdgcn_sched_barrier(0);
+          if (fn + 1 < FN) load_b((g + 1) % 2, h, fn + 1);
+          else if (h == 0) { load_a(1); load_b((g + 1) % 2, 1, 0); }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int fm = 0; fm < FM; fm++) acc[fm][fn] = smfmac32<DT>(av[h][fm], bv[g % 2], acc[fm][fn], iv[h][fm]);
+        }
+      }
+    } else {
+      const uint8_t* la = st;
+      const uint8_t* lb = st + A_VAL;
+      ab_t av[2][FM], bw[2][FN];
+      auto load_d = [&](int slot, int i) {
+#pragma unroll
+        for (int fm = 0; fm < FM; fm++) av[slot][fm] = bchunk(la, wm0 + fm * 32 + l32, 2 * i + q);
+#pragma unroll
+        for (int fn = 0; fn < FN; fn++) bw[slot][fn] = bchunk(lb, wn0 + fn * 32 + l32, 2 * i + q);
+      };
+      load_d(0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; i++) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (i + 1 < 4) load_d((i + 1) % 2, i + 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+          for (int fm = 0; fm < FM; fm++) acc[fm][fn] = mfma32<DT>(av[i % 2][fm], bw[i % 2][fn], acc[fm][fn]);
+      }
+    }
+  }
+
+  // ---- epilogue: D = alpha * acc + beta * C ----
+#pragma unroll
+  for (int fm = 0; fm < FM; fm++)
+#pragma unroll
+    for (int fn = 0; fn < FN; fn++) {
+      const int64_t col = c0 + wn0 + fn * 32 + l32;
+#pragma unroll
+      for (int r = 0; r < 16; r++) {
+        const int64_t row = r0 + wm0 + fm * 32 + 8 * (r / 4) + 4 * q + (r % 4);
+        if constexpr (DT == DT_I8) {
+          int64_t v = (int64_t)A.alpha * acc[fm][fn][r];
+          if (A.beta != 0.0f) v += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.ldc + col];
+          ((int32_t*)A.d)[row * A.ldd + col] = (int32_t)v;
+        } else {
+          float v = A.alpha * acc[fm][fn][r];
+          if (A.beta != 0.0f) v += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.ldc + col]);
+          ((uint16_t*)A.d)[row * A.ldd + col] = to_bits16<DT>(v);
+        }
+      }
+    }
+}
+
+// ---------------------------------------------------------------- tile launch (per element type)
+
+// Block tile: 256 x 256 when that still gives most CUs a tile, 256 x 128 or
+// 128 x 128 otherwise (the dense comparator stops at 256 x 128, whose ring of
+// three stages fits LDS). The general N:M gather path always uses 128 x 128 (its
+// staging needs LDS). NM_FORCE_TILE=128|256x128|256 pins the choice and
+// NM_NO_DMA=1 disables the LDS-DMA kernel (benchmark sweeps only).
+enum TileCfg { T128 = 0, T256x128 = 1, T256 = 2 };
+inline int pick_tile(const nm_plan& pl, int amode) {
+  if (amode == A_GATHER) return T128;
+  const char* f = getenv("NM_FORCE_TILE");
+  if (f) {
+    if (!strcmp(f, "128")) return T128;
+    if (!strcmp(f, "256x128")) return T256x128;
+    if (!strcmp(f, "256")) return amode == A_DENSE ? T256x128 : T256;
+  }
+  const int64_t t256 = ((pl.p.m + 255) / 256) * ((pl.p.n + 255) / 256);
+  const int64_t t256x128 = ((pl.p.m + 255) / 256) * ((pl.p.n + 127) / 128);
+  if (t256 >= 192 && amode != A_DENSE) return T256;
+  if (t256x128 >= 192) return T256x128;
+  return T128;
+}
+
+// Whole tiles, whole k-steps, 16-byte rows and operands addressable with
+// 32-bit offsets: the full-tile kernels apply.
+inline bool full_tiles(const nm_plan& pl, const GemmArgs& A, int TM, int TN, int amode) {
+  const int es = pl.esz_ab;
+  const int64_t kl = KBYTES / es;
+  if (amode == A_GATHER) return false;
+  if (A.m % TM || A.n % TN || A.k % kl || A.k == 0) return false;
+  if ((A.ldb * es) % 16 || (A.lda * es) % 16) return false;
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t b_rows = pl.p.op_b == NM_OP_N ? A.k : A.n;
+  const int64_t a_rows = amode == A_DENSE ? (pl.p.op_a == NM_OP_N ? A.m : A.k) : A.m;
+  return b_rows * A.ldb * es < lim && a_rows * A.lda * es < lim && A.m * A.mld < lim;
+}
+
+// Stages of the LDS-DMA ring: as many as fit (at most 4), keeping two blocks
+// per CU for 128 x 128 tiles.
+template <int DT, int AMODE, int TM, int TN>
+constexpr int dma_stages() {
+  constexpr int ES = DT == DT_I8 ? 1 : 2;
+  constexpr int STG = (AMODE == A_SPARSE24 ? TM * (64 + (ES == 2 ? 8 : 16)) : TM * 128) + TN * 128;
+  constexpr int BUDGET = (TM == 128 && TN == 128) ? 80 * 1024 : 160 * 1024;
+  return 4 * STG <= BUDGET ? 4 : (3 * STG <= BUDGET ? 3 : 2);
+}
+
+template <int DT, int AMODE, int TM, int TN>
+hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
+  const int64_t tiles = ((A.m + TM - 1) / TM) * ((A.n + TN - 1) / TN);
+  const dim3 grid((unsigned)tiles);
+  const bool bkc = pl.p.op_b == NM_OP_T;
+  const bool akc = pl.p.op_a == NM_OP_N || AMODE != A_DENSE;
+  if constexpr (AMODE != A_GATHER) {
+    if (full_tiles(pl, A, TM, TN, AMODE) && bkc && akc && !getenv("NM_NO_DMA")) {
+      // 256-row tiles run eight waves (two per SIMD, 128 x 64 or 64 x 64 each);
+      // 128 x 128 tiles run four waves with two blocks per CU.
+      constexpr int WGM = TM == 256 ? (TN == 256 ? 2 : 4) : 2;
+      constexpr int WGN = TM == 256 ? 4 / (TN == 256 ? 1 : 2) : 2;
+      hipLaunchKernelGGL((gemm_dma_kernel<DT, AMODE, TM, TN, dma_stages<DT, AMODE, TM, TN>(), WGM, WGN>), grid,
+                         dim3(64 * WGM * WGN), 0, s, A);
+      return hipGetLastError();
+    }
+    if (full_tiles(pl, A, TM, TN, AMODE)) {
+      if (bkc && akc) hipLaunchKernelGGL((gemm_fast_kernel<DT, AMODE, 1, 1, TM, TN>), grid, dim3(NTH), 0, s, A);
+      else if (!bkc && akc) hipLaunchKernelGGL((gemm_fast_kernel<DT, AMODE, 0, 1, TM, TN>), grid, dim3(NTH), 0, s, A);
+      else if (AMODE == A_DENSE && bkc) hipLaunchKernelGGL((gemm_fast_kernel<DT, A_DENSE, 1, 0, TM, TN>), grid, dim3(NTH), 0, s, A);
+      else if (AMODE == A_DENSE) hipLaunchKernelGGL((gemm_fast_kernel<DT, A_DENSE, 0, 0, TM, TN>), grid, dim3(NTH), 0, s, A);
+      return hipGetLastError();
+    }
+  }
+  if (bkc && akc) hipLaunchKernelGGL((gemm_kernel<DT, AMODE, 1, 1, TM, TN>), grid, dim3(NTH), 0, s, A);
+  else if (!bkc && akc) hipLaunchKernelGGL((gemm_kernel<DT, AMODE, 0, 1, TM, TN>), grid, dim3(NTH), 0, s, A);
+  else if (AMODE == A_DENSE && bkc) hipLaunchKernelGGL((gemm_kernel<DT, A_DENSE, 1, 0, TM, TN>), grid, dim3(NTH), 0, s, A);
+  else if (AMODE == A_DENSE) hipLaunchKernelGGL((gemm_kernel<DT, A_DENSE, 0, 0, TM, TN>), grid, dim3(NTH), 0, s, A);
+  return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_tiles_dt(const nm_plan& pl, int amode, const GemmArgs& A, hipStream_t s) {
+  if (amode == A_GATHER) return launch_tiles_t<DT, A_GATHER, 128, 128>(pl, A, s);
+  if (amode == A_SPARSE24) {
+    switch (pick_tile(pl, A_SPARSE24)) {
+      case T256: return launch_tiles_t<DT, A_SPARSE24, 256, 256>(pl, A, s);
+      case T256x128: return launch_tiles_t<DT, A_SPARSE24, 256, 128>(pl, A, s);
+      default: return launch_tiles_t<DT, A_SPARSE24, 128, 128>(pl, A, s);
+    }
+  }
+  switch (pick_tile(pl, A_DENSE)) {
+    case T256x128: return launch_tiles_t<DT, A_DENSE, 256, 128>(pl, A, s);
+    default: return launch_tiles_t<DT, A_DENSE, 128, 128>(pl, A, s);
+  }
+}
+
+// defined in nm_gemm_f16.hip, nm_gemm_bf16.hip, nm_gemm_i8.hip
+hipError_t launch_tiles_f16(const nm_plan& pl, int amode, const GemmArgs& A, hipStream_t s);
+hipError_t launch_tiles_bf16(const nm_plan& pl, int amode, const GemmArgs& A, hipStream_t s);
+hipError_t launch_tiles_i8(const nm_plan& pl, int amode, const GemmArgs& A, hipStream_t s);
+
+}  // namespace nm

@@ -68,6 +68,11 @@ WORKLOADS = {
                    a=("normal", 3001, 0.02), b=("normal", 3002, 1.0), b_draw="nk", alpha=1.0, beta=0.0, tile=True),
     "c3_bwd": dict(dtype="bf16", N=2, M=4, m=4096, n=8192, k=11008, op_a="T", op_b="T",
                    a=("normal", 3001, 0.02), b=("normal", 3003, 1.0), b_draw="nk", alpha=1.0, beta=0.0, tile=True),
+    # the training-pair shapes in fp16 (large-shape fp16 measurement)
+    "x1_fwd": dict(dtype="f16", N=2, M=4, m=11008, n=8192, k=4096, op_a="N", op_b="T",
+                   a=("normal", 3101, 0.02), b=("normal", 3102, 1.0), b_draw="nk", alpha=1.0, beta=0.0, tile=True),
+    "x1_bwd": dict(dtype="f16", N=2, M=4, m=4096, n=8192, k=11008, op_a="T", op_b="T",
+                   a=("normal", 3101, 0.02), b=("normal", 3103, 1.0), b_draw="nk", alpha=1.0, beta=0.0, tile=True),
     # int8 with int32 accumulate, beta = 1
     "c4_int8": dict(dtype="i8", N=2, M=4, m=4096, n=4096, k=4096, op_a="N", op_b="N",
                     a=("int", 4001, -127, 127), b=("int", 4002, -127, 127), c=("int32", 4003, -2**20, 2**20),

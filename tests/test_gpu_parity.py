@@ -172,7 +172,10 @@ def run_spmm(dtype, N, M, m, n, k, op_b, alpha, beta, seed, op_a="N"):
 @pytest.mark.parametrize("op_b", ["N", "T"])
 @pytest.mark.parametrize("m,n,k", [(200, 144, 336), (128, 128, 64), (64, 272, 1040), (17, 48, 4)])
 @pytest.mark.parametrize("ab", [(1.0, 0.0), (2.0, -3.0)])
-def test_spmm_2of4(dtype, op_b, m, n, k, ab):
+@pytest.mark.parametrize("tile", ["auto", "128", "256"])
+def test_spmm_2of4(dtype, op_b, m, n, k, ab, tile, monkeypatch):
+    if tile != "auto":
+        monkeypatch.setenv("NM_FORCE_TILE", tile)
     alpha, beta = ab
     if dtype != "i8":
         alpha, beta = (0.75, -1.25) if beta != 0 else (1.0, 0.0)
@@ -223,9 +226,12 @@ def test_spmm_skinny(dtype, N, M, n, op_b):
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
 @pytest.mark.parametrize("op_a", ["N", "T"])
 @pytest.mark.parametrize("op_b", ["N", "T"])
-@pytest.mark.parametrize("n", [8, 144])
-def test_dense_gemm(dtype, op_a, op_b, n):
-    m, k = 144, 208
+@pytest.mark.parametrize("n", [8, 144, 304])
+@pytest.mark.parametrize("tile", ["auto", "256"])
+def test_dense_gemm(dtype, op_a, op_b, n, tile, monkeypatch):
+    if tile != "auto":
+        monkeypatch.setenv("NM_FORCE_TILE", tile)
+    m, k = 272, 208
     a_log = rand(dtype, (m, k), 41)
     a_st = a_log if op_a == "N" else np.ascontiguousarray(a_log.T)
     b_log = rand(dtype, (k, n), 42)
