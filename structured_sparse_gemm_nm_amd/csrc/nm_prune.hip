@@ -24,7 +24,6 @@
 
 namespace nm {
 
-constexpr int TILE_R = 64;    // logical rows per tile
 constexpr int TILE_K = 256;   // logical k per tile
 constexpr int TPB = 256;      // threads per block
 
@@ -98,41 +97,53 @@ __device__ __forceinline__ void lds_set(uint8_t* lds, int idx, uint32_t v) {
   else lds[idx] = (uint8_t)v;
 }
 
-// LDS budget (bytes): dense tile + values tile + metadata tile + mask words.
-constexpr int LDS_DENSE = TILE_R * TILE_K * 2;
-constexpr int LDS_VALS = TILE_R * TILE_K * 2;          // N <= M - 1 < M: values never exceed the dense tile
 // Largest metadata bytes per tile row over all (N, M) supported: (TILE_K / M) * N * b / 8 with N = M - 1:
 // M=4: 64*3*2/8 = 48, M=8: 32*7*3/8 = 84, M=16: 16*15*4/8 = 120, M=32: 8*31*5/8 = 155.
 constexpr int META_ROW_BYTES = 160;                     // rounded up to a whole number of words
-constexpr int LDS_META = TILE_R * META_ROW_BYTES;
-constexpr int LDS_MASK = TILE_R * TILE_K / 8;
 
-template <int DT, int ESZ, int M, int OP>
+// Rows per tile: 16 when groups run along stored rows (op N: each stored row
+// of the tile is 256 contiguous elements), 64 when they run down stored
+// columns (op T: each stored row of the tile is then 64 contiguous elements).
+// Small tiles keep many blocks in flight on BERT-sized weights.
+template <int OPT> struct TileRows { static constexpr int value = OPT ? 64 : 16; };
+
+template <int DT, int ESZ, int M, int OP, int OPT>
 __global__ void __launch_bounds__(TPB) tile_kernel(TileArgs A) {
+  constexpr int TR = TileRows<OPT>::value;
+  constexpr int LDS_DENSE = TR * TILE_K * ESZ;
+  constexpr int LDS_VALS = TR * TILE_K * ESZ;           // N <= M - 1 < M: values never exceed the dense tile
+  constexpr int LDS_META = TR * META_ROW_BYTES;
+  constexpr int LDS_MASK = TR * TILE_K / 8;
   __shared__ __attribute__((aligned(16))) uint8_t s_dense[LDS_DENSE];
   __shared__ __attribute__((aligned(16))) uint8_t s_vals[OP == T_PRUNE ? 16 : LDS_VALS];
   __shared__ __attribute__((aligned(16))) uint32_t s_meta[OP == T_PRUNE ? 4 : LDS_META / 4];
   __shared__ __attribute__((aligned(16))) uint32_t s_mask[OP == T_PRUNE ? LDS_MASK / 4 : 4];
 
   constexpr int GPR = TILE_K / M;           // groups per tile row
+  constexpr int VROW = GPR * (M - 1) * ESZ; // LDS bytes reserved per row of values (>= GPR * N * ESZ)
   const int N = A.N, b = A.bits;
-  const int64_t i0 = (int64_t)blockIdx.y * TILE_R;
+  const int64_t i0 = (int64_t)blockIdx.y * TR;
   const int64_t k0 = (int64_t)blockIdx.x * TILE_K;
-  const bool opT = A.op_t != 0;
-  const int64_t srows = opT ? A.k : A.m, scols = opT ? A.m : A.k;   // stored dims
-  const int64_t sr0 = opT ? k0 : i0, sc0 = opT ? i0 : k0;
-  const int rows_here = (int)min((int64_t)TILE_R, A.m - i0);
+  const int64_t srows = OPT ? A.k : A.m, scols = OPT ? A.m : A.k;   // stored dims
+  const int64_t sr0 = OPT ? k0 : i0, sc0 = OPT ? i0 : k0;
+  const int rows_here = (int)min((int64_t)TR, A.m - i0);
   const int groups_here = (int)(min((int64_t)TILE_K, A.k - k0) / M);
   const int vals_per_row = groups_here * N;                          // elements
   const int meta_bits_row = groups_here * N * b;
   const int meta_bytes_row = (meta_bits_row + 7) / 8;
-  const int meta_words_row = (META_ROW_BYTES) / 4;
+  const int meta_words_row = META_ROW_BYTES / 4;
   const bool last_k_tile = k0 + TILE_K >= A.k;
+  // Value bytes of this tile inside a compressed row: a whole number of dwords,
+  // since (256 / M) * N * esize is a multiple of 8; the last tile of a row runs
+  // on to the row's 16-byte padded end (vld * esize).
+  const int64_t vbyte0 = (k0 / M) * N * ESZ;
+  const int64_t mbase = (k0 / M) * N * b / 8;          // first metadata byte (byte aligned)
+  const int64_t vrow_bytes = A.vld * ESZ;
 
   // ---- stage inputs ----
   if (OP == T_PRUNE || OP == T_COMPRESS) {
-    if (opT) tile_in<ESZ, TILE_K, TILE_R>(s_dense, A.a, sr0, sc0, srows, scols, A.lda, A.vec_ok);
-    else tile_in<ESZ, TILE_R, TILE_K>(s_dense, A.a, sr0, sc0, srows, scols, A.lda, A.vec_ok);
+    if (OPT) tile_in<ESZ, TILE_K, TR>(s_dense, A.a, sr0, sc0, srows, scols, A.lda, A.vec_ok);
+    else tile_in<ESZ, TR, TILE_K>(s_dense, A.a, sr0, sc0, srows, scols, A.lda, A.vec_ok);
   }
   if (OP == T_PRUNE) {
     for (int w = threadIdx.x; w < LDS_MASK / 4; w += TPB) s_mask[w] = 0;
@@ -142,16 +153,15 @@ __global__ void __launch_bounds__(TPB) tile_kernel(TileArgs A) {
   }
   if (OP == T_DECOMPRESS) {
     for (int w = threadIdx.x; w < LDS_DENSE / 16; w += TPB) ((u32x4*)s_dense)[w] = u32x4{0, 0, 0, 0};
-    const int64_t vbase = (k0 / M) * N;                  // first value of this tile in a row
-    const int64_t mbase = (k0 / M) * N * b / 8;          // first metadata byte (byte aligned)
-    for (int e = threadIdx.x; e < TILE_R * vals_per_row; e += TPB) {
-      const int r = e / vals_per_row, c = e % vals_per_row;
+    const int vwords = (vals_per_row * ESZ + 3) / 4;      // dwords covering this tile's values in a row
+    for (int e = threadIdx.x; e < TR * vwords; e += TPB) {
+      const int r = e / vwords, c = e % vwords;
       if (r < rows_here) {
-        const size_t gi = (size_t)((i0 + r) * A.vld + vbase + c);
-        lds_set<ESZ>(s_vals, r * (GPR * N) + c, ESZ == 2 ? (uint32_t)((const uint16_t*)A.vals)[gi] : (uint32_t)A.vals[gi]);
+        const uint32_t v = *(const uint32_t*)(A.vals + (i0 + r) * vrow_bytes + vbyte0 + 4 * c);
+        *(uint32_t*)(s_vals + r * VROW + 4 * c) = v;
       }
     }
-    for (int e = threadIdx.x; e < TILE_R * meta_bytes_row; e += TPB) {
+    for (int e = threadIdx.x; e < TR * meta_bytes_row; e += TPB) {
       const int r = e / meta_bytes_row, c = e % meta_bytes_row;
       if (r < rows_here) ((uint8_t*)s_meta)[r * META_ROW_BYTES + c] = A.meta[(i0 + r) * A.mld + mbase + c];
     }
@@ -159,20 +169,20 @@ __global__ void __launch_bounds__(TPB) tile_kernel(TileArgs A) {
   __syncthreads();
 
   // ---- per-group work out of LDS ----
-  for (int it = threadIdx.x; it < TILE_R * GPR; it += TPB) {
+  for (int it = threadIdx.x; it < TR * GPR; it += TPB) {
     int i, g;
-    if (opT) { i = it % TILE_R; g = it / TILE_R; }
+    if (OPT) { i = it % TR; g = it / TR; }
     else { i = it / GPR; g = it % GPR; }
     if (i >= rows_here || g >= groups_here) continue;
     // element (i, g*M + j) of the logical tile lives at this LDS index:
-    auto at = [&](int j) { return opT ? (g * M + j) * TILE_R + i : i * TILE_K + g * M + j; };
+    auto at = [&](int j) { return OPT ? (g * M + j) * TR + i : i * TILE_K + g * M + j; };
     if (OP == T_DECOMPRESS) {
       const uint8_t* mrow = (const uint8_t*)s_meta + i * META_ROW_BYTES;
       for (int s = 0; s < N; s++) {
         const int t0 = (g * N + s) * b;
         uint32_t w = (uint32_t)mrow[t0 / 8] | ((uint32_t)mrow[t0 / 8 + 1] << 8);
         const int j = (int)((w >> (t0 % 8)) & ((1u << b) - 1u));
-        lds_set<ESZ>(s_dense, at(j), lds_elem<ESZ>(s_vals, i * (GPR * N) + g * N + s));
+        lds_set<ESZ>(s_dense, at(j), lds_elem<ESZ>(s_vals + i * VROW, g * N + s));
       }
       continue;
     }
@@ -185,19 +195,19 @@ __global__ void __launch_bounds__(TPB) tile_kernel(TileArgs A) {
       for (int j = 0; j < M; j++)
         if (!((keep >> j) & 1u)) lds_set<ESZ>(s_dense, at(j), 0u);
       if (A.mask) {
-        if (!opT) {
+        if (!OPT) {
           // bits (i, g*M .. g*M+M-1) of the stored tile; M divides 32
           const int bit = g * M;
           atomicOr(&s_mask[i * (TILE_K / 32) + bit / 32], keep << (bit % 32));
         } else {
 #pragma unroll
           for (int j = 0; j < M; j++)
-            if ((keep >> j) & 1u) atomicOr(&s_mask[(g * M + j) * (TILE_R / 32) + i / 32], 1u << (i % 32));
+            if ((keep >> j) & 1u) atomicOr(&s_mask[(g * M + j) * (TR / 32) + i / 32], 1u << (i % 32));
         }
       }
     } else {  // T_COMPRESS
       int s = 0;
-      uint8_t* vrow = s_vals + (size_t)(i * (GPR * N)) * ESZ;
+      uint8_t* vrow = s_vals + i * VROW;
       uint32_t* mrow = s_meta + i * meta_words_row;
 #pragma unroll
       for (int j = 0; j < M; j++) {
@@ -214,12 +224,12 @@ __global__ void __launch_bounds__(TPB) tile_kernel(TileArgs A) {
 
   // ---- write back ----
   if (OP == T_PRUNE || OP == T_DECOMPRESS) {
-    if (opT) tile_out<ESZ, TILE_K, TILE_R>(A.out, s_dense, sr0, sc0, srows, scols, A.lda, A.vec_ok);
-    else tile_out<ESZ, TILE_R, TILE_K>(A.out, s_dense, sr0, sc0, srows, scols, A.lda, A.vec_ok);
+    if (OPT) tile_out<ESZ, TILE_K, TR>(A.out, s_dense, sr0, sc0, srows, scols, A.lda, A.vec_ok);
+    else tile_out<ESZ, TR, TILE_K>(A.out, s_dense, sr0, sc0, srows, scols, A.lda, A.vec_ok);
   }
   if (OP == T_PRUNE && A.mask) {
-    constexpr int WPR_N = TILE_K / 32, WPR_T = TILE_R / 32;
-    const int SR = opT ? TILE_K : TILE_R, WPR = opT ? WPR_T : WPR_N;
+    constexpr int WPR = OPT ? TR / 32 : TILE_K / 32;
+    constexpr int SR = OPT ? TILE_K : TR;
     for (int e = threadIdx.x; e < SR * WPR; e += TPB) {
       const int r = e / WPR, w = e % WPR;
       const int64_t gr = sr0 + r, gw = sc0 / 32 + w;
@@ -227,17 +237,18 @@ __global__ void __launch_bounds__(TPB) tile_kernel(TileArgs A) {
     }
   }
   if (OP == T_COMPRESS) {
-    const int64_t vbase = (k0 / M) * N;
-    const int64_t mbase = (k0 / M) * N * b / 8;
-    // values (plus the zero padding of the row after its last group)
-    const int64_t vend = last_k_tile ? A.vld : vbase + vals_per_row;
-    const int vcount = (int)(vend - vbase);
-    for (int e = threadIdx.x; e < rows_here * vcount; e += TPB) {
-      const int r = e / vcount, c = e % vcount;
-      const uint32_t v = c < vals_per_row ? lds_elem<ESZ>(s_vals, r * (GPR * N) + c) : 0u;
-      const size_t gi = (size_t)((i0 + r) * A.vld + vbase + c);
-      if (ESZ == 2) ((uint16_t*)A.vals)[gi] = (uint16_t)v;
-      else A.vals[gi] = (uint8_t)v;
+    // values: this tile's dwords, plus the zero padding of the row after its last group
+    const int vbytes = vals_per_row * ESZ;
+    const int64_t vend = last_k_tile ? vrow_bytes : vbyte0 + vbytes;
+    const int vwords = (int)((vend - vbyte0) / 4);
+    for (int e = threadIdx.x; e < rows_here * vwords; e += TPB) {
+      const int r = e / vwords, c = e % vwords;
+      uint32_t v = 0;
+      if (4 * c < vbytes) {
+        v = *(const uint32_t*)(s_vals + r * VROW + 4 * c);
+        if (4 * c + 4 > vbytes) v &= 0xFFFFFFFFu >> (8 * (4 * c + 4 - vbytes));   // bytes past the values are padding
+      }
+      *(uint32_t*)(A.vals + (i0 + r) * vrow_bytes + vbyte0 + 4 * c) = v;
     }
     const int64_t mend = last_k_tile ? A.mld : mbase + meta_bytes_row;
     const int mcount = (int)(mend - mbase);
@@ -418,17 +429,24 @@ static TileArgs make_args(const nm_plan& pl) {
   return A;
 }
 
-template <int OP, int DT, int ESZ>
-static hipError_t dispatch_tile_m(const nm_plan& pl, const TileArgs& A, hipStream_t s) {
-  const dim3 grid((unsigned)((pl.p.k + TILE_K - 1) / TILE_K), (unsigned)((pl.p.m + TILE_R - 1) / TILE_R));
+template <int OP, int DT, int ESZ, int OPT>
+static hipError_t dispatch_tile_mo(const nm_plan& pl, const TileArgs& A, hipStream_t s) {
+  constexpr int TR = TileRows<OPT>::value;
+  const dim3 grid((unsigned)((pl.p.k + TILE_K - 1) / TILE_K), (unsigned)((pl.p.m + TR - 1) / TR));
   switch (pl.p.nm_m) {
-    case 4: hipLaunchKernelGGL((tile_kernel<DT, ESZ, 4, OP>), grid, dim3(TPB), 0, s, A); break;
-    case 8: hipLaunchKernelGGL((tile_kernel<DT, ESZ, 8, OP>), grid, dim3(TPB), 0, s, A); break;
-    case 16: hipLaunchKernelGGL((tile_kernel<DT, ESZ, 16, OP>), grid, dim3(TPB), 0, s, A); break;
-    case 32: hipLaunchKernelGGL((tile_kernel<DT, ESZ, 32, OP>), grid, dim3(TPB), 0, s, A); break;
+    case 4: hipLaunchKernelGGL((tile_kernel<DT, ESZ, 4, OP, OPT>), grid, dim3(TPB), 0, s, A); break;
+    case 8: hipLaunchKernelGGL((tile_kernel<DT, ESZ, 8, OP, OPT>), grid, dim3(TPB), 0, s, A); break;
+    case 16: hipLaunchKernelGGL((tile_kernel<DT, ESZ, 16, OP, OPT>), grid, dim3(TPB), 0, s, A); break;
+    case 32: hipLaunchKernelGGL((tile_kernel<DT, ESZ, 32, OP, OPT>), grid, dim3(TPB), 0, s, A); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int OP, int DT, int ESZ>
+static hipError_t dispatch_tile_m(const nm_plan& pl, const TileArgs& A, hipStream_t s) {
+  if (A.op_t) return dispatch_tile_mo<OP, DT, ESZ, 1>(pl, A, s);
+  return dispatch_tile_mo<OP, DT, ESZ, 0>(pl, A, s);
 }
 
 template <int OP>

@@ -170,7 +170,7 @@ def run_spmm(dtype, N, M, m, n, k, op_b, alpha, beta, seed, op_a="N"):
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
 @pytest.mark.parametrize("op_b", ["N", "T"])
-@pytest.mark.parametrize("m,n,k", [(200, 144, 336), (128, 128, 64), (64, 272, 1040), (17, 48, 4)])
+@pytest.mark.parametrize("m,n,k", [(200, 144, 336), (128, 128, 64), (64, 272, 1040), (17, 48, 4), (256, 256, 128), (512, 256, 192)])
 @pytest.mark.parametrize("ab", [(1.0, 0.0), (2.0, -3.0)])
 @pytest.mark.parametrize("tile", ["auto", "128", "256"])
 def test_spmm_2of4(dtype, op_b, m, n, k, ab, tile, monkeypatch):
