@@ -781,7 +781,15 @@ __device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* lds_wave_base) {
   __builtin_amdgcn_global_load_lds((const void*)g, (lds_ptr_t)lds_wave_base, 4, 0, 0);
 }
 
-template <int DT, int AMODE, int BM, int BN, int S, int WGM, int WGN>
+// op_b = N (B stored k x n): the B stage keeps the 64 k-rows as stored, rows of
+// BN * 2 bytes, with 16-byte slot s of row r holding chunk s ^ (4 * (r & 3)).
+// Fragments come from the gfx950 transposing LDS read (ds_read_b64_tr_b16):
+// within each 16-lane group, output lane j element t is the (j % 4)-th 16-bit
+// value of the 8 bytes addressed by lane 4t + j / 4. With lane s addressing
+// k-row base + s / 4 at columns c + 4 (s % 4), lane j receives column c + j at
+// k = base .. base + 3, i.e. four consecutive k of its own column, which is
+// what the matrix instructions' B operand holds. 16-bit types only.
+template <int DT, int AMODE, int BM, int BN, int S, int WGM, int WGN, int BKC>
 __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   constexpr int NW = WGM * WGN;                          // waves per block
   constexpr int ESZ = DT == DT_I8 ? 1 : 2;
@@ -800,6 +808,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   static_assert(TB % NW == 0 && TA % NW == 0 && TMT % NW == 0, "DMA split");
   constexpr int NB = TB / NW, NA = TA / NW, NMT = TMT / NW;
   constexpr int L = NB + NA + NMT;                       // per wave per stage (same for every wave)
+  static_assert(BKC || ESZ == 2, "transposed B staging is 16-bit only");
+  constexpr int BSLOTS = BN / 8;                         // 16-byte slots per stored k-row (op_b = N)
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S * STAGE];
 
   typedef typename Acc<DT>::t acc_t;
@@ -819,14 +829,21 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
 
   // ---- DMA: block-uniform bases (advanced per step in scalar registers) and
   // per-lane byte offsets computed once ----
-  const uint8_t* bbase = A.b + (size_t)(c0 * A.ldb) * ESZ;
+  const uint8_t* bbase = A.b + (size_t)(BKC ? c0 * A.ldb : c0) * ESZ;
+  const size_t bstep = BKC ? (size_t)KBYTES : (size_t)KL * A.ldb * ESZ;
   const uint8_t* abase = A.a + (size_t)(r0 * A.lda) * ESZ;
   const uint8_t* mbase = A.meta + (size_t)(r0 * A.mld);
   uint32_t ob[NB], oa[NA], om[NMT > 0 ? NMT : 1];
 #pragma unroll
   for (int j = 0; j < NB; j++) {
-    const int row = 8 * (wave * NB + j) + lane / 8, slot = lane % 8;
-    ob[j] = (uint32_t)(row * A.ldb * ESZ + ((slot ^ swz8(row)) << 4));
+    if (BKC) {
+      const int row = 8 * (wave * NB + j) + lane / 8, slot = lane % 8;
+      ob[j] = (uint32_t)(row * A.ldb * ESZ + ((slot ^ swz8(row)) << 4));
+    } else {
+      const int p = 64 * (wave * NB + j) + lane;         // slot index in the stage
+      const int row = p / BSLOTS, slot = p % BSLOTS;
+      ob[j] = (uint32_t)(row * A.ldb * ESZ + ((slot ^ (4 * (row & 3))) << 4));
+    }
   }
 #pragma unroll
   for (int j = 0; j < NA; j++) {
@@ -845,7 +862,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   }
   auto issue = [&](int st) {
     uint8_t* base = ring + (st % S) * STAGE;
-    const uint8_t* bp = bbase + (size_t)st * KBYTES;
+    const uint8_t* bp = bbase + (size_t)st * bstep;
     const uint8_t* ap = abase + (size_t)st * (SP ? 64 : KBYTES);
     const uint8_t* mp = mbase + (size_t)st * MB;
 #pragma unroll
@@ -867,6 +884,18 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   auto bchunk = [&](const uint8_t* lb, int row, int c) -> ab_t {
     return *(const ab_t*)(lb + row * 128 + ((c ^ swz8(row)) << 4));
   };
+  // op_b = N: four consecutive k (kbase .. kbase+3) of column `col0 + (lane & 15)`
+  // for each lane of a 16-lane group, from the stored-row B stage.
+  typedef short short4_t __attribute__((ext_vector_type(4)));
+  auto btr4 = [&](const uint8_t* lb, int kbase, int col0) -> short4_t {
+    const int sidx = lane & 15;
+    const int row = kbase + sidx / 4;
+    const int cbyte = (col0 + 4 * (sidx % 4)) * 2;
+    const int off = row * (BN * 2) + ((((cbyte >> 4) ^ (4 * (row & 3)))) << 4) + (cbyte & 15);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(lb + off));
+  };
+  // column base of this lane's 16-lane group inside a 32-column fragment
+  const int nb16 = lane & 16;
 
 #pragma unroll
   for (int st = 0; st < S - 1; st++)
@@ -901,8 +930,20 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
         }
       };
       auto load_b = [&](int slot, int h, int fn) {
-        const int row = wn0 + fn * 32 + l32;
-        bv[slot] = concat<DT>(bchunk(lb, row, 4 * h + q), bchunk(lb, row, 4 * h + 2 + q));
+        if constexpr (BKC) {
+          const int row = wn0 + fn * 32 + l32;
+          bv[slot] = concat<DT>(bchunk(lb, row, 4 * h + q), bchunk(lb, row, 4 * h + 2 + q));
+        } else {
+          // k = 32h + 8q + {0..3, 4..7, 16..19, 20..23}
+          const int cb = wn0 + fn * 32 + nb16;
+          const int kb = 32 * h + 8 * q;
+          const short4_t r0 = btr4(lb, kb, cb), r1 = btr4(lb, kb + 4, cb), r2 = btr4(lb, kb + 16, cb),
+                         r3 = btr4(lb, kb + 20, cb);
+          typedef short short16_t __attribute__((ext_vector_type(16)));
+          const short16_t v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3],
+                               r2[0], r2[1], r2[2], r2[3], r3[0], r3[1], r3[2], r3[3]};
+          bv[slot] = __builtin_bit_cast(b2_t, v);
+        }
       };
       load_a(0);
       load_b(0, 0, 0);
@@ -927,7 +968,18 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
 #pragma unroll
         for (int fm = 0; fm < FM; fm++) av[slot][fm] = bchunk(la, wm0 + fm * 32 + l32, 2 * i + q);
 #pragma unroll
-        for (int fn = 0; fn < FN; fn++) bw[slot][fn] = bchunk(lb, wn0 + fn * 32 + l32, 2 * i + q);
+        for (int fn = 0; fn < FN; fn++) {
+          if constexpr (BKC) {
+            bw[slot][fn] = bchunk(lb, wn0 + fn * 32 + l32, 2 * i + q);
+          } else {
+            // k = 16i + 8q + 0..7
+            const int cb = wn0 + fn * 32 + nb16;
+            const short4_t r0 = btr4(lb, 16 * i + 8 * q, cb), r1 = btr4(lb, 16 * i + 8 * q + 4, cb);
+            typedef short short8_t __attribute__((ext_vector_type(8)));
+            const short8_t v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+            bw[slot][fn] = __builtin_bit_cast(ab_t, v);
+          }
+        }
       };
       load_d(0, 0);
 #pragma unroll
@@ -1019,13 +1071,18 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
   const bool bkc = pl.p.op_b == NM_OP_T;
   const bool akc = pl.p.op_a == NM_OP_N || AMODE != A_DENSE;
   if constexpr (AMODE != A_GATHER) {
-    if (full_tiles(pl, A, TM, TN, AMODE) && bkc && akc && !getenv("NM_NO_DMA")) {
+    const bool dma_nn = !bkc && DT != DT_I8 && !getenv("NM_NO_DMA_NN");
+    if (full_tiles(pl, A, TM, TN, AMODE) && (bkc || dma_nn) && akc && !getenv("NM_NO_DMA")) {
       // 256-row tiles run eight waves (two per SIMD, 128 x 64 or 64 x 64 each);
       // 128 x 128 tiles run four waves with two blocks per CU.
       constexpr int WGM = TM == 256 ? (TN == 256 ? 2 : 4) : 2;
       constexpr int WGN = TM == 256 ? 4 / (TN == 256 ? 1 : 2) : 2;
-      hipLaunchKernelGGL((gemm_dma_kernel<DT, AMODE, TM, TN, dma_stages<DT, AMODE, TM, TN>(), WGM, WGN>), grid,
-                         dim3(64 * WGM * WGN), 0, s, A);
+      if (bkc)
+        hipLaunchKernelGGL((gemm_dma_kernel<DT, AMODE, TM, TN, dma_stages<DT, AMODE, TM, TN>(), WGM, WGN, 1>), grid,
+                           dim3(64 * WGM * WGN), 0, s, A);
+      else if constexpr (DT != DT_I8)
+        hipLaunchKernelGGL((gemm_dma_kernel<DT, AMODE, TM, TN, dma_stages<DT, AMODE, TM, TN>(), WGM, WGN, 0>), grid,
+                           dim3(64 * WGM * WGN), 0, s, A);
       return hipGetLastError();
     }
     if (full_tiles(pl, A, TM, TN, AMODE)) {

@@ -375,7 +375,7 @@ __device__ __forceinline__ void add_count(int32_t* count, int v) {
 
 template <int DT, int ESZ>
 __global__ void __launch_bounds__(TPB) check1d_kernel(const uint8_t* a, int64_t m, int64_t k, int64_t lda,
-                                                      int N, int M, int op_t, int32_t* count) {
+                                                      int N, int M, int op_t, int vec_ok, int32_t* count) {
   const int64_t groups = k / M;
   const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x;
   int bad = 0;
@@ -384,9 +384,27 @@ __global__ void __launch_bounds__(TPB) check1d_kernel(const uint8_t* a, int64_t 
     if (op_t) { i = t % m; g = t / m; }        // lanes along stored columns
     else { i = t / groups; g = t % groups; }   // lanes along a stored row
     int nz = 0;
-    for (int j = 0; j < M; j++) {
-      const int64_t idx = op_t ? (g * M + j) * lda + i : i * lda + g * M + j;
-      nz += magkey<DT>(load_raw<DT, ESZ>(a, idx)) != 0u;
+    const int gbytes = M * ESZ;
+    if (!op_t && vec_ok && gbytes >= 4) {
+      // the group is M * esize contiguous, naturally aligned bytes: whole-dword loads
+      const uint8_t* p = a + (size_t)(i * lda + g * M) * ESZ;
+      for (int x = 0; x < gbytes; x += 16) {
+        uint32_t w[4] = {0, 0, 0, 0};
+        const int nb = gbytes - x < 16 ? gbytes - x : 16;
+        if (nb == 16) { const u32x4 v = *(const u32x4*)(p + x); w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3]; }
+        else if (nb == 8) { const u32x2 v = *(const u32x2*)(p + x); w[0] = v[0]; w[1] = v[1]; }
+        else w[0] = *(const uint32_t*)(p + x);
+#pragma unroll
+        for (int d = 0; d < 4; d++) {
+          if (ESZ == 2) nz += ((w[d] & 0x7FFFu) != 0u) + (((w[d] >> 16) & 0x7FFFu) != 0u);
+          else nz += ((w[d] & 0xFFu) != 0u) + ((w[d] & 0xFF00u) != 0u) + ((w[d] & 0xFF0000u) != 0u) + ((w[d] & 0xFF000000u) != 0u);
+        }
+      }
+    } else {
+      for (int j = 0; j < M; j++) {
+        const int64_t idx = op_t ? (g * M + j) * lda + i : i * lda + g * M + j;
+        nz += magkey<DT>(load_raw<DT, ESZ>(a, idx)) != 0u;
+      }
     }
     bad = nz > N;
   }
@@ -513,10 +531,11 @@ hipError_t launch_check(const nm_plan& pl, const void* a, int mode, int32_t* cou
   if (total == 0) return hipSuccess;
   const dim3 grid((unsigned)((total + TPB - 1) / TPB));
   const int opt = pl.p.op_a == NM_OP_T;
+  const int vec = (pl.p.lda * pl.esz_ab) % 16 == 0;
   switch (pl.p.type_ab) {
-    case NM_F16: hipLaunchKernelGGL((check1d_kernel<DT_F16, 2>), grid, dim3(TPB), 0, s, ap, pl.p.m, pl.p.k, pl.p.lda, pl.p.nm_n, pl.p.nm_m, opt, count); break;
-    case NM_BF16: hipLaunchKernelGGL((check1d_kernel<DT_BF16, 2>), grid, dim3(TPB), 0, s, ap, pl.p.m, pl.p.k, pl.p.lda, pl.p.nm_n, pl.p.nm_m, opt, count); break;
-    default: hipLaunchKernelGGL((check1d_kernel<DT_I8, 1>), grid, dim3(TPB), 0, s, ap, pl.p.m, pl.p.k, pl.p.lda, pl.p.nm_n, pl.p.nm_m, opt, count); break;
+    case NM_F16: hipLaunchKernelGGL((check1d_kernel<DT_F16, 2>), grid, dim3(TPB), 0, s, ap, pl.p.m, pl.p.k, pl.p.lda, pl.p.nm_n, pl.p.nm_m, opt, vec, count); break;
+    case NM_BF16: hipLaunchKernelGGL((check1d_kernel<DT_BF16, 2>), grid, dim3(TPB), 0, s, ap, pl.p.m, pl.p.k, pl.p.lda, pl.p.nm_n, pl.p.nm_m, opt, vec, count); break;
+    default: hipLaunchKernelGGL((check1d_kernel<DT_I8, 1>), grid, dim3(TPB), 0, s, ap, pl.p.m, pl.p.k, pl.p.lda, pl.p.nm_n, pl.p.nm_m, opt, vec, count); break;
   }
   return hipGetLastError();
 }

@@ -226,12 +226,11 @@ def test_spmm_skinny(dtype, N, M, n, op_b):
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
 @pytest.mark.parametrize("op_a", ["N", "T"])
 @pytest.mark.parametrize("op_b", ["N", "T"])
-@pytest.mark.parametrize("n", [8, 144, 304])
-@pytest.mark.parametrize("tile", ["auto", "256"])
-def test_dense_gemm(dtype, op_a, op_b, n, tile, monkeypatch):
+@pytest.mark.parametrize("m,n,k", [(272, 8, 208), (272, 144, 208), (272, 304, 208), (256, 256, 320), (512, 384, 192)])
+@pytest.mark.parametrize("tile", ["auto", "128", "256"])
+def test_dense_gemm(dtype, op_a, op_b, m, n, k, tile, monkeypatch):
     if tile != "auto":
         monkeypatch.setenv("NM_FORCE_TILE", tile)
-    m, k = 272, 208
     a_log = rand(dtype, (m, k), 41)
     a_st = a_log if op_a == "N" else np.ascontiguousarray(a_log.T)
     b_log = rand(dtype, (k, n), 42)
