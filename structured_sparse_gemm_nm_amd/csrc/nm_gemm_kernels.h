@@ -774,11 +774,25 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ __forceinline__ int swz8(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 __device__ __forceinline__ int swz4(int r) { return (((r >> 2) & 1) << 1) | (((r >> 1) ^ (r >> 3)) & 1); }
 
+// Global -> LDS copies (each lane's 16 or 4 bytes land at the wave's LDS base
+// + lane * size). They are issued from asm so that the compiler does not track
+// them: its own tracking cannot tell the LDS reads of other ring slots apart
+// from the copies in flight and would drain every copy before such a read.
+// The kernels order the copies themselves (per-wave vmcnt waits, then an LDS
+// barrier before a slot is read or refilled). M0 carries the LDS address; it
+// is saved and restored around the copy, with the one wait state a copy needs
+// after M0 is written.
 __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const void*)g, (lds_ptr_t)lds_wave_base, 16, 0, 0);
+  const uint32_t l = (uint32_t)(uintptr_t)(lds_ptr_t)lds_wave_base;
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(save) : "v"(g), "s"(l) : "memory");
 }
 __device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* lds_wave_base) {
-  __builtin_amdgcn_global_load_lds((const void*)g, (lds_ptr_t)lds_wave_base, 4, 0, 0);
+  const uint32_t l = (uint32_t)(uintptr_t)(lds_ptr_t)lds_wave_base;
+  uint32_t save;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+               : "=&s"(save) : "v"(g), "s"(l) : "memory");
 }
 
 // op_b = N (B stored k x n): the B stage keeps the 64 k-rows as stored, rows of
@@ -860,18 +874,25 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
     const int p = 64 * (wave * NMT + j) + lane;
     om[j] = (uint32_t)((p / MDW) * A.mld + (p % MDW) * 4);
   }
-  auto issue = [&](int st) {
+  // Copies of stage st: the wave's L instructions in the order B, A values,
+  // metadata; part `part` of `parts` issues those with index % parts == part,
+  // so a refill can be spread over the fragment groups of a step.
+  auto issue_part = [&](int st, int part, int parts) {
     uint8_t* base = ring + (st % S) * STAGE;
     const uint8_t* bp = bbase + (size_t)st * bstep;
     const uint8_t* ap = abase + (size_t)st * (SP ? 64 : KBYTES);
     const uint8_t* mp = mbase + (size_t)st * MB;
 #pragma unroll
-    for (int j = 0; j < NB; j++) dma16(bp + ob[j], base + A_VAL + A_META + (wave * NB + j) * 1024);
+    for (int j = 0; j < NB; j++)
+      if (j % parts == part) dma16(bp + ob[j], base + A_VAL + A_META + (wave * NB + j) * 1024);
 #pragma unroll
-    for (int j = 0; j < NA; j++) dma16(ap + oa[j], base + (wave * NA + j) * 1024);
+    for (int j = 0; j < NA; j++)
+      if ((NB + j) % parts == part) dma16(ap + oa[j], base + (wave * NA + j) * 1024);
 #pragma unroll
-    for (int j = 0; j < NMT; j++) dma4(mp + om[j], base + A_VAL + (wave * NMT + j) * 256);
+    for (int j = 0; j < NMT; j++)
+      if ((NB + NA + j) % parts == part) dma4(mp + om[j], base + A_VAL + (wave * NMT + j) * 256);
   };
+  auto issue = [&](int st) { issue_part(st, 0, 1); };
 
   acc_t acc[FM][FN];
 #pragma unroll
@@ -897,101 +918,132 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   // column base of this lane's 16-lane group inside a 32-column fragment
   const int nb16 = lane & 16;
 
-#pragma unroll
-  for (int st = 0; st < S - 1; st++)
-    if (st < ksteps) issue(st);
-  for (int ks = 0; ks < ksteps; ks++) {
-    // this wave's copies for step ks are done once at most the later issued
-    // steps (ks+1 .. ks+S-2, as far as they exist) are still outstanding
-    if (ks + S - 2 < ksteps) wait_vmcnt<L * (S - 2)>();
-    else if (S > 3 && ks + S - 3 < ksteps) wait_vmcnt<L * (S > 3 ? S - 3 : 0)>();
-    else wait_vmcnt<0>();
-    lds_barrier();
-    if (ks + S - 1 < ksteps) issue(ks + S - 1);          // refills the slot read in step ks - 1
-    const uint8_t* st = ring + (ks % S) * STAGE;
+  // ---- fragment groups: a step is G groups; group g's LDS reads are issued
+  // before group g-1's matrix instructions. The last group of a step first
+  // waits for the next stage, passes the barrier (which frees the slot of the
+  // current stage) and reads the next step's first group, so the step
+  // boundary does not drain the matrix pipeline. The refill of the freed slot
+  // is spread over the next step's groups: a burst of copies would stall the
+  // issuing waves on the address unit while their matrix work waits. ----
+  constexpr int G = SP ? 2 * FN : 4;
+  static_assert(G % 2 == 0, "fragment slots alternate across steps");
+  ab_t av[2][FM];
+  int iv[2][FM];
+  int ivn[FM];                                           // 16-bit types: second half-step's metadata, staged
+  b2_t bv[2];
+  ab_t bw[2][FN];
+  const int qshift = 16 * q;
+  auto load_group = [&](const uint8_t* st, int g) {
     if constexpr (SP) {
-      // Stream: per half-step, A fragments once, then B column tiles one by
-      // one; the next group's LDS reads are issued before the current group's
-      // matrix instructions.
       const uint8_t* la = st;
       const uint8_t* lm = st + A_VAL;
       const uint8_t* lb = st + A_VAL + A_META;
-      ab_t av[2][FM];
-      int iv[2][FM];
-      b2_t bv[2];
-      auto load_a = [&](int h) {
+      const int h = g / FN, fn = g % FN;
+      if (fn == 0) {
 #pragma unroll
         for (int fm = 0; fm < FM; fm++) {
           const int row = wm0 + fm * 32 + l32;
           const int c = 2 * h + q;
           av[h][fm] = *(const ab_t*)(la + row * 64 + ((c ^ swz4(row)) << 4));
-          iv[h][fm] = ESZ == 2 ? (int)*(const uint16_t*)(lm + row * MB + h * (MB / 2) + 2 * q)
-                               : (int)*(const uint32_t*)(lm + row * MB + h * (MB / 2) + 4 * q);
+          if constexpr (ESZ == 2) {
+            // one 8-byte read per row serves both half-steps and both lane
+            // halves; the lane's 16 bits are selected at use (shift by 16 q)
+            if (h == 0) {
+              typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+              const u32x2_t mw = *(const u32x2_t*)(lm + row * MB);
+              iv[0][fm] = (int)mw[0];
+              ivn[fm] = (int)mw[1];
+            } else {
+              iv[1][fm] = ivn[fm];
+            }
+          } else {
+            iv[h][fm] = (int)*(const uint32_t*)(lm + row * MB + h * (MB / 2) + 4 * q);
+          }
         }
-      };
-      auto load_b = [&](int slot, int h, int fn) {
-        if constexpr (BKC) {
-          const int row = wn0 + fn * 32 + l32;
-          bv[slot] = concat<DT>(bchunk(lb, row, 4 * h + q), bchunk(lb, row, 4 * h + 2 + q));
-        } else {
-          // k = 32h + 8q + {0..3, 4..7, 16..19, 20..23}
-          const int cb = wn0 + fn * 32 + nb16;
-          const int kb = 32 * h + 8 * q;
-          const short4_t r0 = btr4(lb, kb, cb), r1 = btr4(lb, kb + 4, cb), r2 = btr4(lb, kb + 16, cb),
-                         r3 = btr4(lb, kb + 20, cb);
-          typedef short short16_t __attribute__((ext_vector_type(16)));
-          const short16_t v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3],
-                               r2[0], r2[1], r2[2], r2[3], r3[0], r3[1], r3[2], r3[3]};
-          bv[slot] = __builtin_bit_cast(b2_t, v);
-        }
-      };
-      load_a(0);
-      load_b(0, 0, 0);
-#pragma unroll
-      for (int h = 0; h < 2; h++) {
-#pragma unroll
-        for (int fn = 0; fn < FN; fn++) {
-          const int g = h * FN + fn;                     // group index: B fragment slot g % 2
-          __builtin_amdgcn_sched_barrier(0);
-          if (fn + 1 < FN) load_b((g + 1) % 2, h, fn + 1);
-          else if (h == 0) { load_a(1); load_b((g + 1) % 2, 1, 0); }
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int fm = 0; fm < FM; fm++) acc[fm][fn] = smfmac32<DT>(av[h][fm], bv[g % 2], acc[fm][fn], iv[h][fm]);
-        }
+      }
+      if constexpr (BKC) {
+        const int row = wn0 + fn * 32 + l32;
+        bv[g % 2] = concat<DT>(bchunk(lb, row, 4 * h + q), bchunk(lb, row, 4 * h + 2 + q));
+      } else {
+        // k = 32h + 8q + {0..3, 4..7, 16..19, 20..23}
+        const int cb = wn0 + fn * 32 + nb16;
+        const int kb = 32 * h + 8 * q;
+        const short4_t r0 = btr4(lb, kb, cb), r1 = btr4(lb, kb + 4, cb), r2 = btr4(lb, kb + 16, cb),
+                       r3 = btr4(lb, kb + 20, cb);
+        typedef short short16_t __attribute__((ext_vector_type(16)));
+        const short16_t v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3],
+                             r2[0], r2[1], r2[2], r2[3], r3[0], r3[1], r3[2], r3[3]};
+        bv[g % 2] = __builtin_bit_cast(b2_t, v);
       }
     } else {
       const uint8_t* la = st;
       const uint8_t* lb = st + A_VAL;
-      ab_t av[2][FM], bw[2][FN];
-      auto load_d = [&](int slot, int i) {
 #pragma unroll
-        for (int fm = 0; fm < FM; fm++) av[slot][fm] = bchunk(la, wm0 + fm * 32 + l32, 2 * i + q);
+      for (int fm = 0; fm < FM; fm++) av[g % 2][fm] = bchunk(la, wm0 + fm * 32 + l32, 2 * g + q);
 #pragma unroll
-        for (int fn = 0; fn < FN; fn++) {
-          if constexpr (BKC) {
-            bw[slot][fn] = bchunk(lb, wn0 + fn * 32 + l32, 2 * i + q);
-          } else {
-            // k = 16i + 8q + 0..7
-            const int cb = wn0 + fn * 32 + nb16;
-            const short4_t r0 = btr4(lb, 16 * i + 8 * q, cb), r1 = btr4(lb, 16 * i + 8 * q + 4, cb);
-            typedef short short8_t __attribute__((ext_vector_type(8)));
-            const short8_t v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
-            bw[slot][fn] = __builtin_bit_cast(ab_t, v);
-          }
+      for (int fn = 0; fn < FN; fn++) {
+        if constexpr (BKC) {
+          bw[g % 2][fn] = bchunk(lb, wn0 + fn * 32 + l32, 2 * g + q);
+        } else {
+          // k = 16g + 8q + 0..7
+          const int cb = wn0 + fn * 32 + nb16;
+          const short4_t r0 = btr4(lb, 16 * g + 8 * q, cb), r1 = btr4(lb, 16 * g + 8 * q + 4, cb);
+          typedef short short8_t __attribute__((ext_vector_type(8)));
+          const short8_t v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+          bw[g % 2][fn] = __builtin_bit_cast(ab_t, v);
         }
-      };
-      load_d(0, 0);
-#pragma unroll
-      for (int i = 0; i < 4; i++) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (i + 1 < 4) load_d((i + 1) % 2, i + 1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int fn = 0; fn < FN; fn++)
-#pragma unroll
-          for (int fm = 0; fm < FM; fm++) acc[fm][fn] = mfma32<DT>(av[i % 2][fm], bw[i % 2][fn], acc[fm][fn]);
       }
+    }
+  };
+  auto compute_group = [&](int g) {
+    if constexpr (SP) {
+      const int h = g / FN, fn = g % FN;
+#pragma unroll
+      for (int fm = 0; fm < FM; fm++)
+        acc[fm][fn] = smfmac32<DT>(av[h][fm], bv[g % 2], acc[fm][fn],
+                                   ESZ == 2 ? (int)((uint32_t)iv[h][fm] >> qshift) : iv[h][fm]);
+    } else {
+#pragma unroll
+      for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+        for (int fm = 0; fm < FM; fm++) acc[fm][fn] = mfma32<DT>(av[g % 2][fm], bw[g % 2][fn], acc[fm][fn]);
+    }
+  };
+
+  // waits until at most n (0 <= n <= S-1) of this wave's issued stages are outstanding
+  static_assert(L * (S - 1) <= 63, "vmcnt range");
+  auto wait_stages = [&](int n) {
+    if (S > 3 && n >= 3) wait_vmcnt<L * (S > 3 ? 3 : 0)>();
+    else if (n >= 2) wait_vmcnt<L * 2>();
+    else if (n == 1) wait_vmcnt<L>();
+    else wait_vmcnt<0>();
+  };
+  // every slot is filled up front; stage 0 is complete once at most stages
+  // 1 .. min(S-1, ksteps-1) are outstanding
+#pragma unroll
+  for (int st = 0; st < S; st++)
+    if (st < ksteps) issue(st);
+  wait_stages(min(S - 1, ksteps - 1));
+  lds_barrier();
+  load_group(ring, 0);
+  for (int ks = 0; ks < ksteps; ks++) {
+    const uint8_t* st = ring + (ks % S) * STAGE;
+#pragma unroll
+    for (int g = 0; g < G; g++) {
+      __builtin_amdgcn_sched_barrier(0);
+      // stage ks+S-1 goes into the slot freed at the end of step ks-1
+      if (ks >= 1 && ks + S - 1 < ksteps) issue_part(ks + S - 1, g, G);
+      if (g + 1 < G) {
+        load_group(st, g + 1);
+      } else if (ks + 1 < ksteps) {
+        // issued so far: stages up to min(ks+S-1, ksteps-1); stage ks+1 is
+        // complete once at most stages ks+2 .. min(ks+S-1, ksteps-1) are outstanding
+        wait_stages(min(S - 2, ksteps - ks - 2));
+        lds_barrier();                                   // every wave is done reading stage ks
+        load_group(ring + ((ks + 1) % S) * STAGE, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      compute_group(g);
     }
   }
 
