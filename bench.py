@@ -60,11 +60,41 @@ def parse():
     ap.add_argument("--workload", default="bert", choices=sorted(WORKLOAD_SETS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain %d MiB elementwise copy (y = -x) %d times (for counter calibration)" % (CAL_MIB, CAL_REPS))
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic_<workload>.md")
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
+                    help="turn a rocprofv3 --kernel-trace --stats run into a profiles/ summary")
+    ap.add_argument("--command", default="", help="the command that produced the runs (recorded in summaries)")
+    ap.add_argument("--bench-log", default=None, help="stdout of the traced bench run (its JSON line is compared)")
     return ap.parse_args()
+
+
+CAL_MIB, CAL_REPS = 1024, 3
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def source_fingerprint():
+    """sha256 over the library's kernel and host sources: counters taken on other sources do not apply."""
+    import hashlib
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def main():
     args = parse()
+    if args.summarize_counters:
+        summarize_counters(args)
+        return
+    if args.summarize_trace:
+        summarize_trace(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this library's hot path is single-GPU "
               "(sharding is described in DESIGN.md, not implemented); got --gpus %d" % args.gpus, file=sys.stderr)
@@ -113,21 +143,60 @@ def main():
         g["host"] = dict(a=a, b=bs, c=c)
         gemms.append(g)
 
-    # events per SpMM launch (measured on the stream the kernels run on)
+    # The step calls the C ABI with arguments marshalled once, so that the host
+    # enqueues well ahead of the GPU and the events around each SpMM launch
+    # (recorded on the stream the kernels run on) time the kernel, not host gaps.
+    import ctypes
+    L = nm.lib()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr()) if t is not None else None
+    calls = []            # (callable, args, spmm key or None)
+    for g in gemms:
+        h = g["plan"].handle
+        mode = nm.MODES[g["mode"]]
+        g["_ab"] = (ctypes.c_float(g["w"]["alpha"]), ctypes.c_float(g["w"]["beta"]))
+        calls.append((L.nm_prune, (h, P(g["A"]), P(g["Ap"]), mode, None, sp), None))
+        calls.append((L.nm_prune_check, (h, P(g["Ap"]), mode, P(g["cnt"]), sp), None))
+        calls.append((L.nm_compress, (h, P(g["Ap"]), P(g["vals"]), P(g["meta"]), sp), None))
+        for ob in g["layouts"]:
+            calls.append((L.nm_spmm, (g["plans"][ob].handle, ctypes.byref(g["_ab"][0]), P(g["vals"]), P(g["meta"]),
+                                      P(g["B"][ob]), ctypes.byref(g["_ab"][1]), P(g["C"]), P(g["D"][ob]), None, sp),
+                          (g["label"], ob)))
+        calls.append((L.nm_decompress, (h, P(g["vals"]), P(g["meta"]), P(g["Ad"]), sp), None))
+
+    n_spmm = sum(1 for c in calls if c[2] is not None)
+    pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(n_spmm * args.steps)]              # created before the timed region
+    empty_pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(args.steps)]
+    empty = []
+
     def step(ev=None):
-        for g in gemms:
-            nm.nm_prune(g["plan"], g["A"], g["Ap"], g["mode"])
-            nm.nm_prune_check(g["plan"], g["Ap"], g["mode"], g["cnt"])
-            nm.nm_compress(g["plan"], g["Ap"], g["vals"], g["meta"])
-            for ob in g["layouts"]:
-                if ev is not None:
-                    e0 = torch.cuda.Event(enable_timing=True); e0.record(stream)
-                nm.nm_spmm(g["plans"][ob], g["w"]["alpha"], g["vals"], g["meta"], g["B"][ob], g["w"]["beta"],
-                           g["C"], g["D"][ob])
-                if ev is not None:
-                    e1 = torch.cuda.Event(enable_timing=True); e1.record(stream)
-                    ev.append((g, ob, e0, e1))
-            nm.nm_decompress(g["plan"], g["vals"], g["meta"], g["Ad"])
+        if ev is not None:
+            # an event pair around nothing: the events' own cost on the queue
+            e0, e1 = empty_pool[len(empty)]
+            e0.record(stream)
+            e1.record(stream)
+            empty.append((e0, e1))
+        for fn, a, key in calls:
+            if ev is not None and key is not None:
+                e0, e1 = pool[len(ev)]
+                e0.record(stream)
+                st = fn(*a)
+                e1.record(stream)
+                ev.append((key, e0, e1))
+            else:
+                st = fn(*a)
+            if st != 0:
+                raise nm.NmError(st, L.nm_last_error().decode())
+
+    if args.copy_calibration:
+        src = torch.ones(CAL_MIB << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(CAL_REPS):
+            torch.neg(src, out=dst)           # reads and writes CAL_MIB MiB with 16-byte vector accesses
+        torch.cuda.synchronize()
+        del src, dst
 
     for _ in range(args.warmup):
         step()
@@ -140,8 +209,10 @@ def main():
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step(events)
+    t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
+    host_ms_per_step = (t_enq - t0) * 1e3 / args.steps
     ms_per_step = (t1 - t0) * 1e3 / args.steps
 
     def flops_dense_eq(g):
@@ -152,18 +223,19 @@ def main():
 
     # per-launch SpMM durations
     per = {}
-    for g, ob, e0, e1 in events:
-        key = (g["label"], ob)
+    for key, e0, e1 in events:
         per.setdefault(key, []).append(e0.elapsed_time(e1))
-    spmm_ms = {k: float(np.mean(v)) for k, v in per.items()}
+    event_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in empty]))
+    raw_ms = {k: float(np.median(v)) for k, v in per.items()}
+    spmm_ms = {k: max(v - event_ms, 1e-6) for k, v in raw_ms.items()}     # launch duration, events' cost removed
     spmm_total_ms = sum(spmm_ms[(g["label"], ob)] for g in gemms for ob in g["layouts"])
     spmm_only_tflops = step_flops / (spmm_total_ms * 1e-3) / 1e12
 
-    # dominant kernel: the SpMM kernel instantiation (kernel name + layout) with the most time
+    # dominant kernel: the device kernel (as the profiler names it) with the most SpMM time
     kern = {}
     for g in gemms:
         for ob in g["layouts"]:
-            kk = (g["plans"][ob].kernel_name, ob)
+            kk = g["plans"][ob].spmm_kernel
             d = kern.setdefault(kk, dict(ms=0.0, flops=0.0, bytes=0.0, launches=0, dtype=g["dtype"]))
             d["ms"] += spmm_ms[(g["label"], ob)]
             d["launches"] += 1
@@ -186,8 +258,16 @@ def main():
         achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
-    roofline["kernel"] = "%s (op_b=%s)" % dom_key
+    roofline["kernel"] = dom_key
     roofline["launch_ms"] = round(avg_ms, 5)
+    roofline["launch_ms_method"] = ("median over the timed steps of the HIP-event interval around each launch, less the "
+                                    "median interval of an empty event pair in the same steps (%.5f ms)" % event_ms)
+    roofline["launches_per_step"] = dom["launches"]
+    traffic = load_traffic(args.workload, dom_key)
+    if traffic is not None:
+        roofline["traffic"] = traffic["bytes_per_launch"]
+        roofline["traffic_over_algorithmic"] = round(traffic["bytes_per_launch"] / avg_bytes, 3)
+        roofline["traffic_note"] = traffic["note"]
 
     # dense comparator, same shapes, same layouts
     dense = {}
@@ -237,6 +317,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "host_enqueue_ms_per_step": round(host_ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -251,6 +332,110 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def load_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, if taken on these sources."""
+    path = os.path.join(PROFILES, "traffic_%s.md" % workload)
+    if not os.path.exists(path):
+        return None
+    rec = None
+    for line in open(path):
+        if line.startswith("record: "):
+            rec = json.loads(line[len("record: "):])
+    if rec is None or rec.get("sources") != source_fingerprint() or kernel not in rec["kernels"]:
+        return None
+    k = rec["kernels"][kernel]
+    b = k["fetch_kib"] * 1024 * rec["fetch_scale"] + k["write_kib"] * 1024 * rec["write_scale"]
+    return {"bytes_per_launch": round(b), "note": "FETCH_SIZE + WRITE_SIZE per dispatch (%d dispatches), scaled by "
+            "a %d MiB elementwise copy's readings (x%.3f, x%.3f); %s" % (k["dispatches"], CAL_MIB, rec["fetch_scale"],
+                                                             rec["write_scale"], os.path.relpath(path, ROOT))}
+
+
+def _read_counter_csv(d, counter):
+    """{kernel name: [value per dispatch]} from a rocprofv3 --pmc csv output directory."""
+    import csv
+    import glob
+    out = {}
+    for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            if r.get("Counter_Name") != counter:
+                continue
+            out.setdefault(r["Kernel_Name"], {}).setdefault(r.get("Dispatch_Id", len(out)), 0.0)
+            out[r["Kernel_Name"]][r.get("Dispatch_Id")] += float(r["Counter_Value"])
+    return {k: list(v.values()) for k, v in out.items()}
+
+
+def summarize_counters(args):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of every kernel, with the copy calibration."""
+    fetch = _read_counter_csv(args.summarize_counters[0], "FETCH_SIZE")
+    write = _read_counter_csv(args.summarize_counters[1], "WRITE_SIZE")
+    cal_bytes = CAL_MIB * 1048576.0
+
+    def copy_kernel(tab):
+        cands = [k for k, v in tab.items() if "neg" in k.lower() and len(v) >= CAL_REPS]
+        if not cands:
+            raise SystemExit("no calibration copy with %d dispatches in the counter runs (run with --copy-calibration)" % CAL_REPS)
+        return max(cands, key=lambda k: np.median(tab[k]))
+    ck = copy_kernel(fetch)
+    f_scale = cal_bytes / (np.median(fetch[ck]) * 1024)
+    w_scale = cal_bytes / (np.median(write[copy_kernel(write)]) * 1024)
+    kernels = {}
+    for k in fetch:
+        if k in write and "nm::" in k:
+            kernels[k] = {"fetch_kib": round(float(np.mean(fetch[k])), 1), "write_kib": round(float(np.mean(write[k])), 1),
+                          "dispatches": len(fetch[k])}
+    rec = {"workload": args.workload, "sources": source_fingerprint(), "fetch_scale": round(float(f_scale), 4),
+           "write_scale": round(float(w_scale), 4), "copy_kernel": ck[:100], "kernels": kernels}
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, "traffic_%s.md" % args.workload)
+    with open(path, "w") as fh:
+        fh.write("# HBM traffic per dispatch: %s\n\n" % WORKLOAD_DESC[args.workload])
+        fh.write("Commands (each a separate rocprofv3 run of the same bench command):\n\n")
+        for line in args.command.split(" ;; "):
+            fh.write("    %s\n" % line)
+        fh.write("\nCalibration: a plain %d MiB elementwise copy y = -x (`%s`) read FETCH_SIZE %.0f KiB and WRITE_SIZE %.0f KiB "
+                 "per dispatch (median of %d); scale factors %.4f (fetch) and %.4f (write).\n\n"
+                 % (CAL_MIB, ck[:80], np.median(fetch[ck]), np.median(write[copy_kernel(write)]), CAL_REPS, f_scale, w_scale))
+        fh.write("| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | scaled MB/dispatch |\n|---|---|---|---|---|\n")
+        for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["fetch_kib"]):
+            mb = (v["fetch_kib"] * f_scale + v["write_kib"] * w_scale) * 1024 / 1e6
+            fh.write("| `%s` | %d | %.1f | %.1f | %.2f |\n" % (k, v["dispatches"], v["fetch_kib"], v["write_kib"], mb))
+        fh.write("\nSource fingerprint %s: bench.py reports these figures only while the library sources match.\n\n"
+                 % rec["sources"])
+        fh.write("record: %s\n" % json.dumps(rec))
+    print("wrote", path)
+
+
+def summarize_trace(args):
+    """Kernel-trace statistics (rocprofv3 --stats) as a short text summary."""
+    import csv
+    import glob
+    rows = []
+    for f in glob.glob(os.path.join(args.summarize_trace, "**", "*kernel_stats.csv"), recursive=True):
+        rows += list(csv.DictReader(open(f)))
+    if not rows:
+        raise SystemExit("no kernel_stats.csv under %s" % args.summarize_trace)
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, "kernel_trace_%s.md" % args.workload)
+    with open(path, "w") as fh:
+        fh.write("# Kernel trace: %s\n\nCommand:\n\n    %s\n\n" % (WORKLOAD_DESC[args.workload], args.command))
+        fh.write("| kernel | calls | total ms | average us | share % |\n|---|---|---|---|---|\n")
+        for r in rows[:25]:
+            fh.write("| `%s` | %s | %.3f | %.2f | %.1f |\n" % (r["Name"][:120], r["Calls"], float(r["TotalDurationNs"]) / 1e6,
+                                                          float(r["AverageNs"]) / 1e3, float(r["Percentage"])))
+        if args.bench_log:
+            line = [l for l in open(args.bench_log) if l.startswith("{")][-1]
+            roof = json.loads(line)["roofline"]
+            prof = {r["Name"]: float(r["AverageNs"]) / 1e3 for r in rows}
+            avg = prof.get(roof["kernel"])
+            fh.write("\nThe bench line of this same run names `%s` as its dominant kernel: HIP-event median %.2f us "
+                     "per launch over the timed steps; rocprofv3 average over all its dispatches %s us%s.\n"
+                     % (roof["kernel"], roof["launch_ms"] * 1e3, "%.2f" % avg if avg else "n/a",
+                        " (ratio %.3f)" % (roof["launch_ms"] * 1e3 / avg) if avg else ""))
+            fh.write("\nBench line: `%s`\n" % line.strip()[:600])
+    print("wrote", path)
 
 
 def spmm_bytes(g):

@@ -175,6 +175,14 @@ nm_status_t nm_dense_gemm(nm_plan_t plan, const float* alpha, const void* dA, co
 /* Name of the SpMM kernel the plan dispatches to (static string). */
 const char* nm_plan_kernel_name(nm_plan_t plan);
 
+/* The device kernel nm_spmm launches for this plan (whenever m, n > 0), named
+   as profilers print it: demangled, e.g. "void nm::gemm_dma_kernel<0, 0, 256,
+   256, 3, 2, 4, 1>(nm::GemmArgs)". The first call runs the same host logic as
+   nm_spmm without launching anything and caches the result in the plan; the
+   string lives as long as the plan. Needs the HIP runtime to resolve the name
+   ("unknown" otherwise). Calls on one plan must not run concurrently. */
+const char* nm_plan_spmm_kernel(nm_plan_t plan);
+
 /* Static text for a status code. */
 const char* nm_status_string(nm_status_t status);
 

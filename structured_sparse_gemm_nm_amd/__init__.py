@@ -67,6 +67,7 @@ def lib():
         L.nm_spmm.restype = st; L.nm_spmm.argtypes = [P, FP, P, P, P, FP, P, P, P, P]
         L.nm_dense_gemm.restype = st; L.nm_dense_gemm.argtypes = [P, FP, P, P, FP, P, P, P]
         L.nm_plan_kernel_name.restype = ctypes.c_char_p; L.nm_plan_kernel_name.argtypes = [P]
+        L.nm_plan_spmm_kernel.restype = ctypes.c_char_p; L.nm_plan_spmm_kernel.argtypes = [P]
         L.nm_status_string.restype = ctypes.c_char_p; L.nm_status_string.argtypes = [st]
         L.nm_last_error.restype = ctypes.c_char_p; L.nm_last_error.argtypes = []
         L.nm_version.restype = I32; L.nm_version.argtypes = []
@@ -131,6 +132,11 @@ class Plan:
     @property
     def k(self):
         return self.problem.k
+
+    @property
+    def spmm_kernel(self):
+        """Device kernel nm_spmm launches for this plan (profiler naming)."""
+        return lib().nm_plan_spmm_kernel(self.handle).decode()
 
     def destroy(self):
         if self.handle is not None:
@@ -214,6 +220,10 @@ def nm_dense_gemm(plan, alpha, dA, dB, beta, dC, dD, stream=None):
     a, b = ctypes.c_float(alpha), ctypes.c_float(beta)
     _check(lib().nm_dense_gemm(plan.handle, ctypes.byref(a), _ptr(dA), _ptr(dB), ctypes.byref(b), _ptr(dC), _ptr(dD),
                                _stream(stream)))
+
+
+def nm_plan_spmm_kernel(plan):
+    return plan.spmm_kernel
 
 
 def nm_status_string(status):

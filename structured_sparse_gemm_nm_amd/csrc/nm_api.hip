@@ -8,6 +8,9 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <cxxabi.h>
+#include <stdlib.h>
+
 #include <new>
 #include <string>
 
@@ -18,6 +21,11 @@ namespace nm {
 static thread_local std::string g_last_error;
 
 void set_error(const std::string& msg) { g_last_error = msg; }
+
+LaunchProbe& launch_probe() {
+  thread_local LaunchProbe probe;
+  return probe;
+}
 
 static nm_status_t fail(nm_status_t st, const std::string& msg) {
   set_error(msg);
@@ -112,6 +120,16 @@ nm_status_t nm_plan_init(nm_plan_t* plan, const nm_problem_t* p) {
   pl->vld = (nvals + per16 - 1) / per16 * per16;
   const int64_t mbytes = (p->k / M * N * b + 7) / 8;
   pl->mld = (mbytes + 15) / 16 * 16;
+  // benchmark-sweep overrides (read once here, not per launch)
+  pl->force_tile = -1;
+  if (const char* f = getenv("NM_FORCE_TILE")) {
+    if (!strcmp(f, "128")) pl->force_tile = nm::T128;
+    else if (!strcmp(f, "256x128")) pl->force_tile = nm::T256x128;
+    else if (!strcmp(f, "256")) pl->force_tile = nm::T256;
+  }
+  pl->no_dma = getenv("NM_NO_DMA") != nullptr;
+  pl->no_dma_nn = getenv("NM_NO_DMA_NN") != nullptr;
+  pl->old_skinny = getenv("NM_OLD_SKINNY") != nullptr;
   // kernel choice
   if (p->n <= 16) pl->kernel = K_SKINNY;
   else if (N == 2 && M == 4) pl->kernel = K_SMFMAC_24;
@@ -124,6 +142,31 @@ nm_status_t nm_plan_init(nm_plan_t* plan, const nm_problem_t* p) {
 nm_status_t nm_plan_destroy(nm_plan_t plan) {
   delete plan;
   return NM_OK;
+}
+
+const char* nm_plan_spmm_kernel(nm_plan_t plan) {
+  if (!plan) return "none";
+  if (plan->spmm_symbol.empty()) {
+    nm::LaunchProbe& pr = nm::launch_probe();
+    pr.armed = true;
+    pr.kernel = nullptr;
+    switch (plan->kernel) {
+      case K_SMFMAC_24: (void)launch_spmm_smfmac(*plan, 1.0f, nullptr, nullptr, nullptr, 0.0f, nullptr, nullptr, 0); break;
+      case K_GATHER_MFMA: (void)launch_spmm_gather(*plan, 1.0f, nullptr, nullptr, nullptr, 0.0f, nullptr, nullptr, 0); break;
+      default: (void)launch_spmm_skinny(*plan, 1.0f, nullptr, nullptr, nullptr, 0.0f, nullptr, nullptr, 0); break;
+    }
+    pr.armed = false;
+    std::string name = "unknown";
+    const char* raw = pr.kernel ? hipKernelNameRefByPtr(pr.kernel, nullptr) : nullptr;
+    if (raw) {
+      int st = 0;
+      char* dm = abi::__cxa_demangle(raw, nullptr, nullptr, &st);
+      name = (st == 0 && dm) ? dm : raw;
+      free(dm);
+    }
+    plan->spmm_symbol = name;
+  }
+  return plan->spmm_symbol.c_str();
 }
 
 const char* nm_plan_kernel_name(nm_plan_t plan) {

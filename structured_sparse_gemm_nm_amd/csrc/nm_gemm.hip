@@ -317,12 +317,12 @@ static hipError_t launch_skinny2_np(const nm_plan& pl, const GemmArgs& A, hipStr
   const dim3 grid((unsigned)blocks);
   const int bt = pl.p.op_b == NM_OP_T;
   const int64_t n = A.n;
-  if (n <= 1) hipLaunchKernelGGL((skinny2_kernel<DT, 1, DENSE_A>), grid, dim3(NTH), 0, s, A, bt);
-  else if (n <= 2) hipLaunchKernelGGL((skinny2_kernel<DT, 2, DENSE_A>), grid, dim3(NTH), 0, s, A, bt);
-  else if (n <= 4) hipLaunchKernelGGL((skinny2_kernel<DT, 4, DENSE_A>), grid, dim3(NTH), 0, s, A, bt);
-  else if (n <= 8) hipLaunchKernelGGL((skinny2_kernel<DT, 8, DENSE_A>), grid, dim3(NTH), 0, s, A, bt);
-  else hipLaunchKernelGGL((skinny2_kernel<DT, 16, DENSE_A>), grid, dim3(NTH), 0, s, A, bt);
-  return hipGetLastError();
+  if (n <= 1) NM_LAUNCH((skinny2_kernel<DT, 1, DENSE_A>), grid, dim3(NTH), 0, s, A, bt);
+  else if (n <= 2) NM_LAUNCH((skinny2_kernel<DT, 2, DENSE_A>), grid, dim3(NTH), 0, s, A, bt);
+  else if (n <= 4) NM_LAUNCH((skinny2_kernel<DT, 4, DENSE_A>), grid, dim3(NTH), 0, s, A, bt);
+  else if (n <= 8) NM_LAUNCH((skinny2_kernel<DT, 8, DENSE_A>), grid, dim3(NTH), 0, s, A, bt);
+  else NM_LAUNCH((skinny2_kernel<DT, 16, DENSE_A>), grid, dim3(NTH), 0, s, A, bt);
+  return launch_status();
 }
 
 // The streamed small-n kernel needs each group's kept values to be one
@@ -337,7 +337,7 @@ static bool skinny2_ok(const nm_plan& pl, bool dense_a) {
 
 template <bool DENSE_A>
 static hipError_t launch_skinny_dt(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
-  if (skinny2_ok(pl, DENSE_A) && !getenv("NM_OLD_SKINNY")) {
+  if (skinny2_ok(pl, DENSE_A) && !pl.old_skinny) {
     switch (pl.p.type_ab) {
       case NM_F16: return launch_skinny2_np<DT_F16, DENSE_A>(pl, A, s);
       case NM_BF16: return launch_skinny2_np<DT_BF16, DENSE_A>(pl, A, s);
@@ -347,11 +347,11 @@ static hipError_t launch_skinny_dt(const nm_plan& pl, const GemmArgs& A, hipStre
   const dim3 grid((unsigned)((A.m + 4 * SK_ROWS_PER_WAVE - 1) / (4 * SK_ROWS_PER_WAVE)));
   const int bt = pl.p.op_b == NM_OP_T, at = pl.p.op_a == NM_OP_T;
   switch (pl.p.type_ab) {
-    case NM_F16: hipLaunchKernelGGL((skinny_kernel<DT_F16, DENSE_A>), grid, dim3(NTH), 0, s, A, bt, at); break;
-    case NM_BF16: hipLaunchKernelGGL((skinny_kernel<DT_BF16, DENSE_A>), grid, dim3(NTH), 0, s, A, bt, at); break;
-    default: hipLaunchKernelGGL((skinny_kernel<DT_I8, DENSE_A>), grid, dim3(NTH), 0, s, A, bt, at); break;
+    case NM_F16: NM_LAUNCH((skinny_kernel<DT_F16, DENSE_A>), grid, dim3(NTH), 0, s, A, bt, at); break;
+    case NM_BF16: NM_LAUNCH((skinny_kernel<DT_BF16, DENSE_A>), grid, dim3(NTH), 0, s, A, bt, at); break;
+    default: NM_LAUNCH((skinny_kernel<DT_I8, DENSE_A>), grid, dim3(NTH), 0, s, A, bt, at); break;
   }
-  return hipGetLastError();
+  return launch_status();
 }
 
 hipError_t launch_spmm_smfmac(const nm_plan& pl, float alpha, const void* vals, const void* meta, const void* b,

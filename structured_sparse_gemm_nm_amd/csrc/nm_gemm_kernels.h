@@ -1076,15 +1076,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
 // three stages fits LDS). The general N:M gather path always uses 128 x 128 (its
 // staging needs LDS). NM_FORCE_TILE=128|256x128|256 pins the choice and
 // NM_NO_DMA=1 disables the LDS-DMA kernel (benchmark sweeps only).
-enum TileCfg { T128 = 0, T256x128 = 1, T256 = 2 };
 inline int pick_tile(const nm_plan& pl, int amode) {
   if (amode == A_GATHER) return T128;
-  const char* f = getenv("NM_FORCE_TILE");
-  if (f) {
-    if (!strcmp(f, "128")) return T128;
-    if (!strcmp(f, "256x128")) return T256x128;
-    if (!strcmp(f, "256")) return amode == A_DENSE ? T256x128 : T256;
-  }
+  if (pl.force_tile == T128 || pl.force_tile == T256x128) return pl.force_tile;   // -1: automatic
+  if (pl.force_tile == T256) return amode == A_DENSE ? T256x128 : T256;
   const int64_t t256 = ((pl.p.m + 255) / 256) * ((pl.p.n + 255) / 256);
   const int64_t t256x128 = ((pl.p.m + 255) / 256) * ((pl.p.n + 127) / 128);
   if (t256 >= 192 && amode != A_DENSE) return T256;
@@ -1123,33 +1118,33 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
   const bool bkc = pl.p.op_b == NM_OP_T;
   const bool akc = pl.p.op_a == NM_OP_N || AMODE != A_DENSE;
   if constexpr (AMODE != A_GATHER) {
-    const bool dma_nn = !bkc && DT != DT_I8 && !getenv("NM_NO_DMA_NN");
-    if (full_tiles(pl, A, TM, TN, AMODE) && (bkc || dma_nn) && akc && !getenv("NM_NO_DMA")) {
+    const bool dma_nn = !bkc && DT != DT_I8 && !pl.no_dma_nn;
+    if (full_tiles(pl, A, TM, TN, AMODE) && (bkc || dma_nn) && akc && !pl.no_dma) {
       // 256-row tiles run eight waves (two per SIMD, 128 x 64 or 64 x 64 each);
       // 128 x 128 tiles run four waves with two blocks per CU.
       constexpr int WGM = TM == 256 ? (TN == 256 ? 2 : 4) : 2;
       constexpr int WGN = TM == 256 ? 4 / (TN == 256 ? 1 : 2) : 2;
       if (bkc)
-        hipLaunchKernelGGL((gemm_dma_kernel<DT, AMODE, TM, TN, dma_stages<DT, AMODE, TM, TN>(), WGM, WGN, 1>), grid,
+        NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, dma_stages<DT, AMODE, TM, TN>(), WGM, WGN, 1>), grid,
                            dim3(64 * WGM * WGN), 0, s, A);
       else if constexpr (DT != DT_I8)
-        hipLaunchKernelGGL((gemm_dma_kernel<DT, AMODE, TM, TN, dma_stages<DT, AMODE, TM, TN>(), WGM, WGN, 0>), grid,
+        NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, dma_stages<DT, AMODE, TM, TN>(), WGM, WGN, 0>), grid,
                            dim3(64 * WGM * WGN), 0, s, A);
-      return hipGetLastError();
+      return launch_status();
     }
     if (full_tiles(pl, A, TM, TN, AMODE)) {
-      if (bkc && akc) hipLaunchKernelGGL((gemm_fast_kernel<DT, AMODE, 1, 1, TM, TN>), grid, dim3(NTH), 0, s, A);
-      else if (!bkc && akc) hipLaunchKernelGGL((gemm_fast_kernel<DT, AMODE, 0, 1, TM, TN>), grid, dim3(NTH), 0, s, A);
-      else if (AMODE == A_DENSE && bkc) hipLaunchKernelGGL((gemm_fast_kernel<DT, A_DENSE, 1, 0, TM, TN>), grid, dim3(NTH), 0, s, A);
-      else if (AMODE == A_DENSE) hipLaunchKernelGGL((gemm_fast_kernel<DT, A_DENSE, 0, 0, TM, TN>), grid, dim3(NTH), 0, s, A);
-      return hipGetLastError();
+      if (bkc && akc) NM_LAUNCH((gemm_fast_kernel<DT, AMODE, 1, 1, TM, TN>), grid, dim3(NTH), 0, s, A);
+      else if (!bkc && akc) NM_LAUNCH((gemm_fast_kernel<DT, AMODE, 0, 1, TM, TN>), grid, dim3(NTH), 0, s, A);
+      else if (AMODE == A_DENSE && bkc) NM_LAUNCH((gemm_fast_kernel<DT, A_DENSE, 1, 0, TM, TN>), grid, dim3(NTH), 0, s, A);
+      else if (AMODE == A_DENSE) NM_LAUNCH((gemm_fast_kernel<DT, A_DENSE, 0, 0, TM, TN>), grid, dim3(NTH), 0, s, A);
+      return launch_status();
     }
   }
-  if (bkc && akc) hipLaunchKernelGGL((gemm_kernel<DT, AMODE, 1, 1, TM, TN>), grid, dim3(NTH), 0, s, A);
-  else if (!bkc && akc) hipLaunchKernelGGL((gemm_kernel<DT, AMODE, 0, 1, TM, TN>), grid, dim3(NTH), 0, s, A);
-  else if (AMODE == A_DENSE && bkc) hipLaunchKernelGGL((gemm_kernel<DT, A_DENSE, 1, 0, TM, TN>), grid, dim3(NTH), 0, s, A);
-  else if (AMODE == A_DENSE) hipLaunchKernelGGL((gemm_kernel<DT, A_DENSE, 0, 0, TM, TN>), grid, dim3(NTH), 0, s, A);
-  return hipGetLastError();
+  if (bkc && akc) NM_LAUNCH((gemm_kernel<DT, AMODE, 1, 1, TM, TN>), grid, dim3(NTH), 0, s, A);
+  else if (!bkc && akc) NM_LAUNCH((gemm_kernel<DT, AMODE, 0, 1, TM, TN>), grid, dim3(NTH), 0, s, A);
+  else if (AMODE == A_DENSE && bkc) NM_LAUNCH((gemm_kernel<DT, A_DENSE, 1, 0, TM, TN>), grid, dim3(NTH), 0, s, A);
+  else if (AMODE == A_DENSE) NM_LAUNCH((gemm_kernel<DT, A_DENSE, 0, 0, TM, TN>), grid, dim3(NTH), 0, s, A);
+  return launch_status();
 }
 
 template <int DT>

@@ -17,9 +17,18 @@ struct nm_plan {
   int64_t vld;          // values row stride (elements)
   int64_t mld;          // metadata row stride (bytes)
   int kernel;           // SpMM kernel id (nm::KernelId)
+  std::string spmm_symbol;  // device kernel nm_spmm launches (filled on first query)
+  // kernel-selection overrides for benchmark sweeps, read from the environment
+  // once at plan creation (NM_FORCE_TILE = 128 | 256x128 | 256, NM_NO_DMA,
+  // NM_NO_DMA_NN, NM_OLD_SKINNY), so launches do not scan the environment
+  int force_tile;           // -1 = automatic, else nm::TileCfg
+  bool no_dma, no_dma_nn, old_skinny;
 };
 
 namespace nm {
+
+// block tile of the matrix-core kernels
+enum TileCfg { T128 = 0, T256x128 = 1, T256 = 2 };
 
 enum KernelId {
   K_NONE = 0,
@@ -29,6 +38,21 @@ enum KernelId {
 };
 
 void set_error(const std::string& msg);
+
+// Dry run of a launch: while the calling thread's probe is armed, NM_LAUNCH
+// records the kernel's host stub instead of launching it, so the same host
+// logic that picks a kernel can also name it.
+struct LaunchProbe {
+  bool armed = false;
+  const void* kernel = nullptr;
+};
+LaunchProbe& launch_probe();
+inline hipError_t launch_status() { return launch_probe().armed ? hipSuccess : hipGetLastError(); }
+#define NM_LAUNCH(KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                              \
+  do {                                                                                  \
+    if (::nm::launch_probe().armed) ::nm::launch_probe().kernel = (const void*)(KERNEL); \
+    else hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);           \
+  } while (0)
 
 // ---- launchers (return hipError_t from the launch) ----
 hipError_t launch_prune_1d(const nm_plan& pl, const void* a, void* out, uint32_t* mask, hipStream_t s);

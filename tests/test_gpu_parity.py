@@ -204,6 +204,18 @@ def test_spmm_identity_is_bit_exact(dtype):
         assert np.array_equal(got, ahat)
 
 
+def test_spmm_kernel_names_the_launched_kernel():
+    # the name comes from the same host logic that launches (dry run)
+    big = plan_for("f16", 4096, 4096, 1024, 2, 4, op_b="T").spmm_kernel
+    assert big.startswith("void nm::gemm_dma_kernel<0, 0, 256, 256,") and big.endswith(", 1>(nm::GemmArgs)"), big
+    nn = plan_for("bf16", 1024, 4096, 4096, 2, 4, op_b="N").spmm_kernel
+    assert nn.startswith("void nm::gemm_dma_kernel<1, 0, 128, 128,") and nn.endswith(", 0>(nm::GemmArgs)"), nn
+    ragged = plan_for("f16", 200, 144, 336, 2, 4).spmm_kernel
+    assert ragged.startswith("void nm::gemm_kernel<0, 0,"), ragged
+    assert "skinny2_kernel" in plan_for("f16", 100, 8, 1088, 2, 4).spmm_kernel
+    assert "gemm_kernel<0, 2," in plan_for("f16", 150, 80, 544, 4, 32).spmm_kernel
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
 @pytest.mark.parametrize("N,M", [(1, 4), (3, 4), (2, 8), (5, 16), (4, 32), (8, 32)])
 @pytest.mark.parametrize("op_b", ["N", "T"])
