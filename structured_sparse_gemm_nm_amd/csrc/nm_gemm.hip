@@ -102,17 +102,24 @@ __global__ void __launch_bounds__(NTH) skinny_kernel(GemmArgs A, int b_op_t, int
 
 // ---------------------------------------------------------------- small n, streamed
 
-// Small-n product built for bandwidth: op(B) is staged once per block in LDS
-// in its own element type, [k][NP] (NP = n rounded up to 1, 2, 4, 8 or 16);
-// each wave owns 4 rows and keeps all four in flight; a lane takes whole
-// groups: one vector load brings the group's N kept values, a 3-dword window
-// of the row's metadata brings their offsets, and each kept value meets the
-// B row its offset selects. DENSE_A streams a dense row instead (16-byte
-// chunks per lane, op_a = N). Partial sums are combined across the wave with
+// Small-n product built for latency and bandwidth. A block of SK2_WAVES waves
+// takes SK2_WAVES rows, one per wave; a lane takes whole groups (one vector
+// load brings a group's N kept values, a 3-dword window of the row's bit
+// stream its offsets; DENSE_A takes 16-byte chunks of a dense row instead).
+// op(B) is staged in LDS once per block (when k fits one chunk) as records of
+// RB bytes: the n values of one k in B's own type, zero-padded to NP columns
+// and to at least 4 bytes. Records are laid out so a wave's reads never share
+// a bank: within each window of 64 groups of MG consecutive k (MG = M, or the
+// elements of a 16-byte chunk for DENSE_A), the record of k = 64 MG w + MG g
+// + j sits at 64 MG w + 64 j + g, so lane g reads record 64 j + g whatever its
+// offset j. The first A loads of a row are issued before the staging barrier
+// and the next iteration's loads before the current one's arithmetic, so
+// the memory latencies overlap. Partial sums are combined across the wave with
 // butterfly shuffles. Requirements (checked by the launcher): N * ESZ a power
-// of two up to 16 bytes, N * b <= 64, and k small enough that... any k works:
-// B is staged in chunks of KC rows.
-constexpr int SK2_RW = 4;   // rows per wave
+// of two up to 16 bytes and N * b <= 64; DENSE_A needs op_a = N.
+constexpr int SK2_WAVES = 16;
+constexpr int SK2_DEPTH = 4;         // iterations of A loads in flight per lane (2 for the int8 dense rows)
+constexpr int SK2_LDS = 64 * 1024;   // bytes of staged B per chunk
 
 template <int ESZ>
 __device__ __forceinline__ void load_group_vals(const uint8_t* p, int nbytes, uint32_t (&w)[4]) {
@@ -126,157 +133,192 @@ __device__ __forceinline__ void load_group_vals(const uint8_t* p, int nbytes, ui
   }
 }
 
+template <int DT, int NP>
+struct SkinnyRec {
+  static constexpr int ESZ = DT == DT_I8 ? 1 : 2;
+  static constexpr int RB = NP * ESZ < 4 ? 4 : NP * ESZ;   // bytes per staged k
+  static constexpr int KC = SK2_LDS / RB;                   // k per chunk (a multiple of every window)
+};
+
 template <int DT, int NP, bool DENSE_A>
-__global__ void __launch_bounds__(NTH) skinny2_kernel(GemmArgs A, int b_op_t) {
-  constexpr int ESZ = DT == DT_I8 ? 1 : 2;
+__global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int b_op_t) {
+  constexpr int ESZ = SkinnyRec<DT, NP>::ESZ;
+  constexpr int RB = SkinnyRec<DT, NP>::RB;
+  constexpr int KC = SkinnyRec<DT, NP>::KC;
   constexpr int FDT = DT == DT_I8 ? DT_F16 : DT;
-  constexpr int KC = (64 * 1024) / (NP * ESZ);           // k rows of B per LDS chunk
+  constexpr int EPC = 16 / ESZ;                             // DENSE_A: elements per 16-byte chunk
+  constexpr int DEPTH = DENSE_A && ESZ == 1 ? 2 : SK2_DEPTH;
   typedef typename std::conditional<DT == DT_I8, int32_t, float>::type acc_t;
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[KC * NP * ESZ];
+  extern __shared__ __attribute__((aligned(16))) uint8_t s_b[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = (int)A.n;
-  const int64_t groups = (A.m + 4 * SK2_RW - 1) / (4 * SK2_RW);     // row groups of 4 waves x SK2_RW rows
-  const bool one_chunk = A.k <= KC;                               // then B is staged once per block
-  // contiguous k x NP block (op_b = N, ld = n = NP): 16-byte staging copies
-  const bool b_flat = !b_op_t && n == NP && A.ldb == NP && ((A.k * NP * ESZ) % 16 == 0);
-  auto bval = [&](int kk, int c) -> acc_t {          // staged B element
-    if constexpr (ESZ == 2) return from_bits16<FDT>(((const uint16_t*)s_b)[kk * NP + c]);
-    else return (acc_t)(int8_t)s_b[kk * NP + c];
-  };
-  auto elem = [&](uint32_t raw) -> acc_t {
-    if constexpr (ESZ == 2) return from_bits16<FDT>((uint16_t)raw);
-    else return (acc_t)(int8_t)(uint8_t)raw;
-  };
-  const int M = A.M, N = A.N, b = A.bits;
+  const int M = DENSE_A ? EPC : A.M, N = A.N, b = A.bits;
+  const int W = 64 * M;                                     // k per window
+  const int64_t row_groups = (A.m + SK2_WAVES - 1) / SK2_WAVES;
+  const bool one_chunk = A.k <= KC;
   const int vbytes = N * ESZ;
   const int64_t mwords = A.mld / 4;
 
-  for (int64_t grp = blockIdx.x; grp < groups; grp += (one_chunk ? gridDim.x : groups)) {
-  const int64_t row0 = (grp * 4 + wave) * SK2_RW;
-  acc_t acc[SK2_RW][NP];
+  auto elem = [&](uint32_t raw) __attribute__((always_inline)) -> acc_t {
+    if constexpr (ESZ == 2) return from_bits16<FDT>((uint16_t)raw);
+    else return (acc_t)(int8_t)(uint8_t)raw;
+  };
+  // the NP staged values of record r
+  auto brec = [&](int r, acc_t (&bv)[NP]) __attribute__((always_inline)) {
+    const uint8_t* p = s_b + r * RB;
+    uint32_t w[RB / 4];
+    if constexpr (RB == 4) w[0] = *(const uint32_t*)p;
+    else if constexpr (RB == 8) { const u32x2 v = *(const u32x2*)p; w[0] = v[0]; w[1] = v[1]; }
+    else {
 #pragma unroll
-  for (int r = 0; r < SK2_RW; r++)
-#pragma unroll
-    for (int c = 0; c < NP; c++) acc[r][c] = 0;
-  for (int64_t kc = 0; kc < A.k; kc += KC) {
-    const int kn = (int)((A.k - kc) < KC ? (A.k - kc) : KC);
-    const bool stage = !(one_chunk && grp != blockIdx.x);         // staged already on this block's first group
-    if (stage) __syncthreads();
-    if (stage && b_flat) {
-      const int nbytes = kn * NP * ESZ;
-      const uint8_t* src = A.b + (size_t)kc * NP * ESZ;
-      for (int e = threadIdx.x * 16; e < nbytes; e += NTH * 16) *(u32x4*)(s_b + e) = *(const u32x4*)(src + e);
-    }
-    for (int e = threadIdx.x; stage && !b_flat && e < kn * NP; e += NTH) {
-      const int kk = b_op_t ? e % kn : e / NP, c = b_op_t ? e / kn : e % NP;
-      uint32_t raw = 0;
-      if (c < n) {
-        const int64_t gi = b_op_t ? (int64_t)c * A.ldb + kc + kk : (kc + kk) * A.ldb + c;
-        raw = ESZ == 2 ? (uint32_t)((const uint16_t*)A.b)[gi] : (uint32_t)A.b[gi];
+      for (int q = 0; q < RB / 16; q++) {
+        const u32x4 v = *(const u32x4*)(p + 16 * q);
+        w[4 * q] = v[0]; w[4 * q + 1] = v[1]; w[4 * q + 2] = v[2]; w[4 * q + 3] = v[3];
       }
-      if (ESZ == 2) ((uint16_t*)s_b)[kk * NP + c] = (uint16_t)raw;
-      else s_b[kk * NP + c] = (uint8_t)raw;
     }
-    if (stage) __syncthreads();
+#pragma unroll
+    for (int c = 0; c < NP; c++) bv[c] = elem(w[(c * ESZ) / 4] >> (8 * ((c * ESZ) % 4)));
+  };
+  // A data of one iteration of one lane: up to 16 value bytes, 3 metadata words
+  struct Piece { uint32_t v[4]; uint32_t m[3]; };
+  auto load_piece = [&](int64_t row, int64_t kc, int kn, int it, Piece& pc) __attribute__((always_inline)) {
+    pc.v[0] = pc.v[1] = pc.v[2] = pc.v[3] = 0;
+    pc.m[0] = pc.m[1] = pc.m[2] = 0;
+    if (row >= A.m) return;
+    const int g = it * 64 + lane;
     if constexpr (DENSE_A) {
-      constexpr int EPC = 16 / ESZ;
-      for (int kk0 = lane * EPC; kk0 < kn; kk0 += 64 * EPC) {
-        uint32_t w[SK2_RW][4];
+      const int kk0 = g * EPC;
+      if (kk0 >= kn) return;
+      const uint8_t* p = A.a + (size_t)(row * A.lda + kc + kk0) * ESZ;
+      if (kk0 + EPC <= kn && A.a_vec) {
+        const u32x4 v = *(const u32x4*)p;
+        pc.v[0] = v[0]; pc.v[1] = v[1]; pc.v[2] = v[2]; pc.v[3] = v[3];
+      } else {
 #pragma unroll
-        for (int r = 0; r < SK2_RW; r++) {
-          const int64_t row = row0 + r;
-          w[r][0] = w[r][1] = w[r][2] = w[r][3] = 0;
-          if (row < A.m) {
-            const uint8_t* p = A.a + (size_t)(row * A.lda + kc + kk0) * ESZ;
-            if (kk0 + EPC <= kn && A.a_vec) {
-              const u32x4 v = *(const u32x4*)p;
-              w[r][0] = v[0]; w[r][1] = v[1]; w[r][2] = v[2]; w[r][3] = v[3];
-            } else {
-              for (int e = 0; e < EPC && kk0 + e < kn; e++) {
-                const uint32_t x = ESZ == 2 ? (uint32_t)((const uint16_t*)p)[e] : (uint32_t)p[e];
-                w[r][(e * ESZ) / 4] |= x << (8 * ((e * ESZ) % 4));
-              }
-            }
+        for (int wi = 0; wi < 4; wi++) {
+          uint32_t word = 0;
+          for (int t = 0; t < 4 / ESZ; t++) {
+            const int e = wi * (4 / ESZ) + t;
+            if (kk0 + e >= kn) break;
+            const uint32_t x = ESZ == 2 ? (uint32_t)((const uint16_t*)p)[e] : (uint32_t)p[e];
+            word |= x << (8 * ESZ * t);
           }
-        }
-#pragma unroll
-        for (int e = 0; e < EPC; e++) {
-          if (kk0 + e >= kn) break;
-          acc_t bv[NP];
-#pragma unroll
-          for (int c = 0; c < NP; c++) bv[c] = bval(kk0 + e, c);
-#pragma unroll
-          for (int r = 0; r < SK2_RW; r++) {
-            const uint32_t raw = (w[r][(e * ESZ) / 4] >> (8 * ((e * ESZ) % 4))) & (ESZ == 2 ? 0xFFFFu : 0xFFu);
-            const acc_t av = elem(raw);
-#pragma unroll
-            for (int c = 0; c < NP; c++) acc[r][c] += av * bv[c];
-          }
+          pc.v[wi] = word;
         }
       }
     } else {
-      const int gps = kn / M;
-      const int64_t g0 = kc / M;
-      for (int g = lane; g < gps; g += 64) {
-        uint32_t vw[SK2_RW][4];
-        uint32_t mw[SK2_RW][3];
-        const int64_t t0 = (g0 + g) * N * b;                // first metadata bit of the group
-        const int64_t w0 = t0 >> 5;
+      if (g >= kn / M) return;
+      const int64_t gg = kc / M + g;
+      load_group_vals<ESZ>(A.a + (size_t)(row * A.lda + gg * N) * ESZ, vbytes, pc.v);
+      const int64_t w0 = (gg * N * b) >> 5;
+      const uint32_t* mr = (const uint32_t*)(A.meta + row * A.mld);
 #pragma unroll
-        for (int r = 0; r < SK2_RW; r++) {
-          const int64_t row = row0 + r;
-          if (row < A.m) {
-            load_group_vals<ESZ>(A.a + (size_t)(row * A.lda + (g0 + g) * N) * ESZ, vbytes, vw[r]);
-            const uint32_t* mr = (const uint32_t*)(A.meta + row * A.mld);
+      for (int x = 0; x < 3; x++) pc.m[x] = (w0 + x < mwords) ? mr[w0 + x] : 0u;
+    }
+  };
+  auto use_piece = [&](int64_t kc, int kn, int it, const Piece& pc, acc_t (&acc)[NP]) __attribute__((always_inline)) {
+    const int g = it * 64 + lane;
+    const int rbase = it * W + lane;                        // record of offset 0 of this lane's group
+    if constexpr (DENSE_A) {
+      const int kk0 = g * EPC;
 #pragma unroll
-            for (int x = 0; x < 3; x++) mw[r][x] = (w0 + x < mwords) ? mr[w0 + x] : 0u;
-          } else {
-            vw[r][0] = vw[r][1] = vw[r][2] = vw[r][3] = 0;
-            mw[r][0] = mw[r][1] = mw[r][2] = 0;
-          }
+      for (int wi = 0; wi < 4; wi++) {                      // value word, then its elements
+        const uint32_t word = pc.v[wi];
+        for (int t = 0; t < 4 / ESZ; t++) {
+          const int e = wi * (4 / ESZ) + t;
+          if (kk0 + e >= kn) break;
+          acc_t bv[NP];
+          brec(rbase + 64 * e, bv);
+          const acc_t av = elem(word >> (8 * ESZ * t));
+#pragma unroll
+          for (int c = 0; c < NP; c++) acc[c] += av * bv[c];
         }
-        const int off = (int)(t0 & 31);
-        for (int s = 0; s < N; s++) {
+      }
+    } else {
+      if (g >= kn / M) return;
+      const int off = (int)(((kc / M + g) * N * b) & 31);
+      const uint64_t lo = ((uint64_t)pc.m[1] << 32) | pc.m[0], hi = ((uint64_t)pc.m[2] << 32) | pc.m[1];
+#pragma unroll
+      for (int wi = 0; wi < 4; wi++) {                      // N * ESZ <= 16: value word, then its slots
+        const uint32_t word = pc.v[wi];
+        for (int t = 0; t < 4 / ESZ; t++) {
+          const int s = wi * (4 / ESZ) + t;
+          if (s >= N) break;
           const int pbit = off + s * b;
+          const uint64_t win = pbit < 32 ? lo >> pbit : hi >> (pbit - 32);
+          const int j = (int)(win & ((1u << b) - 1u));
+          acc_t bv[NP];
+          brec(rbase + 64 * j, bv);
+          const acc_t av = elem(word >> (8 * ESZ * t));
 #pragma unroll
-          for (int r = 0; r < SK2_RW; r++) {
-            const uint64_t win = pbit < 32 ? (((uint64_t)mw[r][1] << 32) | mw[r][0]) >> pbit
-                                           : (((uint64_t)mw[r][2] << 32) | mw[r][1]) >> (pbit - 32);
-            const int j = (int)(win & ((1u << b) - 1u));
-            const uint32_t raw = (vw[r][(s * ESZ) / 4] >> (8 * ((s * ESZ) % 4))) & (ESZ == 2 ? 0xFFFFu : 0xFFu);
-            const acc_t av = elem(raw);
-            const int kk = g * M + j;
-#pragma unroll
-            for (int c = 0; c < NP; c++) acc[r][c] += av * bval(kk, c);
-          }
+          for (int c = 0; c < NP; c++) acc[c] += av * bv[c];
         }
       }
     }
-  }
-  // combine across the wave; every lane ends with the sums, lane c writes column c
+  };
+
+  for (int64_t grp = blockIdx.x; grp < row_groups; grp += (one_chunk ? gridDim.x : row_groups)) {
+    const int64_t row = grp * SK2_WAVES + wave;
+    acc_t acc[NP];
 #pragma unroll
-  for (int r = 0; r < SK2_RW; r++)
+    for (int c = 0; c < NP; c++) acc[c] = 0;
+    for (int64_t kc = 0; kc < A.k; kc += KC) {
+      const int kn = (int)((A.k - kc) < KC ? (A.k - kc) : KC);
+      const int units = DENSE_A ? (kn + EPC - 1) / EPC : kn / M;   // groups (chunks) of this k chunk
+      const int nit = (units + 63) / 64;
+      // DEPTH iterations in flight per lane; the first ones while B is staged
+      Piece pc[DEPTH];
+#pragma unroll
+      for (int u = 0; u < DEPTH; u++) load_piece(row, kc, kn, u, pc[u]);
+      const bool stage = !(one_chunk && grp != blockIdx.x);
+      if (stage) {
+        __syncthreads();                                    // previous chunk's readers are done
+        for (int kk = threadIdx.x; kk < kn; kk += 64 * SK2_WAVES) {
+          uint32_t w[RB / 4];
+#pragma unroll
+          for (int q = 0; q < RB / 4; q++) w[q] = 0;
+#pragma unroll
+          for (int c = 0; c < NP; c++) {
+            if (c >= n) break;
+            const int64_t gi = b_op_t ? (int64_t)c * A.ldb + kc + kk : (kc + kk) * A.ldb + c;
+            const uint32_t raw = ESZ == 2 ? (uint32_t)((const uint16_t*)A.b)[gi] : (uint32_t)A.b[gi];
+            w[(c * ESZ) / 4] |= raw << (8 * ((c * ESZ) % 4));
+          }
+          const int win = kk / W, in = kk % W;
+          const int r = win * W + (in % M) * 64 + in / M;
+          uint8_t* d = s_b + r * RB;
+#pragma unroll
+          for (int q = 0; q < RB / 4; q++) ((uint32_t*)d)[q] = w[q];
+        }
+        __syncthreads();
+      }
+      for (int it0 = 0; it0 < nit; it0 += DEPTH) {
+#pragma unroll
+        for (int u = 0; u < DEPTH; u++) {
+          if (it0 + u < nit) use_piece(kc, kn, it0 + u, pc[u], acc);
+          load_piece(row, kc, kn, it0 + u + DEPTH, pc[u]);        // empty beyond the chunk
+        }
+      }
+    }
+    // combine across the wave; lane c writes column c
 #pragma unroll
     for (int c = 0; c < NP; c++)
-      for (int o = 32; o > 0; o >>= 1) acc[r][c] += __shfl_xor(acc[r][c], o);
+      for (int o = 32; o > 0; o >>= 1) acc[c] += __shfl_xor(acc[c], o);
+    if (row < A.m) {
 #pragma unroll
-  for (int r = 0; r < SK2_RW; r++) {
-    const int64_t row = row0 + r;
-    if (row >= A.m) continue;
-#pragma unroll
-    for (int c = 0; c < NP; c++) {
-      if (lane != c || c >= n) continue;
-      if constexpr (DT == DT_I8) {
-        int64_t iv = (int64_t)A.alpha * acc[r][c];
-        if (A.beta != 0.0f) iv += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.ldc + c];
-        ((int32_t*)A.d)[row * A.ldd + c] = (int32_t)iv;
-      } else {
-        float o = A.alpha * acc[r][c];
-        if (A.beta != 0.0f) o += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.ldc + c]);
-        ((uint16_t*)A.d)[row * A.ldd + c] = to_bits16<DT>(o);
+      for (int c = 0; c < NP; c++) {
+        if (lane != c || c >= n) continue;
+        if constexpr (DT == DT_I8) {
+          int64_t iv = (int64_t)A.alpha * acc[c];
+          if (A.beta != 0.0f) iv += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.ldc + c];
+          ((int32_t*)A.d)[row * A.ldd + c] = (int32_t)iv;
+        } else {
+          float o = A.alpha * acc[c];
+          if (A.beta != 0.0f) o += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.ldc + c]);
+          ((uint16_t*)A.d)[row * A.ldd + c] = to_bits16<DT>(o);
+        }
       }
     }
-  }
   }  // row groups
 }
 
@@ -306,23 +348,34 @@ static hipError_t launch_tiles_any(const nm_plan& pl, int amode, const GemmArgs&
   }
 }
 
+template <int DT, bool DENSE_A, int NP>
+static hipError_t launch_skinny2_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
+  // one block per SK2_WAVES rows; when all of k fits one LDS chunk the grid is
+  // capped at two blocks per CU and each block stages B once and walks
+  // several row groups
+  constexpr int KC = SkinnyRec<DT, NP>::KC;
+  const int64_t groups = (A.m + SK2_WAVES - 1) / SK2_WAVES;
+  const int64_t blocks = A.k <= KC ? (groups < 512 ? groups : 512) : groups;
+  // records are placed within whole windows of 64 groups (64 M, or 64 chunks
+  // of 16 bytes for a dense A), so the staged chunk is rounded up to a window;
+  // KC is a multiple of every window, so this stays within SK2_LDS
+  const int64_t win = 64 * (DENSE_A ? (int64_t)(16 / SkinnyRec<DT, NP>::ESZ) : (int64_t)A.M);
+  const int64_t kn = A.k < KC ? A.k : KC;
+  const int64_t kr = kn > 0 ? (kn + win - 1) / win * win : win;
+  const size_t lds = (size_t)kr * SkinnyRec<DT, NP>::RB;
+  NM_LAUNCH((skinny2_kernel<DT, NP, DENSE_A>), dim3((unsigned)blocks), dim3(64 * SK2_WAVES), lds, s, A,
+            (int)(pl.p.op_b == NM_OP_T));
+  return launch_status();
+}
+
 template <int DT, bool DENSE_A>
 static hipError_t launch_skinny2_np(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
-  // one block per row group, at most 512 blocks (two per CU) when all of k fits
-  // one LDS chunk (each block then stages B once and walks several groups)
-  const int64_t groups = (A.m + 4 * SK2_RW - 1) / (4 * SK2_RW);
-  const int np = A.n <= 1 ? 1 : A.n <= 2 ? 2 : A.n <= 4 ? 4 : A.n <= 8 ? 8 : 16;
-  const int64_t kc = (64 * 1024) / (np * pl.esz_ab);
-  const int64_t blocks = A.k <= kc ? (groups < 512 ? groups : 512) : groups;
-  const dim3 grid((unsigned)blocks);
-  const int bt = pl.p.op_b == NM_OP_T;
   const int64_t n = A.n;
-  if (n <= 1) NM_LAUNCH((skinny2_kernel<DT, 1, DENSE_A>), grid, dim3(NTH), 0, s, A, bt);
-  else if (n <= 2) NM_LAUNCH((skinny2_kernel<DT, 2, DENSE_A>), grid, dim3(NTH), 0, s, A, bt);
-  else if (n <= 4) NM_LAUNCH((skinny2_kernel<DT, 4, DENSE_A>), grid, dim3(NTH), 0, s, A, bt);
-  else if (n <= 8) NM_LAUNCH((skinny2_kernel<DT, 8, DENSE_A>), grid, dim3(NTH), 0, s, A, bt);
-  else NM_LAUNCH((skinny2_kernel<DT, 16, DENSE_A>), grid, dim3(NTH), 0, s, A, bt);
-  return launch_status();
+  if (n <= 1) return launch_skinny2_t<DT, DENSE_A, 1>(pl, A, s);
+  if (n <= 2) return launch_skinny2_t<DT, DENSE_A, 2>(pl, A, s);
+  if (n <= 4) return launch_skinny2_t<DT, DENSE_A, 4>(pl, A, s);
+  if (n <= 8) return launch_skinny2_t<DT, DENSE_A, 8>(pl, A, s);
+  return launch_skinny2_t<DT, DENSE_A, 16>(pl, A, s);
 }
 
 // The streamed small-n kernel needs each group's kept values to be one
