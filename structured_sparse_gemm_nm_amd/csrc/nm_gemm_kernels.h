@@ -822,8 +822,14 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   static_assert(TB % NW == 0 && TA % NW == 0 && TMT % NW == 0, "DMA split");
   constexpr int NB = TB / NW, NA = TA / NW, NMT = TMT / NW;
   constexpr int L = NB + NA + NMT;                       // per wave per stage (same for every wave)
-  static_assert(BKC || ESZ == 2, "transposed B staging is 16-bit only");
-  constexpr int BSLOTS = BN / 8;                         // 16-byte slots per stored k-row (op_b = N)
+  constexpr int BSLOTS = BN * ESZ / 16;                  // 16-byte slots per stored k-row (op_b = N)
+  // op_b = N: LDS slot of 16-byte chunk c of stored k-row r. A 16-lane
+  // transposing read covers 4 rows x 32 bytes (16-bit) or 8 rows x 16 bytes
+  // (8-bit); these XORs keep every 32-lane phase of it on distinct banks.
+  auto nn_slot = [](int r, int c) -> int {
+    if constexpr (ESZ == 2) return c ^ (4 * (r & 3));
+    else return c ^ (2 * ((r / (256 / BN)) % (BSLOTS / 2)));
+  };
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S * STAGE];
 
   typedef typename Acc<DT>::t acc_t;
@@ -856,7 +862,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
     } else {
       const int p = 64 * (wave * NB + j) + lane;         // slot index in the stage
       const int row = p / BSLOTS, slot = p % BSLOTS;
-      ob[j] = (uint32_t)(row * A.ldb * ESZ + ((slot ^ (4 * (row & 3))) << 4));
+      ob[j] = (uint32_t)(row * A.ldb * ESZ + (nn_slot(row, slot) << 4));
     }
   }
 #pragma unroll
@@ -912,8 +918,20 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
     const int sidx = lane & 15;
     const int row = kbase + sidx / 4;
     const int cbyte = (col0 + 4 * (sidx % 4)) * 2;
-    const int off = row * (BN * 2) + ((((cbyte >> 4) ^ (4 * (row & 3)))) << 4) + (cbyte & 15);
+    const int off = row * (BN * 2) + (nn_slot(row, cbyte >> 4) << 4) + (cbyte & 15);
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(lb + off));
+  };
+  // int8: eight consecutive k (kbase .. kbase+7) of column `col0 + (lane & 15)`;
+  // with lane s addressing k-row kbase + s / 2 at columns col0 + 8 (s % 2), lane
+  // j of each 16-lane group receives byte j % 8 of the 8 bytes addressed by
+  // lane 2t + j / 8 as its element t (ds_read_b64_tr_b8, measured on gfx950)
+  typedef int int2_t __attribute__((ext_vector_type(2)));
+  auto btr8 = [&](const uint8_t* lb, int kbase, int col0) -> int2_t {
+    const int sidx = lane & 15;
+    const int row = kbase + sidx / 2;
+    const int cbyte = col0 + 8 * (sidx % 2);
+    const int off = row * BN + (nn_slot(row, cbyte >> 4) << 4) + (cbyte & 15);
+    return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) int2_t*)(lb + off));
   };
   // column base of this lane's 16-lane group inside a 32-column fragment
   const int nb16 = lane & 16;
@@ -964,7 +982,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
       if constexpr (BKC) {
         const int row = wn0 + fn * 32 + l32;
         bv[g % 2] = concat<DT>(bchunk(lb, row, 4 * h + q), bchunk(lb, row, 4 * h + 2 + q));
-      } else {
+      } else if constexpr (ESZ == 2) {
         // k = 32h + 8q + {0..3, 4..7, 16..19, 20..23}
         const int cb = wn0 + fn * 32 + nb16;
         const int kb = 32 * h + 8 * q;
@@ -974,6 +992,13 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
         const short16_t v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3],
                              r2[0], r2[1], r2[2], r2[3], r3[0], r3[1], r3[2], r3[3]};
         bv[g % 2] = __builtin_bit_cast(b2_t, v);
+      } else {
+        // int8: k = 64h + 16q + {0..7, 8..15, 32..39, 40..47}
+        const int cb = wn0 + fn * 32 + nb16;
+        const int kb = 64 * h + 16 * q;
+        const int2_t r0 = btr8(lb, kb, cb), r1 = btr8(lb, kb + 8, cb), r2 = btr8(lb, kb + 32, cb),
+                     r3 = btr8(lb, kb + 40, cb);
+        bv[g % 2] = b2_t{r0[0], r0[1], r1[0], r1[1], r2[0], r2[1], r3[0], r3[1]};
       }
     } else {
       const uint8_t* la = st;
@@ -984,13 +1009,18 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
       for (int fn = 0; fn < FN; fn++) {
         if constexpr (BKC) {
           bw[g % 2][fn] = bchunk(lb, wn0 + fn * 32 + l32, 2 * g + q);
-        } else {
+        } else if constexpr (ESZ == 2) {
           // k = 16g + 8q + 0..7
           const int cb = wn0 + fn * 32 + nb16;
           const short4_t r0 = btr4(lb, 16 * g + 8 * q, cb), r1 = btr4(lb, 16 * g + 8 * q + 4, cb);
           typedef short short8_t __attribute__((ext_vector_type(8)));
           const short8_t v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
           bw[g % 2][fn] = __builtin_bit_cast(ab_t, v);
+        } else {
+          // int8: k = 32g + 16q + 0..15
+          const int cb = wn0 + fn * 32 + nb16;
+          const int2_t r0 = btr8(lb, 32 * g + 16 * q, cb), r1 = btr8(lb, 32 * g + 16 * q + 8, cb);
+          bw[g % 2][fn] = ab_t{r0[0], r0[1], r1[0], r1[1]};
         }
       }
     }
@@ -1118,7 +1148,7 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
   const bool bkc = pl.p.op_b == NM_OP_T;
   const bool akc = pl.p.op_a == NM_OP_N || AMODE != A_DENSE;
   if constexpr (AMODE != A_GATHER) {
-    const bool dma_nn = !bkc && DT != DT_I8 && !pl.no_dma_nn;
+    const bool dma_nn = !bkc && !pl.no_dma_nn;
     if (full_tiles(pl, A, TM, TN, AMODE) && (bkc || dma_nn) && akc && !pl.no_dma) {
       // 256-row tiles run eight waves (two per SIMD, 128 x 64 or 64 x 64 each);
       // 128 x 128 tiles run four waves with two blocks per CU.
@@ -1127,7 +1157,7 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
       if (bkc)
         NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, dma_stages<DT, AMODE, TM, TN>(), WGM, WGN, 1>), grid,
                            dim3(64 * WGM * WGN), 0, s, A);
-      else if constexpr (DT != DT_I8)
+      else
         NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, dma_stages<DT, AMODE, TM, TN>(), WGM, WGN, 0>), grid,
                            dim3(64 * WGM * WGN), 0, s, A);
       return launch_status();

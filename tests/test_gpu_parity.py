@@ -170,7 +170,8 @@ def run_spmm(dtype, N, M, m, n, k, op_b, alpha, beta, seed, op_a="N"):
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
 @pytest.mark.parametrize("op_b", ["N", "T"])
-@pytest.mark.parametrize("m,n,k", [(200, 144, 336), (128, 128, 64), (64, 272, 1040), (17, 48, 4), (256, 256, 128), (512, 256, 192)])
+@pytest.mark.parametrize("m,n,k", [(200, 144, 336), (128, 128, 64), (64, 272, 1040), (17, 48, 4), (256, 256, 128), (512, 256, 192),
+                                   (256, 512, 640)])
 @pytest.mark.parametrize("ab", [(1.0, 0.0), (2.0, -3.0)])
 @pytest.mark.parametrize("tile", ["auto", "128", "256"])
 def test_spmm_2of4(dtype, op_b, m, n, k, ab, tile, monkeypatch):
@@ -238,7 +239,8 @@ def test_spmm_skinny(dtype, N, M, n, op_b):
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
 @pytest.mark.parametrize("op_a", ["N", "T"])
 @pytest.mark.parametrize("op_b", ["N", "T"])
-@pytest.mark.parametrize("m,n,k", [(272, 8, 208), (272, 144, 208), (272, 304, 208), (256, 256, 320), (512, 384, 192)])
+@pytest.mark.parametrize("m,n,k", [(272, 8, 208), (272, 144, 208), (272, 304, 208), (256, 256, 320), (512, 384, 192),
+                                   (256, 512, 640)])
 @pytest.mark.parametrize("tile", ["auto", "128", "256"])
 def test_dense_gemm(dtype, op_a, op_b, m, n, k, tile, monkeypatch):
     if tile != "auto":
