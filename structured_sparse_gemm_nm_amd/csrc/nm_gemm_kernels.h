@@ -345,6 +345,7 @@ __device__ __forceinline__ typename Acc<DT>::t mfma32(const typename Frag<DT>::a
 // resident on one XCD at the same time cover a compact GROUP x (CUs / GROUP)
 // patch and share both A row tiles and B column tiles in that XCD's L2.
 constexpr int NUM_XCD = 8;
+constexpr int NUM_CU = 256;
 __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
   constexpr int GROUP = 8;
   const int64_t nb = gridDim.x;
@@ -1041,10 +1042,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   };
 
   // waits until at most n (0 <= n <= S-1) of this wave's issued stages are outstanding
-  static_assert(L * (S - 1) <= 63, "vmcnt range");
+  static_assert(L * (S - 1) <= 63 && S <= 6, "vmcnt range");
   auto wait_stages = [&](int n) {
-    if (S > 3 && n >= 3) wait_vmcnt<L * (S > 3 ? 3 : 0)>();
-    else if (n >= 2) wait_vmcnt<L * 2>();
+    if (S > 5 && n >= 5) wait_vmcnt<L * (S > 5 ? 5 : 0)>();
+    else if (S > 4 && n == 4) wait_vmcnt<L * (S > 4 ? 4 : 0)>();
+    else if (S > 3 && n == 3) wait_vmcnt<L * (S > 3 ? 3 : 0)>();
+    else if (n == 2) wait_vmcnt<L * 2>();
     else if (n == 1) wait_vmcnt<L>();
     else wait_vmcnt<0>();
   };
@@ -1132,13 +1135,16 @@ inline bool full_tiles(const nm_plan& pl, const GemmArgs& A, int TM, int TN, int
 }
 
 // Stages of the LDS-DMA ring: as many as fit (at most 4), keeping two blocks
-// per CU for 128 x 128 tiles.
-template <int DT, int AMODE, int TM, int TN>
+// per CU for 128 x 128 tiles; DEEP: one block per CU (grids of at most one
+// block per CU), so the ring takes the whole LDS (up to 6 stages): the copies
+// are latency-bound and more of them in flight is what helps.
+template <int DT, int AMODE, int TM, int TN, bool DEEP = false>
 constexpr int dma_stages() {
   constexpr int ES = DT == DT_I8 ? 1 : 2;
   constexpr int STG = (AMODE == A_SPARSE24 ? TM * (64 + (ES == 2 ? 8 : 16)) : TM * 128) + TN * 128;
-  constexpr int BUDGET = (TM == 128 && TN == 128) ? 80 * 1024 : 160 * 1024;
-  return 4 * STG <= BUDGET ? 4 : (3 * STG <= BUDGET ? 3 : 2);
+  constexpr int BUDGET = (TM == 128 && TN == 128 && !DEEP) ? 80 * 1024 : 160 * 1024;
+  constexpr int MAXS = DEEP ? 6 : 4;
+  return MAXS * STG <= BUDGET ? MAXS : (MAXS - 1) * STG <= BUDGET ? MAXS - 1 : (MAXS - 2) * STG <= BUDGET ? MAXS - 2 : 2;
 }
 
 template <int DT, int AMODE, int TM, int TN>
@@ -1154,12 +1160,19 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
       // 128 x 128 tiles run four waves with two blocks per CU.
       constexpr int WGM = TM == 256 ? (TN == 256 ? 2 : 4) : 2;
       constexpr int WGN = TM == 256 ? 4 / (TN == 256 ? 1 : 2) : 2;
-      if (bkc)
-        NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, dma_stages<DT, AMODE, TM, TN>(), WGM, WGN, 1>), grid,
-                           dim3(64 * WGM * WGN), 0, s, A);
+      constexpr int S1 = dma_stages<DT, AMODE, TM, TN>();
+      constexpr int SD = dma_stages<DT, AMODE, TM, TN, true>();
+      // measured: the deep ring lifts the dense 128 x 128 kernel (BERT FC2: 545 ->
+      // 700 TFLOP/s) but not the 2:4 one, which stays on the shallow ring
+      const bool deep = AMODE == A_DENSE && TM == 128 && TN == 128 && tiles <= NUM_CU && !pl.no_deep_ring;
+      if (bkc && deep)
+        NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, SD, WGM, WGN, 1>), grid, dim3(64 * WGM * WGN), 0, s, A);
+      else if (bkc)
+        NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, S1, WGM, WGN, 1>), grid, dim3(64 * WGM * WGN), 0, s, A);
+      else if (deep)
+        NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, SD, WGM, WGN, 0>), grid, dim3(64 * WGM * WGN), 0, s, A);
       else
-        NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, dma_stages<DT, AMODE, TM, TN>(), WGM, WGN, 0>), grid,
-                           dim3(64 * WGM * WGN), 0, s, A);
+        NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, S1, WGM, WGN, 0>), grid, dim3(64 * WGM * WGN), 0, s, A);
       return launch_status();
     }
     if (full_tiles(pl, A, TM, TN, AMODE)) {

@@ -20,9 +20,10 @@ struct nm_plan {
   std::string spmm_symbol;  // device kernel nm_spmm launches (filled on first query)
   // kernel-selection overrides for benchmark sweeps, read from the environment
   // once at plan creation (NM_FORCE_TILE = 128 | 256x128 | 256, NM_NO_DMA,
-  // NM_NO_DMA_NN, NM_OLD_SKINNY), so launches do not scan the environment
+  // NM_NO_DMA_NN, NM_NO_DEEP_RING, NM_OLD_SKINNY), so launches do not scan the
+  // environment
   int force_tile;           // -1 = automatic, else nm::TileCfg
-  bool no_dma, no_dma_nn, old_skinny;
+  bool no_dma, no_dma_nn, no_deep_ring, old_skinny;
 };
 
 namespace nm {
