@@ -38,6 +38,7 @@ WORKLOAD_SETS = {
     "c3": [("fwd", "c3_fwd"), ("bwd", "c3_bwd")],
     "c4": [("int8", "c4_int8")],
     "x1": [("fwd", "x1_fwd"), ("bwd", "x1_bwd")],
+    "x3": [("qkv", "x3_qkv"), ("proj", "x3_proj"), ("fc1", "x3_fc1"), ("fc2", "x3_fc2")],
     "c5_4of32": [("n1", "c5_4of32_n1"), ("n8", "c5_4of32_n8"), ("n4096", "c5_4of32_n4096")],
     "c5_8of32": [("n1", "c5_8of32_n1"), ("n8", "c5_8of32_n8"), ("n4096", "c5_8of32_n4096")],
 }
@@ -47,6 +48,8 @@ WORKLOAD_DESC = {
     "c3": "bf16 transposable 2:4 training pair, W 11008x4096, X 8192x4096, dY 8192x11008, NT",
     "c4": "int8 2:4, 4096^3, int32 C/D, beta=1, NN+NT",
     "x1": "fp16 transposable 2:4 pair at the training shapes: W 11008x4096, X 8192x4096, dY 8192x11008, NT",
+    "x3": "the cuSPARSELt blog's Table 1 shapes: QKV 3072x1024, PROJ 1024x1024, FC1 4096x1024, FC2 1024x4096 "
+          "weights, 16384 tokens, fp16 2:4, NT (D row-major; the blog's is column-major)",
     "c5_4of32": "fp16 4:32, A 4096x4096, B 4096 x {1, 8, 4096}, NN",
     "c5_8of32": "fp16 8:32, A 4096x4096, B 4096 x {1, 8, 4096}, NN",
 }
@@ -303,6 +306,16 @@ def main():
     if dense:
         speedup = round(sum(dense.values()) / spmm_total_ms, 3)
 
+    # measured achievable peaks (calibration loops, outside the timed region)
+    cal = calibrate(torch, stream, dom["dtype"])
+    if cal is not None:
+        roofline["achievable"] = cal
+        if roofline["bound"] == "mfma" and cal["sparse_matrix"] > 0:
+            # the kept multiply-adds of the sparse instruction run at half its dense-equivalent rate
+            roofline["frac_of_achievable"] = round(roofline["achieved"] / (cal["sparse_matrix"] / 2), 4)
+        elif roofline["bound"] == "hbm" and cal["copy_gbs"] > 0:
+            roofline["frac_of_achievable"] = round(roofline["achieved"] / cal["copy_gbs"], 4)
+
     # CPU oracle on one step of the same workload
     cpu = None
     if not args.no_cpu_baseline:
@@ -332,6 +345,37 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out))
+
+
+def calibrate(torch, stream, dtype):
+    """Achievable peaks on this GPU: the 2:4 and dense matrix instructions with no
+    memory traffic, and a streaming copy (libnmcal.so, built with the library)."""
+    import ctypes
+    path = os.path.join(ROOT, "structured_sparse_gemm_nm_amd", "libnmcal.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    L.nmcal_matrix_tflops.restype = ctypes.c_double
+    L.nmcal_matrix_tflops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p]
+    L.nmcal_copy_gbs.restype = ctypes.c_double
+    L.nmcal_copy_gbs.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p]
+    sp = ctypes.c_void_p(stream.cuda_stream)
+    blocks, iters = 1024, 2000
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    i8 = 1 if dtype == "i8" else 0
+    sparse = L.nmcal_matrix_tflops(1, i8, ctypes.c_void_p(out.data_ptr()), blocks, iters, sp)
+    dense = L.nmcal_matrix_tflops(0, i8, ctypes.c_void_p(out.data_ptr()), blocks, iters, sp)
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    copy = L.nmcal_copy_gbs(ctypes.c_void_p(src.data_ptr()), ctypes.c_void_p(dst.data_ptr()), nbytes, sp)
+    del src, dst, out
+    return {"sparse_matrix": round(sparse, 1), "dense_matrix": round(dense, 1),
+            "unit": "TFLOP/s" if not i8 else "TOP/s", "copy_gbs": round(copy, 1),
+            "method": "%s matrix instructions in a loop with no memory traffic (%d blocks x 4 waves, %d x 8 "
+                      "instructions; sparse figure dense-equivalent), and a 1 GiB streaming copy (read + write "
+                      "bytes)" % ("int8" if i8 else "fp16", blocks, iters)}
 
 
 def load_traffic(workload, kernel):

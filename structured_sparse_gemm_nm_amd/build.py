@@ -16,6 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnmsparse.so")
+CAL_LIB = os.path.join(HERE, "libnmcal.so")       # calibration loops for the benchmark (not the ABI)
 SOURCES = ["nm_api.hip", "nm_prune.hip", "nm_gemm.hip", "nm_gemm_f16.hip", "nm_gemm_bf16.hip", "nm_gemm_i8.hip"]
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
@@ -45,11 +46,27 @@ def _compile(src):
     return obj
 
 
+def _link(objs, out, soname):
+    tl = torch_lib_dir()
+    hip_rt = os.path.join(tl, "libamdhip64.so")
+    if not os.path.exists(hip_rt):
+        raise RuntimeError("torch's HIP runtime not found at " + hip_rt)
+    tmp = out + ".tmp"
+    cmd = [CLANG, "-shared", "-fPIC", "-o", tmp] + objs + [
+        "-L" + tl, "-l:libamdhip64.so", "-Wl,-rpath," + tl, "-Wl,--no-undefined", "-Wl,-soname," + soname]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("link failed: %s\n%s%s" % (" ".join(cmd), r.stdout, r.stderr))
+    os.replace(tmp, out)
+
+
 def build(verbose=True):
-    """Compile every HIP source for gfx950 and link libnmsparse.so (always rebuilds)."""
+    """Compile every HIP source for gfx950 and link libnmsparse.so and libnmcal.so (always rebuilds)."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+        objs = list(ex.map(_compile, SOURCES + ["nm_calib.hip"]))
+    _link(objs[-1:], CAL_LIB, "libnmcal.so")
+    objs = objs[:-1]
     tl = torch_lib_dir()
     hip_rt = os.path.join(tl, "libamdhip64.so")
     if not os.path.exists(hip_rt):
