@@ -39,6 +39,7 @@ WORKLOAD_SETS = {
     "c4": [("int8", "c4_int8")],
     "x1": [("fwd", "x1_fwd"), ("bwd", "x1_bwd")],
     "x3": [("qkv", "x3_qkv"), ("proj", "x3_proj"), ("fc1", "x3_fc1"), ("fc2", "x3_fc2")],
+    "x2": [("n1", "x2_4of32_n1"), ("n8", "x2_4of32_n8")],
     "c5_4of32": [("n1", "c5_4of32_n1"), ("n8", "c5_4of32_n8"), ("n4096", "c5_4of32_n4096")],
     "c5_8of32": [("n1", "c5_8of32_n1"), ("n8", "c5_8of32_n8"), ("n4096", "c5_8of32_n4096")],
 }
@@ -48,6 +49,7 @@ WORKLOAD_DESC = {
     "c3": "bf16 transposable 2:4 training pair, W 11008x4096, X 8192x4096, dY 8192x11008, NT",
     "c4": "int8 2:4, 4096^3, int32 C/D, beta=1, NN+NT",
     "x1": "fp16 transposable 2:4 pair at the training shapes: W 11008x4096, X 8192x4096, dY 8192x11008, NT",
+    "x2": "fp16 4:32 GEMV and n = 8 beyond the Infinity Cache: A 32768x32768 (compressed 268 MB + 84 MB metadata), NN",
     "x3": "the cuSPARSELt blog's Table 1 shapes: QKV 3072x1024, PROJ 1024x1024, FC1 4096x1024, FC2 1024x4096 "
           "weights, 16384 tokens, fp16 2:4, NT (D row-major; the blog's is column-major)",
     "c5_4of32": "fp16 4:32, A 4096x4096, B 4096 x {1, 8, 4096}, NN",

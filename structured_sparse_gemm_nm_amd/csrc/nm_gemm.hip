@@ -136,25 +136,25 @@ __device__ __forceinline__ void load_group_vals(const uint8_t* p, int nbytes, ui
 template <int DT, int NP>
 struct SkinnyRec {
   static constexpr int ESZ = DT == DT_I8 ? 1 : 2;
-  static constexpr int RB = NP * ESZ < 4 ? 4 : NP * ESZ;   // bytes per staged k
+  static constexpr int RB = NP * ESZ;                       // bytes per staged k
   static constexpr int KC = SK2_LDS / RB;                   // k per chunk (a multiple of every window)
 };
 
-template <int DT, int NP, bool DENSE_A>
+template <int DT, int NP, bool DENSE_A, int RW>
 __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int b_op_t) {
   constexpr int ESZ = SkinnyRec<DT, NP>::ESZ;
   constexpr int RB = SkinnyRec<DT, NP>::RB;
   constexpr int KC = SkinnyRec<DT, NP>::KC;
   constexpr int FDT = DT == DT_I8 ? DT_F16 : DT;
   constexpr int EPC = 16 / ESZ;                             // DENSE_A: elements per 16-byte chunk
-  constexpr int DEPTH = DENSE_A && ESZ == 1 ? 2 : SK2_DEPTH;
+  constexpr int DEPTH = RW > 1 || (DENSE_A && ESZ == 1) ? 2 : SK2_DEPTH;
   typedef typename std::conditional<DT == DT_I8, int32_t, float>::type acc_t;
   extern __shared__ __attribute__((aligned(16))) uint8_t s_b[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = (int)A.n;
   const int M = DENSE_A ? EPC : A.M, N = A.N, b = A.bits;
   const int W = 64 * M;                                     // k per window
-  const int64_t row_groups = (A.m + SK2_WAVES - 1) / SK2_WAVES;
+  const int64_t row_groups = (A.m + SK2_WAVES * RW - 1) / (SK2_WAVES * RW);
   const bool one_chunk = A.k <= KC;
   const int vbytes = N * ESZ;
   const int64_t mwords = A.mld / 4;
@@ -166,8 +166,10 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
   // the NP staged values of record r
   auto brec = [&](int r, acc_t (&bv)[NP]) __attribute__((always_inline)) {
     const uint8_t* p = s_b + r * RB;
-    uint32_t w[RB / 4];
-    if constexpr (RB == 4) w[0] = *(const uint32_t*)p;
+    uint32_t w[RB < 4 ? 1 : RB / 4];
+    if constexpr (RB == 1) w[0] = *p;
+    else if constexpr (RB == 2) w[0] = *(const uint16_t*)p;
+    else if constexpr (RB == 4) w[0] = *(const uint32_t*)p;
     else if constexpr (RB == 8) { const u32x2 v = *(const u32x2*)p; w[0] = v[0]; w[1] = v[1]; }
     else {
 #pragma unroll
@@ -258,25 +260,29 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
   };
 
   for (int64_t grp = blockIdx.x; grp < row_groups; grp += (one_chunk ? gridDim.x : row_groups)) {
-    const int64_t row = grp * SK2_WAVES + wave;
-    acc_t acc[NP];
+    const int64_t row0 = (grp * SK2_WAVES + wave) * RW;    // this wave's RW rows
+    acc_t acc[RW][NP];
 #pragma unroll
-    for (int c = 0; c < NP; c++) acc[c] = 0;
+    for (int rr = 0; rr < RW; rr++)
+#pragma unroll
+      for (int c = 0; c < NP; c++) acc[rr][c] = 0;
     for (int64_t kc = 0; kc < A.k; kc += KC) {
       const int kn = (int)((A.k - kc) < KC ? (A.k - kc) : KC);
       const int units = DENSE_A ? (kn + EPC - 1) / EPC : kn / M;   // groups (chunks) of this k chunk
       const int nit = (units + 63) / 64;
       // DEPTH iterations in flight per lane; the first ones while B is staged
-      Piece pc[DEPTH];
+      Piece pc[RW][DEPTH];
 #pragma unroll
-      for (int u = 0; u < DEPTH; u++) load_piece(row, kc, kn, u, pc[u]);
+      for (int u = 0; u < DEPTH; u++)
+#pragma unroll
+        for (int rr = 0; rr < RW; rr++) load_piece(row0 + rr, kc, kn, u, pc[rr][u]);
       const bool stage = !(one_chunk && grp != blockIdx.x);
       if (stage) {
         __syncthreads();                                    // previous chunk's readers are done
         for (int kk = threadIdx.x; kk < kn; kk += 64 * SK2_WAVES) {
-          uint32_t w[RB / 4];
+          uint32_t w[RB < 4 ? 1 : RB / 4];
 #pragma unroll
-          for (int q = 0; q < RB / 4; q++) w[q] = 0;
+          for (int q = 0; q < (RB < 4 ? 1 : RB / 4); q++) w[q] = 0;
 #pragma unroll
           for (int c = 0; c < NP; c++) {
             if (c >= n) break;
@@ -287,35 +293,46 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
           const int win = kk / W, in = kk % W;
           const int r = win * W + (in % M) * 64 + in / M;
           uint8_t* d = s_b + r * RB;
+          if constexpr (RB == 1) *d = (uint8_t)w[0];
+          else if constexpr (RB == 2) *(uint16_t*)d = (uint16_t)w[0];
+          else {
 #pragma unroll
-          for (int q = 0; q < RB / 4; q++) ((uint32_t*)d)[q] = w[q];
+            for (int q = 0; q < RB / 4; q++) ((uint32_t*)d)[q] = w[q];
+          }
         }
         __syncthreads();
       }
       for (int it0 = 0; it0 < nit; it0 += DEPTH) {
 #pragma unroll
         for (int u = 0; u < DEPTH; u++) {
-          if (it0 + u < nit) use_piece(kc, kn, it0 + u, pc[u], acc);
-          load_piece(row, kc, kn, it0 + u + DEPTH, pc[u]);        // empty beyond the chunk
+#pragma unroll
+          for (int rr = 0; rr < RW; rr++) {
+            if (it0 + u < nit) use_piece(kc, kn, it0 + u, pc[rr][u], acc[rr]);
+            load_piece(row0 + rr, kc, kn, it0 + u + DEPTH, pc[rr][u]);   // empty beyond the chunk
+          }
         }
       }
     }
     // combine across the wave; lane c writes column c
 #pragma unroll
-    for (int c = 0; c < NP; c++)
-      for (int o = 32; o > 0; o >>= 1) acc[c] += __shfl_xor(acc[c], o);
-    if (row < A.m) {
+    for (int rr = 0; rr < RW; rr++) {
+      const int64_t row = row0 + rr;
 #pragma unroll
-      for (int c = 0; c < NP; c++) {
-        if (lane != c || c >= n) continue;
-        if constexpr (DT == DT_I8) {
-          int64_t iv = (int64_t)A.alpha * acc[c];
-          if (A.beta != 0.0f) iv += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.ldc + c];
-          ((int32_t*)A.d)[row * A.ldd + c] = (int32_t)iv;
-        } else {
-          float o = A.alpha * acc[c];
-          if (A.beta != 0.0f) o += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.ldc + c]);
-          ((uint16_t*)A.d)[row * A.ldd + c] = to_bits16<DT>(o);
+      for (int c = 0; c < NP; c++)
+        for (int o = 32; o > 0; o >>= 1) acc[rr][c] += __shfl_xor(acc[rr][c], o);
+      if (row < A.m) {
+#pragma unroll
+        for (int c = 0; c < NP; c++) {
+          if (lane != c || c >= n) continue;
+          if constexpr (DT == DT_I8) {
+            int64_t iv = (int64_t)A.alpha * acc[rr][c];
+            if (A.beta != 0.0f) iv += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.ldc + c];
+            ((int32_t*)A.d)[row * A.ldd + c] = (int32_t)iv;
+          } else {
+            float o = A.alpha * acc[rr][c];
+            if (A.beta != 0.0f) o += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.ldc + c]);
+            ((uint16_t*)A.d)[row * A.ldd + c] = to_bits16<DT>(o);
+          }
         }
       }
     }
@@ -348,13 +365,13 @@ static hipError_t launch_tiles_any(const nm_plan& pl, int amode, const GemmArgs&
   }
 }
 
-template <int DT, bool DENSE_A, int NP>
-static hipError_t launch_skinny2_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
-  // one block per SK2_WAVES rows; when all of k fits one LDS chunk the grid is
-  // capped at two blocks per CU and each block stages B once and walks
-  // several row groups
+template <int DT, bool DENSE_A, int NP, int RW>
+static hipError_t launch_skinny2_rw(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
+  // one block per SK2_WAVES * RW rows; when all of k fits one LDS chunk the
+  // grid is capped at two blocks per CU and each block stages B once and
+  // walks several row groups
   constexpr int KC = SkinnyRec<DT, NP>::KC;
-  const int64_t groups = (A.m + SK2_WAVES - 1) / SK2_WAVES;
+  const int64_t groups = (A.m + SK2_WAVES * RW - 1) / (SK2_WAVES * RW);
   const int64_t blocks = A.k <= KC ? (groups < 512 ? groups : 512) : groups;
   // records are placed within whole windows of 64 groups (64 M, or 64 chunks
   // of 16 bytes for a dense A), so the staged chunk is rounded up to a window;
@@ -363,9 +380,19 @@ static hipError_t launch_skinny2_t(const nm_plan& pl, const GemmArgs& A, hipStre
   const int64_t kn = A.k < KC ? A.k : KC;
   const int64_t kr = kn > 0 ? (kn + win - 1) / win * win : win;
   const size_t lds = (size_t)kr * SkinnyRec<DT, NP>::RB;
-  NM_LAUNCH((skinny2_kernel<DT, NP, DENSE_A>), dim3((unsigned)blocks), dim3(64 * SK2_WAVES), lds, s, A,
+  NM_LAUNCH((skinny2_kernel<DT, NP, DENSE_A, RW>), dim3((unsigned)blocks), dim3(64 * SK2_WAVES), lds, s, A,
             (int)(pl.p.op_b == NM_OP_T));
   return launch_status();
+}
+
+// Tall problems (m >= 16384 rows) give each wave several rows, so that the
+// staged B serves more rows per block (16-bit types; the int8 variants would
+// spill).
+template <int DT, bool DENSE_A, int NP>
+static hipError_t launch_skinny2_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
+  constexpr int RW_TALL = DT == DT_I8 ? 1 : NP <= 2 ? 4 : NP <= 8 ? 2 : 1;
+  if (A.m >= 16384 && RW_TALL > 1) return launch_skinny2_rw<DT, DENSE_A, NP, RW_TALL>(pl, A, s);
+  return launch_skinny2_rw<DT, DENSE_A, NP, 1>(pl, A, s);
 }
 
 template <int DT, bool DENSE_A>

@@ -6,8 +6,10 @@ oracle and the GPU path can both consume its bytes without sharing code.
 
 Recipe: numpy PCG64 ``default_rng(seed)``; normal draws are fp64, scaled by
 sigma, rounded to fp32 and then to the element format with round-to-nearest-even
-(numpy's float16 cast for fp16, the bit-level rule below for bf16). Integer
-draws are uniform over the closed range.
+(numpy's float16 cast for fp16, the bit-level rule below for bf16); the
+out-of-cache GEMV workload (2^30 elements) draws fp32 normals directly
+('normal32'), which halves the host memory and time of the draw. Integer draws
+are uniform over the closed range.
 
 The workloads mirror the shapes of the pages' examples: the BERT-Large GEMMs of
 the cuSPARSELt blog (Table 1; batch 32 x seq 128 tokens), a transposable 2:4
@@ -28,6 +30,19 @@ def normal(shape, seed, sigma=1.0, dtype="f16"):
     """N(0, sigma^2) draws as raw element bits (uint16) for 'f16' / 'bf16'."""
     rng = np.random.default_rng(seed)
     x = (rng.standard_normal(size=shape) * sigma).astype(np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    if dtype == "bf16":
+        return _fp32_to_bf16_bits(x).reshape(shape)
+    raise ValueError(dtype)
+
+
+def normal32(shape, seed, sigma=1.0, dtype="f16"):
+    """As normal(), but drawn as fp32 (for very large operands)."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal(size=shape, dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
     if dtype == "f16":
         return x.astype(np.float16).view(np.uint16)
     if dtype == "bf16":
@@ -87,6 +102,12 @@ WORKLOADS = {
     "c4_int8": dict(dtype="i8", N=2, M=4, m=4096, n=4096, k=4096, op_a="N", op_b="N",
                     a=("int", 4001, -127, 127), b=("int", 4002, -127, 127), c=("int32", 4003, -2**20, 2**20),
                     alpha=1.0, beta=1.0),
+    # general N:M GEMV beyond the Infinity Cache: m = k = 32768 at 4:32
+    # (compressed values 268 MB + metadata 84 MB)
+    "x2_4of32_n1": dict(dtype="f16", N=4, M=32, m=32768, n=1, k=32768, op_a="N", op_b="N",
+                        a=("normal32", 8001, 1.0), b=("normal", 8002, 1.0), alpha=1.0, beta=0.0),
+    "x2_4of32_n8": dict(dtype="f16", N=4, M=32, m=32768, n=8, k=32768, op_a="N", op_b="N",
+                        a=("normal32", 8001, 1.0), b=("normal", 8003, 1.0), alpha=1.0, beta=0.0),
     # general N:M with M = 32
     "c5_4of32_n1": dict(dtype="f16", N=4, M=32, m=4096, n=1, k=4096, op_a="N", op_b="N",
                         a=("normal", 5001, 1.0), b=("normal", 5002, 1.0), alpha=1.0, beta=0.0),
@@ -111,10 +132,25 @@ def stored_shape_b(w):
     return (w["k"], w["n"]) if w.get("op_b", "N") == "N" else (w["n"], w["k"])
 
 
+_LARGE = {}   # the most recent large draw (>= 2^28 elements), reused when asked for again
+
+
 def draw(spec, shape, dtype):
+    key = (tuple(spec), tuple(shape), dtype)
+    if int(np.prod(shape)) >= (1 << 28):
+        if key not in _LARGE:
+            _LARGE.clear()
+            _LARGE[key] = _draw(spec, shape, dtype)
+        return _LARGE[key]
+    return _draw(spec, shape, dtype)
+
+
+def _draw(spec, shape, dtype):
     kind = spec[0]
     if kind == "normal":
         return normal(shape, spec[1], spec[2], dtype)
+    if kind == "normal32":
+        return normal32(shape, spec[1], spec[2], dtype)
     if kind == "int":
         return uniform_int(shape, spec[1], spec[2], spec[3], np.int8)
     if kind == "int32":

@@ -237,6 +237,34 @@ def test_spmm_skinny(dtype, N, M, n, op_b):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("N,M,n,k", [(2, 4, 1, 1088), (4, 32, 2, 1088), (2, 4, 4, 1088), (4, 32, 8, 4160)])
+def test_spmm_skinny_tall(dtype, N, M, n, k):
+    """At least 16384 rows: each wave takes several rows (16-bit types); 16400 rows
+    leave a ragged last block and k = 4160 with n = 8 spans two staged chunks."""
+    alpha, beta = (1.0, 1.0) if dtype == "i8" else (0.5, -0.25)
+    plan = run_spmm(dtype, N, M, 16400, n, k, "N" if n != 2 else "T", alpha, beta, 5000 + n)
+    assert plan.kernel_name == "spmm_skinny"
+    rw = 1 if dtype == "i8" else (4 if n <= 2 else 2)
+    assert plan.spmm_kernel.endswith(", false, %d>(nm::GemmArgs, int)" % rw), plan.spmm_kernel
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("n,k", [(1, 4160), (8, 1040)])
+def test_dense_skinny_tall(dtype, n, k):
+    m = 16400
+    a = rand(dtype, (m, k), 51)
+    b = rand(dtype, (k, n), 52)
+    plan = plan_for(dtype, m, n, k, 2, 4)
+    odt = torch.int32 if dtype == "i8" else torch.int16
+    d = Guarded((m, n), odt)
+    nm.nm_dense_gemm(plan, 1.0, dev(a), dev(b), 0.0, None, d.t)
+    sync()
+    d.check()
+    ref, tol = ref_product(dtype, a, b, 1.0, 0.0, None)
+    assert_close(dtype, host(d.t, np.int32 if dtype == "i8" else np.uint16), ref, tol)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
 @pytest.mark.parametrize("op_a", ["N", "T"])
 @pytest.mark.parametrize("op_b", ["N", "T"])
 @pytest.mark.parametrize("m,n,k", [(272, 8, 208), (272, 144, 208), (272, 304, 208), (256, 256, 320), (512, 384, 192),

@@ -54,7 +54,8 @@ CASES = [("c1_fp16_256", "N"), ("c2_fc1", "T"), ("c2_fc1", "N"), ("c2_fc2", "T")
          ("c2_proj", "T"), ("c2_proj", "N"), ("c3_fwd", "T"), ("c3_bwd", "T"), ("c4_int8", "N"),
          ("c4_int8", "T"), ("c5_4of32_n1", "N"), ("c5_4of32_n8", "N"), ("c5_4of32_n4096", "N"),
          ("c5_8of32_n1", "N"), ("c5_8of32_n8", "N"), ("c5_8of32_n4096", "N"),
-         ("x1_fwd", "T"), ("x1_bwd", "T"), ("x3_qkv", "T"), ("x3_proj", "T"), ("x3_fc1", "T"), ("x3_fc2", "T")]
+         ("x1_fwd", "T"), ("x1_bwd", "T"), ("x3_qkv", "T"), ("x3_proj", "T"), ("x3_fc1", "T"), ("x3_fc2", "T"),
+         ("x2_4of32_n1", "N"), ("x2_4of32_n8", "N")]
 
 
 @pytest.mark.parametrize("name,op_b", CASES, ids=["%s-%s" % c for c in CASES])
