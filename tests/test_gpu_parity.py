@@ -244,8 +244,8 @@ def test_spmm_skinny_tall(dtype, N, M, n, k):
     alpha, beta = (1.0, 1.0) if dtype == "i8" else (0.5, -0.25)
     plan = run_spmm(dtype, N, M, 16400, n, k, "N" if n != 2 else "T", alpha, beta, 5000 + n)
     assert plan.kernel_name == "spmm_skinny"
-    rw = 1 if dtype == "i8" else (4 if n <= 2 else 2)
-    assert plan.spmm_kernel.endswith(", false, %d>(nm::GemmArgs, int)" % rw), plan.spmm_kernel
+    rw = 4 if n <= 2 else 2                                 # rows per wave for N <= 4 kept values per group
+    assert plan.spmm_kernel.endswith(", false, %d, %d>(nm::GemmArgs, int)" % (rw, N)), plan.spmm_kernel
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
