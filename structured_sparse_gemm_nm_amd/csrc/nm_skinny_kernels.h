@@ -26,7 +26,7 @@
 namespace nm {
 
 constexpr int SK2_WAVES = 16;
-constexpr int SK2_LDS = 64 * 1024;   // bytes of staged B per chunk
+constexpr int SK2_LDS = 128 * 1024;  // bytes of staged B per chunk (one block per CU: registers allow no more)
 
 template <int DT, int NP>
 struct SkinnyRec {
@@ -52,7 +52,9 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
   constexpr bool BIG = ELS * NP >= 256;                     // too many products to unroll the words
   // offset bits of a group start at bit 0..31 of the first word and span at most 5 NV bits
   constexpr int MW = DENSE_A ? 0 : (31 + 5 * NV + 31) / 32 < 3 ? (31 + 5 * NV + 31) / 32 : 3;
-  constexpr int DEPTH = RW > 1 || (DENSE_A && ESZ == 1) ? 2 : 4;
+  // iterations of A loads in flight per lane: about 8 pieces per wave across
+  // its RW rows, fewer for wide groups (registers)
+  constexpr int DEPTH = ELS >= 16 ? 2 : ELS == 8 ? (RW > 1 ? 2 : 4) : (8 / RW > 2 ? 8 / RW : 2);
   static_assert(DENSE_A ? NV == 0 : (VB == 1 || VB == 2 || VB == 4 || VB == 8 || VB == 16), "group width");
   typedef typename std::conditional<DT == DT_I8, int32_t, float>::type acc_t;
   extern __shared__ __attribute__((aligned(16))) uint8_t s_b[];
@@ -71,9 +73,10 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
     if constexpr (ESZ == 2) return from_bits16<FDT>((uint16_t)raw);
     else return (acc_t)(int8_t)(uint8_t)raw;
   };
+  const uint8_t* s_cur = s_b;                               // the staged chunk being read
   // the NP staged values of record r
   auto brec = [&](int r, acc_t (&bv)[NP]) __attribute__((always_inline)) {
-    const uint8_t* p = s_b + r * RB;
+    const uint8_t* p = s_cur + r * RB;
     uint32_t w[RB < 4 ? 1 : RB / 4];
     if constexpr (RB == 1) w[0] = *p;
     else if constexpr (RB == 2) w[0] = *(const uint16_t*)p;
@@ -166,8 +169,8 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
     const int win = r >> lw, rem = r & (W - 1);
     return (win << lw) + ((rem & 63) << lm) + (rem >> 6);
   };
-  auto put_rec = [&](int r, const uint32_t* w) __attribute__((always_inline)) {
-    uint8_t* d = s_b + r * RB;
+  auto put_rec = [&](uint8_t* base, int r, const uint32_t* w) __attribute__((always_inline)) {
+    uint8_t* d = base + r * RB;
     if constexpr (RB == 1) *d = (uint8_t)w[0];
     else if constexpr (RB == 2) *(uint16_t*)d = (uint16_t)w[0];
     else if constexpr (RB == 4) *(uint32_t*)d = w[0];
@@ -202,7 +205,7 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
           const bool in = rec_k(r) < kn;
 #pragma unroll
           for (int x = 0; x < RWD; x++) w[q][x] = in ? w[q][x] : 0u;
-          put_rec(r, w[q]);
+          put_rec(s_b, r, w[q]);
         }
       }
     } else {                                                // column by column (op T, or n < NP)
@@ -231,9 +234,42 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
 #pragma unroll
           for (int c = 0; c < NP; c++)
             if (in && c < n) w[(c * ESZ) / 4] |= raw[q][c] << (8 * ((c * ESZ) % 4));
-          put_rec(r, w);
+          put_rec(s_b, r, w);
         }
       }
+    }
+  };
+  // Double-buffered staging (B rows copied whole into 16-byte records; for
+  // narrower records the registers it takes cost more than it saves): the
+  // block reads one half of the LDS while the next chunk's rows, loaded into
+  // registers at the start of the current chunk, are written into the other
+  // half at its last iteration.
+  constexpr bool DB_OK = RB == 16;
+  constexpr int RWDB = RB < 4 ? 1 : RB / 4;                 // words per record
+  constexpr int RPT = DB_OK ? (KC / 2) / (64 * SK2_WAVES) : 1;   // records per thread in half a chunk
+  const bool db = DB_OK && !one_chunk && b_rowvec;
+  uint32_t sreg[RPT][RWDB];
+  auto db_issue = [&](int64_t kc, int kn) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < RPT; q++) {
+      const int kk = rec_k(threadIdx.x + q * 64 * SK2_WAVES);
+      const uint8_t* g = A.b + ((kc + (kk < kn ? kk : kn - 1)) * A.ldb) * ESZ;
+      if constexpr (RB == 4) sreg[q][0] = *(const uint32_t*)g;
+      else if constexpr (RB == 8) { const u32x2 v = *(const u32x2*)g; sreg[q][0] = v[0]; sreg[q][1] = v[1]; }
+      else if constexpr (RB == 16) {
+        const u32x4 v = *(const u32x4*)g;
+        sreg[q][0] = v[0]; sreg[q][1] = v[1]; sreg[q][2] = v[2]; sreg[q][3] = v[3];
+      }
+    }
+  };
+  auto db_put = [&](uint8_t* base, int kn) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < RPT; q++) {
+      const int r = threadIdx.x + q * 64 * SK2_WAVES;
+      const bool in = rec_k(r) < kn;
+#pragma unroll
+      for (int x = 0; x < RWDB; x++) sreg[q][x] = in ? sreg[q][x] : 0u;
+      put_rec(base, r, sreg[q]);
     }
   };
   // combine this wave's sums of row group grp, write them, clear them
@@ -271,13 +307,14 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
 #pragma unroll
     for (int c = 0; c < NP; c++) acc[rr][c] = 0;
   const int64_t gstride = gridDim.x;                        // blocks walk row groups blockIdx.x + j gridDim.x
-  const int nchunks = (int)((A.k + KC - 1) / KC);
+  const int kcs = db ? KC / 2 : KC;                         // k per chunk (a multiple of every window)
+  const int nchunks = (int)((A.k + kcs - 1) / kcs);
   if (nchunks == 0) {                                       // k = 0: D = beta C
     for (int64_t grp = blockIdx.x; grp < row_groups; grp += gstride) flush(grp, acc);
     return;
   }
-  const int kn_last = (int)(A.k - (int64_t)(nchunks - 1) * KC);
-  const int nit_full = KC / W;
+  const int kn_last = (int)(A.k - (int64_t)(nchunks - 1) * kcs);
+  const int nit_full = kcs / W;
   const int nit_last = DENSE_A ? ((kn_last + EPC - 1) / EPC + 63) / 64 : (kn_last / M + 63) / 64;
   struct Cur { int64_t grp; int c, it; };
   auto advance = [&](Cur& q) __attribute__((always_inline)) {
@@ -293,31 +330,56 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
     const int64_t row0 = (ld.grp * SK2_WAVES + wave) * RW;
 #pragma unroll
     for (int rr = 0; rr < RW; rr++)
-      load_piece(row0 + rr, (int64_t)ld.c * KC, ld.c == nchunks - 1 ? kn_last : KC, ld.it, pc[rr][u]);
+      load_piece(row0 + rr, (int64_t)ld.c * kcs, ld.c == nchunks - 1 ? kn_last : kcs, ld.it, pc[rr][u]);
     advance(ld);
   }
   bool staged = false;
+  const int half = (KC / 2) * RB;                           // bytes of one LDS half (double-buffered)
+  int begun = 0;                                            // chunks begun (double-buffered)
+  bool pend = false;                                        // the next chunk is in registers
+  int pend_kn = 0;
+  if (db) {                                                 // chunk 0 into half 0
+    db_issue(0, nchunks == 1 ? kn_last : kcs);
+    db_put(s_b, nchunks == 1 ? kn_last : kcs);
+  }
   while (us.grp < row_groups) {
 #pragma unroll
     for (int u = 0; u < DEPTH; u++) {
       if (us.grp >= row_groups) break;
-      const int64_t kc = (int64_t)us.c * KC;
+      const int64_t kc = (int64_t)us.c * kcs;
+      const int kn = us.c == nchunks - 1 ? kn_last : kcs;
       if (us.it == 0) {
         if (us.c == 0 && us.grp != blockIdx.x) flush(us.grp - gstride, acc);
-        if (!(one_chunk && staged)) {
+        if (db) {
+          // this chunk is in its half; every wave is done with the previous
+          // chunk, so the other half is free
+          __syncthreads();
+          s_cur = s_b + (begun & 1) * half;
+          begun++;
+          const int nc = us.c + 1 == nchunks ? 0 : us.c + 1;
+          pend = (nc == 0 ? us.grp + gstride : us.grp) < row_groups;
+          if (pend) {
+            pend_kn = nc == nchunks - 1 ? kn_last : kcs;
+            db_issue((int64_t)nc * kcs, pend_kn);
+          }
+        } else if (!(one_chunk && staged)) {
           __syncthreads();                                  // the previous chunk's readers are done
-          stage_chunk(kc, us.c == nchunks - 1 ? kn_last : KC);
+          stage_chunk(kc, kn);
           __syncthreads();
           staged = true;
         }
       }
       const int64_t lrow0 = (ld.grp * SK2_WAVES + wave) * RW;
-      const int64_t lkc = (int64_t)ld.c * KC;
-      const int lkn = ld.c == nchunks - 1 ? kn_last : KC;
+      const int64_t lkc = (int64_t)ld.c * kcs;
+      const int lkn = ld.c == nchunks - 1 ? kn_last : kcs;
 #pragma unroll
       for (int rr = 0; rr < RW; rr++) {
-        use_piece(kc, us.c == nchunks - 1 ? kn_last : KC, us.it, pc[rr][u], acc[rr]);
+        use_piece(kc, kn, us.it, pc[rr][u], acc[rr]);
         load_piece(lrow0 + rr, lkc, lkn, ld.it, pc[rr][u]);   // rows past m load nothing
+      }
+      if (pend && us.it == (us.c == nchunks - 1 ? nit_last : nit_full) - 1) {
+        db_put(s_b + (begun & 1) * half, pend_kn);          // the next chunk, into the free half
+        pend = false;
       }
       advance(ld);
       advance(us);

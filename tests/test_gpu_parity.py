@@ -249,6 +249,30 @@ def test_spmm_skinny_tall(dtype, N, M, n, k):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("N,M,m", [(2, 4, 200), (4, 32, 4200), (0, 0, 300)])
+def test_skinny_double_buffered(dtype, N, M, m):
+    """16-byte B records (n = 8 for 16-bit types, 16 for int8) with k past one
+    LDS chunk: the next chunk is staged while the current one is read; k = 12352
+    leaves a 64-wide last chunk, 4200 rows give blocks a second row group.
+    N = 0 runs the dense comparator on the same path."""
+    n, k = (16 if dtype == "i8" else 8), 12352
+    if N:
+        plan = run_spmm(dtype, N, M, m, n, k, "N", 1.0, 0.0, 6000 + m)
+        assert plan.kernel_name == "spmm_skinny"
+        return
+    a = rand(dtype, (m, k), 61)
+    b = rand(dtype, (k, n), 62)
+    plan = plan_for(dtype, m, n, k, 2, 4)
+    odt = torch.int32 if dtype == "i8" else torch.int16
+    d = Guarded((m, n), odt)
+    nm.nm_dense_gemm(plan, 1.0, dev(a), dev(b), 0.0, None, d.t)
+    sync()
+    d.check()
+    ref, tol = ref_product(dtype, a, b, 1.0, 0.0, None)
+    assert_close(dtype, host(d.t, np.int32 if dtype == "i8" else np.uint16), ref, tol)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
 @pytest.mark.parametrize("n,k", [(1, 4160), (8, 1040)])
 def test_dense_skinny_tall(dtype, n, k):
     m = 16400
