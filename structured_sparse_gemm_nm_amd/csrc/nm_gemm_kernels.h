@@ -302,6 +302,82 @@ __device__ __forceinline__ void expand_gather(uint8_t* adense, const uint8_t* st
   }
 }
 
+// General N:M with M = 32 and GV value bytes per group (4, 8 or 16): each
+// thread owns (row, group) pairs of the block's k-step, loads a pair's kept
+// values and the metadata words holding its offsets straight into registers
+// one step ahead (indices clamped into the operand: rows past m load row
+// m - 1, groups past k the last group), and expands it into the idle dense A
+// buffer: zero the group's 32 elements, then write its kept values at their
+// offsets.
+template <int ESZ, int ROWS, int GV>
+struct G32Regs {
+  static constexpr int GPS = KBYTES / ESZ / 32;               // groups per row per step
+  static constexpr int PAIRS = ROWS * GPS / NTH;
+  static constexpr int NV = GV / ESZ;                         // kept values per group
+  static constexpr int MW = (31 + 5 * NV + 31) / 32 < 3 ? (31 + 5 * NV + 31) / 32 : 3;
+  uint32_t v[PAIRS > 0 ? PAIRS : 1][GV / 4];
+  uint32_t m[PAIRS > 0 ? PAIRS : 1][MW];
+};
+
+template <int ESZ, int ROWS, int GV>
+__device__ __forceinline__ void load_g32(G32Regs<ESZ, ROWS, GV>& R, const GemmArgs& A, int64_t r0, int ks) {
+  typedef G32Regs<ESZ, ROWS, GV> G;
+  static_assert(G::PAIRS > 0 && (ROWS * G::GPS) % NTH == 0 && (GV == 4 || GV == 8 || GV == 16), "pairs per thread");
+  const int64_t groups = A.k >> 5, mwords = A.mld / 4;
+#pragma unroll
+  for (int i = 0; i < G::PAIRS; i++) {
+    const int p = threadIdx.x + i * NTH, r = p / G::GPS, g = p % G::GPS;
+    const int64_t row = r0 + r < A.m ? r0 + r : A.m - 1;
+    const int64_t gg0 = (int64_t)ks * G::GPS + g;
+    const int64_t gg = gg0 < groups ? gg0 : groups - 1;
+    const uint8_t* pv = A.a + (row * A.lda + gg * G::NV) * ESZ;
+    if constexpr (GV == 16) {
+      const u32x4 v = *(const u32x4*)pv;
+      R.v[i][0] = v[0]; R.v[i][1] = v[1]; R.v[i][2] = v[2]; R.v[i][3] = v[3];
+    } else if constexpr (GV == 8) {
+      const u32x2 v = *(const u32x2*)pv;
+      R.v[i][0] = v[0]; R.v[i][1] = v[1];
+    } else {
+      R.v[i][0] = *(const uint32_t*)pv;
+    }
+    const int64_t w0 = (gg * G::NV * 5) >> 5;                  // the group's bits end inside the row
+    const uint32_t* mr = (const uint32_t*)(A.meta + row * A.mld);
+#pragma unroll
+    for (int x = 0; x < G::MW; x++) R.m[i][x] = mr[w0 + x < mwords ? w0 + x : mwords - 1];
+  }
+}
+
+template <int ESZ, int ROWS, int GV>
+__device__ __forceinline__ void expand_g32(uint8_t* adense, const G32Regs<ESZ, ROWS, GV>& R, const GemmArgs& A,
+                                           int ks) {
+  typedef G32Regs<ESZ, ROWS, GV> G;
+  const int64_t groups = A.k >> 5;
+#pragma unroll
+  for (int i = 0; i < G::PAIRS; i++) {
+    const int p = threadIdx.x + i * NTH, r = p / G::GPS, g = p % G::GPS;
+    const int64_t gg = (int64_t)ks * G::GPS + g;
+    uint8_t* dst = adense + r * BSTRIDE + g * 32 * ESZ;
+#pragma unroll
+    for (int x = 0; x < 2 * ESZ; x++) *(u32x4*)(dst + 16 * x) = u32x4{0u, 0u, 0u, 0u};
+    if (gg >= groups) continue;                                 // past k: zeros
+    const int off = (int)((gg * G::NV * 5) & 31);
+    const uint64_t lo = ((uint64_t)R.m[i][1] << 32) | R.m[i][0];
+    uint64_t hi = 0;
+    if constexpr (G::MW == 3) hi = ((uint64_t)R.m[i][2] << 32) | R.m[i][1];
+#pragma unroll
+    for (int s = 0; s < G::NV; s++) {
+      const int pbit = off + 5 * s;
+      uint64_t w;
+      if constexpr (G::MW == 3) w = pbit < 32 ? lo >> pbit : hi >> (pbit - 32);
+      else w = lo >> pbit;
+      const int j = (int)(w & 31u);
+      const uint32_t word = R.v[i][(s * ESZ) / 4];
+      if constexpr (ESZ == 2) *(uint16_t*)(dst + 2 * j) = (uint16_t)(word >> (16 * (s & 1)));
+      else dst[j] = (uint8_t)(word >> (8 * (s & 3)));
+    }
+  }
+}
+
 // ---------------------------------------------------------------- matrix instructions
 
 template <int DT> struct Frag;
@@ -372,15 +448,17 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, in
 //   and 16+8q..16+8q+7.  int8 32x32x64: A = compressed bytes 16q..16q+15,
 //   index 32 bits; B = k 16q..16q+15 and 32+16q..32+16q+15.
 //  dense 32x32x16 (16-bit) / 32x32x32 (int8): A and B = 16 bytes at 16q.
-template <int DT, int AMODE, int BKC, int AKC, int BM, int BN>
+template <int DT, int AMODE, int BKC, int AKC, int BM, int BN, int GV = 0>
 __global__ void __launch_bounds__(NTH) gemm_kernel(GemmArgs A) {
   constexpr int ESZ = DT == DT_I8 ? 1 : 2;
   constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
   constexpr int LDS_A = AMODE == A_SPARSE24 ? BM * ASTRIDE_SP : BM * BSTRIDE;
   constexpr int LDS_B = BN * BSTRIDE;
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[AMODE == A_GATHER ? 1 : 2][LDS_A];
+  constexpr bool SERIAL_GATHER = AMODE == A_GATHER && GV == 0;   // general N:M through LDS staging
+  constexpr bool REG_GATHER = AMODE == A_GATHER && GV > 0;       // M = 32 through registers
+  __shared__ __attribute__((aligned(16))) uint8_t s_a[SERIAL_GATHER ? 1 : 2][LDS_A];
   __shared__ __attribute__((aligned(16))) uint8_t s_b[2][LDS_B];
-  __shared__ __attribute__((aligned(16))) uint8_t s_stg[AMODE == A_GATHER ? BM * (STG_V + STG_M) : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t s_stg[SERIAL_GATHER ? BM * (STG_V + STG_M) : 16];
 
   typedef typename Acc<DT>::t acc_t;
   typedef typename Frag<DT>::ab ab_t;
@@ -408,6 +486,7 @@ __global__ void __launch_bounds__(NTH) gemm_kernel(GemmArgs A) {
   KChunks<BN> rb;
   KChunks<BM> ra;
   SpChunks<BM> rs;
+  G32Regs<ESZ, BM, GV == 0 ? 4 : GV> rg;
   auto load_step = [&](int ks) {
     const int64_t k0 = (int64_t)ks * KL;
     if (BKC) load_kcontig<ESZ, BN>(rb, A.b, c0, A.n, A.ldb, k0, A.k, A.b_vec);
@@ -417,8 +496,9 @@ __global__ void __launch_bounds__(NTH) gemm_kernel(GemmArgs A) {
       else load_mncontig<ESZ, BM>(ra, A.a, r0, A.m, A.lda, k0, A.k, A.a_vec);
     }
     if (AMODE == A_SPARSE24) load_sp24<ESZ, BM>(rs, A, r0, ks);
+    if constexpr (REG_GATHER) load_g32(rg, A, r0, ks);
   };
-  auto store_step = [&](int buf) {
+  auto store_step = [&](int buf, int ks) {
     if (BKC) store_kcontig<BN>(s_b[buf], rb);
     else store_mncontig<ESZ, BN>(s_b[buf], rb);
     if (AMODE == A_DENSE) {
@@ -426,6 +506,7 @@ __global__ void __launch_bounds__(NTH) gemm_kernel(GemmArgs A) {
       else store_mncontig<ESZ, BM>(s_a[buf], ra);
     }
     if (AMODE == A_SPARSE24) store_sp24<ESZ, BM>(s_a[buf], rs);
+    if constexpr (REG_GATHER) expand_g32(s_a[buf], rg, A, ks);
   };
 
   auto compute = [&](const uint8_t* la, const uint8_t* lb) {
@@ -466,11 +547,11 @@ __global__ void __launch_bounds__(NTH) gemm_kernel(GemmArgs A) {
     }
   };
 
-  if constexpr (AMODE == A_GATHER) {
+  if constexpr (SERIAL_GATHER) {
     for (int ks = 0; ks < ksteps; ks++) {
       load_step(ks);
       stage_gather<ESZ, BM>(s_stg, A, r0, ks);
-      store_step(0);
+      store_step(0, ks);
       __syncthreads();
       expand_gather<ESZ, BM>(s_a[0], s_stg, A, ks);
       __syncthreads();
@@ -482,14 +563,14 @@ __global__ void __launch_bounds__(NTH) gemm_kernel(GemmArgs A) {
     // go to the idle LDS buffer afterwards and the loads for s+2 start.
     if (ksteps > 0) {
       load_step(0);
-      store_step(0);
+      store_step(0, 0);
     }
     if (ksteps > 1) load_step(1);
     __syncthreads();
     for (int ks = 0; ks < ksteps; ks++) {
       const int buf = ks & 1;
       compute(s_a[buf], s_b[buf]);
-      if (ks + 1 < ksteps) store_step(buf ^ 1);
+      if (ks + 1 < ksteps) store_step(buf ^ 1, ks + 1);
       if (ks + 2 < ksteps) load_step(ks + 2);
       __syncthreads();
     }
@@ -1180,6 +1261,19 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
       else if (!bkc && akc) NM_LAUNCH((gemm_fast_kernel<DT, AMODE, 0, 1, TM, TN>), grid, dim3(NTH), 0, s, A);
       else if (AMODE == A_DENSE && bkc) NM_LAUNCH((gemm_fast_kernel<DT, A_DENSE, 1, 0, TM, TN>), grid, dim3(NTH), 0, s, A);
       else if (AMODE == A_DENSE) NM_LAUNCH((gemm_fast_kernel<DT, A_DENSE, 0, 0, TM, TN>), grid, dim3(NTH), 0, s, A);
+      return launch_status();
+    }
+  }
+  if constexpr (AMODE == A_GATHER) {
+    // M = 32 with 4-, 8- or 16-byte groups: expanded from registers, pipelined
+    const int gv = (int)(A.N * pl.esz_ab);
+    if (A.M == 32 && !pl.old_skinny && (gv == 4 || gv == 8 || gv == 16)) {
+      if (gv == 4 && bkc) NM_LAUNCH((gemm_kernel<DT, AMODE, 1, 1, TM, TN, 4>), grid, dim3(NTH), 0, s, A);
+      else if (gv == 4) NM_LAUNCH((gemm_kernel<DT, AMODE, 0, 1, TM, TN, 4>), grid, dim3(NTH), 0, s, A);
+      else if (gv == 8 && bkc) NM_LAUNCH((gemm_kernel<DT, AMODE, 1, 1, TM, TN, 8>), grid, dim3(NTH), 0, s, A);
+      else if (gv == 8) NM_LAUNCH((gemm_kernel<DT, AMODE, 0, 1, TM, TN, 8>), grid, dim3(NTH), 0, s, A);
+      else if (bkc) NM_LAUNCH((gemm_kernel<DT, AMODE, 1, 1, TM, TN, 16>), grid, dim3(NTH), 0, s, A);
+      else NM_LAUNCH((gemm_kernel<DT, AMODE, 0, 1, TM, TN, 16>), grid, dim3(NTH), 0, s, A);
       return launch_status();
     }
   }

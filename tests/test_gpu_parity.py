@@ -218,7 +218,7 @@ def test_spmm_kernel_names_the_launched_kernel():
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
-@pytest.mark.parametrize("N,M", [(1, 4), (3, 4), (2, 8), (5, 16), (4, 32), (8, 32)])
+@pytest.mark.parametrize("N,M", [(1, 4), (3, 4), (2, 8), (5, 16), (2, 32), (4, 32), (8, 32), (16, 32)])
 @pytest.mark.parametrize("op_b", ["N", "T"])
 def test_spmm_gather(dtype, N, M, op_b):
     alpha, beta = (1.0, 1.0) if dtype == "i8" else (0.5, 0.25)
