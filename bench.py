@@ -69,6 +69,8 @@ def parse():
                     help="also run a plain %d MiB elementwise copy (y = -x) %d times (for counter calibration)" % (CAL_MIB, CAL_REPS))
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic_<workload>.md")
+    ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
+                    help="turn a rocprofv3 --pmc run of the matrix-core counters into profiles/mfma_<workload>.md")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="turn a rocprofv3 --kernel-trace --stats run into a profiles/ summary")
     ap.add_argument("--command", default="", help="the command that produced the runs (recorded in summaries)")
@@ -99,6 +101,9 @@ def main():
         return
     if args.summarize_trace:
         summarize_trace(args)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this library's hot path is single-GPU "
@@ -149,7 +154,7 @@ def main():
         gemms.append(g)
 
     # The step calls the C ABI with arguments marshalled once, so that the host
-    # enqueues well ahead of the GPU and the events around each SpMM launch
+    # enqueues well ahead of the GPU and the events around a SpMM launch
     # (recorded on the stream the kernels run on) time the kernel, not host gaps.
     import ctypes
     L = nm.lib()
@@ -170,21 +175,25 @@ def main():
         calls.append((L.nm_decompress, (h, P(g["vals"]), P(g["meta"]), P(g["Ad"]), sp), None))
 
     n_spmm = sum(1 for c in calls if c[2] is not None)
+    spmm_kernel = {(g["label"], ob): g["plans"][ob].spmm_kernel for g in gemms for ob in g["layouts"]}
+    # events are created before any timed pass
     pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(n_spmm * args.steps)]              # created before the timed region
+            for _ in range(n_spmm * args.steps)]
     empty_pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                   for _ in range(args.steps)]
-    empty = []
 
-    def step(ev=None):
-        if ev is not None:
-            # an event pair around nothing: the events' own cost on the queue
+    def step(ev=None, only=None, empty=None):
+        """One pass of the hot path. With `ev`, the SpMM launches whose device
+        kernel is in `only` (all when None) are bracketed by an event pair on the
+        launch stream; with `empty`, an event pair around nothing is recorded first
+        (the events' own cost on the queue)."""
+        if empty is not None:
             e0, e1 = empty_pool[len(empty)]
             e0.record(stream)
             e1.record(stream)
             empty.append((e0, e1))
         for fn, a, key in calls:
-            if ev is not None and key is not None:
+            if ev is not None and key is not None and (only is None or spmm_kernel[key] in only):
                 e0, e1 = pool[len(ev)]
                 e0.record(stream)
                 st = fn(*a)
@@ -209,11 +218,29 @@ def main():
     viol = [int(g["cnt"].item()) for g in gemms]
     assert all(v == 0 for v in viol), "prune check failed: %s" % viol
 
+    # Per-launch pass (not the timed region): every SpMM launch bracketed by
+    # events, to time each GEMM and find the device kernel with the most time.
+    all_ev, empty = [], []
+    for _ in range(args.steps):
+        step(all_ev, None, empty)
+    torch.cuda.synchronize()
+    event_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in empty]))
+    per = {}
+    for key, e0, e1 in all_ev:
+        per.setdefault(key, []).append(e0.elapsed_time(e1))
+    spmm_ms = {k: max(float(np.median(v)) - event_ms, 1e-6) for k, v in per.items()}   # events' cost removed
+    kern_ms = {}
+    for key, t in spmm_ms.items():
+        kern_ms[spmm_kernel[key]] = kern_ms.get(spmm_kernel[key], 0.0) + t
+    dom_key = max(kern_ms, key=kern_ms.get)
+
+    # Timed region: K steps; only the dominant kernel's launches carry events
+    # (each event pair adds its own few microseconds to the queue).
     events = []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(events)
+        step(events, {dom_key})
     t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -225,31 +252,22 @@ def main():
 
     step_flops = sum(flops_dense_eq(g) * len(g["layouts"]) for g in gemms)
     value = step_flops / (ms_per_step * 1e-3) / 1e12
-
-    # per-launch SpMM durations
-    per = {}
-    for key, e0, e1 in events:
-        per.setdefault(key, []).append(e0.elapsed_time(e1))
-    event_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in empty]))
-    raw_ms = {k: float(np.median(v)) for k, v in per.items()}
-    spmm_ms = {k: max(v - event_ms, 1e-6) for k, v in raw_ms.items()}     # launch duration, events' cost removed
     spmm_total_ms = sum(spmm_ms[(g["label"], ob)] for g in gemms for ob in g["layouts"])
     spmm_only_tflops = step_flops / (spmm_total_ms * 1e-3) / 1e12
+    dom_launch_ms = max(float(np.median([e0.elapsed_time(e1) for _, e0, e1 in events])) - event_ms, 1e-6)
 
     # dominant kernel: the device kernel (as the profiler names it) with the most SpMM time
     kern = {}
     for g in gemms:
         for ob in g["layouts"]:
             kk = g["plans"][ob].spmm_kernel
-            d = kern.setdefault(kk, dict(ms=0.0, flops=0.0, bytes=0.0, launches=0, dtype=g["dtype"]))
-            d["ms"] += spmm_ms[(g["label"], ob)]
+            d = kern.setdefault(kk, dict(flops=0.0, bytes=0.0, launches=0, dtype=g["dtype"]))
             d["launches"] += 1
             keep = g["N"] / g["M"]
             d["flops"] += 2.0 * g["m"] * g["n"] * g["k"] * keep            # multiply-adds actually required
             d["bytes"] += spmm_bytes(g)
-    dom_key = max(kern, key=lambda kk: kern[kk]["ms"])
     dom = kern[dom_key]
-    avg_ms = dom["ms"] / dom["launches"]
+    avg_ms = dom_launch_ms
     avg_flops = dom["flops"] / dom["launches"]
     avg_bytes = dom["bytes"] / dom["launches"]
     ai = avg_flops / avg_bytes
@@ -265,8 +283,9 @@ def main():
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
     roofline["kernel"] = dom_key
     roofline["launch_ms"] = round(avg_ms, 5)
-    roofline["launch_ms_method"] = ("median over the timed steps of the HIP-event interval around each launch, less the "
-                                    "median interval of an empty event pair in the same steps (%.5f ms)" % event_ms)
+    roofline["launch_ms_method"] = ("median over the timed steps of the HIP-event interval around each launch of this "
+                                    "kernel (the only events in the timed region), less the median interval of an empty "
+                                    "event pair (%.5f ms)" % event_ms)
     roofline["launches_per_step"] = dom["launches"]
     traffic = load_traffic(args.workload, dom_key)
     if traffic is not None:
@@ -450,6 +469,71 @@ def summarize_counters(args):
         fh.write("\nSource fingerprint %s: bench.py reports these figures only while the library sources match.\n\n"
                  % rec["sources"])
         fh.write("record: %s\n" % json.dumps(rec))
+    print("wrote", path)
+
+
+# Matrix-core rate per clock of the whole GPU at the datasheet peaks (2516.6 dense
+# fp16/bf16 TFLOP/s at 2.4 GHz): MOPS counters count 512 flops each (dense
+# equivalent for the 2:4 instructions), so 2048 MOPS/clock dense, 4096 sparse.
+NOMINAL_MOPS_PER_CLK = {"dense": 2048.0, "sparse": 4096.0}
+SPARSE_PEAK_F16 = 2 * PEAK_TFLOPS["f16"]          # 2:4 dense-equivalent datasheet figure
+N_XCD, N_SIMD = 8, 1024
+
+
+def summarize_mfma(args):
+    """Matrix-core use per kernel from one rocprofv3 --pmc run of SQ_INSTS_VALU_MFMA_MOPS_<type>,
+    SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE (the bench's calibration loops run in the same process)."""
+    import csv
+    import glob
+    vals, dur = {}, {}
+    for f in glob.glob(os.path.join(args.summarize_mfma, "**", "*counter_collection.csv"), recursive=True):
+        for r in csv.DictReader(open(f)):
+            k = r["Kernel_Name"]
+            key = (r["Dispatch_Id"], r["Counter_Name"])
+            vals.setdefault(k, {}).setdefault(key, 0.0)
+            vals[k][key] += float(r["Counter_Value"])
+            dur.setdefault(k, {})[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    if not vals:
+        raise SystemExit("no counter_collection.csv under %s" % args.summarize_mfma)
+    rows = []
+    for k, d in vals.items():
+        per = {}
+        for (disp, cname), v in d.items():
+            per.setdefault(cname, []).append(v)
+        mops_name = [c for c in per if c.startswith("SQ_INSTS_VALU_MFMA_MOPS_")]
+        if not mops_name or "GRBM_GUI_ACTIVE" not in per:
+            continue
+        mops = float(np.mean(per[mops_name[0]]))
+        if mops <= 0:
+            continue
+        cyc = float(np.mean(per["GRBM_GUI_ACTIVE"])) / N_XCD          # GRBM counts once per XCD
+        busy = float(np.mean(per.get("SQ_VALU_MFMA_BUSY_CYCLES", [0.0])))
+        sec = float(np.mean(list(dur[k].values())))
+        rows.append(dict(kernel=k, dispatches=len(per["GRBM_GUI_ACTIVE"]), us=sec * 1e6, mops=mops, cycles=cyc,
+                         ghz=cyc / sec / 1e9, tflops=mops * 512 / sec / 1e12, mops_clk=mops / cyc,
+                         busy=busy / (cyc * N_SIMD), counter=mops_name[0]))
+    rows.sort(key=lambda r: -r["us"] * r["dispatches"])
+    loops = {("sparse" if "<true" in r["kernel"] else "dense"): r for r in rows if "matrix_loop" in r["kernel"]}
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, "mfma_%s.md" % args.workload)
+    with open(path, "w") as fh:
+        fh.write("# Matrix-core use: %s\n\nCommand:\n\n    %s\n\n" % (WORKLOAD_DESC[args.workload], args.command))
+        fh.write("Columns: dense-equivalent TFLOP/s = MOPS x 512 / dispatch time; clock = GRBM_GUI_ACTIVE / %d XCDs "
+                 "/ dispatch time; MOPS/clk against the datasheet rate per clock (%d dense, %d sparse for the whole "
+                 "GPU); busy = SQ_VALU_MFMA_BUSY_CYCLES / (%d SIMDs x clocks). The `matrix_loop` rows are the "
+                 "bench's calibration loops (matrix instructions only, no memory traffic): the achievable rate.\n\n"
+                 % (N_XCD, NOMINAL_MOPS_PER_CLK["dense"], NOMINAL_MOPS_PER_CLK["sparse"], N_SIMD))
+        fh.write("For dispatches of a few tens of microseconds GRBM_GUI_ACTIVE also counts the dispatch's own "
+                 "overhead (the clock column then reads above the real clock), so the per-clock columns understate "
+                 "those kernels; `of sparse peak` (dense-equivalent TFLOP/s / %.1f) uses time only.\n\n" % SPARSE_PEAK_F16)
+        fh.write("| kernel | dispatches | us | dense-eq TFLOP/s | of sparse peak | clock GHz | MOPS/clk | of dense rate "
+                 "| of sparse rate | of sparse loop | MFMA busy |\n|---|---|---|---|---|---|---|---|---|---|---|\n")
+        for r in rows:
+            sl = loops.get("sparse")
+            fh.write("| `%s` | %d | %.1f | %.1f | %.3f | %.2f | %.0f | %.3f | %.3f | %s | %.3f |\n" % (
+                r["kernel"][:90], r["dispatches"], r["us"], r["tflops"], r["tflops"] / SPARSE_PEAK_F16, r["ghz"], r["mops_clk"],
+                r["mops_clk"] / NOMINAL_MOPS_PER_CLK["dense"], r["mops_clk"] / NOMINAL_MOPS_PER_CLK["sparse"],
+                "%.3f" % (r["mops_clk"] / sl["mops_clk"]) if sl else "n/a", r["busy"]))
     print("wrote", path)
 
 

@@ -131,6 +131,7 @@ nm_status_t nm_plan_init(nm_plan_t* plan, const nm_problem_t* p) {
   pl->no_dma_nn = getenv("NM_NO_DMA_NN") != nullptr;
   pl->no_deep_ring = getenv("NM_NO_DEEP_RING") != nullptr;
   pl->old_skinny = getenv("NM_OLD_SKINNY") != nullptr;
+  pl->tile_elemwise = getenv("NM_TILE_ELEMWISE") != nullptr;
   // kernel choice
   if (p->n <= 16) pl->kernel = K_SKINNY;
   else if (N == 2 && M == 4) pl->kernel = K_SMFMAC_24;

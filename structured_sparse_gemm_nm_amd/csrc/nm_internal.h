@@ -20,10 +20,11 @@ struct nm_plan {
   std::string spmm_symbol;  // device kernel nm_spmm launches (filled on first query)
   // kernel-selection overrides for benchmark sweeps, read from the environment
   // once at plan creation (NM_FORCE_TILE = 128 | 256x128 | 256, NM_NO_DMA,
-  // NM_NO_DMA_NN, NM_NO_DEEP_RING, NM_OLD_SKINNY), so launches do not scan the
-  // environment
+  // NM_NO_DMA_NN, NM_NO_DEEP_RING, NM_OLD_SKINNY, NM_TILE_ELEMWISE), so
+  // launches do not scan the environment
   int force_tile;           // -1 = automatic, else nm::TileCfg
   bool no_dma, no_dma_nn, no_deep_ring, old_skinny;
+  bool tile_elemwise;       // prune/compress/decompress on the LDS tile kernels even where the row path applies
 };
 
 namespace nm {
@@ -57,6 +58,11 @@ inline hipError_t launch_status() { return launch_probe().armed ? hipSuccess : h
 
 // ---- launchers (return hipError_t from the launch) ----
 hipError_t launch_prune_1d(const nm_plan& pl, const void* a, void* out, uint32_t* mask, hipStream_t s);
+// register path for op_a = N with 16-byte rows and N:M in {2:4, 4:32, 8:32}
+bool row_path_ok(const nm_plan& pl);
+hipError_t launch_row_prune(const nm_plan& pl, const void* a, void* out, uint32_t* mask, hipStream_t s);
+hipError_t launch_row_compress(const nm_plan& pl, const void* a, void* vals, void* meta, hipStream_t s);
+hipError_t launch_row_decompress(const nm_plan& pl, const void* vals, const void* meta, void* out, hipStream_t s);
 hipError_t launch_prune_tile(const nm_plan& pl, const void* a, void* out, uint32_t* mask, hipStream_t s);
 hipError_t launch_check(const nm_plan& pl, const void* a, int mode, int32_t* count, hipStream_t s);
 hipError_t launch_compress(const nm_plan& pl, const void* a, void* vals, void* meta, hipStream_t s);

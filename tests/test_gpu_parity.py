@@ -122,6 +122,61 @@ def test_compress_decompress(dtype, N, M, op):
     assert np.array_equal(host(out.t, RAW[dtype]), dref)
 
 
+ROW_NM = [(2, 4), (4, 32), (8, 32)]
+
+
+def row_shapes(dtype, M):
+    """(m, k) for the register path: one group; a ragged last 16-byte unit; a ragged
+    last segment of 64 units; several whole segments plus a ragged one."""
+    es = 1 if dtype == "i8" else 2
+    gu = max(1, 16 // (M * es))                 # groups per 16-byte unit
+    return [(3, M), (5, (gu * 64 + 1) * M), (4, 3 * M), (2, (gu * 64 * 3 + gu + 1) * M)]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("N,M", ROW_NM)
+@pytest.mark.parametrize("path", ["row", "tile"])
+def test_row_path_ragged(dtype, N, M, path, monkeypatch):
+    """Prune, compress and decompress for op_a = N on padded rows (lda > k): the
+    register path and, forced, the LDS tile path. Bytes between k and lda are the
+    caller's and must be left alone."""
+    if path == "tile":
+        monkeypatch.setenv("NM_TILE_ELEMWISE", "1")
+    es = 1 if dtype == "i8" else 2
+    for (m, k) in row_shapes(dtype, M):
+        lda = -(-k // (16 // es)) * (16 // es) + 16 // es
+        full = rand(dtype, (m, lda), 600 + k + N)
+        a = np.ascontiguousarray(full[:, :k])
+        plan = plan_for(dtype, m, 8, k, N, M, lda=lda)
+        ref, keep = oracle.prune_1d(a, dtype, N, M)
+        sentinel = np.full((m, lda), 0x5A if es == 1 else 0x5A5A, dtype=RAW[dtype])
+        out = Guarded((m, lda), TRAW[dtype], fill=dev(sentinel))
+        mask = Guarded((plan.mask_bytes // 4,), torch.int32)
+        nm.nm_prune(plan, dev(full), out.t, "1d", mask.t)
+        sync()
+        out.check(); mask.check()
+        got = host(out.t, RAW[dtype])
+        assert np.array_equal(got[:, :k], ref), (m, k)
+        assert np.array_equal(got[:, k:], sentinel[:, k:]), (m, k)
+        assert np.array_equal(host(mask.t, np.uint32).reshape(m, -1), oracle.mask_bits(keep)), (m, k)
+        vref, mref = oracle.compress(a, dtype, N, M)
+        vals = Guarded((m, plan.values_ld), TRAW[dtype], fill=torch.full((m, plan.values_ld), -1, dtype=TRAW[dtype]))
+        meta = Guarded((m, plan.meta_ld), torch.uint8, fill=torch.full((m, plan.meta_ld), 0xEE, dtype=torch.uint8))
+        nm.nm_compress(plan, dev(full), vals.t, meta.t)
+        sync()
+        vals.check(); meta.check()
+        assert np.array_equal(host(vals.t, RAW[dtype]), vref), (m, k)
+        assert np.array_equal(host(meta.t, np.uint8), mref), (m, k)
+        dref = oracle.decompress(vref, mref, dtype, m, k, N, M)
+        dec = Guarded((m, lda), TRAW[dtype], fill=dev(sentinel))
+        nm.nm_decompress(plan, dev(vref), dev(mref), dec.t)
+        sync()
+        dec.check()
+        got = host(dec.t, RAW[dtype])
+        assert np.array_equal(got[:, :k], dref), (m, k)
+        assert np.array_equal(got[:, k:], sentinel[:, k:]), (m, k)
+
+
 # ------------------------------------------------------------------ products
 
 def ref_product(dtype, ahat_logical, b_logical, alpha, beta, c):
