@@ -51,7 +51,7 @@ WORKLOAD_DESC = {
     "x1": "fp16 transposable 2:4 pair at the training shapes: W 11008x4096, X 8192x4096, dY 8192x11008, NT",
     "x2": "fp16 4:32 GEMV and n = 8 beyond the Infinity Cache: A 32768x32768 (compressed 268 MB + 84 MB metadata), NN",
     "x3": "the cuSPARSELt blog's Table 1 shapes: QKV 3072x1024, PROJ 1024x1024, FC1 4096x1024, FC2 1024x4096 "
-          "weights, 16384 tokens, fp16 2:4, NT (D row-major; the blog's is column-major)",
+          "weights, 16384 tokens, fp16 2:4, NT, D column-major as in the blog",
     "c5_4of32": "fp16 4:32, A 4096x4096, B 4096 x {1, 8, 4096}, NN",
     "c5_8of32": "fp16 8:32, A 4096x4096, B 4096 x {1, 8, 4096}, NN",
 }
@@ -137,8 +137,10 @@ def main():
             bs[ob] = inputs.workload_inputs(wname, ob)[1]
         mode = "tile" if w.get("tile") else "1d"
         g = dict(label=label, name=wname, w=w, dtype=dtype, m=m, n=n, k=k, N=N, M=M, mode=mode, op_a=op_a)
-        g["plan"] = nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=layouts[0], dtype=dtype)
-        g["plans"] = {ob: nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=ob, dtype=dtype) for ob in layouts}
+        order = w.get("order_cd", "row")
+        g["plan"] = nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=layouts[0], dtype=dtype, order_cd=order)
+        g["plans"] = {ob: nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=ob, dtype=dtype, order_cd=order)
+                      for ob in layouts}
         g["A"] = to_dev(a)
         g["Ap"] = torch.empty_like(g["A"])
         g["Ad"] = torch.empty_like(g["A"])
@@ -148,7 +150,8 @@ def main():
         g["B"] = {ob: to_dev(bs[ob]) for ob in layouts}
         g["C"] = to_dev(c) if c is not None else None
         odt = torch.int32 if dtype == "i8" else torch.float16 if dtype == "f16" else torch.bfloat16
-        g["D"] = {ob: torch.empty((m, n), dtype=odt, device=dev) for ob in layouts}
+        dshape = (n, m) if order == "col" else (m, n)
+        g["D"] = {ob: torch.empty(dshape, dtype=odt, device=dev) for ob in layouts}
         g["layouts"] = layouts
         g["host"] = dict(a=a, b=bs, c=c)
         gemms.append(g)

@@ -22,19 +22,21 @@
  *
  * Conventions used by every entry point
  * -------------------------------------
- *  - Every matrix is row-major. op_a / op_b say whether the stored array is
+ *  - A and B are row-major. op_a / op_b say whether the stored array is
  *    used as is (NM_OP_N) or transposed (NM_OP_T):
  *      op_a = N: A stored m x k (lda >= k);  op_a = T: A stored k x m (lda >= m)
  *      op_b = N: B stored k x n (ldb >= n);  op_b = T: B stored n x k (ldb >= k)
- *      C and D: m x n (ldc, ldd >= n).
+ *      C and D: m x n, row-major (ldc, ldd >= n) or, with order_cd =
+ *      NM_COL_MAJOR, column-major (ldc, ldd >= m).
  *    (The blog defines N/T on column-major storage; its column-major "TN" is
- *    byte-for-byte this library's "NT" with D written transposed.)
+ *    byte-for-byte this library's "NT" with order_cd = NM_COL_MAJOR.)
  *  - Element types (type_ab, type_cd): (NM_F16, NM_F16), (NM_BF16, NM_BF16)
  *    with fp32 accumulation; (NM_I8, NM_I32) with exact int32 accumulation
  *    (the blog's type list; C and D are int32 for the integer path).
  *  - Leading dimensions are in elements. All device pointers must be 16-byte
- *    aligned, and every row of a matrix whose row is at least 16 bytes long
- *    must start on a 16-byte boundary (ld * element size % 16 == 0).
+ *    aligned, and every stored row (column, for column-major C/D) that is at
+ *    least 16 bytes long must start on a 16-byte boundary
+ *    (ld * element size % 16 == 0).
  *  - Ownership: the caller allocates and owns every device buffer. A plan owns
  *    host memory only. The library never allocates device memory and never
  *    synchronises the device: device work is enqueued on the caller's stream
@@ -84,7 +86,12 @@ typedef enum {
 
 typedef enum { NM_F16 = 0, NM_BF16 = 1, NM_I8 = 2, NM_I32 = 3 } nm_dtype_t;
 typedef enum { NM_OP_N = 0, NM_OP_T = 1 } nm_op_t;
-typedef enum { NM_ROW_MAJOR = 0 } nm_order_t;
+/* Storage order of C and D. NM_ROW_MAJOR: element (i, j) at i * ld + j
+ * (ld >= n). NM_COL_MAJOR: element (i, j) at j * ld + i (ld >= m), the
+ * column-major output of the cuSPARSELt blog's matmul descriptors (its
+ * Table 1 runs use column-major matrices); D^T is then a row-major n x m
+ * matrix, e.g. Y = X W^T for activations X stored tokens x features. */
+typedef enum { NM_ROW_MAJOR = 0, NM_COL_MAJOR = 1 } nm_order_t;
 typedef enum { NM_PRUNE_1D = 0, NM_PRUNE_TILE4X4 = 1 } nm_prune_mode_t;
 
 /* Problem descriptor: the blog's structured / dense / matmul descriptors
@@ -95,7 +102,7 @@ typedef struct {
   int32_t op_a, op_b;       /* nm_op_t */
   int32_t type_ab, type_cd; /* nm_dtype_t pair, see above */
   int64_t lda, ldb, ldc, ldd;
-  int32_t order_cd;         /* NM_ROW_MAJOR (the only order in this build) */
+  int32_t order_cd;         /* nm_order_t of C and D (both the same order) */
   int32_t reserved;         /* must be 0 */
 } nm_problem_t;
 
@@ -159,8 +166,9 @@ nm_status_t nm_decompress(nm_plan_t plan, const void* d_values, const void* d_me
 /* D = alpha * op(A) * op(B) + beta * C with A given as (values, meta).
  * alpha and beta are host floats (the blog's example passes host floats);
  * on the int8 path both must be integers. dC may be NULL when *beta == 0 and
- * may equal dD. fp16/bf16 outputs are alpha*acc + beta*C evaluated in fp32 and
- * rounded to nearest even. d_workspace must be NULL (no workspace needed). */
+ * may equal dD. C and D are stored in the plan's order_cd (row- or
+ * column-major). fp16/bf16 outputs are alpha*acc + beta*C evaluated in fp32
+ * and rounded to nearest even. d_workspace must be NULL (no workspace needed). */
 nm_status_t nm_spmm(nm_plan_t plan, const float* alpha, const void* d_values, const void* d_meta,
                     const void* dB, const float* beta, const void* dC, void* dD, void* d_workspace,
                     void* stream);

@@ -162,8 +162,9 @@ class Plan:
         return torch.empty((rows, self.mask_ld_words), dtype=torch.int32, device=device)
 
 
-def nm_plan_init(m, n, k, nm_n=2, nm_m=4, op_a="N", op_b="N", dtype="f16", lda=None, ldb=None, ldc=None, ldd=None):
-    """Validate a problem and return a Plan (host only)."""
+def nm_plan_init(m, n, k, nm_n=2, nm_m=4, op_a="N", op_b="N", dtype="f16", lda=None, ldb=None, ldc=None, ldd=None,
+                 order_cd="row"):
+    """Validate a problem and return a Plan (host only). order_cd: "row" or "col" (C and D storage)."""
     ta, tc = DTYPES[dtype]
     oa = NM_OP_T if op_a == "T" else NM_OP_N
     ob = NM_OP_T if op_b == "T" else NM_OP_N
@@ -174,9 +175,12 @@ def nm_plan_init(m, n, k, nm_n=2, nm_m=4, op_a="N", op_b="N", dtype="f16", lda=N
     p.type_ab, p.type_cd = ta, tc
     p.lda = lda if lda is not None else max(1, k if oa == NM_OP_N else m)
     p.ldb = ldb if ldb is not None else max(1, n if ob == NM_OP_N else k)
-    p.ldc = ldc if ldc is not None else max(1, n)
-    p.ldd = ldd if ldd is not None else max(1, n)
-    p.order_cd, p.reserved = 0, 0
+    if order_cd not in ("row", "col"):
+        raise ValueError("order_cd must be 'row' or 'col'")
+    cd_len = m if order_cd == "col" else n
+    p.ldc = ldc if ldc is not None else max(1, cd_len)
+    p.ldd = ldd if ldd is not None else max(1, cd_len)
+    p.order_cd, p.reserved = (1 if order_cd == "col" else 0), 0
     h = ctypes.c_void_p()
     _check(lib().nm_plan_init(ctypes.byref(h), ctypes.byref(p)))
     return Plan(h, p, dtype)

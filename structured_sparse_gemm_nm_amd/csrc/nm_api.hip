@@ -85,7 +85,8 @@ nm_status_t nm_plan_init(nm_plan_t* plan, const nm_problem_t* p) {
                        (p->type_ab == NM_BF16 && p->type_cd == NM_BF16) ||
                        (p->type_ab == NM_I8 && p->type_cd == NM_I32);
   if (!pair_ok) return fail(NM_ERR_INVALID_ARG, "type pair must be (F16,F16), (BF16,BF16) or (I8,I32)");
-  if (p->order_cd != NM_ROW_MAJOR) return fail(NM_ERR_UNSUPPORTED, "only row-major C/D");
+  if (p->order_cd != NM_ROW_MAJOR && p->order_cd != NM_COL_MAJOR)
+    return fail(NM_ERR_INVALID_ARG, "order_cd must be NM_ROW_MAJOR or NM_COL_MAJOR");
   if (p->reserved != 0) return fail(NM_ERR_INVALID_ARG, "reserved must be 0");
   if (p->k % M != 0) return fail(NM_ERR_SHAPE, "k must be a multiple of M");
   const int ea = esize(p->type_ab), ec = esize(p->type_cd);
@@ -93,16 +94,19 @@ nm_status_t nm_plan_init(nm_plan_t* plan, const nm_problem_t* p) {
   const int64_t a_cols = p->op_a == NM_OP_N ? p->k : p->m;
   const int64_t b_rows = p->op_b == NM_OP_N ? p->k : p->n;
   const int64_t b_cols = p->op_b == NM_OP_N ? p->n : p->k;
+  // C/D stored lines: rows of n (row-major) or columns of m (column-major)
+  const bool cd_col = p->order_cd == NM_COL_MAJOR;
+  const int64_t cd_lines = cd_col ? p->n : p->m, cd_len = cd_col ? p->m : p->n;
   if (p->lda < (a_cols > 0 ? a_cols : 1) || p->ldb < (b_cols > 0 ? b_cols : 1) ||
-      p->ldc < (p->n > 0 ? p->n : 1) || p->ldd < (p->n > 0 ? p->n : 1))
-    return fail(NM_ERR_SHAPE, "leading dimension smaller than the row length");
+      p->ldc < (cd_len > 0 ? cd_len : 1) || p->ldd < (cd_len > 0 ? cd_len : 1))
+    return fail(NM_ERR_SHAPE, "leading dimension smaller than the row (column, for column-major C/D) length");
   if (p->lda > kMaxElems || p->ldb > kMaxElems || p->ldc > kMaxElems || p->ldd > kMaxElems)
     return fail(NM_ERR_SHAPE, "leading dimension too large");
   if ((double)a_rows * (double)p->lda > (double)kMaxElems || (double)b_rows * (double)p->ldb > (double)kMaxElems ||
-      (double)p->m * (double)p->ldd > (double)kMaxElems || (double)p->m * (double)p->ldc > (double)kMaxElems)
+      (double)cd_lines * (double)p->ldd > (double)kMaxElems || (double)cd_lines * (double)p->ldc > (double)kMaxElems)
     return fail(NM_ERR_SHAPE, "matrix too large");
-  if (!ld_ok(a_cols, p->lda, ea) || !ld_ok(b_cols, p->ldb, ea) || !ld_ok(p->n, p->ldc, ec) ||
-      !ld_ok(p->n, p->ldd, ec))
+  if (!ld_ok(a_cols, p->lda, ea) || !ld_ok(b_cols, p->ldb, ea) || !ld_ok(cd_len, p->ldc, ec) ||
+      !ld_ok(cd_len, p->ldd, ec))
     return fail(NM_ERR_ALIGN, "rows of 16 bytes or more must start on 16-byte boundaries (ld * elem size % 16)");
 
   nm_plan* pl = new (std::nothrow) nm_plan();

@@ -90,12 +90,12 @@ __global__ void __launch_bounds__(NTH) skinny_kernel(GemmArgs A, int b_op_t, int
       if (lane == 0 && row < A.m) {
         if constexpr (DT == DT_I8) {
           int64_t iv = (int64_t)A.alpha * v;
-          if (A.beta != 0.0f) iv += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.ldc + c];
-          ((int32_t*)A.d)[row * A.ldd + c] = (int32_t)iv;
+          if (A.beta != 0.0f) iv += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.c_rs + c * A.c_cs];
+          ((int32_t*)A.d)[row * A.d_rs + c * A.d_cs] = (int32_t)iv;
         } else {
           float o = A.alpha * v;
-          if (A.beta != 0.0f) o += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.ldc + c]);
-          ((uint16_t*)A.d)[row * A.ldd + c] = to_bits16<DT>(o);
+          if (A.beta != 0.0f) o += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.c_rs + c * A.c_cs]);
+          ((uint16_t*)A.d)[row * A.d_rs + c * A.d_cs] = to_bits16<DT>(o);
         }
       }
     }
@@ -110,7 +110,11 @@ static GemmArgs make_gemm_args(const nm_plan& pl, float alpha, const void* a, co
   A.m = pl.p.m; A.n = pl.p.n; A.k = pl.p.k;
   A.lda = dense_a ? pl.p.lda : pl.vld;
   A.mld = pl.mld;
-  A.ldb = pl.p.ldb; A.ldc = pl.p.ldc; A.ldd = pl.p.ldd;
+  A.ldb = pl.p.ldb;
+  const bool col = pl.p.order_cd == NM_COL_MAJOR;
+  A.c_rs = col ? 1 : pl.p.ldc; A.c_cs = col ? pl.p.ldc : 1;
+  A.d_rs = col ? 1 : pl.p.ldd; A.d_cs = col ? pl.p.ldd : 1;
+  A.cd_col = col;
   A.alpha = alpha; A.beta = beta;
   A.N = pl.p.nm_n; A.M = pl.p.nm_m; A.bits = pl.bits;
   A.a_vec = (A.lda * pl.esz_ab) % 16 == 0;

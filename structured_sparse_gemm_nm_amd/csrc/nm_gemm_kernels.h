@@ -61,7 +61,9 @@ struct GemmArgs {
   int64_t m, n, k;
   int64_t lda;          // dense A leading dim (elements) or values_ld
   int64_t mld;          // metadata row stride (bytes)
-  int64_t ldb, ldc, ldd;
+  int64_t ldb;
+  int64_t c_rs, c_cs, d_rs, d_cs;   // C/D element (row, col) at row * rs + col * cs (row- or column-major)
+  int cd_col;                       // C/D column-major (rs = 1, cs = ld)
   float alpha, beta;
   int N, M, bits;
   int a_vec, b_vec;     // 16-byte vector loads allowed on A / B rows
@@ -589,12 +591,12 @@ __global__ void __launch_bounds__(NTH) gemm_kernel(GemmArgs A) {
         if (row >= A.m) continue;
         if constexpr (DT == DT_I8) {
           int64_t v = (int64_t)A.alpha * acc[fm][fn][r];
-          if (A.beta != 0.0f) v += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.ldc + col];
-          ((int32_t*)A.d)[row * A.ldd + col] = (int32_t)v;
+          if (A.beta != 0.0f) v += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.c_rs + col * A.c_cs];
+          ((int32_t*)A.d)[row * A.d_rs + col * A.d_cs] = (int32_t)v;
         } else {
           float v = A.alpha * acc[fm][fn][r];
-          if (A.beta != 0.0f) v += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.ldc + col]);
-          ((uint16_t*)A.d)[row * A.ldd + col] = to_bits16<DT>(v);
+          if (A.beta != 0.0f) v += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.c_rs + col * A.c_cs]);
+          ((uint16_t*)A.d)[row * A.d_rs + col * A.d_cs] = to_bits16<DT>(v);
         }
       }
     }
@@ -811,12 +813,12 @@ __global__ void __launch_bounds__(NTH) gemm_fast_kernel(GemmArgs A) {
         const int64_t row = r0 + wm0 + fm * 32 + 8 * (r / 4) + 4 * q + (r % 4);
         if constexpr (DT == DT_I8) {
           int64_t v = (int64_t)A.alpha * acc[fm][fn][r];
-          if (A.beta != 0.0f) v += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.ldc + col];
-          ((int32_t*)A.d)[row * A.ldd + col] = (int32_t)v;
+          if (A.beta != 0.0f) v += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.c_rs + col * A.c_cs];
+          ((int32_t*)A.d)[row * A.d_rs + col * A.d_cs] = (int32_t)v;
         } else {
           float v = A.alpha * acc[fm][fn][r];
-          if (A.beta != 0.0f) v += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.ldc + col]);
-          ((uint16_t*)A.d)[row * A.ldd + col] = to_bits16<DT>(v);
+          if (A.beta != 0.0f) v += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.c_rs + col * A.c_cs]);
+          ((uint16_t*)A.d)[row * A.d_rs + col * A.d_cs] = to_bits16<DT>(v);
         }
       }
     }
@@ -1162,6 +1164,47 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   }
 
   // ---- epilogue: D = alpha * acc + beta * C ----
+  if (A.cd_col) {
+    // column-major C/D: accumulator elements 4(r/4) .. 4(r/4)+3 of a lane are
+    // four consecutive rows of one column, i.e. 8 (16-bit) or 16 (int32)
+    // contiguous bytes; full tiles and the 16-byte column rule keep them aligned
+#pragma unroll
+    for (int fm = 0; fm < FM; fm++)
+#pragma unroll
+      for (int fn = 0; fn < FN; fn++) {
+        const int64_t col = c0 + wn0 + fn * 32 + l32;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; r4++) {
+          const int64_t row = r0 + wm0 + fm * 32 + 8 * r4 + 4 * q;
+          if constexpr (DT == DT_I8) {
+            int64_t v[4];
+#pragma unroll
+            for (int t = 0; t < 4; t++) v[t] = (int64_t)A.alpha * acc[fm][fn][4 * r4 + t];
+            if (A.beta != 0.0f) {
+              const intx4 cv = *(const intx4*)((const int32_t*)A.c + col * A.c_cs + row);
+#pragma unroll
+              for (int t = 0; t < 4; t++) v[t] += (int64_t)A.beta * cv[t];
+            }
+            *(intx4*)((int32_t*)A.d + col * A.d_cs + row) = intx4{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
+          } else {
+            float v[4];
+#pragma unroll
+            for (int t = 0; t < 4; t++) v[t] = A.alpha * acc[fm][fn][4 * r4 + t];
+            if (A.beta != 0.0f) {
+              const u32x2 cv = *(const u32x2*)((const uint16_t*)A.c + col * A.c_cs + row);
+              v[0] += A.beta * from_bits16<DT>((uint16_t)(cv[0] & 0xFFFFu));
+              v[1] += A.beta * from_bits16<DT>((uint16_t)(cv[0] >> 16));
+              v[2] += A.beta * from_bits16<DT>((uint16_t)(cv[1] & 0xFFFFu));
+              v[3] += A.beta * from_bits16<DT>((uint16_t)(cv[1] >> 16));
+            }
+            const uint32_t lo = (uint32_t)to_bits16<DT>(v[0]) | ((uint32_t)to_bits16<DT>(v[1]) << 16);
+            const uint32_t hi = (uint32_t)to_bits16<DT>(v[2]) | ((uint32_t)to_bits16<DT>(v[3]) << 16);
+            *(u32x2*)((uint16_t*)A.d + col * A.d_cs + row) = u32x2{lo, hi};
+          }
+        }
+      }
+    return;
+  }
 #pragma unroll
   for (int fm = 0; fm < FM; fm++)
 #pragma unroll
@@ -1172,12 +1215,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
         const int64_t row = r0 + wm0 + fm * 32 + 8 * (r / 4) + 4 * q + (r % 4);
         if constexpr (DT == DT_I8) {
           int64_t v = (int64_t)A.alpha * acc[fm][fn][r];
-          if (A.beta != 0.0f) v += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.ldc + col];
-          ((int32_t*)A.d)[row * A.ldd + col] = (int32_t)v;
+          if (A.beta != 0.0f) v += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.c_rs + col];
+          ((int32_t*)A.d)[row * A.d_rs + col] = (int32_t)v;
         } else {
           float v = A.alpha * acc[fm][fn][r];
-          if (A.beta != 0.0f) v += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.ldc + col]);
-          ((uint16_t*)A.d)[row * A.ldd + col] = to_bits16<DT>(v);
+          if (A.beta != 0.0f) v += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.c_rs + col]);
+          ((uint16_t*)A.d)[row * A.d_rs + col] = to_bits16<DT>(v);
         }
       }
     }

@@ -287,12 +287,12 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
           if (lane != c || c >= n) continue;
           if constexpr (DT == DT_I8) {
             int64_t iv = (int64_t)A.alpha * acc[rr][c];
-            if (A.beta != 0.0f) iv += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.ldc + c];
-            ((int32_t*)A.d)[row * A.ldd + c] = (int32_t)iv;
+            if (A.beta != 0.0f) iv += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.c_rs + c * A.c_cs];
+            ((int32_t*)A.d)[row * A.d_rs + c * A.d_cs] = (int32_t)iv;
           } else {
             float o = A.alpha * acc[rr][c];
-            if (A.beta != 0.0f) o += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.ldc + c]);
-            ((uint16_t*)A.d)[row * A.ldd + c] = to_bits16<DT>(o);
+            if (A.beta != 0.0f) o += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.c_rs + c * A.c_cs]);
+            ((uint16_t*)A.d)[row * A.d_rs + c * A.d_cs] = to_bits16<DT>(o);
           }
         }
       }

@@ -89,15 +89,16 @@ WORKLOADS = {
     "x1_bwd": dict(dtype="f16", N=2, M=4, m=4096, n=8192, k=11008, op_a="T", op_b="T",
                    a=("normal", 3101, 0.02), b=("normal", 3103, 1.0), b_draw="nk", alpha=1.0, beta=0.0, tile=True),
     # the cuSPARSELt blog's Table 1 shapes (BERT-Large, sequence 128 x batch 128 =
-    # 16384 tokens), for side-by-side context with the blog's figures
+    # 16384 tokens), for side-by-side context with the blog's figures; D is
+    # column-major as in the blog's runs (D^T = tokens x features, row-major)
     "x3_qkv": dict(dtype="f16", N=2, M=4, m=3072, n=16384, k=1024, a=("normal", 7001, 0.02),
-                   b=("normal", 7011, 1.0), b_draw="nk", op_a="N", op_b="T", alpha=1.0, beta=0.0),
+                   b=("normal", 7011, 1.0), b_draw="nk", op_a="N", op_b="T", alpha=1.0, beta=0.0, order_cd="col"),
     "x3_proj": dict(dtype="f16", N=2, M=4, m=1024, n=16384, k=1024, a=("normal", 7002, 0.02),
-                    b=("normal", 7011, 1.0), b_draw="nk", op_a="N", op_b="T", alpha=1.0, beta=0.0),
+                    b=("normal", 7011, 1.0), b_draw="nk", op_a="N", op_b="T", alpha=1.0, beta=0.0, order_cd="col"),
     "x3_fc1": dict(dtype="f16", N=2, M=4, m=4096, n=16384, k=1024, a=("normal", 7003, 0.02),
-                   b=("normal", 7011, 1.0), b_draw="nk", op_a="N", op_b="T", alpha=1.0, beta=0.0),
+                   b=("normal", 7011, 1.0), b_draw="nk", op_a="N", op_b="T", alpha=1.0, beta=0.0, order_cd="col"),
     "x3_fc2": dict(dtype="f16", N=2, M=4, m=1024, n=16384, k=4096, a=("normal", 7004, 0.02),
-                   b=("normal", 7014, 1.0), b_draw="nk", op_a="N", op_b="T", alpha=1.0, beta=0.0),
+                   b=("normal", 7014, 1.0), b_draw="nk", op_a="N", op_b="T", alpha=1.0, beta=0.0, order_cd="col"),
     # int8 with int32 accumulate, beta = 1
     "c4_int8": dict(dtype="i8", N=2, M=4, m=4096, n=4096, k=4096, op_a="N", op_b="N",
                     a=("int", 4001, -127, 127), b=("int", 4002, -127, 127), c=("int32", 4003, -2**20, 2**20),

@@ -68,13 +68,28 @@ def test_plan_init_rejects_bad_type_pair_and_order():
     assert nm.lib().nm_plan_init(ctypes.byref(h), ctypes.byref(p)) == nm.NM_ERR_INVALID_ARG
     assert h.value is None
     p.type_cd = nm.NM_F16
-    p.order_cd = 1
-    assert nm.lib().nm_plan_init(ctypes.byref(h), ctypes.byref(p)) == nm.NM_ERR_UNSUPPORTED
+    p.order_cd = 2
+    assert nm.lib().nm_plan_init(ctypes.byref(h), ctypes.byref(p)) == nm.NM_ERR_INVALID_ARG
     p.order_cd = 0
     p.reserved = 7
     assert nm.lib().nm_plan_init(ctypes.byref(h), ctypes.byref(p)) == nm.NM_ERR_INVALID_ARG
     assert nm.lib().nm_plan_init(None, ctypes.byref(p)) == nm.NM_ERR_INVALID_ARG
     assert nm.lib().nm_plan_init(ctypes.byref(h), None) == nm.NM_ERR_INVALID_ARG
+
+
+def test_column_major_cd_leading_dimensions():
+    # column-major C/D: ld counts rows (>= m), and columns of >= 16 bytes start on 16-byte boundaries
+    _init(m=24, n=40, order_cd="col")
+    _init(m=24, n=40, ldc=32, ldd=40, order_cd="col")
+    with pytest.raises(nm.NmError) as e:
+        _init(m=24, n=40, ldd=16, order_cd="col")             # ldd < m
+    assert e.value.status == nm.NM_ERR_SHAPE
+    with pytest.raises(nm.NmError) as e:
+        _init(m=24, n=40, ldd=28, order_cd="col")             # 56-byte column stride
+    assert e.value.status == nm.NM_ERR_ALIGN
+    _init(m=4, n=40, ldc=5, ldd=7, order_cd="col")            # 8-byte columns: any ld >= m
+    with pytest.raises(ValueError):
+        _init(m=4, n=4, order_cd="diagonal")
 
 
 def test_small_rows_may_use_any_leading_dimension():

@@ -383,6 +383,90 @@ def test_k_zero_gives_beta_c(dtype, n):
         assert np.array_equal(oracle.decode(got, dtype), 0.5 * oracle.decode(c, dtype))
 
 
+COL_CASES = [
+    # (label, N, M, m, n, k, op_b, force_tile): sparse 2:4 full tiles (copy-ring kernel, both B layouts,
+    # 128 and 256 tiles), ragged 2:4, general N:M gather, small n, and N = 0 for the dense comparator
+    ("24-ring-NT", 2, 4, 256, 256, 256, "T", None),
+    ("24-ring-NN", 2, 4, 256, 384, 192, "N", None),
+    ("24-ring-256", 2, 4, 512, 512, 128, "T", "256"),
+    ("24-ragged", 2, 4, 200, 144, 336, "N", None),
+    ("gather-4of32", 4, 32, 150, 80, 544, "T", None),
+    ("skinny-24", 2, 4, 100, 8, 1088, "N", None),
+    ("skinny-4of32", 4, 32, 100, 3, 1088, "T", None),
+    ("dense-ring", 0, 0, 256, 256, 320, "T", None),
+    ("dense-ragged", 0, 0, 272, 144, 208, "N", None),
+    ("dense-skinny", 0, 0, 200, 8, 1040, "N", None),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("case", COL_CASES, ids=[c[0] for c in COL_CASES])
+@pytest.mark.parametrize("beta", [0.0, 1.0])
+def test_col_major_cd(dtype, case, beta, monkeypatch):
+    """Column-major C and D (the blog's column-major output): D element (i, j) at
+    j * ldd + i, with ldd > m so that the rows past m of every column (the caller's
+    bytes) must stay untouched; C read column-major the same way."""
+    label, N, M, m, n, k, op_b, tile = case
+    if tile:
+        monkeypatch.setenv("NM_FORCE_TILE", tile)
+    es_cd = 4 if dtype == "i8" else 2
+    ld = -(-m // (16 // es_cd)) * (16 // es_cd) + 16 // es_cd      # 16-byte columns, padded past m
+    seed = 7000 + m + n + k
+    alpha = 1.0 if dtype == "i8" else 0.75
+    a = rand(dtype, (m, k), seed)
+    b_log = rand(dtype, (k, n), seed + 1)
+    b_st = b_log if op_b == "N" else np.ascontiguousarray(b_log.T)
+    c = None
+    if beta != 0:
+        c = (inputs.uniform_int((m, n), seed + 2, -2**20, 2**20, np.int32) if dtype == "i8"
+             else rand(dtype, (m, n), seed + 2))
+    plan = plan_for(dtype, m, n, k, N or 2, M or 4, op_b=op_b, ldc=ld, ldd=ld, order_cd="col")
+    raw = np.int32 if dtype == "i8" else np.uint16
+    sentinel = np.full((n, ld), 0x3C3C if es_cd == 2 else 0x3C3C3C3C, dtype=raw)
+    d = Guarded((n, ld), torch.int32 if dtype == "i8" else torch.int16, fill=dev(sentinel))
+    dc = None
+    if c is not None:
+        c_col = np.zeros((n, ld), dtype=raw)
+        c_col[:, :m] = c.T
+        dc = dev(c_col)
+    if N:
+        ahat, _ = oracle.prune_1d(a, dtype, N, M)
+        vref, mref = oracle.compress(a, dtype, N, M)
+        nm.nm_spmm(plan, alpha, dev(vref), dev(mref), dev(b_st), beta, dc, d.t)
+    else:
+        ahat = a
+        nm.nm_dense_gemm(plan, alpha, dev(a), dev(b_st), beta, dc, d.t)
+    sync()
+    d.check()
+    got = host(d.t, raw)
+    assert np.array_equal(got[:, m:], sentinel[:, m:]), label
+    ref, tol = ref_product(dtype, ahat, b_log, alpha, beta, c)
+    assert_close(dtype, np.ascontiguousarray(got[:, :m].T), ref, tol)
+
+
+def test_col_major_k_zero_and_alias():
+    m, n = 40, 24
+    c = rand("f16", (m, n), 11)
+    plan = plan_for("f16", m, n, 0, 2, 4, order_cd="col")
+    d = torch.empty((n, m), dtype=torch.int16, device="cuda")
+    nm.nm_spmm(plan, 1.0, None, None, None, 0.5, dev(np.ascontiguousarray(c.T)), d)
+    sync()
+    assert np.array_equal(oracle.decode(host(d, np.uint16).T, "f16"), 0.5 * oracle.decode(c, "f16"))
+    # C == D, column-major, on the copy-ring kernel
+    m, n, k = 256, 256, 128
+    a = rand("f16", (m, k), 12)
+    v, meta = oracle.compress(a, "f16", 2, 4)
+    ahat, _ = oracle.prune_1d(a, "f16", 2, 4)
+    b = rand("f16", (n, k), 13)
+    c = rand("f16", (m, n), 14)
+    plan = plan_for("f16", m, n, k, 2, 4, op_b="T", order_cd="col")
+    dc = dev(np.ascontiguousarray(c.T))
+    nm.nm_spmm(plan, 1.0, dev(v), dev(meta), dev(b), -1.0, dc, dc)
+    sync()
+    ref, tol = ref_product("f16", ahat, np.ascontiguousarray(b.T), 1.0, -1.0, c)
+    assert_close("f16", np.ascontiguousarray(host(dc, np.uint16).T), ref, tol)
+
+
 def test_c_may_alias_d():
     m, n, k = 64, 64, 128
     a = rand("f16", (m, k), 8)

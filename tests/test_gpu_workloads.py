@@ -65,7 +65,8 @@ def test_workload(name, op_b):
     op_a = w.get("op_a", "N")
     print("workload", name, "op_b", op_b, flush=True)
     a, b, c = inputs.workload_inputs(name, op_b)
-    plan = nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=op_b, dtype=dtype)
+    order = w.get("order_cd", "row")
+    plan = nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=op_b, dtype=dtype, order_cd=order)
     mode = "tile" if w.get("tile") else "1d"
     # prune on the GPU, bit-exact against the oracle
     if mode == "tile":
@@ -108,10 +109,12 @@ def test_workload(name, op_b):
     db = dev(b)
     dc = dev(c) if c is not None else None
     odt = torch.int32 if dtype == "i8" else torch.int16
-    d = torch.empty((m, n), dtype=odt, device="cuda")
+    d = torch.empty((n, m) if order == "col" else (m, n), dtype=odt, device="cuda")
     nm.nm_spmm(plan, w["alpha"], vals, meta, db, w["beta"], dc, d)
     sync()
     got = host(d, np.int32 if dtype == "i8" else np.uint16)
+    if order == "col":
+        got = got.T                                        # D^T is stored row-major
     ahat_log = ref_p if op_a == "N" else np.ascontiguousarray(ref_p.T)
     if m * n * k <= 256 * 256 * 256:
         pi, pj = np.divmod(np.arange(m * n), n)
