@@ -24,7 +24,7 @@ struct nm_plan {
   // launches do not scan the environment
   int force_tile;           // -1 = automatic, else nm::TileCfg
   bool no_dma, no_dma_nn, no_deep_ring, old_skinny;
-  bool tile_elemwise;       // prune/compress/decompress on the LDS tile kernels even where the row path applies
+  bool tile_elemwise;       // prune/check/compress/decompress on the older kernels even where the row path applies
 };
 
 namespace nm {
@@ -63,6 +63,9 @@ bool row_path_ok(const nm_plan& pl);
 hipError_t launch_row_prune(const nm_plan& pl, const void* a, void* out, uint32_t* mask, hipStream_t s);
 hipError_t launch_row_compress(const nm_plan& pl, const void* a, void* vals, void* meta, hipStream_t s);
 hipError_t launch_row_decompress(const nm_plan& pl, const void* vals, const void* meta, void* out, hipStream_t s);
+// 1-D prune check for op_a = N with 16-byte rows, any N:M (the counter must already be zero)
+bool check_row_ok(const nm_plan& pl);
+hipError_t launch_check_row(const nm_plan& pl, const void* a, int32_t* count, hipStream_t s);
 hipError_t launch_prune_tile(const nm_plan& pl, const void* a, void* out, uint32_t* mask, hipStream_t s);
 hipError_t launch_check(const nm_plan& pl, const void* a, int mode, int32_t* count, hipStream_t s);
 hipError_t launch_compress(const nm_plan& pl, const void* a, void* vals, void* meta, hipStream_t s);

@@ -532,6 +532,7 @@ hipError_t launch_check(const nm_plan& pl, const void* a, int mode, int32_t* cou
   }
   const int64_t total = pl.p.m * (pl.p.k / pl.p.nm_m);
   if (total == 0) return hipSuccess;
+  if (check_row_ok(pl) && !pl.tile_elemwise) return launch_check_row(pl, a, count, s);
   const dim3 grid((unsigned)((total + TPB - 1) / TPB));
   const int opt = pl.p.op_a == NM_OP_T;
   const int vec = (pl.p.lda * pl.esz_ab) % 16 == 0;

@@ -133,11 +133,102 @@ __device__ __forceinline__ void store_seg_meta(uint8_t* dst, uint64_t f, int ndw
   }
 }
 
+// ---- top-N of a 32-element group by a selection network (M = 32, N = 4 or 8)
+//
+// Each element gets the unique key (|x| << 6) | ((31 - j) << 1) | sign: larger
+// magnitude first, equal magnitudes by lower offset j (the sign never decides,
+// since j is unique), and the key still holds the element's bits. Sorting runs
+// of four, (for N = 8) merging them into sorted runs of eight, then keeping the
+// N largest of each pair of runs (the element-wise maximum of one run against
+// the other reversed is the top N, as a bitonic sequence) takes about a third
+// of the operations of N rounds of a 32-wide maximum.
+__device__ __forceinline__ void cx(uint32_t& a, uint32_t& b) {
+  const uint32_t h = max(a, b), l = min(a, b);
+  a = h; b = l;
+}
+
+template <int L>   // sorts a bitonic run k[o .. o+L) into descending order
+__device__ __forceinline__ void bitonic_desc(uint32_t* k) {
+#pragma unroll
+  for (int st = L / 2; st >= 1; st /= 2)
+#pragma unroll
+    for (int i = 0; i < L; i++)
+      if ((i & st) == 0) cx(k[i], k[i + st]);
+}
+
+template <int N>
+__device__ __forceinline__ void top_n32(uint32_t (&k)[32], uint32_t (&out)[N]) {
+  static_assert(N == 4 || N == 8, "network for N = 4 or 8 of 32");
+#pragma unroll
+  for (int g = 0; g < 8; g++) {
+    cx(k[4 * g], k[4 * g + 1]); cx(k[4 * g + 2], k[4 * g + 3]);
+    cx(k[4 * g], k[4 * g + 2]); cx(k[4 * g + 1], k[4 * g + 3]); cx(k[4 * g + 1], k[4 * g + 2]);
+  }
+  if constexpr (N == 8) {
+#pragma unroll
+    for (int h = 0; h < 4; h++) {   // runs 2h, 2h+1 -> one sorted run of 8 (second run reversed: bitonic)
+      uint32_t t = k[8 * h + 4]; k[8 * h + 4] = k[8 * h + 7]; k[8 * h + 7] = t;
+      t = k[8 * h + 5]; k[8 * h + 5] = k[8 * h + 6]; k[8 * h + 6] = t;
+      bitonic_desc<8>(k + 8 * h);
+    }
+  }
+#pragma unroll
+  for (int runs = 32 / N; runs > 1; runs /= 2) {
+#pragma unroll
+    for (int i = 0; i < runs / 2; i++) {
+      uint32_t c[N];
+#pragma unroll
+      for (int t = 0; t < N; t++) c[t] = max(k[2 * i * N + t], k[(2 * i + 1) * N + N - 1 - t]);
+      if (runs > 2) bitonic_desc<N>(c);
+#pragma unroll
+      for (int t = 0; t < N; t++) k[i * N + t] = c[t];
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < N; t++) out[t] = k[t];
+}
+
+template <int DT>
+__device__ __forceinline__ uint32_t net_key(uint32_t raw, int j) {
+  uint32_t mag, sign;
+  if constexpr (DT == DT_I8) {
+    const int v = (int)(int8_t)(uint8_t)raw;
+    mag = (uint32_t)(v < 0 ? -v : v); sign = v < 0;
+  } else {
+    mag = raw & 0x7FFFu; sign = raw >> 15;
+  }
+  return (mag << 6) | ((uint32_t)(31 - j) << 1) | sign;
+}
+
+// (offset, bits) of a selected key: rk = (31 - j) << 16 | sign << 15 | magnitude
+__device__ __forceinline__ uint32_t by_offset(uint32_t key) {
+  return (((key >> 1) & 31u) << 16) | ((key & 1u) << 15) | (key >> 6);
+}
+template <int DT>
+__device__ __forceinline__ uint32_t raw_of(uint32_t rk) {
+  if constexpr (DT == DT_I8) {
+    const int mag = (int)(rk & 0x7FFFu);
+    return (uint32_t)(uint8_t)(((rk >> 15) & 1u) ? -mag : mag);
+  } else {
+    return rk & 0xFFFFu;
+  }
+}
+
 enum RowOp { R_PRUNE = 0, R_COMPRESS = 1, R_DECOMPRESS = 2 };
 
 template <int DT, int ESZ, int N, int M, int OP>
 __global__ void __launch_bounds__(256) row_kernel(RowArgs A) {
   using G = RowGeom<ESZ, N, M>;
+  // decompress at M = 32: one LDS slot per lane (the unit plus 16 bytes, so the
+  // 16-byte accesses of 16 consecutive lanes fall on distinct banks)
+  // (prune at M = 32 stages its loads and its output the same way, one slot
+  // per lane and segment, so that every wave instruction moves 1 KB of
+  // contiguous row; a lane reads and then overwrites only its own slot)
+  constexpr int SLOT_BYTES = G::UB + 16;
+  constexpr bool STAGED = M == 32;
+  constexpr bool STAGE_IN = STAGED && OP == R_PRUNE;   // compress reads its units directly (measured faster)
+  __shared__ __attribute__((aligned(16))) uint32_t s_unit[STAGED ? G::SPW * 256 * SLOT_BYTES / 4 : 4];
+  constexpr int PPU = G::UB / 16;                          // 16-byte pieces per unit
   const int lane = threadIdx.x & 63;
   const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t groups_row = A.k / M;
@@ -178,8 +269,42 @@ __global__ void __launch_bounds__(256) row_kernel(RowArgs A) {
         f |= (uint64_t)d2 << (64 - sh);
       }
       fld[s] = f & ((1ull << G::FB) - 1ull);
-    } else {
+    } else if (!STAGE_IN) {
       load_unit<ESZ, G::DW>(d[s], A.a + (r * A.lda + u * G::EPU) * ESZ, vg * G::GD);
+    }
+  }
+  if constexpr (STAGE_IN) {
+    // coalesced loads: lane l takes 16-byte piece l % PPU of unit c * 64 / PPU + l / PPU
+    u32x4 pc[G::SPW][PPU];
+#pragma unroll
+    for (int s = 0; s < G::SPW; s++) {
+      const int64_t seg = wave * G::SPW + s;
+      const int64_t r = seg / A.segs, sr = seg % A.segs;
+#pragma unroll
+      for (int c = 0; c < PPU; c++) {
+        const int uu = c * (64 / PPU) + lane / PPU;
+        pc[s][c] = u32x4{0, 0, 0, 0};
+        if (r < A.m && sr * 64 + uu < A.units)
+          pc[s][c] = __builtin_nontemporal_load(
+              (const u32x4*)(A.a + (r * A.lda + (sr * 64 + uu) * G::EPU) * ESZ + 16 * (lane % PPU)));
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < G::SPW; s++) {
+      uint8_t* wave_slots = (uint8_t*)s_unit + (s * 4 + (threadIdx.x >> 6)) * 64 * SLOT_BYTES;
+#pragma unroll
+      for (int c = 0; c < PPU; c++)
+        *(u32x4*)(wave_slots + (c * (64 / PPU) + lane / PPU) * SLOT_BYTES + 16 * (lane % PPU)) = pc[s][c];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < G::SPW; s++) {
+      const uint8_t* mine = (const uint8_t*)s_unit + ((s * 4 + (threadIdx.x >> 6)) * 64 + lane) * SLOT_BYTES;
+#pragma unroll
+      for (int c = 0; c < PPU; c++) {
+        const u32x4 v = *(const u32x4*)(mine + 16 * c);
+        d[s][4 * c] = v[0]; d[s][4 * c + 1] = v[1]; d[s][4 * c + 2] = v[2]; d[s][4 * c + 3] = v[3];
+      }
     }
   }
 
@@ -193,6 +318,36 @@ __global__ void __launch_bounds__(256) row_kernel(RowArgs A) {
     const bool row_ok = r < A.m;                      // uniform across the wave
     const bool live = row_ok && u < A.units;
     const int vg = live ? (int)min((int64_t)G::GU, groups_row - u * G::GU) : 0;
+    if (OP == R_DECOMPRESS && M == 32) {
+      // scatter the kept values into the lane's own zeroed LDS slot (in order:
+      // later slots win when offsets repeat), then read the unit back
+      uint8_t* slot_base = (uint8_t*)s_unit + ((s * 4 + (threadIdx.x >> 6)) * 64 + lane) * SLOT_BYTES;
+#pragma unroll
+      for (int c = 0; c < G::DW / 4; c++) *(u32x4*)(slot_base + 16 * c) = u32x4{0, 0, 0, 0};
+      if (live) {
+#pragma unroll
+        for (int sl = 0; sl < N; sl++) {
+          const int j = (int)((fld[s] >> (sl * G::B)) & (uint64_t)(M - 1));
+          const uint32_t v = elem_of<ESZ>(d[s], sl);
+          if (ESZ == 2) *(uint16_t*)(slot_base + 2 * j) = (uint16_t)v;
+          else slot_base[j] = (uint8_t)v;
+        }
+      }
+      // the wave's 64 units are consecutive in the row: store them as whole
+      // 1 KB wave instructions (lane l takes 16-byte piece l % PPU of unit
+      // c * 64 / PPU + l / PPU), which keeps every store a full line and lets
+      // the dense output stream past the caches
+      __syncthreads();
+      const uint8_t* wave_slots = (const uint8_t*)s_unit + (s * 4 + (threadIdx.x >> 6)) * 64 * SLOT_BYTES;
+#pragma unroll
+      for (int c = 0; c < PPU; c++) {
+        const int uu = c * (64 / PPU) + lane / PPU;         // unit within the segment
+        const u32x4 v = *(const u32x4*)(wave_slots + uu * SLOT_BYTES + 16 * (lane % PPU));
+        if (row_ok && sr * 64 + uu < A.units)
+          __builtin_nontemporal_store(v, (u32x4*)(A.out + (r * A.lda + (sr * 64 + uu) * G::EPU) * ESZ + 16 * (lane % PPU)));
+      }
+      continue;
+    }
     if (OP == R_DECOMPRESS) {
       uint32_t o[G::DW];
 #pragma unroll
@@ -220,12 +375,39 @@ __global__ void __launch_bounds__(256) row_kernel(RowArgs A) {
       continue;
     }
     uint32_t keep[G::GU];
+    uint32_t sel[N];                 // M = 32: the kept elements as by_offset() keys, offsets ascending
+    if constexpr (M == 32) {
+      uint32_t key[32];
 #pragma unroll
-    for (int g = 0; g < G::GU; g++) {
-      uint32_t mag[M];
+      for (int j = 0; j < 32; j++) key[j] = net_key<DT>(elem_of<ESZ>(d[s], j), j);
+      uint32_t top[N];
+      top_n32<N>(key, top);
+      keep[0] = 0;
 #pragma unroll
-      for (int j = 0; j < M; j++) mag[j] = magkey<DT>(elem_of<ESZ>(d[s], g * M + j));
-      keep[g] = g < vg ? select_topn<M>(mag, N) : 0u;
+      for (int t = 0; t < N; t++) {
+        sel[t] = by_offset(top[t]);
+        keep[0] |= 1u << (31 - (sel[t] >> 16));
+      }
+      if (OP == R_COMPRESS) {        // offsets ascending = (31 - offset) descending
+        if constexpr (N == 4) {
+          cx(sel[0], sel[1]); cx(sel[2], sel[3]); cx(sel[0], sel[2]); cx(sel[1], sel[3]); cx(sel[1], sel[2]);
+        } else {
+          cx(sel[0], sel[1]); cx(sel[2], sel[3]); cx(sel[0], sel[2]); cx(sel[1], sel[3]); cx(sel[1], sel[2]);
+          cx(sel[4], sel[5]); cx(sel[6], sel[7]); cx(sel[4], sel[6]); cx(sel[5], sel[7]); cx(sel[5], sel[6]);
+          uint32_t t = sel[4]; sel[4] = sel[7]; sel[7] = t;
+          t = sel[5]; sel[5] = sel[6]; sel[6] = t;
+          bitonic_desc<8>(sel);
+        }
+      }
+      if (vg == 0) keep[0] = 0;
+    } else {
+#pragma unroll
+      for (int g = 0; g < G::GU; g++) {
+        uint32_t mag[M];
+#pragma unroll
+        for (int j = 0; j < M; j++) mag[j] = magkey<DT>(elem_of<ESZ>(d[s], g * M + j));
+        keep[g] = g < vg ? select_topn<M>(mag, N) : 0u;
+      }
     }
     if (OP == R_PRUNE) {
       if (!live) continue;
@@ -238,7 +420,14 @@ __global__ void __launch_bounds__(256) row_kernel(RowArgs A) {
           const int wd = ESZ == 2 ? ge >> 1 : ge >> 2;
           if (!((keep[g] >> j) & 1u)) d[s][wd] &= ~((ESZ == 2 ? 0xFFFFu : 0xFFu) << sft);
         }
-      store_unit<G::DW>(A.out + (r * A.lda + u * G::EPU) * ESZ, d[s], vg * G::GD);
+      if constexpr (STAGED) {
+        uint8_t* mine = (uint8_t*)s_unit + ((s * 4 + (threadIdx.x >> 6)) * 64 + lane) * SLOT_BYTES;
+#pragma unroll
+        for (int c = 0; c < PPU; c++)
+          *(u32x4*)(mine + 16 * c) = u32x4{d[s][4 * c], d[s][4 * c + 1], d[s][4 * c + 2], d[s][4 * c + 3]};
+      } else {
+        store_unit<G::DW>(A.out + (r * A.lda + u * G::EPU) * ESZ, d[s], vg * G::GD);
+      }
       if (A.mask) {
         uint32_t bits = 0;
 #pragma unroll
@@ -258,6 +447,17 @@ __global__ void __launch_bounds__(256) row_kernel(RowArgs A) {
 #pragma unroll
     for (int t = 0; t < G::VB / 4; t++) vo[t] = 0;
     uint64_t f = 0;
+    if constexpr (M == 32) {
+      if (vg > 0) {
+#pragma unroll
+        for (int sl = 0; sl < N; sl++) {
+          const uint32_t v = raw_of<DT>(sel[sl]);
+          const int sft = ESZ == 2 ? 16 * (sl & 1) : 8 * (sl & 3);
+          vo[ESZ == 2 ? sl >> 1 : sl >> 2] |= v << sft;
+          f |= (uint64_t)(31u - (sel[sl] >> 16)) << (sl * G::B);
+        }
+      }
+    } else
 #pragma unroll
     for (int g = 0; g < G::GU; g++) {
       uint32_t kb = keep[g];
@@ -287,6 +487,117 @@ __global__ void __launch_bounds__(256) row_kernel(RowArgs A) {
       store_seg_meta<G::FB>(A.meta + r * A.mld + mbyte0, f, ndw, lane);
     }
   }
+  if constexpr (STAGED && OP == R_PRUNE) {
+    // the pruned units went to the lanes' slots: store them as whole 1 KB wave instructions
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < G::SPW; s++) {
+      const int64_t seg = wave * G::SPW + s;
+      const int64_t r = seg / A.segs, sr = seg % A.segs;
+      const uint8_t* wave_slots = (const uint8_t*)s_unit + (s * 4 + (threadIdx.x >> 6)) * 64 * SLOT_BYTES;
+#pragma unroll
+      for (int c = 0; c < PPU; c++) {
+        const int uu = c * (64 / PPU) + lane / PPU;
+        const u32x4 v = *(const u32x4*)(wave_slots + uu * SLOT_BYTES + 16 * (lane % PPU));
+        if (r < A.m && sr * 64 + uu < A.units)
+          __builtin_nontemporal_store(v, (u32x4*)(A.out + (r * A.lda + (sr * 64 + uu) * G::EPU) * ESZ + 16 * (lane % PPU)));
+      }
+    }
+  }
+}
+
+// ---- prune check for row-contiguous groups: one 16-byte chunk per lane and
+// wave instruction (1 KB of row), non-zeros counted per chunk; a group wider
+// than 16 bytes spans PPU = M * esize / 16 consecutive lanes, whose counts are
+// summed with cross-lane reads (chunks per row is a multiple of PPU, so the
+// lanes of a group never straddle a row or a wave).
+constexpr int CHECK_CHUNKS_PER_LANE = 4;
+
+template <int DT, int ESZ, int M>
+__global__ void __launch_bounds__(256) check_row_kernel(const uint8_t* a, int64_t m, int64_t k, int64_t lda,
+                                                        int64_t chunks_row, int N, int32_t* count) {
+  constexpr int GB = M * ESZ;
+  constexpr int PPU = GB > 16 ? GB / 16 : 1;            // chunks per group
+  constexpr int GPC = GB >= 16 ? 1 : 16 / GB;           // groups per chunk
+  const int lane = threadIdx.x & 63;
+  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int64_t total = m * chunks_row;
+  const int64_t row_bytes = k * ESZ;
+  u32x4 v[CHECK_CHUNKS_PER_LANE];
+#pragma unroll
+  for (int i = 0; i < CHECK_CHUNKS_PER_LANE; i++) {
+    const int64_t t = (wave * CHECK_CHUNKS_PER_LANE + i) * 64 + lane;
+    v[i] = u32x4{0, 0, 0, 0};
+    if (t < total) {
+      const int64_t r = t / chunks_row, c = t % chunks_row;
+      const uint8_t* p = a + r * lda * ESZ + 16 * c;
+      if (16 * c + 16 <= row_bytes) {
+        v[i] = *(const u32x4*)p;
+      } else {                                          // ragged last chunk: whole groups (dwords) only
+        const int nd = (int)((row_bytes - 16 * c) / 4);
+#pragma unroll
+        for (int d = 0; d < 4; d++) v[i][d] = d < nd ? ((const uint32_t*)p)[d] : 0u;
+      }
+    }
+  }
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < CHECK_CHUNKS_PER_LANE; i++) {
+    const int64_t t = (wave * CHECK_CHUNKS_PER_LANE + i) * 64 + lane;
+    int nz[GPC];
+#pragma unroll
+    for (int g = 0; g < GPC; g++) nz[g] = 0;
+#pragma unroll
+    for (int d = 0; d < 4; d++) {
+      const uint32_t w = v[i][d];
+#pragma unroll
+      for (int e = 0; e < 4 / ESZ; e++) {
+        const uint32_t x = ESZ == 2 ? (w >> (16 * e)) & 0xFFFFu : (w >> (8 * e)) & 0xFFu;
+        nz[(d * (4 / ESZ) + e) / (M < 16 / ESZ ? M : 16 / ESZ)] += magkey<DT>(x) != 0u;
+      }
+    }
+    if constexpr (PPU > 1) {
+#pragma unroll
+      for (int off = 1; off < PPU; off <<= 1) nz[0] += __shfl_xor(nz[0], off);
+      if (t < total && lane % PPU == 0) bad += nz[0] > N;
+    } else {
+#pragma unroll
+      for (int g = 0; g < GPC; g++) bad += nz[g] > N;     // zero-filled groups past k count 0
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) bad += __shfl_xor(bad, off);
+  if (lane == 0 && bad) atomicAdd(count, bad);
+}
+
+bool check_row_ok(const nm_plan& pl) {
+  return pl.p.op_a == NM_OP_N && (pl.p.lda * pl.esz_ab) % 16 == 0;
+}
+
+hipError_t launch_check_row(const nm_plan& pl, const void* a, int32_t* count, hipStream_t s) {
+  const int64_t chunks_row = (pl.p.k * pl.esz_ab + 15) / 16;
+  const int64_t waves = (pl.p.m * chunks_row + 64 * CHECK_CHUNKS_PER_LANE - 1) / (64 * CHECK_CHUNKS_PER_LANE);
+  const int64_t blocks = (waves + 3) / 4;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const uint8_t* ap = (const uint8_t*)a;
+  const dim3 grid((unsigned)blocks), block(256);
+  const int64_t m = pl.p.m, k = pl.p.k, lda = pl.p.lda;
+  const int n = pl.p.nm_n;
+#define NM_CHECK_ROW(DT, ESZ, MM) NM_LAUNCH((check_row_kernel<DT, ESZ, MM>), grid, block, 0, s, ap, m, k, lda, chunks_row, n, count)
+#define NM_CHECK_ROW_M(DT, ESZ)                         \
+  switch (pl.p.nm_m) {                                  \
+    case 4: NM_CHECK_ROW(DT, ESZ, 4); break;            \
+    case 8: NM_CHECK_ROW(DT, ESZ, 8); break;            \
+    case 16: NM_CHECK_ROW(DT, ESZ, 16); break;          \
+    default: NM_CHECK_ROW(DT, ESZ, 32); break;          \
+  }
+  switch (pl.p.type_ab) {
+    case NM_F16: NM_CHECK_ROW_M(DT_F16, 2); break;
+    case NM_BF16: NM_CHECK_ROW_M(DT_BF16, 2); break;
+    default: NM_CHECK_ROW_M(DT_I8, 1); break;
+  }
+#undef NM_CHECK_ROW_M
+#undef NM_CHECK_ROW
+  return launch_status();
 }
 
 template <int DT, int ESZ, int N, int M, int OP>

@@ -122,6 +122,33 @@ def test_compress_decompress(dtype, N, M, op):
     assert np.array_equal(host(out.t, RAW[dtype]), dref)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("N,M", NM_CASES)
+@pytest.mark.parametrize("path", ["row", "tile"])
+def test_check_1d_ragged_padded(dtype, N, M, path, monkeypatch):
+    """1-D prune check on padded rows (lda > k) with a ragged last 16-byte chunk,
+    groups narrower and wider than 16 bytes, and planted violations."""
+    if path == "tile":
+        monkeypatch.setenv("NM_TILE_ELEMWISE", "1")
+    es = 1 if dtype == "i8" else 2
+    for m, groups in [(3, 1), (5, 67), (2, 261)]:
+        k = groups * M
+        lda = -(-k // (16 // es)) * (16 // es) + 16 // es
+        full = rand(dtype, (m, lda), 900 + groups + M)
+        a = np.ascontiguousarray(full[:, :k])
+        plan = plan_for(dtype, m, 8, k, N, M, lda=lda)
+        cnt = torch.full((1,), -7, dtype=torch.int32, device="cuda")
+        nm.nm_prune_check(plan, dev(full), "1d", cnt)
+        sync()
+        assert int(cnt.item()) == oracle.check_1d(a, dtype, N, M), (m, k)
+        p, _ = oracle.prune_1d(a, dtype, N, M)
+        pf = full.copy()
+        pf[:, :k] = p
+        nm.nm_prune_check(plan, dev(pf), "1d", cnt)
+        sync()
+        assert int(cnt.item()) == 0, (m, k)
+
+
 ROW_NM = [(2, 4), (4, 32), (8, 32)]
 
 
