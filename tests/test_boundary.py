@@ -163,3 +163,13 @@ def test_empty_problems_enqueue_nothing():
     nm.nm_compress(plan, None, None, None, stream=0)
     nm.nm_decompress(plan, None, None, None, stream=0)
     nm.nm_prune(plan, None, None, stream=0)
+
+
+def test_sparse_linear_validates_on_host():
+    # shape errors are raised before any device work
+    import torch
+    from structured_sparse_gemm_nm_amd.linear import SemiStructuredSparseLinear
+    with pytest.raises(ValueError):
+        SemiStructuredSparseLinear(100, 64)
+    with pytest.raises(ValueError):
+        SemiStructuredSparseLinear(64, 64, dtype=torch.float32)
