@@ -296,13 +296,23 @@ def main():
         roofline["traffic_over_algorithmic"] = round(traffic["bytes_per_launch"] / avg_bytes, 3)
         roofline["traffic_note"] = traffic["note"]
 
-    # dense comparator, same shapes, same layouts
+    # dense comparator, same shapes, same B layouts. Dense A is always given row
+    # by row of op(A) (op_a = N): for a backward operand (op_a = T) that means
+    # the pruned weight transposed once outside the timing, the faster layout
+    # for the dense kernels (their op_a = T path stages A through registers), so
+    # the comparison is against the better dense formulation of the product.
     dense = {}
     if not args.no_dense:
         for g in gemms:
+            a_dense = g["Ap"]
+            if g["op_a"] == "T":
+                a_dense = g["Ap"].t().contiguous()
             for ob in g["layouts"]:
                 pl = g["plans"][ob]
-                f = lambda: nm.nm_dense_gemm(pl, g["w"]["alpha"], g["Ap"], g["B"][ob], g["w"]["beta"], g["C"], g["D"][ob])
+                if g["op_a"] == "T":
+                    pl = nm.nm_plan_init(g["m"], g["n"], g["k"], g["N"], g["M"], op_a="N", op_b=ob, dtype=g["dtype"],
+                                         order_cd=g["w"].get("order_cd", "row"))
+                f = lambda: nm.nm_dense_gemm(pl, g["w"]["alpha"], a_dense, g["B"][ob], g["w"]["beta"], g["C"], g["D"][ob])
                 for _ in range(max(2, args.warmup)):
                     f()
                 e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)

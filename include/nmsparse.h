@@ -32,7 +32,9 @@
  *    byte-for-byte this library's "NT" with order_cd = NM_COL_MAJOR.)
  *  - Element types (type_ab, type_cd): (NM_F16, NM_F16), (NM_BF16, NM_BF16)
  *    with fp32 accumulation; (NM_I8, NM_I32) with exact int32 accumulation
- *    (the blog's type list; C and D are int32 for the integer path).
+ *    (the blog's type list; C and D are int32 for the integer path); and
+ *    (NM_I8, NM_I8), the blog's int8 output: C and D int8, D = alpha * acc +
+ *    beta * C evaluated exactly and saturated to [-128, 127].
  *  - Leading dimensions are in elements. All device pointers must be 16-byte
  *    aligned, and every stored row (column, for column-major C/D) that is at
  *    least 16 bytes long must start on a 16-byte boundary

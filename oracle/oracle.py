@@ -13,7 +13,8 @@ What is computed, and from which page:
   check_*       -- cuSPARSELt blog, the prune-check snippet (non-zero = invalid).
   compress /
   decompress    -- cuSPARSELt blog, Figure 2 text: kept values + index metadata.
-  gemm_*        -- cuSPARSELt blog: D = alpha*op(A)*op(B) + beta*C.
+  gemm_*        -- cuSPARSELt blog: D = alpha*op(A)*op(B) + beta*C (int8
+                   output: the exact integer saturated to int8).
 """
 import ctypes
 import os
@@ -223,6 +224,15 @@ def gemm_i64(A, B, alpha=1, beta=0, C=None):
     Cc = _c(C, np.int32) if C is not None else None
     lib().or_gemm_i64(_ptr(A), _ptr(B), _ptr(Cc), _ptr(D), m, n, k, int(alpha), int(beta))
     return D
+
+
+def gemm_i8_saturated(A, B, alpha=1, beta=0, C=None):
+    """int8 output (cuSPARSELt blog: int8 inputs and outputs with int32
+    accumulation): the exact integer alpha*A@B + beta*C, int8 C widened
+    exactly, saturated to [-128, 127] (saturation is the reading taken for
+    the int8 store)."""
+    Cw = np.asarray(C, np.int32) if C is not None else None
+    return np.clip(gemm_i64(A, B, alpha, beta, Cw), -128, 127).astype(np.int8)
 
 
 def spmm_compressed_f64(vals, meta, dtype, m, k, N, M, B, alpha=1.0, beta=0.0, C=None):

@@ -163,9 +163,12 @@ class Plan:
 
 
 def nm_plan_init(m, n, k, nm_n=2, nm_m=4, op_a="N", op_b="N", dtype="f16", lda=None, ldb=None, ldc=None, ldd=None,
-                 order_cd="row"):
-    """Validate a problem and return a Plan (host only). order_cd: "row" or "col" (C and D storage)."""
+                 order_cd="row", out_dtype=None):
+    """Validate a problem and return a Plan (host only). order_cd: "row" or "col" (C and D storage).
+    out_dtype: C/D type when it differs from the default of `dtype` ("i8" with dtype "i8": saturated int8 D)."""
     ta, tc = DTYPES[dtype]
+    if out_dtype is not None:
+        tc = {"f16": NM_F16, "bf16": NM_BF16, "i8": NM_I8, "i32": NM_I32}[out_dtype]
     oa = NM_OP_T if op_a == "T" else NM_OP_N
     ob = NM_OP_T if op_b == "T" else NM_OP_N
     p = nm_problem_t()

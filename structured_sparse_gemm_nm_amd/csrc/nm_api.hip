@@ -83,8 +83,8 @@ nm_status_t nm_plan_init(nm_plan_t* plan, const nm_problem_t* p) {
     return fail(NM_ERR_INVALID_ARG, "op_a / op_b must be NM_OP_N or NM_OP_T");
   const bool pair_ok = (p->type_ab == NM_F16 && p->type_cd == NM_F16) ||
                        (p->type_ab == NM_BF16 && p->type_cd == NM_BF16) ||
-                       (p->type_ab == NM_I8 && p->type_cd == NM_I32);
-  if (!pair_ok) return fail(NM_ERR_INVALID_ARG, "type pair must be (F16,F16), (BF16,BF16) or (I8,I32)");
+                       (p->type_ab == NM_I8 && (p->type_cd == NM_I32 || p->type_cd == NM_I8));
+  if (!pair_ok) return fail(NM_ERR_INVALID_ARG, "type pair must be (F16,F16), (BF16,BF16), (I8,I32) or (I8,I8)");
   if (p->order_cd != NM_ROW_MAJOR && p->order_cd != NM_COL_MAJOR)
     return fail(NM_ERR_INVALID_ARG, "order_cd must be NM_ROW_MAJOR or NM_COL_MAJOR");
   if (p->reserved != 0) return fail(NM_ERR_INVALID_ARG, "reserved must be 0");

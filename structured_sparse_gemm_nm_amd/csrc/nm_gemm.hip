@@ -89,9 +89,7 @@ __global__ void __launch_bounds__(NTH) skinny_kernel(GemmArgs A, int b_op_t, int
       for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
       if (lane == 0 && row < A.m) {
         if constexpr (DT == DT_I8) {
-          int64_t iv = (int64_t)A.alpha * v;
-          if (A.beta != 0.0f) iv += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.c_rs + c * A.c_cs];
-          ((int32_t*)A.d)[row * A.d_rs + c * A.d_cs] = (int32_t)iv;
+          int_store(A, row * A.d_rs + c * A.d_cs, int_epilogue(A, v, row * A.c_rs + c * A.c_cs));
         } else {
           float o = A.alpha * v;
           if (A.beta != 0.0f) o += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.c_rs + c * A.c_cs]);
@@ -115,6 +113,7 @@ static GemmArgs make_gemm_args(const nm_plan& pl, float alpha, const void* a, co
   A.c_rs = col ? 1 : pl.p.ldc; A.c_cs = col ? pl.p.ldc : 1;
   A.d_rs = col ? 1 : pl.p.ldd; A.d_cs = col ? pl.p.ldd : 1;
   A.cd_col = col;
+  A.cd_i8 = pl.p.type_cd == NM_I8;
   A.alpha = alpha; A.beta = beta;
   A.N = pl.p.nm_n; A.M = pl.p.nm_m; A.bits = pl.bits;
   A.a_vec = (A.lda * pl.esz_ab) % 16 == 0;

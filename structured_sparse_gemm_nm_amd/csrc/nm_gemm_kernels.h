@@ -64,10 +64,25 @@ struct GemmArgs {
   int64_t ldb;
   int64_t c_rs, c_cs, d_rs, d_cs;   // C/D element (row, col) at row * rs + col * cs (row- or column-major)
   int cd_col;                       // C/D column-major (rs = 1, cs = ld)
+  int cd_i8;                        // integer path: C/D are int8 (D saturated) instead of int32
   float alpha, beta;
   int N, M, bits;
   int a_vec, b_vec;     // 16-byte vector loads allowed on A / B rows
 };
+
+// Integer-path epilogue: v = alpha * acc + beta * C exactly in int64, stored as
+// int32 (D = v) or, with int8 C/D, saturated to [-128, 127].
+__device__ __forceinline__ int64_t int_epilogue(const GemmArgs& A, int64_t acc, int64_t cidx) {
+  int64_t v = (int64_t)A.alpha * acc;
+  if (A.beta != 0.0f)
+    v += (int64_t)A.beta * (A.cd_i8 ? (int64_t)((const int8_t*)A.c)[cidx] : (int64_t)((const int32_t*)A.c)[cidx]);
+  return v;
+}
+__device__ __forceinline__ int32_t sat_i8(int64_t v) { return (int32_t)(v < -128 ? -128 : (v > 127 ? 127 : v)); }
+__device__ __forceinline__ void int_store(const GemmArgs& A, int64_t didx, int64_t v) {
+  if (A.cd_i8) ((int8_t*)A.d)[didx] = (int8_t)sat_i8(v);
+  else ((int32_t*)A.d)[didx] = (int32_t)v;
+}
 
 // ---------------------------------------------------------------- operand staging
 
@@ -590,9 +605,7 @@ __global__ void __launch_bounds__(NTH) gemm_kernel(GemmArgs A) {
         const int64_t row = r0 + wm0 + fm * 32 + 8 * (r / 4) + 4 * q + (r % 4);
         if (row >= A.m) continue;
         if constexpr (DT == DT_I8) {
-          int64_t v = (int64_t)A.alpha * acc[fm][fn][r];
-          if (A.beta != 0.0f) v += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.c_rs + col * A.c_cs];
-          ((int32_t*)A.d)[row * A.d_rs + col * A.d_cs] = (int32_t)v;
+          int_store(A, row * A.d_rs + col * A.d_cs, int_epilogue(A, acc[fm][fn][r], row * A.c_rs + col * A.c_cs));
         } else {
           float v = A.alpha * acc[fm][fn][r];
           if (A.beta != 0.0f) v += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.c_rs + col * A.c_cs]);
@@ -812,9 +825,7 @@ __global__ void __launch_bounds__(NTH) gemm_fast_kernel(GemmArgs A) {
       for (int r = 0; r < 16; r++) {
         const int64_t row = r0 + wm0 + fm * 32 + 8 * (r / 4) + 4 * q + (r % 4);
         if constexpr (DT == DT_I8) {
-          int64_t v = (int64_t)A.alpha * acc[fm][fn][r];
-          if (A.beta != 0.0f) v += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.c_rs + col * A.c_cs];
-          ((int32_t*)A.d)[row * A.d_rs + col * A.d_cs] = (int32_t)v;
+          int_store(A, row * A.d_rs + col * A.d_cs, int_epilogue(A, acc[fm][fn][r], row * A.c_rs + col * A.c_cs));
         } else {
           float v = A.alpha * acc[fm][fn][r];
           if (A.beta != 0.0f) v += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.c_rs + col * A.c_cs]);
@@ -1166,8 +1177,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   // ---- epilogue: D = alpha * acc + beta * C ----
   if (A.cd_col) {
     // column-major C/D: accumulator elements 4(r/4) .. 4(r/4)+3 of a lane are
-    // four consecutive rows of one column, i.e. 8 (16-bit) or 16 (int32)
-    // contiguous bytes; full tiles and the 16-byte column rule keep them aligned
+    // four consecutive rows of one column, i.e. 8 (16-bit), 16 (int32) or 4
+    // (int8) contiguous bytes; full tiles and the 16-byte column rule keep
+    // them aligned
 #pragma unroll
     for (int fm = 0; fm < FM; fm++)
 #pragma unroll
@@ -1180,6 +1192,18 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
             int64_t v[4];
 #pragma unroll
             for (int t = 0; t < 4; t++) v[t] = (int64_t)A.alpha * acc[fm][fn][4 * r4 + t];
+            if (A.cd_i8) {   // four int8 rows: one dword
+              if (A.beta != 0.0f) {
+                const uint32_t cv = *(const uint32_t*)((const int8_t*)A.c + col * A.c_cs + row);
+#pragma unroll
+                for (int t = 0; t < 4; t++) v[t] += (int64_t)A.beta * (int64_t)(int8_t)(cv >> (8 * t));
+              }
+              uint32_t o = 0;
+#pragma unroll
+              for (int t = 0; t < 4; t++) o |= ((uint32_t)sat_i8(v[t]) & 0xFFu) << (8 * t);
+              *(uint32_t*)((int8_t*)A.d + col * A.d_cs + row) = o;
+              continue;
+            }
             if (A.beta != 0.0f) {
               const intx4 cv = *(const intx4*)((const int32_t*)A.c + col * A.c_cs + row);
 #pragma unroll
@@ -1214,9 +1238,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
       for (int r = 0; r < 16; r++) {
         const int64_t row = r0 + wm0 + fm * 32 + 8 * (r / 4) + 4 * q + (r % 4);
         if constexpr (DT == DT_I8) {
-          int64_t v = (int64_t)A.alpha * acc[fm][fn][r];
-          if (A.beta != 0.0f) v += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.c_rs + col];
-          ((int32_t*)A.d)[row * A.d_rs + col] = (int32_t)v;
+          int_store(A, row * A.d_rs + col, int_epilogue(A, acc[fm][fn][r], row * A.c_rs + col));
         } else {
           float v = A.alpha * acc[fm][fn][r];
           if (A.beta != 0.0f) v += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.c_rs + col]);

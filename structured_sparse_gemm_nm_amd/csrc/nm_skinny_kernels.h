@@ -286,9 +286,7 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
         for (int c = 0; c < NP; c++) {
           if (lane != c || c >= n) continue;
           if constexpr (DT == DT_I8) {
-            int64_t iv = (int64_t)A.alpha * acc[rr][c];
-            if (A.beta != 0.0f) iv += (int64_t)A.beta * ((const int32_t*)A.c)[row * A.c_rs + c * A.c_cs];
-            ((int32_t*)A.d)[row * A.d_rs + c * A.d_cs] = (int32_t)iv;
+            int_store(A, row * A.d_rs + c * A.d_cs, int_epilogue(A, acc[rr][c], row * A.c_rs + c * A.c_cs));
           } else {
             float o = A.alpha * acc[rr][c];
             if (A.beta != 0.0f) o += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.c_rs + c * A.c_cs]);

@@ -471,6 +471,60 @@ def test_col_major_cd(dtype, case, beta, monkeypatch):
     assert_close(dtype, np.ascontiguousarray(got[:, :m].T), ref, tol)
 
 
+I8OUT_CASES = [
+    # (label, N, M, m, n, k, op_b, order_cd): copy-ring kernel (both B layouts, both C/D orders),
+    # ragged, general N:M gather, small n, and N = 0 for the dense comparator
+    ("24-ring-NT", 2, 4, 256, 256, 256, "T", "row"),
+    ("24-ring-NN-col", 2, 4, 256, 256, 256, "N", "col"),
+    ("24-ragged", 2, 4, 200, 144, 336, "N", "row"),
+    ("24-ragged-col", 2, 4, 200, 144, 336, "T", "col"),
+    ("gather-4of32", 4, 32, 150, 80, 544, "T", "row"),
+    ("skinny-24", 2, 4, 100, 8, 1088, "N", "row"),
+    ("skinny-8of32-col", 8, 32, 100, 3, 1088, "N", "col"),
+    ("dense-ring", 0, 0, 256, 256, 320, "T", "row"),
+    ("dense-ragged-col", 0, 0, 272, 144, 208, "N", "col"),
+]
+
+
+@pytest.mark.parametrize("case", I8OUT_CASES, ids=[c[0] for c in I8OUT_CASES])
+@pytest.mark.parametrize("ab", [(1.0, 0.0), (2.0, -1.0)])
+def test_int8_output(case, ab):
+    """int8 C and D: the exact integer alpha acc + beta C saturated to int8, bit
+    for bit. Inputs in [-3, 3] put outputs both inside and beyond the int8 range."""
+    label, N, M, m, n, k, op_b, order = case
+    alpha, beta = ab
+    seed = 8100 + m + n + k
+    a = inputs.uniform_int((m, k), seed, -3, 3)
+    b_log = inputs.uniform_int((k, n), seed + 1, -3, 3)
+    b_st = b_log if op_b == "N" else np.ascontiguousarray(b_log.T)
+    c = inputs.uniform_int((m, n), seed + 2, -128, 127) if beta != 0 else None
+    lines, length = (n, m) if order == "col" else (m, n)
+    ld = -(-length // 16) * 16                                  # 16-byte rows (columns) of int8
+    plan = plan_for("i8", m, n, k, N or 2, M or 4, op_b=op_b, order_cd=order, out_dtype="i8", ldc=ld, ldd=ld)
+    d = Guarded((lines, ld), torch.int8)
+    dc = None
+    if c is not None:
+        c_st = np.zeros((lines, ld), np.int8)
+        c_st[:, :length] = c.T if order == "col" else c
+        dc = dev(c_st)
+    if N:
+        ahat, _ = oracle.prune_1d(a, "i8", N, M)
+        vref, mref = oracle.compress(a, "i8", N, M)
+        nm.nm_spmm(plan, alpha, dev(vref), dev(mref), dev(b_st), beta, dc, d.t)
+    else:
+        ahat = a
+        nm.nm_dense_gemm(plan, alpha, dev(a), dev(b_st), beta, dc, d.t)
+    sync()
+    d.check()
+    got = host(d.t, np.int8)[:, :length]
+    if order == "col":
+        got = got.T
+    ref = oracle.gemm_i8_saturated(ahat, b_log, int(alpha), int(beta), c)
+    assert np.array_equal(got, ref), (label, np.argwhere(got != ref)[:5])
+    exact = oracle.gemm_i64(ahat, b_log, int(alpha), int(beta), c.astype(np.int32) if c is not None else None)
+    assert (np.abs(exact) > 127).any() and (np.abs(exact) <= 127).any()   # both regimes are exercised
+
+
 def test_col_major_k_zero_and_alias():
     m, n = 40, 24
     c = rand("f16", (m, n), 11)

@@ -386,3 +386,22 @@ def test_tolerance_formula():
     assert np.allclose(oracle.tolerance(absA, absB), [[0.111]], rtol=0, atol=1e-15)
     C = np.array([[10.0]])
     assert np.allclose(oracle.tolerance(absA, absB, 2.0, -1.0, C), [[1e-2 * (22 + 10) + 1e-3]], rtol=0, atol=1e-15)
+
+
+def test_int8_output_saturates_the_exact_integer():
+    """Closed forms: a row of 127s against a column of 127s sums to 127^2 k
+    (saturates high), its negation saturates low, alternating signs cancel to
+    0, and small sums pass through unchanged; beta * C with int8 C adds in."""
+    k = 8
+    a = np.full((1, k), 127, np.int8)
+    b = np.full((k, 1), 127, np.int8)
+    assert oracle.gemm_i8_saturated(a, b)[0, 0] == 127
+    assert oracle.gemm_i8_saturated(a, -b)[0, 0] == -128
+    alt = np.array([[1, -1] * (k // 2)], np.int8)
+    assert oracle.gemm_i8_saturated(alt, b)[0, 0] == 0
+    small = np.array([[1, 2, 3, 0, 0, 0, 0, -1]], np.int8)
+    ones = np.ones((k, 1), np.int8)
+    assert oracle.gemm_i8_saturated(small, ones)[0, 0] == 5
+    c = np.array([[-100]], np.int8)
+    assert oracle.gemm_i8_saturated(small, ones, 2, 1, c)[0, 0] == -90
+    assert oracle.gemm_i8_saturated(small, ones, 1, 3, c)[0, 0] == -128
