@@ -182,6 +182,21 @@ nm_status_t nm_spmm(nm_plan_t plan, const float* alpha, const void* d_values, co
 nm_status_t nm_dense_gemm(nm_plan_t plan, const float* alpha, const void* dA, const void* dB,
                           const float* beta, const void* dC, void* dD, void* stream);
 
+/* Algorithm selection: the blog's algorithm-selection object with its
+ * configuration-id attribute, reduced to one id on the plan. The ids pin the
+ * block tile of the matrix-core products (nm_spmm on the 2:4 and general N:M
+ * paths and nm_dense_gemm): NM_ALG_AUTO (the default: the plan picks by shape),
+ * NM_ALG_TILE128 (128 x 128), NM_ALG_TILE256X128 (256 x 128),
+ * NM_ALG_TILE256 (256 x 256 for 2:4; 256 x 128 for the dense product). The
+ * general N:M expansion always uses 128 x 128 and small n (n <= 16) its own
+ * kernel; there the id has no effect. Results do not depend on the id beyond
+ * fp32 summation order (bit-exact for int8). Host-only; invalid ids give
+ * NM_ERR_INVALID_ARG and leave the plan unchanged. */
+enum { NM_ALG_AUTO = 0, NM_ALG_TILE128 = 1, NM_ALG_TILE256X128 = 2, NM_ALG_TILE256 = 3, NM_ALG_COUNT = 4 };
+int32_t nm_plan_algorithm_count(nm_plan_t plan);   /* NM_ALG_COUNT (0 for a NULL plan) */
+nm_status_t nm_plan_set_algorithm(nm_plan_t plan, int32_t alg);
+nm_status_t nm_plan_get_algorithm(nm_plan_t plan, int32_t* alg);
+
 /* Name of the SpMM kernel the plan dispatches to (static string). */
 const char* nm_plan_kernel_name(nm_plan_t plan);
 

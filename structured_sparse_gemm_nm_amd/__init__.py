@@ -67,6 +67,9 @@ def lib():
         L.nm_spmm.restype = st; L.nm_spmm.argtypes = [P, FP, P, P, P, FP, P, P, P, P]
         L.nm_dense_gemm.restype = st; L.nm_dense_gemm.argtypes = [P, FP, P, P, FP, P, P, P]
         L.nm_plan_kernel_name.restype = ctypes.c_char_p; L.nm_plan_kernel_name.argtypes = [P]
+        L.nm_plan_algorithm_count.restype = I32; L.nm_plan_algorithm_count.argtypes = [P]
+        L.nm_plan_set_algorithm.restype = st; L.nm_plan_set_algorithm.argtypes = [P, I32]
+        L.nm_plan_get_algorithm.restype = st; L.nm_plan_get_algorithm.argtypes = [P, ctypes.POINTER(I32)]
         L.nm_plan_spmm_kernel.restype = ctypes.c_char_p; L.nm_plan_spmm_kernel.argtypes = [P]
         L.nm_status_string.restype = ctypes.c_char_p; L.nm_status_string.argtypes = [st]
         L.nm_last_error.restype = ctypes.c_char_p; L.nm_last_error.argtypes = []
@@ -227,6 +230,23 @@ def nm_dense_gemm(plan, alpha, dA, dB, beta, dC, dD, stream=None):
     a, b = ctypes.c_float(alpha), ctypes.c_float(beta)
     _check(lib().nm_dense_gemm(plan.handle, ctypes.byref(a), _ptr(dA), _ptr(dB), ctypes.byref(b), _ptr(dC), _ptr(dD),
                                _stream(stream)))
+
+
+NM_ALG_AUTO, NM_ALG_TILE128, NM_ALG_TILE256X128, NM_ALG_TILE256, NM_ALG_COUNT = range(5)
+
+
+def nm_plan_algorithm_count(plan):
+    return lib().nm_plan_algorithm_count(plan.handle)
+
+
+def nm_plan_set_algorithm(plan, alg):
+    _check(lib().nm_plan_set_algorithm(plan.handle, int(alg)))
+
+
+def nm_plan_get_algorithm(plan):
+    a = ctypes.c_int32()
+    _check(lib().nm_plan_get_algorithm(plan.handle, ctypes.byref(a)))
+    return a.value
 
 
 def nm_plan_spmm_kernel(plan):

@@ -126,6 +126,7 @@ nm_status_t nm_plan_init(nm_plan_t* plan, const nm_problem_t* p) {
   pl->mld = (mbytes + 15) / 16 * 16;
   // benchmark-sweep overrides (read once here, not per launch)
   pl->force_tile = -1;
+  pl->algorithm = NM_ALG_AUTO;
   if (const char* f = getenv("NM_FORCE_TILE")) {
     if (!strcmp(f, "128")) pl->force_tile = nm::T128;
     else if (!strcmp(f, "256x128")) pl->force_tile = nm::T256x128;
@@ -173,6 +174,25 @@ const char* nm_plan_spmm_kernel(nm_plan_t plan) {
     plan->spmm_symbol = name;
   }
   return plan->spmm_symbol.c_str();
+}
+
+int32_t nm_plan_algorithm_count(nm_plan_t plan) { return plan ? NM_ALG_COUNT : 0; }
+
+nm_status_t nm_plan_set_algorithm(nm_plan_t plan, int32_t alg) {
+  if (!plan) return fail(NM_ERR_INVALID_ARG, "plan is NULL");
+  if (alg < 0 || alg >= NM_ALG_COUNT) return fail(NM_ERR_INVALID_ARG, "algorithm id out of range");
+  static const int tile_of[NM_ALG_COUNT] = {-1, nm::T128, nm::T256x128, nm::T256};
+  plan->force_tile = tile_of[alg];
+  plan->algorithm = alg;
+  plan->spmm_symbol.clear();          // the launched kernel may change
+  set_error("");
+  return NM_OK;
+}
+
+nm_status_t nm_plan_get_algorithm(nm_plan_t plan, int32_t* alg) {
+  if (!plan || !alg) return fail(NM_ERR_INVALID_ARG, "plan / alg is NULL");
+  *alg = plan->algorithm;
+  return NM_OK;
 }
 
 const char* nm_plan_kernel_name(nm_plan_t plan) {

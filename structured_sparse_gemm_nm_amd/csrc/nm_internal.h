@@ -23,6 +23,7 @@ struct nm_plan {
   // NM_NO_DMA_NN, NM_NO_DEEP_RING, NM_OLD_SKINNY, NM_TILE_ELEMWISE), so
   // launches do not scan the environment
   int force_tile;           // -1 = automatic, else nm::TileCfg
+  int algorithm;            // nm_plan_set_algorithm id (NM_ALG_AUTO unless set)
   bool no_dma, no_dma_nn, no_deep_ring, old_skinny;
   bool tile_elemwise;       // prune/check/compress/decompress on the older kernels even where the row path applies
 };

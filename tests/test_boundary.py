@@ -173,3 +173,17 @@ def test_sparse_linear_validates_on_host():
         SemiStructuredSparseLinear(100, 64)
     with pytest.raises(ValueError):
         SemiStructuredSparseLinear(64, 64, dtype=torch.float32)
+
+
+def test_algorithm_ids_validate_on_host():
+    plan = _init()
+    assert nm.nm_plan_algorithm_count(plan) == nm.NM_ALG_COUNT == 4
+    assert nm.nm_plan_get_algorithm(plan) == nm.NM_ALG_AUTO
+    for alg in range(nm.NM_ALG_COUNT):
+        nm.nm_plan_set_algorithm(plan, alg)
+        assert nm.nm_plan_get_algorithm(plan) == alg
+    for bad in (-1, nm.NM_ALG_COUNT):
+        with pytest.raises(nm.NmError) as e:
+            nm.nm_plan_set_algorithm(plan, bad)
+        assert e.value.status == nm.NM_ERR_INVALID_ARG
+    assert nm.nm_plan_get_algorithm(plan) == nm.NM_ALG_COUNT - 1     # unchanged by the rejected ids

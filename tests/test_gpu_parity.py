@@ -525,6 +525,39 @@ def test_int8_output(case, ab):
     assert (np.abs(exact) > 127).any() and (np.abs(exact) <= 127).any()   # both regimes are exercised
 
 
+@pytest.mark.parametrize("dtype", ["f16", "i8"])
+def test_algorithm_ids_pin_the_tile_and_autotune(dtype):
+    """Each algorithm id launches its tile's kernel and gives the oracle's result;
+    autotuning times them all and leaves the fastest pinned on the plan."""
+    from structured_sparse_gemm_nm_amd.tuning import autotune_spmm
+    m, n, k = 512, 512, 256
+    a = rand(dtype, (m, k), 31)
+    b = rand(dtype, (n, k), 32)
+    ahat, _ = oracle.prune_1d(a, dtype, 2, 4)
+    v, meta = oracle.compress(a, dtype, 2, 4)
+    plan = plan_for(dtype, m, n, k, 2, 4, op_b="T")
+    odt, raw = (torch.int32, np.int32) if dtype == "i8" else (torch.int16, np.uint16)
+    dv, dm, db = dev(v), dev(meta), dev(b)
+    ref, tol = ref_product(dtype, ahat, np.ascontiguousarray(b.T), 1.0, 0.0, None)
+    tiles = {nm.NM_ALG_TILE128: "128, 128,", nm.NM_ALG_TILE256X128: "256, 128,", nm.NM_ALG_TILE256: "256, 256,"}
+    for alg in range(nm.NM_ALG_COUNT):
+        nm.nm_plan_set_algorithm(plan, alg)
+        kern = plan.spmm_kernel
+        if alg in tiles:
+            assert tiles[alg] in kern, (alg, kern)
+        d = Guarded((m, n), odt)
+        nm.nm_spmm(plan, 1.0, dv, dm, db, 0.0, None, d.t)
+        sync()
+        d.check()
+        assert_close(dtype, host(d.t, raw), ref, tol)
+    d = Guarded((m, n), odt)
+    times = autotune_spmm(plan, 1.0, dv, dm, db, 0.0, None, d.t, reps=3)
+    best = nm.nm_plan_get_algorithm(plan)
+    assert set(times) == set(range(nm.NM_ALG_COUNT)) and times[best][0] == min(t for t, _ in times.values())
+    sync()
+    assert_close(dtype, host(d.t, raw), ref, tol)
+
+
 def test_col_major_k_zero_and_alias():
     m, n = 40, 24
     c = rand("f16", (m, n), 11)
