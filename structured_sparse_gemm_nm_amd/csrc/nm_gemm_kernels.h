@@ -1175,6 +1175,66 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   }
 
   // ---- epilogue: D = alpha * acc + beta * C ----
+  if constexpr (DT != DT_I8) {
+    // column-major 16-bit D with beta = 0: the block tile goes through the
+    // (now idle) ring in column-major order, then every 16-byte store covers
+    // consecutive rows of one column, so a column of the tile leaves as whole
+    // lines instead of one 8-byte piece per lane and line
+    constexpr int CP = BM + 8;                               // LDS column pitch (elements)
+    if constexpr (BN * CP * 2 <= S * STAGE) {
+      if (A.cd_col && A.beta == 0.0f) {
+        __syncthreads();                                     // every wave is done reading the ring
+        uint16_t* tile = (uint16_t*)ring;
+#pragma unroll
+        for (int fm = 0; fm < FM; fm++)
+#pragma unroll
+          for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+            for (int r4 = 0; r4 < 4; r4++) {
+              const int cl = wn0 + fn * 32 + l32, rl = wm0 + fm * 32 + 8 * r4 + 4 * q;
+              const uint32_t lo = (uint32_t)to_bits16<DT>(A.alpha * acc[fm][fn][4 * r4]) |
+                                  ((uint32_t)to_bits16<DT>(A.alpha * acc[fm][fn][4 * r4 + 1]) << 16);
+              const uint32_t hi = (uint32_t)to_bits16<DT>(A.alpha * acc[fm][fn][4 * r4 + 2]) |
+                                  ((uint32_t)to_bits16<DT>(A.alpha * acc[fm][fn][4 * r4 + 3]) << 16);
+              *(u32x2*)(tile + cl * CP + rl) = u32x2{lo, hi};
+            }
+        __syncthreads();
+        constexpr int PIECES = BM * 2 / 16;                  // 16-byte pieces per tile column
+        for (int i = threadIdx.x; i < BN * PIECES; i += 64 * NW) {
+          const int c = i / PIECES, pc = i % PIECES;
+          const u32x4 v = *(const u32x4*)(tile + c * CP + 8 * pc);
+          *(u32x4*)((uint16_t*)A.d + (c0 + c) * A.d_cs + r0 + 8 * pc) = v;
+        }
+        return;
+      }
+    }
+    // row-major 16-bit D with beta = 0: the same through a row-major image of
+    // the tile, so the stores run along rows 16 bytes per lane
+    constexpr int RP = BN + 8;                               // LDS row pitch (elements)
+    if constexpr (BM * RP * 2 <= S * STAGE) {
+      if (!A.cd_col && A.beta == 0.0f) {
+        __syncthreads();
+        uint16_t* tile = (uint16_t*)ring;
+#pragma unroll
+        for (int fm = 0; fm < FM; fm++)
+#pragma unroll
+          for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+            for (int r = 0; r < 16; r++) {
+              const int rl = wm0 + fm * 32 + 8 * (r / 4) + 4 * q + (r % 4), cl = wn0 + fn * 32 + l32;
+              tile[rl * RP + cl] = to_bits16<DT>(A.alpha * acc[fm][fn][r]);
+            }
+        __syncthreads();
+        constexpr int PIECES = BN * 2 / 16;                  // 16-byte pieces per tile row
+        for (int i = threadIdx.x; i < BM * PIECES; i += 64 * NW) {
+          const int rr = i / PIECES, pc = i % PIECES;
+          const u32x4 v = *(const u32x4*)(tile + rr * RP + 8 * pc);
+          *(u32x4*)((uint16_t*)A.d + (r0 + rr) * A.d_rs + c0 + 8 * pc) = v;
+        }
+        return;
+      }
+    }
+  }
   if (A.cd_col) {
     // column-major C/D: accumulator elements 4(r/4) .. 4(r/4)+3 of a lane are
     // four consecutive rows of one column, i.e. 8 (16-bit), 16 (int32) or 4
