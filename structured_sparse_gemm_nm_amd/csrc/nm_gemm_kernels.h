@@ -1235,6 +1235,126 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
       }
     }
   }
+  {
+    // beta != 0 (any D type; 16-bit D with beta = 0 took the path above): the raw 4-byte
+    // accumulators go through the ring (in rounds of one wave row or column
+    // group when the whole tile does not fit), then each thread step takes four
+    // consecutive elements of a D row (column) with one 16-byte LDS read, reads
+    // the matching C elements as one vector, applies alpha and beta exactly as
+    // the direct path does and stores one vector
+    typedef typename std::conditional<DT == DT_I8, int32_t, float>::type raw_t;
+    typedef typename std::conditional<DT == DT_I8, intx4, floatx4>::type raw4_t;
+    constexpr int P4 = 4;                                    // pitch padding (elements)
+    constexpr int LINE = BN + P4, COLP = BM + P4;
+    constexpr int RR = BM * LINE * 4 <= S * STAGE ? 1 : WGM; // rounds, row-major image
+    constexpr int RC = BN * COLP * 4 <= S * STAGE ? 1 : WGN; // rounds, column-major image
+    constexpr bool FIT_R = (BM / RR) * LINE * 4 <= S * STAGE, FIT_C = (BN / RC) * COLP * 4 <= S * STAGE;
+    // measured (4096^3 int8, copy-ring kernel): beta != 0 int32 110 -> 85 us, int8 92 -> 77 us; with
+    // beta = 0 the integer stores straight from the accumulators are as fast or faster (61 vs 63 us,
+    // int8 65 vs 73 us), so only a C operand takes this path
+    if constexpr (FIT_R && FIT_C) if (A.beta != 0.0f) {
+      raw_t* img = (raw_t*)ring;
+      const int wr = wave / WGN, wc = wave % WGN;
+      auto finish4 = [&](const raw_t (&a4)[4], int64_t row, int64_t col, bool colmajor) {
+        // four consecutive elements of one D row (colmajor: one D column) from (row, col)
+        const int64_t cidx = colmajor ? col * A.c_cs + row : row * A.c_rs + col;
+        const int64_t didx = colmajor ? col * A.d_cs + row : row * A.d_rs + col;
+        if constexpr (DT == DT_I8) {
+          int64_t v[4];
+#pragma unroll
+          for (int t = 0; t < 4; t++) v[t] = (int64_t)A.alpha * a4[t];
+          if (A.beta != 0.0f) {
+            if (A.cd_i8) {
+              const uint32_t cv = *(const uint32_t*)((const int8_t*)A.c + cidx);
+#pragma unroll
+              for (int t = 0; t < 4; t++) v[t] += (int64_t)A.beta * (int64_t)(int8_t)(cv >> (8 * t));
+            } else {
+              const intx4 cv = *(const intx4*)((const int32_t*)A.c + cidx);
+#pragma unroll
+              for (int t = 0; t < 4; t++) v[t] += (int64_t)A.beta * cv[t];
+            }
+          }
+          if (A.cd_i8) {
+            uint32_t o = 0;
+#pragma unroll
+            for (int t = 0; t < 4; t++) o |= ((uint32_t)sat_i8(v[t]) & 0xFFu) << (8 * t);
+            *(uint32_t*)((int8_t*)A.d + didx) = o;
+          } else {
+            *(intx4*)((int32_t*)A.d + didx) = intx4{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
+          }
+        } else {
+          float v[4];
+#pragma unroll
+          for (int t = 0; t < 4; t++) v[t] = A.alpha * a4[t];
+          if (A.beta != 0.0f) {
+            const u32x2 cv = *(const u32x2*)((const uint16_t*)A.c + cidx);
+            v[0] += A.beta * from_bits16<DT>((uint16_t)(cv[0] & 0xFFFFu));
+            v[1] += A.beta * from_bits16<DT>((uint16_t)(cv[0] >> 16));
+            v[2] += A.beta * from_bits16<DT>((uint16_t)(cv[1] & 0xFFFFu));
+            v[3] += A.beta * from_bits16<DT>((uint16_t)(cv[1] >> 16));
+          }
+          const uint32_t lo = (uint32_t)to_bits16<DT>(v[0]) | ((uint32_t)to_bits16<DT>(v[1]) << 16);
+          const uint32_t hi = (uint32_t)to_bits16<DT>(v[2]) | ((uint32_t)to_bits16<DT>(v[3]) << 16);
+          *(u32x2*)((uint16_t*)A.d + didx) = u32x2{lo, hi};
+        }
+      };
+      if (!A.cd_col) {
+        constexpr int ROWS = BM / RR, QPR = BN / 4;
+#pragma unroll 1
+        for (int rd = 0; rd < RR; rd++) {
+          __syncthreads();                                   // the ring (or the previous round) is free
+          if (RR == 1 || wr == rd) {
+#pragma unroll
+            for (int fm = 0; fm < FM; fm++)
+#pragma unroll
+              for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+                for (int r = 0; r < 16; r++) {
+                  const int rl = wm0 + fm * 32 + 8 * (r / 4) + 4 * q + (r % 4) - rd * ROWS;
+                  img[rl * LINE + wn0 + fn * 32 + l32] = (raw_t)acc[fm][fn][r];
+                }
+          }
+          __syncthreads();
+          for (int i = threadIdx.x; i < ROWS * QPR; i += 64 * NW) {
+            const int rr = i / QPR, qc = i % QPR;
+            const raw4_t w = *(const raw4_t*)(img + rr * LINE + 4 * qc);
+            raw_t a4[4];
+#pragma unroll
+            for (int t = 0; t < 4; t++) a4[t] = w[t];
+            finish4(a4, r0 + rd * ROWS + rr, c0 + 4 * qc, false);
+          }
+        }
+      } else {
+        constexpr int COLS = BN / RC, QPC = BM / 4;
+#pragma unroll 1
+        for (int rd = 0; rd < RC; rd++) {
+          __syncthreads();
+          if (RC == 1 || wc == rd) {
+#pragma unroll
+            for (int fm = 0; fm < FM; fm++)
+#pragma unroll
+              for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+                for (int r4 = 0; r4 < 4; r4++) {
+                  const int cl = wn0 + fn * 32 + l32 - rd * COLS, rl = wm0 + fm * 32 + 8 * r4 + 4 * q;
+                  *(raw4_t*)(img + cl * COLP + rl) = raw4_t{(raw_t)acc[fm][fn][4 * r4], (raw_t)acc[fm][fn][4 * r4 + 1],
+                                                           (raw_t)acc[fm][fn][4 * r4 + 2], (raw_t)acc[fm][fn][4 * r4 + 3]};
+                }
+          }
+          __syncthreads();
+          for (int i = threadIdx.x; i < COLS * QPC; i += 64 * NW) {
+            const int cc = i / QPC, qr = i % QPC;
+            const raw4_t w = *(const raw4_t*)(img + cc * COLP + 4 * qr);
+            raw_t a4[4];
+#pragma unroll
+            for (int t = 0; t < 4; t++) a4[t] = w[t];
+            finish4(a4, r0 + 4 * qr, c0 + rd * COLS + cc, true);
+          }
+        }
+      }
+      return;
+    }
+  }
   if (A.cd_col) {
     // column-major C/D: accumulator elements 4(r/4) .. 4(r/4)+3 of a lane are
     // four consecutive rows of one column, i.e. 8 (16-bit), 16 (int32) or 4
