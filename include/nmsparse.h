@@ -82,7 +82,7 @@ typedef enum {
   NM_ERR_INVALID_ARG = 1, /* null pointer, unknown enum, bad N:M, non-integral alpha/beta on the int path */
   NM_ERR_SHAPE = 2,       /* k % M != 0, tile mode on dims not divisible by 4, ld too small, size overflow */
   NM_ERR_ALIGN = 3,       /* pointer or leading dimension breaks the 16-byte rule */
-  NM_ERR_UNSUPPORTED = 4, /* valid request this build does not implement (e.g. column-major D) */
+  NM_ERR_UNSUPPORTED = 4, /* valid request this build does not implement (reserved: no call returns it today) */
   NM_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
 } nm_status_t;
 
