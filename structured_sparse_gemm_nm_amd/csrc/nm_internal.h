@@ -64,6 +64,10 @@ bool row_path_ok(const nm_plan& pl);
 hipError_t launch_row_prune(const nm_plan& pl, const void* a, void* out, uint32_t* mask, hipStream_t s);
 hipError_t launch_row_compress(const nm_plan& pl, const void* a, void* vals, void* meta, hipStream_t s);
 hipError_t launch_row_decompress(const nm_plan& pl, const void* vals, const void* meta, void* out, hipStream_t s);
+// 2:4 compress / decompress for op_a = T (groups down stored columns), dword-aligned stored rows
+bool colT_path_ok(const nm_plan& pl);
+hipError_t launch_colT_compress(const nm_plan& pl, const void* a, void* vals, void* meta, hipStream_t s);
+hipError_t launch_colT_decompress(const nm_plan& pl, const void* vals, const void* meta, void* out, hipStream_t s);
 // 1-D prune check for op_a = N with 16-byte rows, any N:M (the counter must already be zero)
 bool check_row_ok(const nm_plan& pl);
 hipError_t launch_check_row(const nm_plan& pl, const void* a, int32_t* count, hipStream_t s);

@@ -486,6 +486,7 @@ hipError_t launch_prune_1d(const nm_plan& pl, const void* a, void* out, uint32_t
 
 hipError_t launch_compress(const nm_plan& pl, const void* a, void* vals, void* meta, hipStream_t s) {
   if (row_path_ok(pl) && !pl.tile_elemwise) return launch_row_compress(pl, a, vals, meta, s);
+  if (colT_path_ok(pl) && !pl.tile_elemwise) return launch_colT_compress(pl, a, vals, meta, s);
   TileArgs A = make_args(pl);
   A.a = (const uint8_t*)a; A.vals = (uint8_t*)vals; A.meta = (uint8_t*)meta;
   // k == 0 gives zero-length compressed rows: nothing to write.
@@ -494,6 +495,7 @@ hipError_t launch_compress(const nm_plan& pl, const void* a, void* vals, void* m
 
 hipError_t launch_decompress(const nm_plan& pl, const void* vals, const void* meta, void* out, hipStream_t s) {
   if (row_path_ok(pl) && !pl.tile_elemwise) return launch_row_decompress(pl, vals, meta, out, s);
+  if (colT_path_ok(pl) && !pl.tile_elemwise) return launch_colT_decompress(pl, vals, meta, out, s);
   TileArgs A = make_args(pl);
   A.vals = (uint8_t*)vals; A.meta = (uint8_t*)meta; A.out = (uint8_t*)out;
   return dispatch_tile<T_DECOMPRESS>(pl, A, s);

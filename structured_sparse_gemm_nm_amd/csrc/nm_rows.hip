@@ -663,3 +663,197 @@ hipError_t launch_row_decompress(const nm_plan& pl, const void* vals, const void
 }
 
 }  // namespace nm
+
+namespace nm {
+
+// ---- 2:4 compress / decompress for groups down stored columns (op_a = T)
+//
+// Logical row i of op(A) is stored column i, and a group is 4 consecutive
+// stored rows of it. A lane takes CPL = 4 / esize adjacent stored columns (one
+// dword of every stored row) over 32 consecutive stored rows (8 groups), so
+// each of its 32 loads (stores, for decompress) is one dword and a wave
+// instruction covers 64 * 4 contiguous bytes of a stored row. Per logical row
+// the 8 groups give 16 kept values (32 bytes for 16-bit types, 16 for int8,
+// one or two 16-byte stores) and 32 offset bits (one dword), at offsets that
+// are multiples of their size because the 8 groups start at a multiple of 8.
+constexpr int CT_GROUPS = 8;                                  // groups per lane
+constexpr int CT_ROWS = 4 * CT_GROUPS;                        // stored rows per lane
+
+struct ColTArgs {
+  const uint8_t* a;       // stored k x m (compress input)
+  uint8_t* out;           // stored k x m (decompress output)
+  uint8_t* vals;
+  uint8_t* meta;
+  int64_t m, k, lda, vld, mld;
+  int64_t col_lanes;      // lanes across the stored columns: ceil(m / CPL)
+};
+
+template <int DT, int ESZ, int OP>
+__global__ void __launch_bounds__(256) colT24_kernel(ColTArgs A) {
+  constexpr int CPL = 4 / ESZ;                                // stored columns per lane
+  constexpr int VBYTES = CT_GROUPS * 2 * ESZ;                 // kept-value bytes per logical row and lane
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t cl = t % A.col_lanes, kb = t / A.col_lanes;   // column lane, 32-row block
+  const int64_t c0 = cl * CPL, s0 = kb * CT_ROWS;             // first stored column, first stored row
+  if (s0 >= A.k) return;
+  const int groups_here = (int)min((int64_t)CT_GROUPS, (A.k - s0) / 4);
+  const int cols_here = (int)min((int64_t)CPL, A.m - c0);
+  if (cols_here <= 0) return;
+  const bool full_cols = cols_here == CPL;
+  const bool last_kb = s0 + CT_ROWS >= A.k;
+  auto elem = [&](uint32_t w, int c) -> uint32_t {
+    return ESZ == 2 ? (w >> (16 * c)) & 0xFFFFu : (w >> (8 * c)) & 0xFFu;
+  };
+  if (OP == R_COMPRESS) {
+    uint32_t w[CT_ROWS];
+#pragma unroll
+    for (int r = 0; r < CT_ROWS; r++) {
+      w[r] = 0;
+      if (r < 4 * groups_here) {
+        const uint8_t* p = A.a + ((s0 + r) * A.lda + c0) * ESZ;
+        if (full_cols) {
+          w[r] = *(const uint32_t*)p;
+        } else {
+          for (int c = 0; c < cols_here; c++)
+            w[r] |= (ESZ == 2 ? (uint32_t)((const uint16_t*)p)[c] : (uint32_t)p[c]) << (8 * ESZ * c);
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; c++) {
+      if (c >= cols_here) break;
+      const int64_t i = c0 + c;                               // logical row
+      uint32_t vo[VBYTES / 4];
+#pragma unroll
+      for (int x = 0; x < VBYTES / 4; x++) vo[x] = 0;
+      uint32_t mw = 0;
+#pragma unroll
+      for (int g = 0; g < CT_GROUPS; g++) {
+        if (g >= groups_here) break;
+        uint32_t mag[4], raw[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) { raw[j] = elem(w[4 * g + j], c); mag[j] = magkey<DT>(raw[j]); }
+        const uint32_t keep = select_topn<4>(mag, 2);
+        const int j0 = __builtin_ctz(keep), j1 = 31 - __builtin_clz(keep);
+        const uint32_t v0 = j0 == 0 ? raw[0] : j0 == 1 ? raw[1] : j0 == 2 ? raw[2] : raw[3];
+        const uint32_t v1 = j1 == 0 ? raw[0] : j1 == 1 ? raw[1] : j1 == 2 ? raw[2] : raw[3];
+        const int s = 2 * g;                                  // first slot of the group
+        if (ESZ == 2) { vo[g] = v0 | (v1 << 16); }
+        else { vo[s >> 2] |= (v0 << (8 * (s & 3))) | (v1 << (8 * ((s + 1) & 3))); }
+        mw |= (uint32_t)(j0 | (j1 << 2)) << (4 * g);
+      }
+      uint8_t* vrow = A.vals + i * A.vld * ESZ;
+      const int64_t vb0 = (s0 / 4) * 2 * ESZ;                 // byte offset of this lane's first value
+      if (groups_here == CT_GROUPS) {
+#pragma unroll
+        for (int x = 0; x < VBYTES / 16; x++)
+          *(u32x4*)(vrow + vb0 + 16 * x) = u32x4{vo[4 * x], vo[4 * x + 1], vo[4 * x + 2], vo[4 * x + 3]};
+      } else {
+        const int nb = groups_here * 2 * ESZ;                 // value bytes present (even)
+        for (int x = 0; x < nb / 4; x++) *(uint32_t*)(vrow + vb0 + 4 * x) = vo[x];
+        if (nb & 2) *(uint16_t*)(vrow + vb0 + 4 * (nb / 4)) = (uint16_t)vo[nb / 4];
+      }
+      uint8_t* mrow = A.meta + i * A.mld;
+      const int64_t mb0 = s0 / 8;                             // 4 bits per group
+      if (groups_here == CT_GROUPS) *(uint32_t*)(mrow + mb0) = mw;
+      else for (int x = 0; x < groups_here / 2 + (groups_here & 1); x++) mrow[mb0 + x] = (uint8_t)(mw >> (8 * x));
+      if (last_kb) {                                          // zero padding of both compressed rows
+        const int64_t vend = vb0 + groups_here * 2 * ESZ;
+        for (int64_t b = vend; b < A.vld * ESZ; b++) vrow[b] = 0;
+        const int64_t mend = mb0 + (groups_here + 1) / 2;
+        for (int64_t b = mend; b < A.mld; b++) mrow[b] = 0;
+      }
+    }
+  } else {  // decompress
+    uint32_t w[CT_ROWS];
+#pragma unroll
+    for (int r = 0; r < CT_ROWS; r++) w[r] = 0;
+#pragma unroll
+    for (int c = 0; c < CPL; c++) {
+      if (c >= cols_here) break;
+      const int64_t i = c0 + c;
+      const uint8_t* vrow = A.vals + i * A.vld * ESZ;
+      const int64_t vb0 = (s0 / 4) * 2 * ESZ;
+      uint32_t vo[VBYTES / 4];
+      if (groups_here == CT_GROUPS) {
+#pragma unroll
+        for (int x = 0; x < VBYTES / 16; x++) {
+          const u32x4 v = *(const u32x4*)(vrow + vb0 + 16 * x);
+          vo[4 * x] = v[0]; vo[4 * x + 1] = v[1]; vo[4 * x + 2] = v[2]; vo[4 * x + 3] = v[3];
+        }
+      } else {
+        const int nb = groups_here * 2 * ESZ;                 // value bytes present (even)
+#pragma unroll
+        for (int x = 0; x < VBYTES / 4; x++) vo[x] = x < nb / 4 ? *(const uint32_t*)(vrow + vb0 + 4 * x) : 0u;
+        if (nb & 2) vo[nb / 4] = *(const uint16_t*)(vrow + vb0 + 4 * (nb / 4));
+      }
+      const uint8_t* mrow = A.meta + i * A.mld;
+      const int64_t mb0 = s0 / 8;
+      uint32_t mw = 0;
+      if (groups_here == CT_GROUPS) mw = *(const uint32_t*)(mrow + mb0);
+      else for (int x = 0; x < (groups_here + 1) / 2; x++) mw |= (uint32_t)mrow[mb0 + x] << (8 * x);
+#pragma unroll
+      for (int g = 0; g < CT_GROUPS; g++) {
+        if (g >= groups_here) break;
+#pragma unroll
+        for (int sl = 0; sl < 2; sl++) {                      // later slot wins on a repeated offset
+          const int j = (int)((mw >> (4 * g + 2 * sl)) & 3u);
+          const int s = 2 * g + sl;
+          const uint32_t v = ESZ == 2 ? (vo[s >> 1] >> (16 * (s & 1))) & 0xFFFFu : (vo[s >> 2] >> (8 * (s & 3))) & 0xFFu;
+          const uint32_t sh = 8 * ESZ * c;
+          const uint32_t msk = (ESZ == 2 ? 0xFFFFu : 0xFFu) << sh;
+#pragma unroll
+          for (int jj = 0; jj < 4; jj++)
+            if (j == jj) w[4 * g + jj] = (w[4 * g + jj] & ~msk) | (v << sh);
+        }
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < CT_ROWS; r++) {
+      if (r >= 4 * groups_here) break;
+      uint8_t* p = A.out + ((s0 + r) * A.lda + c0) * ESZ;
+      if (full_cols) {
+        *(uint32_t*)p = w[r];
+      } else {
+        for (int c = 0; c < cols_here; c++) {
+          if (ESZ == 2) ((uint16_t*)p)[c] = (uint16_t)(w[r] >> (16 * c));
+          else p[c] = (uint8_t)(w[r] >> (8 * c));
+        }
+      }
+    }
+  }
+}
+
+bool colT_path_ok(const nm_plan& pl) {
+  return pl.p.op_a == NM_OP_T && pl.p.nm_n == 2 && pl.p.nm_m == 4 && (pl.p.lda * pl.esz_ab) % 4 == 0;
+}
+
+template <int OP>
+static hipError_t launch_colT(const nm_plan& pl, ColTArgs A, hipStream_t s) {
+  const int cpl = 4 / pl.esz_ab;
+  A.m = pl.p.m; A.k = pl.p.k; A.lda = pl.p.lda; A.vld = pl.vld; A.mld = pl.mld;
+  A.col_lanes = (A.m + cpl - 1) / cpl;
+  const int64_t threads = A.col_lanes * ((A.k + CT_ROWS - 1) / CT_ROWS);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  switch (pl.p.type_ab) {
+    case NM_F16: NM_LAUNCH((colT24_kernel<DT_F16, 2, OP>), dim3((unsigned)blocks), dim3(256), 0, s, A); break;
+    case NM_BF16: NM_LAUNCH((colT24_kernel<DT_BF16, 2, OP>), dim3((unsigned)blocks), dim3(256), 0, s, A); break;
+    default: NM_LAUNCH((colT24_kernel<DT_I8, 1, OP>), dim3((unsigned)blocks), dim3(256), 0, s, A); break;
+  }
+  return launch_status();
+}
+
+hipError_t launch_colT_compress(const nm_plan& pl, const void* a, void* vals, void* meta, hipStream_t s) {
+  ColTArgs A{};
+  A.a = (const uint8_t*)a; A.vals = (uint8_t*)vals; A.meta = (uint8_t*)meta;
+  return launch_colT<R_COMPRESS>(pl, A, s);
+}
+
+hipError_t launch_colT_decompress(const nm_plan& pl, const void* vals, const void* meta, void* out, hipStream_t s) {
+  ColTArgs A{};
+  A.vals = (uint8_t*)vals; A.meta = (uint8_t*)meta; A.out = (uint8_t*)out;
+  return launch_colT<R_DECOMPRESS>(pl, A, s);
+}
+
+}  // namespace nm

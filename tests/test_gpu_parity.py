@@ -149,6 +149,56 @@ def test_check_1d_ragged_padded(dtype, N, M, path, monkeypatch):
         assert int(cnt.item()) == 0, (m, k)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+def test_prune_tile_unaligned_short_rows(dtype):
+    """Rows shorter than 16 bytes may use any leading dimension: ld = 5 leaves tile
+    rows unaligned; padding columns untouched."""
+    rows, cols, ld = 8, 4, 5
+    full = rand(dtype, (rows, ld), 78, 0.02)
+    a = np.ascontiguousarray(full[:, :cols])
+    ref, _ = oracle.prune_tile(a, dtype)
+    plan = plan_for(dtype, rows, 16, cols, 2, 4, lda=ld)
+    out = Guarded((rows, ld), TRAW[dtype], fill=dev(full))
+    nm.nm_prune(plan, dev(full), out.t, "tile")
+    sync()
+    out.check()
+    got = host(out.t, RAW[dtype])
+    assert np.array_equal(got[:, :cols], ref)
+    assert np.array_equal(got[:, cols:], full[:, cols:])
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("path", ["colT", "tile"])
+def test_compress_op_t_ragged_padded(dtype, path, monkeypatch):
+    """2:4 compress and decompress with groups down stored columns (op_a = T), on
+    padded stored rows: ragged column counts for the dword-wide lanes, a ragged
+    last block of 32 stored rows (odd group counts), several blocks."""
+    if path == "tile":
+        monkeypatch.setenv("NM_TILE_ELEMWISE", "1")
+    es = 1 if dtype == "i8" else 2
+    for m, k in [(7, 4), (33, 100), (130, 268), (5, 36), (64, 96)]:
+        lda = -(-m // (16 // es)) * (16 // es) + 16 // es
+        full = rand(dtype, (k, lda), 700 + m + k)
+        a = np.ascontiguousarray(full[:, :m])                  # stored k x m
+        plan = plan_for(dtype, m, 8, k, 2, 4, op_a="T", lda=lda)
+        vref, mref = oracle.compress(a, dtype, 2, 4, "T")
+        vals = Guarded((m, plan.values_ld), TRAW[dtype], fill=torch.full((m, plan.values_ld), -1, dtype=TRAW[dtype]))
+        meta = Guarded((m, plan.meta_ld), torch.uint8, fill=torch.full((m, plan.meta_ld), 0xEE, dtype=torch.uint8))
+        nm.nm_compress(plan, dev(full), vals.t, meta.t)
+        sync()
+        vals.check(); meta.check()
+        assert np.array_equal(host(vals.t, RAW[dtype]), vref), (m, k)
+        assert np.array_equal(host(meta.t, np.uint8), mref), (m, k)
+        sentinel = np.full((k, lda), 0x5A if es == 1 else 0x5A5A, dtype=RAW[dtype])
+        out = Guarded((k, lda), TRAW[dtype], fill=dev(sentinel))
+        nm.nm_decompress(plan, dev(vref), dev(mref), out.t)
+        sync()
+        out.check()
+        got = host(out.t, RAW[dtype])
+        assert np.array_equal(got[:, :m], oracle.decompress(vref, mref, dtype, m, k, 2, 4, "T")), (m, k)
+        assert np.array_equal(got[:, m:], sentinel[:, m:]), (m, k)
+
+
 ROW_NM = [(2, 4), (4, 32), (8, 32)]
 
 
