@@ -513,7 +513,8 @@ def summarize_mfma(args):
         per = {}
         for (disp, cname), v in d.items():
             per.setdefault(cname, []).append(v)
-        mops_name = [c for c in per if c.startswith("SQ_INSTS_VALU_MFMA_MOPS_")]
+        mops_name = sorted((c for c in per if c.startswith("SQ_INSTS_VALU_MFMA_MOPS_")),
+                           key=lambda c: -float(np.mean(per[c])))          # the type this kernel runs
         if not mops_name or "GRBM_GUI_ACTIVE" not in per:
             continue
         mops = float(np.mean(per[mops_name[0]]))
@@ -522,18 +523,20 @@ def summarize_mfma(args):
         cyc = float(np.mean(per["GRBM_GUI_ACTIVE"])) / N_XCD          # GRBM counts once per XCD
         busy = float(np.mean(per.get("SQ_VALU_MFMA_BUSY_CYCLES", [0.0])))
         sec = float(np.mean(list(dur[k].values())))
+        scale = 2.0 if mops_name[0].endswith("_I8") else 1.0     # int8 matrix rate per clock is twice fp16's
         rows.append(dict(kernel=k, dispatches=len(per["GRBM_GUI_ACTIVE"]), us=sec * 1e6, mops=mops, cycles=cyc,
-                         ghz=cyc / sec / 1e9, tflops=mops * 512 / sec / 1e12, mops_clk=mops / cyc,
-                         busy=busy / (cyc * N_SIMD), counter=mops_name[0]))
+                         ghz=cyc / sec / 1e9, tflops=mops * 512 / sec / 1e12, mops_clk=mops / cyc / scale,
+                         busy=busy / (cyc * N_SIMD), counter=mops_name[0], scale=scale))
     rows.sort(key=lambda r: -r["us"] * r["dispatches"])
     loops = {("sparse" if "<true" in r["kernel"] else "dense"): r for r in rows if "matrix_loop" in r["kernel"]}
     os.makedirs(PROFILES, exist_ok=True)
     path = os.path.join(PROFILES, "mfma_%s.md" % args.workload)
     with open(path, "w") as fh:
         fh.write("# Matrix-core use: %s\n\nCommand:\n\n    %s\n\n" % (WORKLOAD_DESC[args.workload], args.command))
-        fh.write("Columns: dense-equivalent TFLOP/s = MOPS x 512 / dispatch time; clock = GRBM_GUI_ACTIVE / %d XCDs "
-                 "/ dispatch time; MOPS/clk against the datasheet rate per clock (%d dense, %d sparse for the whole "
-                 "GPU); busy = SQ_VALU_MFMA_BUSY_CYCLES / (%d SIMDs x clocks). The `matrix_loop` rows are the "
+        fh.write("Counters: %s. " % ", ".join(sorted(set(r["counter"] for r in rows))))
+        fh.write("Columns: dense-equivalent TFLOP/s (TOP/s for int8) = MOPS x 512 / dispatch time; clock = GRBM_GUI_ACTIVE / %d XCDs "
+                 "/ dispatch time; MOPS/clk (halved for int8, whose datasheet rate is twice fp16's) against the datasheet "
+                 "rate per clock (%d dense, %d sparse for the whole GPU); busy = SQ_VALU_MFMA_BUSY_CYCLES / (%d SIMDs x clocks). The `matrix_loop` rows are the "
                  "bench's calibration loops (matrix instructions only, no memory traffic): the achievable rate.\n\n"
                  % (N_XCD, NOMINAL_MOPS_PER_CLK["dense"], NOMINAL_MOPS_PER_CLK["sparse"], N_SIMD))
         fh.write("For dispatches of a few tens of microseconds GRBM_GUI_ACTIVE also counts the dispatch's own "
@@ -544,7 +547,7 @@ def summarize_mfma(args):
         for r in rows:
             sl = loops.get("sparse")
             fh.write("| `%s` | %d | %.1f | %.1f | %.3f | %.2f | %.0f | %.3f | %.3f | %s | %.3f |\n" % (
-                r["kernel"][:90], r["dispatches"], r["us"], r["tflops"], r["tflops"] / SPARSE_PEAK_F16, r["ghz"], r["mops_clk"],
+                r["kernel"][:90], r["dispatches"], r["us"], r["tflops"], r["tflops"] / (SPARSE_PEAK_F16 * r["scale"]), r["ghz"], r["mops_clk"],
                 r["mops_clk"] / NOMINAL_MOPS_PER_CLK["dense"], r["mops_clk"] / NOMINAL_MOPS_PER_CLK["sparse"],
                 "%.3f" % (r["mops_clk"] / sl["mops_clk"]) if sl else "n/a", r["busy"]))
     print("wrote", path)
