@@ -137,6 +137,7 @@ nm_status_t nm_plan_init(nm_plan_t* plan, const nm_problem_t* p) {
   pl->no_deep_ring = getenv("NM_NO_DEEP_RING") != nullptr;
   pl->old_skinny = getenv("NM_OLD_SKINNY") != nullptr;
   pl->tile_elemwise = getenv("NM_TILE_ELEMWISE") != nullptr;
+  pl->sp128_w8 = getenv("NM_SP128_W8") != nullptr;
   // kernel choice
   if (p->n <= 16) pl->kernel = K_SKINNY;
   else if (N == 2 && M == 4) pl->kernel = K_SMFMAC_24;

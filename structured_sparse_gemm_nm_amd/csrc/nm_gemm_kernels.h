@@ -914,8 +914,12 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   static_assert(S * STAGE <= 160 * 1024, "LDS ring too large");
   // DMA wave instructions per stage (64 lanes x 16 or 4 bytes), split evenly over the waves
   constexpr int TB = BN / 8, TA = SP ? BM / 16 : BM / 8, TMT = SP ? BM * MDW / 64 : 0;
-  static_assert(TB % NW == 0 && TA % NW == 0 && TMT % NW == 0, "DMA split");
-  constexpr int NB = TB / NW, NA = TA / NW, NMT = TMT / NW;
+  // HALF_META: twice as many waves as metadata instructions; each wave then
+  // copies its share with the lower 32 lanes (one instruction, so every wave
+  // still issues the same number of copies per stage)
+  constexpr bool HALF_META = SP && TMT % NW != 0 && 2 * TMT == NW;
+  static_assert(TB % NW == 0 && TA % NW == 0 && (TMT % NW == 0 || HALF_META), "DMA split");
+  constexpr int NB = TB / NW, NA = TA / NW, NMT = HALF_META ? 1 : TMT / NW;
   constexpr int L = NB + NA + NMT;                       // per wave per stage (same for every wave)
   constexpr int BSLOTS = BN * ESZ / 16;                  // 16-byte slots per stored k-row (op_b = N)
   // op_b = N: LDS slot of 16-byte chunk c of stored k-row r. A 16-lane
@@ -972,7 +976,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   }
 #pragma unroll
   for (int j = 0; j < NMT; j++) {                        // 4-byte pieces, MDW per row
-    const int p = 64 * (wave * NMT + j) + lane;
+    const int p = HALF_META ? 32 * wave + (lane & 31) : 64 * (wave * NMT + j) + lane;
     om[j] = (uint32_t)((p / MDW) * A.mld + (p % MDW) * 4);
   }
   // Copies of stage st: the wave's L instructions in the order B, A values,
@@ -990,8 +994,14 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
     for (int j = 0; j < NA; j++)
       if ((NB + j) % parts == part) dma16(ap + oa[j], base + (wave * NA + j) * 1024);
 #pragma unroll
-    for (int j = 0; j < NMT; j++)
-      if ((NB + NA + j) % parts == part) dma4(mp + om[j], base + A_VAL + (wave * NMT + j) * 256);
+    for (int j = 0; j < NMT; j++) {
+      if ((NB + NA + j) % parts != part) continue;
+      if (HALF_META) {
+        if (lane < 32) dma4(mp + om[j], base + A_VAL + wave * 128);
+      } else {
+        dma4(mp + om[j], base + A_VAL + (wave * NMT + j) * 256);
+      }
+    }
   };
   auto issue = [&](int st) { issue_part(st, 0, 1); };
 
@@ -1491,6 +1501,17 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
       // measured: the deep ring lifts the dense 128 x 128 kernel (BERT FC2: 545 ->
       // 700 TFLOP/s) but not the 2:4 one, which stays on the shallow ring
       const bool deep = AMODE == A_DENSE && TM == 128 && TN == 128 && tiles <= NUM_CU && !pl.no_deep_ring;
+      if constexpr (AMODE == A_SPARSE24 && TM == 128 && TN == 128) {
+        // eight waves (2 x 4 of 64 x 32) instead of four: measured faster for B
+        // stored k x n when every CU has at most one tile (BERT FC2 NN 41.2 ->
+        // 38.4 us, PROJ NN 12.5 -> 11.7 us) and slower for B stored n x k
+        // (FC2 NT 37 -> 39.5 us); NM_SP128_W8 forces it for both
+        if (pl.sp128_w8 || (!bkc && tiles <= NUM_CU)) {
+          if (bkc) NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, S1, 2, 4, 1>), grid, dim3(512), 0, s, A);
+          else NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, S1, 2, 4, 0>), grid, dim3(512), 0, s, A);
+          return launch_status();
+        }
+      }
       if (bkc && deep)
         NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, SD, WGM, WGN, 1>), grid, dim3(64 * WGM * WGN), 0, s, A);
       else if (bkc)
