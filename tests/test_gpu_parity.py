@@ -610,6 +610,29 @@ def test_algorithm_ids_pin_the_tile_and_autotune(dtype):
     assert_close(dtype, host(d.t, raw), ref, tol)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "i8"])
+def test_c_may_alias_d_full_tiles(dtype):
+    """C == D on the copy-ring kernel with beta != 0 (the staged epilogue reads
+    each C quad and writes the same D quad from one thread)."""
+    m, n, k = 256, 256, 128
+    a = rand(dtype, (m, k), 81)
+    v, meta = oracle.compress(a, dtype, 2, 4)
+    ahat, _ = oracle.prune_1d(a, dtype, 2, 4)
+    b = rand(dtype, (n, k), 82)
+    if dtype == "i8":
+        c = inputs.uniform_int((m, n), 83, -2**20, 2**20, np.int32)
+        alpha, beta, raw = 2.0, -1.0, np.int32
+    else:
+        c = rand(dtype, (m, n), 83)
+        alpha, beta, raw = 0.5, 1.5, np.uint16
+    plan = plan_for(dtype, m, n, k, 2, 4, op_b="T")
+    dc = dev(c)
+    nm.nm_spmm(plan, alpha, dev(v), dev(meta), dev(b), beta, dc, dc)
+    sync()
+    ref, tol = ref_product(dtype, ahat, np.ascontiguousarray(b.T), alpha, beta, c)
+    assert_close(dtype, host(dc, raw), ref, tol)
+
+
 def test_col_major_k_zero_and_alias():
     m, n = 40, 24
     c = rand("f16", (m, n), 11)
