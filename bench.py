@@ -71,6 +71,9 @@ def parse():
                     help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) into profiles/traffic_<workload>.md")
     ap.add_argument("--summarize-mfma", metavar="PMC_DIR",
                     help="turn a rocprofv3 --pmc run of the matrix-core counters into profiles/mfma_<workload>.md")
+    ap.add_argument("--summarize-units", nargs="+", metavar="PMC_DIR",
+                    help="turn rocprofv3 --pmc runs of memory-unit counters (with GRBM_GUI_ACTIVE) into "
+                         "profiles/units_<workload>.md: each counter per CU and clock, per kernel")
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR",
                     help="turn a rocprofv3 --kernel-trace --stats run into a profiles/ summary")
     ap.add_argument("--command", default="", help="the command that produced the runs (recorded in summaries)")
@@ -104,6 +107,9 @@ def main():
         return
     if args.summarize_mfma:
         summarize_mfma(args)
+        return
+    if args.summarize_units:
+        summarize_units(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on exactly one GPU: this library's hot path is single-GPU "
@@ -550,6 +556,47 @@ def summarize_mfma(args):
                 r["kernel"][:90], r["dispatches"], r["us"], r["tflops"], r["tflops"] / (SPARSE_PEAK_F16 * r["scale"]), r["ghz"], r["mops_clk"],
                 r["mops_clk"] / NOMINAL_MOPS_PER_CLK["dense"], r["mops_clk"] / NOMINAL_MOPS_PER_CLK["sparse"],
                 "%.3f" % (r["mops_clk"] / sl["mops_clk"]) if sl else "n/a", r["busy"]))
+    print("wrote", path)
+
+
+def summarize_units(args):
+    """Memory-unit counters per kernel as a fraction of CU clocks (counter / (clocks x 256 CUs), clocks =
+    GRBM_GUI_ACTIVE / 8 XCDs of the same pass), one column per counter, from one or more --pmc passes."""
+    import csv
+    import glob
+    cols, table = [], {}
+    for d in args.summarize_units:
+        vals = {}
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            for r in csv.DictReader(open(f)):
+                key = (r["Kernel_Name"], r["Dispatch_Id"])
+                vals.setdefault(key, {}).setdefault(r["Counter_Name"], 0.0)
+                vals[key][r["Counter_Name"]] += float(r["Counter_Value"])
+        per = {}
+        for (k, _), cv in vals.items():
+            if "GRBM_GUI_ACTIVE" not in cv or "nm::" not in k:
+                continue
+            cyc = cv["GRBM_GUI_ACTIVE"] / N_XCD
+            for c, v in cv.items():
+                if c != "GRBM_GUI_ACTIVE" and cyc > 0:
+                    per.setdefault(k, {}).setdefault(c, []).append(v / (cyc * 256))
+        for k, cv in per.items():
+            for c, v in cv.items():
+                if c not in cols:
+                    cols.append(c)
+                table.setdefault(k, {})[c] = float(np.mean(v))
+    os.makedirs(PROFILES, exist_ok=True)
+    path = os.path.join(PROFILES, "units_%s.md" % args.workload)
+    with open(path, "w") as fh:
+        fh.write("# Memory-unit counters: %s\n\nCommands (one rocprofv3 --pmc pass each):\n\n" % WORKLOAD_DESC[args.workload])
+        for line in args.command.split(" ;; "):
+            fh.write("    %s\n" % line)
+        fh.write("\nEach entry: the counter summed over the GPU per dispatch, divided by the dispatch's clocks "
+                 "(GRBM_GUI_ACTIVE / %d XCDs) times 256 CUs, i.e. the fraction of CU clocks the event held "
+                 "(short dispatches also count their dispatch overhead in the clocks, so their fractions read low).\n\n" % N_XCD)
+        fh.write("| kernel | " + " | ".join(cols) + " |\n|---|" + "---|" * len(cols) + "\n")
+        for k in sorted(table):
+            fh.write("| `%s` | " % k[:80] + " | ".join("%.3f" % table[k][c] if c in table[k] else "" for c in cols) + " |\n")
     print("wrote", path)
 
 
