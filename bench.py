@@ -291,6 +291,10 @@ def main():
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
     roofline["kernel"] = dom_key
+    # operands of one launch against the 256 MB Infinity Cache: below it, repeated
+    # steps can find them there (cache-warm); above it, every launch streams from HBM
+    roofline["working_set_mb"] = round(avg_bytes / 1e6, 1)
+    roofline["cache"] = "warm (below the 256 MB Infinity Cache)" if avg_bytes < 256e6 else "cold (beyond the 256 MB Infinity Cache)"
     roofline["launch_ms"] = round(avg_ms, 5)
     roofline["launch_ms_method"] = ("median over the timed steps of the HIP-event interval around each launch of this "
                                     "kernel (the only events in the timed region), less the median interval of an empty "
