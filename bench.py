@@ -36,6 +36,7 @@ WORKLOAD_SETS = {
     "bert": [("fc1", "c2_fc1"), ("fc2", "c2_fc2"), ("proj", "c2_proj")],
     "c1": [("c1", "c1_fp16_256")],
     "c3": [("fwd", "c3_fwd"), ("bwd", "c3_bwd")],
+    "linear": [("fwd", "c3_fwd"), ("dx", "c3_bwd")],
     "c4": [("int8", "c4_int8")],
     "x1": [("fwd", "x1_fwd"), ("bwd", "x1_bwd")],
     "x3": [("qkv", "x3_qkv"), ("proj", "x3_proj"), ("fc1", "x3_fc1"), ("fc2", "x3_fc2")],
@@ -48,6 +49,9 @@ WORKLOAD_DESC = {
     "c1": "fp16 2:4, A 256x256, B 256x64, NN",
     "c3": "bf16 transposable 2:4 training pair, W 11008x4096, X 8192x4096, dY 8192x11008, NT",
     "c4": "int8 2:4, 4096^3, int32 C/D, beta=1, NN+NT",
+    "linear": "training step of the runtime-sparsified linear layer at the bf16 pair's shapes (W 11008x4096, "
+              "8192 tokens): tile prune, check, compress along k and along m, Y = X W^T and dX = dY W on 2:4 "
+              "with column-major D, dense dW = dY^T X",
     "x1": "fp16 transposable 2:4 pair at the training shapes: W 11008x4096, X 8192x4096, dY 8192x11008, NT",
     "x2": "fp16 4:32 GEMV and n = 8 beyond the Infinity Cache: A 32768x32768 (compressed 268 MB + 84 MB metadata), NN",
     "x3": "the cuSPARSELt blog's Table 1 shapes: QKV 3072x1024, PROJ 1024x1024, FC1 4096x1024, FC2 1024x4096 "
@@ -143,7 +147,7 @@ def main():
             bs[ob] = inputs.workload_inputs(wname, ob)[1]
         mode = "tile" if w.get("tile") else "1d"
         g = dict(label=label, name=wname, w=w, dtype=dtype, m=m, n=n, k=k, N=N, M=M, mode=mode, op_a=op_a)
-        order = w.get("order_cd", "row")
+        order = "col" if args.workload == "linear" else w.get("order_cd", "row")
         g["plan"] = nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=layouts[0], dtype=dtype, order_cd=order)
         g["plans"] = {ob: nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=ob, dtype=dtype, order_cd=order)
                       for ob in layouts}
@@ -182,6 +186,31 @@ def main():
                                       P(g["B"][ob]), ctypes.byref(g["_ab"][1]), P(g["C"]), P(g["D"][ob]), None, sp),
                           (g["label"], ob)))
         calls.append((L.nm_decompress, (h, P(g["vals"]), P(g["meta"]), P(g["Ad"]), sp), None))
+
+    if args.workload == "linear":
+        # the layer's step as the C-ABI calls SemiStructuredSparseLinear makes:
+        # one weight, pruned and checked once, compressed along k (forward) and
+        # along m (input gradient); the weight gradient on the dense product
+        gf, gx = gemms
+        gx["Ap"] = gf["Ap"]                                  # the same pruned weight, read as op_a = T
+        tok, out_f, in_f = gf["n"], gf["m"], gf["k"]
+        plan_dw = nm.nm_plan_init(out_f, in_f, tok, 2, 4, op_a="T", op_b="N", dtype=gf["dtype"])
+        gf["dW"] = torch.empty((out_f, in_f), dtype=torch.bfloat16, device=dev)
+        one, zero = ctypes.c_float(1.0), ctypes.c_float(0.0)
+        tile = nm.MODES["tile"]
+        calls = [
+            (L.nm_prune, (gf["plan"].handle, P(gf["A"]), P(gf["Ap"]), tile, None, sp), None),
+            (L.nm_prune_check, (gf["plan"].handle, P(gf["Ap"]), tile, P(gf["cnt"]), sp), None),
+            (L.nm_compress, (gf["plan"].handle, P(gf["Ap"]), P(gf["vals"]), P(gf["meta"]), sp), None),
+            (L.nm_compress, (gx["plan"].handle, P(gf["Ap"]), P(gx["vals"]), P(gx["meta"]), sp), None),
+            (L.nm_spmm, (gf["plans"]["T"].handle, ctypes.byref(one), P(gf["vals"]), P(gf["meta"]), P(gf["B"]["T"]),
+                         ctypes.byref(zero), None, P(gf["D"]["T"]), None, sp), ("fwd", "T")),
+            (L.nm_spmm, (gx["plans"]["T"].handle, ctypes.byref(one), P(gx["vals"]), P(gx["meta"]), P(gx["B"]["T"]),
+                         ctypes.byref(zero), None, P(gx["D"]["T"]), None, sp), ("dx", "T")),
+            (L.nm_dense_gemm, (plan_dw.handle, ctypes.byref(one), P(gx["B"]["T"]), P(gf["B"]["T"]), ctypes.byref(zero),
+                               None, P(gf["dW"]), sp), None),
+        ]
+        args.no_cpu_baseline = True                          # the oracle baseline is quoted on the default workload
 
     n_spmm = sum(1 for c in calls if c[2] is not None)
     spmm_kernel = {(g["label"], ob): g["plans"][ob].spmm_kernel for g in gemms for ob in g["layouts"]}
