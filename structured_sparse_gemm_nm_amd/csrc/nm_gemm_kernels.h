@@ -898,8 +898,13 @@ __device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* lds_wave_base) {
 // k-row base + s / 4 at columns c + 4 (s % 4), lane j receives column c + j at
 // k = base .. base + 3, i.e. four consecutive k of its own column, which is
 // what the matrix instructions' B operand holds. 16-bit types only.
-template <int DT, int AMODE, int BM, int BN, int S, int WGM, int WGN, int BKC>
+// LAYOUT bit 0: B stored n x k (k-contiguous rows); bit 1: dense A stored k x m
+// (op_a = T), staged and read like B stored k x n.
+template <int DT, int AMODE, int BM, int BN, int S, int WGM, int WGN, int LAYOUT>
 __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
+  constexpr int BKC = LAYOUT & 1;
+  constexpr bool AT = (LAYOUT & 2) != 0;
+  static_assert(!AT || AMODE == A_DENSE, "transposed A is dense only");
   constexpr int NW = WGM * WGN;                          // waves per block
   constexpr int ESZ = DT == DT_I8 ? 1 : 2;
   constexpr int KL = KBYTES / ESZ;
@@ -925,10 +930,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   // op_b = N: LDS slot of 16-byte chunk c of stored k-row r. A 16-lane
   // transposing read covers 4 rows x 32 bytes (16-bit) or 8 rows x 16 bytes
   // (8-bit); these XORs keep every 32-lane phase of it on distinct banks.
-  auto nn_slot = [](int r, int c) -> int {
+  auto nn_slot_w = [](int r, int c, int W) -> int {        // W: tile width (columns) of the stored k-rows
     if constexpr (ESZ == 2) return c ^ (4 * (r & 3));
-    else return c ^ (2 * ((r / (256 / BN)) % (BSLOTS / 2)));
+    else return c ^ (2 * ((r / (256 / W)) % (W * ESZ / 16 / 2)));
   };
+  auto nn_slot = [&](int r, int c) -> int { return nn_slot_w(r, c, BN); };
   __shared__ __attribute__((aligned(1024))) uint8_t ring[S * STAGE];
 
   typedef typename Acc<DT>::t acc_t;
@@ -950,7 +956,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   // per-lane byte offsets computed once ----
   const uint8_t* bbase = A.b + (size_t)(BKC ? c0 * A.ldb : c0) * ESZ;
   const size_t bstep = BKC ? (size_t)KBYTES : (size_t)KL * A.ldb * ESZ;
-  const uint8_t* abase = A.a + (size_t)(r0 * A.lda) * ESZ;
+  const uint8_t* abase = A.a + (size_t)(AT ? r0 : r0 * A.lda) * ESZ;
+  const size_t astep = AT ? (size_t)KL * A.lda * ESZ : (size_t)(SP ? 64 : KBYTES);
+  constexpr int ASLOTS = BM * ESZ / 16;                  // 16-byte slots per stored k-row of A (AT)
   const uint8_t* mbase = A.meta + (size_t)(r0 * A.mld);
   uint32_t ob[NB], oa[NA], om[NMT > 0 ? NMT : 1];
 #pragma unroll
@@ -966,7 +974,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   }
 #pragma unroll
   for (int j = 0; j < NA; j++) {
-    if (SP) {
+    if (AT) {
+      const int p = 64 * (wave * NA + j) + lane;         // slot index in the stage
+      const int row = p / ASLOTS, slot = p % ASLOTS;
+      oa[j] = (uint32_t)(row * A.lda * ESZ + (nn_slot_w(row, slot, BM) << 4));
+    } else if (SP) {
       const int row = 16 * (wave * NA + j) + lane / 4, slot = lane % 4;
       oa[j] = (uint32_t)(row * A.lda * ESZ + ((slot ^ swz4(row)) << 4));
     } else {
@@ -985,7 +997,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   auto issue_part = [&](int st, int part, int parts) {
     uint8_t* base = ring + (st % S) * STAGE;
     const uint8_t* bp = bbase + (size_t)st * bstep;
-    const uint8_t* ap = abase + (size_t)st * (SP ? 64 : KBYTES);
+    const uint8_t* ap = abase + (size_t)st * astep;
     const uint8_t* mp = mbase + (size_t)st * MB;
 #pragma unroll
     for (int j = 0; j < NB; j++)
@@ -1019,11 +1031,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   // op_b = N: four consecutive k (kbase .. kbase+3) of column `col0 + (lane & 15)`
   // for each lane of a 16-lane group, from the stored-row B stage.
   typedef short short4_t __attribute__((ext_vector_type(4)));
-  auto btr4 = [&](const uint8_t* lb, int kbase, int col0) -> short4_t {
+  auto btr4 = [&](const uint8_t* lb, int kbase, int col0, int W = BN) -> short4_t {
     const int sidx = lane & 15;
     const int row = kbase + sidx / 4;
     const int cbyte = (col0 + 4 * (sidx % 4)) * 2;
-    const int off = row * (BN * 2) + (nn_slot(row, cbyte >> 4) << 4) + (cbyte & 15);
+    const int off = row * (W * 2) + (nn_slot_w(row, cbyte >> 4, W) << 4) + (cbyte & 15);
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) short4_t*)(lb + off));
   };
   // int8: eight consecutive k (kbase .. kbase+7) of column `col0 + (lane & 15)`;
@@ -1031,11 +1043,11 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   // j of each 16-lane group receives byte j % 8 of the 8 bytes addressed by
   // lane 2t + j / 8 as its element t (ds_read_b64_tr_b8, measured on gfx950)
   typedef int int2_t __attribute__((ext_vector_type(2)));
-  auto btr8 = [&](const uint8_t* lb, int kbase, int col0) -> int2_t {
+  auto btr8 = [&](const uint8_t* lb, int kbase, int col0, int W = BN) -> int2_t {
     const int sidx = lane & 15;
     const int row = kbase + sidx / 2;
     const int cbyte = col0 + 8 * (sidx % 2);
-    const int off = row * BN + (nn_slot(row, cbyte >> 4) << 4) + (cbyte & 15);
+    const int off = row * W + (nn_slot_w(row, cbyte >> 4, W) << 4) + (cbyte & 15);
     return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) int2_t*)(lb + off));
   };
   // column base of this lane's 16-lane group inside a 32-column fragment
@@ -1109,7 +1121,22 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
       const uint8_t* la = st;
       const uint8_t* lb = st + A_VAL;
 #pragma unroll
-      for (int fm = 0; fm < FM; fm++) av[g % 2][fm] = bchunk(la, wm0 + fm * 32 + l32, 2 * g + q);
+      for (int fm = 0; fm < FM; fm++) {
+        if constexpr (!AT) {
+          av[g % 2][fm] = bchunk(la, wm0 + fm * 32 + l32, 2 * g + q);
+        } else if constexpr (ESZ == 2) {
+          // the same k of the lane's row (column of the stored k-rows) as bchunk gives
+          const int ca = wm0 + fm * 32 + nb16;
+          const short4_t r0 = btr4(la, 16 * g + 8 * q, ca, BM), r1 = btr4(la, 16 * g + 8 * q + 4, ca, BM);
+          typedef short short8_t __attribute__((ext_vector_type(8)));
+          const short8_t v = {r0[0], r0[1], r0[2], r0[3], r1[0], r1[1], r1[2], r1[3]};
+          av[g % 2][fm] = __builtin_bit_cast(ab_t, v);
+        } else {
+          const int ca = wm0 + fm * 32 + nb16;
+          const int2_t r0 = btr8(la, 32 * g + 16 * q, ca, BM), r1 = btr8(la, 32 * g + 16 * q + 8, ca, BM);
+          av[g % 2][fm] = ab_t{r0[0], r0[1], r1[0], r1[1]};
+        }
+      }
 #pragma unroll
       for (int fn = 0; fn < FN; fn++) {
         if constexpr (BKC) {
@@ -1491,7 +1518,7 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
   const bool akc = pl.p.op_a == NM_OP_N || AMODE != A_DENSE;
   if constexpr (AMODE != A_GATHER) {
     const bool dma_nn = !bkc && !pl.no_dma_nn;
-    if (full_tiles(pl, A, TM, TN, AMODE) && (bkc || dma_nn) && akc && !pl.no_dma) {
+    if (full_tiles(pl, A, TM, TN, AMODE) && (bkc || dma_nn) && (akc || AMODE == A_DENSE) && !pl.no_dma) {
       // 256-row tiles run eight waves (two per SIMD, 128 x 64 or 64 x 64 each);
       // 128 x 128 tiles run four waves with two blocks per CU.
       constexpr int WGM = TM == 256 ? (TN == 256 ? 2 : 4) : 2;
@@ -1501,6 +1528,21 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
       // measured: the deep ring lifts the dense 128 x 128 kernel (BERT FC2: 545 ->
       // 700 TFLOP/s) but not the 2:4 one, which stays on the shallow ring
       const bool deep = AMODE == A_DENSE && TM == 128 && TN == 128 && tiles <= NUM_CU && !pl.no_deep_ring;
+      if constexpr (AMODE == A_DENSE) {
+        // dense A stored k x m (op_a = T): its stored k-rows are staged like
+        // those of B stored k x n and read with the transposing LDS reads
+        if (!akc) {
+          if (bkc && deep)
+            NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, SD, WGM, WGN, 3>), grid, dim3(64 * WGM * WGN), 0, s, A);
+          else if (bkc)
+            NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, S1, WGM, WGN, 3>), grid, dim3(64 * WGM * WGN), 0, s, A);
+          else if (deep)
+            NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, SD, WGM, WGN, 2>), grid, dim3(64 * WGM * WGN), 0, s, A);
+          else
+            NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, S1, WGM, WGN, 2>), grid, dim3(64 * WGM * WGN), 0, s, A);
+          return launch_status();
+        }
+      }
       if constexpr (AMODE == A_SPARSE24 && TM == 128 && TN == 128) {
         // eight waves (2 x 4 of 64 x 32) instead of four: measured faster for B
         // stored k x n when every CU has at most one tile (BERT FC2 NN 41.2 ->

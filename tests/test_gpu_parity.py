@@ -445,6 +445,34 @@ def test_dense_gemm(dtype, op_a, op_b, m, n, k, tile, monkeypatch):
     assert_close(dtype, host(d.t, np.int32 if dtype == "i8" else np.uint16), ref, tol)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("op_b", ["N", "T"])
+@pytest.mark.parametrize("m,n,k,pad,tile", [(256, 256, 256, 64, "256"), (384, 256, 512, 32, "128"),
+                                            (2304, 2048, 256, 0, "128"), (2304, 256, 256, 16, "256")])
+def test_dense_op_a_t_full_tiles(dtype, op_b, m, n, k, pad, tile, monkeypatch):
+    """A stored k x m (op_a = T) with a padded leading dimension and beta != 0 on
+    whole tiles: the copy-ring kernel's transposed-A staging, on both tile shapes
+    and both ring depths (more 128 x 128 tiles than compute units takes the
+    shallow ring)."""
+    monkeypatch.setenv("NM_FORCE_TILE", tile)
+    a_log = rand(dtype, (m, k), 51)
+    lda = m + pad
+    a_st = np.zeros((k, lda), dtype=a_log.dtype)
+    a_st[:, :m] = a_log.T
+    b_log = rand(dtype, (k, n), 52)
+    b_st = b_log if op_b == "N" else np.ascontiguousarray(b_log.T)
+    c = (inputs.uniform_int((m, n), 53, -2**20, 2**20, np.int32) if dtype == "i8" else rand(dtype, (m, n), 53))
+    alpha, beta = (2.0, -1.0) if dtype == "i8" else (0.75, 0.5)
+    plan = plan_for(dtype, m, n, k, 2, 4, op_a="T", op_b=op_b, lda=lda)
+    odt = torch.int32 if dtype == "i8" else torch.int16
+    d = Guarded((m, n), odt)
+    nm.nm_dense_gemm(plan, alpha, dev(a_st), dev(b_st), beta, dev(c), d.t)
+    sync()
+    d.check()
+    ref, tol = ref_product(dtype, a_log, b_log, alpha, beta, c)
+    assert_close(dtype, host(d.t, np.int32 if dtype == "i8" else np.uint16), ref, tol)
+
+
 @pytest.mark.parametrize("dtype", ["f16", "i8"])
 @pytest.mark.parametrize("n", [4, 48])
 def test_k_zero_gives_beta_c(dtype, n):
