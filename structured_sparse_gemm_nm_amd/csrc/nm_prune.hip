@@ -312,9 +312,13 @@ __global__ void __launch_bounds__(TPB) tile4_prune_kernel(const uint8_t* a, uint
   for (int r = 0; r < 4; r++)
 #pragma unroll
     for (int p = 0; p < 6; p++) s[r][p] = w[r][PA[p]] + w[r][PB[p]];
-  // scan candidates in order (p0 outermost); replace only on a strictly larger score
+  // scan candidates in order (p0 outermost); replace only on a strictly larger
+  // score. The winner is kept as its four row masks packed in one constant (one
+  // select per candidate), and the best score as a running maximum (the same
+  // value the strict replacement keeps; a NaN score changes neither).
   double best = -1.0;
-  int bp0 = 0, bp1 = 0, bp2 = 0, bp3 = 0;
+  uint32_t bmask = (1u << PA[0]) | (1u << PB[0]);
+  bmask |= bmask << 4 | bmask << 8 | bmask << 12;
 #pragma unroll
   for (int p0 = 0; p0 < 6; p0++)
 #pragma unroll
@@ -334,13 +338,15 @@ __global__ void __launch_bounds__(TPB) tile4_prune_kernel(const uint8_t* a, uint
 #pragma unroll
         for (int p = 0; p < 6; p++) if (PA[p] == lo && PB[p] == hi) p3 = p;
         const double score = ((s[0][p0] + s[1][p1]) + s[2][p2]) + s[3][p3];
-        if (score > best) { best = score; bp0 = p0; bp1 = p1; bp2 = p2; bp3 = p3; }
+        constexpr auto bits = [](int p) { return (1u << PA[p]) | (1u << PB[p]); };
+        const uint32_t cand = bits(p0) | bits(p1) << 4 | bits(p2) << 8 | bits(p3) << 12;
+        bmask = score > best ? cand : bmask;
+        best = fmax(best, score);
       }
-  const int bp[4] = {bp0, bp1, bp2, bp3};
   uint32_t rowbits[4];
 #pragma unroll
   for (int r = 0; r < 4; r++) {
-    rowbits[r] = (1u << PA[bp[r]]) | (1u << PB[bp[r]]);
+    rowbits[r] = (bmask >> (4 * r)) & 15u;
     if (active) {
 #pragma unroll
       for (int c = 0; c < 4; c++) {
