@@ -680,39 +680,51 @@ def spmm_bytes(g):
 CPU_SAMPLE_FLOPS = 2.0e11   # bound on the oracle's product work (about 10-20 s on 8-16 cores)
 
 
+CPU_MIN_SECONDS = 10.0                              # whole steps are repeated until at least this much CPU work
+
+
 def cpu_baseline(gemms):
-    """The oracle (test infrastructure, untuned) doing one step of the same work on the host cores."""
+    """The oracle (test infrastructure, untuned) doing whole steps of the same work on the host cores,
+    repeated until at least CPU_MIN_SECONDS have passed."""
     import oracle
-    flops = 0.0
     total = sum(2.0 * g["m"] * g["n"] * g["k"] * len(g["layouts"]) for g in gemms)
     frac = min(1.0, CPU_SAMPLE_FLOPS / total)
-    t0 = time.perf_counter()
-    for g in gemms:
-        dtype, N, M = g["dtype"], g["N"], g["M"]
-        a = g["host"]["a"]
-        if g["mode"] == "tile":
-            p, _ = oracle.prune_tile(a, dtype)
-        else:
-            p, _ = oracle.prune_1d(a, dtype, N, M, g["op_a"])
-        oracle.check_1d(p, dtype, N, M, g["op_a"])
-        v, meta = oracle.compress(p, dtype, N, M, g["op_a"])
-        ahat = oracle.decompress(v, meta, dtype, g["m"], g["k"], N, M, g["op_a"])
-        ahat_log = ahat if g["op_a"] == "N" else np.ascontiguousarray(ahat.T)
-        rows = max(1, int(round(g["m"] * frac)))          # the product on the first rows only
-        for ob in g["layouts"]:
-            b = g["host"]["b"][ob]
-            b_log = b if ob == "N" else np.ascontiguousarray(b.T)
-            if dtype == "i8":
-                c = g["host"]["c"][:rows] if g["host"]["c"] is not None else None
-                oracle.gemm_i64(ahat_log[:rows], b_log, int(g["w"]["alpha"]), int(g["w"]["beta"]), c)
+
+    def one_step():
+        flops = 0.0
+        for g in gemms:
+            dtype, N, M = g["dtype"], g["N"], g["M"]
+            a = g["host"]["a"]
+            if g["mode"] == "tile":
+                p, _ = oracle.prune_tile(a, dtype)
             else:
-                oracle.gemm_f64(oracle.decode(ahat_log[:rows], dtype), oracle.decode(b_log, dtype), g["w"]["alpha"], 0.0)
-            flops += 2.0 * rows * g["n"] * g["k"]
+                p, _ = oracle.prune_1d(a, dtype, N, M, g["op_a"])
+            oracle.check_1d(p, dtype, N, M, g["op_a"])
+            v, meta = oracle.compress(p, dtype, N, M, g["op_a"])
+            ahat = oracle.decompress(v, meta, dtype, g["m"], g["k"], N, M, g["op_a"])
+            ahat_log = ahat if g["op_a"] == "N" else np.ascontiguousarray(ahat.T)
+            rows = max(1, int(round(g["m"] * frac)))      # the product on the first rows only
+            for ob in g["layouts"]:
+                b = g["host"]["b"][ob]
+                b_log = b if ob == "N" else np.ascontiguousarray(b.T)
+                if dtype == "i8":
+                    c = g["host"]["c"][:rows] if g["host"]["c"] is not None else None
+                    oracle.gemm_i64(ahat_log[:rows], b_log, int(g["w"]["alpha"]), int(g["w"]["beta"]), c)
+                else:
+                    oracle.gemm_f64(oracle.decode(ahat_log[:rows], dtype), oracle.decode(b_log, dtype), g["w"]["alpha"], 0.0)
+                flops += 2.0 * rows * g["n"] * g["k"]
+        return flops
+
+    flops, steps = 0.0, 0
+    t0 = time.perf_counter()
+    while steps == 0 or time.perf_counter() - t0 < CPU_MIN_SECONDS:
+        flops += one_step()
+        steps += 1
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": "one step of the workload: prune, check, compress, decompress of every weight in full, and "
+            "sample": "%d step(s) of the workload, each: prune, check, compress, decompress of every weight in full, and "
                       "the fp64 dense-loop product for every GEMM and layout on the first %.1f%% of the rows "
-                      "(value = product flops done / total time), %.1f s" % (100 * frac, dt)}
+                      "(value = product flops done / total time), %.1f s" % (steps, 100 * frac, dt)}
 
 
 if __name__ == "__main__":
