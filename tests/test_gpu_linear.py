@@ -53,6 +53,49 @@ def test_sparse_linear_forward_backward(dtype, shape):
     assert np.array_equal(host(layer.weight.detach().view(torch.int16), np.uint16), w)
 
 
+def check_sampled(dtype, got, a_rows, bt_rows, seed, count=2000):
+    """Sampled outputs of got = A op(B), each computed by the oracle from row i of
+    A (a_rows(i)) and column j of op(B) (bt_rows(j)), within the same bound."""
+    m, n = got.shape
+    rng = np.random.default_rng(seed)
+    pi = np.concatenate([rng.integers(0, m, count), [0, 0, m - 1, m - 1, m // 2]])
+    pj = np.concatenate([rng.integers(0, n, count), [0, n - 1, 0, n - 1, n // 2]])
+    ui, inv_i = np.unique(pi, return_inverse=True)
+    uj, inv_j = np.unique(pj, return_inverse=True)
+    A = oracle.decode(a_rows(ui), dtype)
+    Bt = oracle.decode(bt_rows(uj), dtype)
+    ref = oracle.gemm_f64_points(A, Bt, inv_i, inv_j)
+    tol = 1e-2 * oracle.gemm_f64_points(np.abs(A), np.abs(Bt), inv_i, inv_j) + 1e-3
+    g = oracle.decode(host(got.contiguous().view(torch.int16), np.uint16)[pi, pj], dtype)
+    assert np.isfinite(g).all()
+    err = np.abs(g - ref)
+    assert (err <= tol).all(), (err.max(), np.argmax(err - tol))
+
+
+def test_sparse_linear_full_size_sampled():
+    """The layer at the bf16 training shapes (W 11008 x 4096, 8192 tokens in two
+    batch halves), the launch configuration the linear-layer benchmark times:
+    Y, dX and dW on sampled outputs that the oracle computes one by one from its
+    own tile prune of W."""
+    dtype = "bf16"
+    w, x, _ = inputs.workload_inputs("c3_fwd", "T")        # W (out, in), X stored (tokens, in)
+    _, dy, _ = inputs.workload_inputs("c3_bwd", "T")       # dY stored (tokens, out)
+    out_f, in_f = w.shape
+    tokens = x.shape[0]
+    print("linear full size", tokens, in_f, out_f, flush=True)
+    layer = SemiStructuredSparseLinear(in_f, out_f, dtype=torch.bfloat16, weight=to_torch(w, dtype))
+    xt = to_torch(x, dtype).view(2, tokens // 2, in_f).requires_grad_(True)
+    y = layer(xt)
+    y.backward(to_torch(dy, dtype).view(2, tokens // 2, out_f))
+    sync()
+    w_hat, _ = oracle.prune_tile(w, dtype)
+    check_sampled(dtype, y.reshape(tokens, out_f), lambda i: x[i], lambda j: w_hat[j], 11)
+    check_sampled(dtype, xt.grad.reshape(tokens, in_f), lambda i: dy[i],
+                  lambda j: np.ascontiguousarray(w_hat[:, j].T), 12)
+    check_sampled(dtype, layer.weight.grad, lambda i: np.ascontiguousarray(dy[:, i].T),
+                  lambda j: np.ascontiguousarray(x[:, j].T), 13)
+
+
 def test_sparse_linear_rejects_bad_shapes():
     with pytest.raises(ValueError):
         SemiStructuredSparseLinear(100, 64)
