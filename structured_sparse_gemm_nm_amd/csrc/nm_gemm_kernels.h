@@ -1028,8 +1028,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   auto bchunk = [&](const uint8_t* lb, int row, int c) -> ab_t {
     return *(const ab_t*)(lb + row * 128 + ((c ^ swz8(row)) << 4));
   };
-  // op_b = N: four consecutive k (kbase .. kbase+3) of column `col0 + (lane & 15)`
-  // for each lane of a 16-lane group, from the stored-row B stage.
+  // Four consecutive k (kbase .. kbase+3) of column `col0 + (lane & 15)` for
+  // each lane of a 16-lane group, from a stage of stored k-rows W columns wide:
+  // B stored k x n (W = BN) or dense A stored k x m (W = BM).
   typedef short short4_t __attribute__((ext_vector_type(4)));
   auto btr4 = [&](const uint8_t* lb, int kbase, int col0, int W = BN) -> short4_t {
     const int sidx = lane & 15;
