@@ -692,9 +692,19 @@ template <int DT, int ESZ, int OP>
 __global__ void __launch_bounds__(256) colT24_kernel(ColTArgs A) {
   constexpr int CPL = 4 / ESZ;                                // stored columns per lane
   constexpr int VBYTES = CT_GROUPS * 2 * ESZ;                 // kept-value bytes per logical row and lane
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t cl = t % A.col_lanes, kb = t / A.col_lanes;   // column lane, 32-row block
+  // a block's four waves take four consecutive 32-row blocks of the same 64
+  // column lanes (64 CPL logical rows, 128 stored rows)
+  const int64_t ncg = (A.col_lanes + 63) / 64;
+  const int64_t cg = blockIdx.x % ncg, kg = blockIdx.x / ncg;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t cl = cg * 64 + lane, kb = kg * 4 + wv;        // column lane, 32-row block
   const int64_t c0 = cl * CPL, s0 = kb * CT_ROWS;             // first stored column, first stored row
+  // compress, 16-bit types, every lane of the block with whole columns and 8
+  // whole groups: the kept values and offsets go through LDS so that each
+  // store instruction writes whole 128-byte pieces of 8 compressed rows
+  // (a lane owns logical rows, so its own stores would touch 64 rows each)
+  constexpr int LR = 64 * CPL;                                // logical rows per block
+  const bool staged = OP == R_COMPRESS && ESZ == 2 && (kg * 4 + 4) * CT_ROWS <= A.k && (cg + 1) * LR <= A.m;
   if (s0 >= A.k) return;
   const int groups_here = (int)min((int64_t)CT_GROUPS, (A.k - s0) / 4);
   const int cols_here = (int)min((int64_t)CPL, A.m - c0);
@@ -704,7 +714,10 @@ __global__ void __launch_bounds__(256) colT24_kernel(ColTArgs A) {
   auto elem = [&](uint32_t w, int c) -> uint32_t {
     return ESZ == 2 ? (w >> (16 * c)) & 0xFFFFu : (w >> (8 * c)) & 0xFFu;
   };
-  if (OP == R_COMPRESS) {
+  if constexpr (OP == R_COMPRESS) {
+    constexpr int VP = 4 * VBYTES + 16;                       // LDS pitch of a logical row's values (padded)
+    __shared__ __attribute__((aligned(16))) uint8_t s_vals[ESZ == 2 ? LR * VP : 16];
+    __shared__ __attribute__((aligned(16))) uint32_t s_meta[ESZ == 2 ? LR * 4 : 4];
     uint32_t w[CT_ROWS];
 #pragma unroll
     for (int r = 0; r < CT_ROWS; r++) {
@@ -744,7 +757,15 @@ __global__ void __launch_bounds__(256) colT24_kernel(ColTArgs A) {
       }
       uint8_t* vrow = A.vals + i * A.vld * ESZ;
       const int64_t vb0 = (s0 / 4) * 2 * ESZ;                 // byte offset of this lane's first value
-      if (groups_here == CT_GROUPS) {
+      uint8_t* mrow = A.meta + i * A.mld;
+      const int64_t mb0 = s0 / 8;                             // 4 bits per group
+      if (staged) {
+        const int lr = lane * CPL + c;                        // logical row in the block
+#pragma unroll
+        for (int x = 0; x < VBYTES / 16; x++)
+          *(u32x4*)(s_vals + lr * VP + wv * VBYTES + 16 * x) = u32x4{vo[4 * x], vo[4 * x + 1], vo[4 * x + 2], vo[4 * x + 3]};
+        s_meta[lr * 4 + wv] = mw;
+      } else if (groups_here == CT_GROUPS) {
 #pragma unroll
         for (int x = 0; x < VBYTES / 16; x++)
           *(u32x4*)(vrow + vb0 + 16 * x) = u32x4{vo[4 * x], vo[4 * x + 1], vo[4 * x + 2], vo[4 * x + 3]};
@@ -753,15 +774,33 @@ __global__ void __launch_bounds__(256) colT24_kernel(ColTArgs A) {
         for (int x = 0; x < nb / 4; x++) *(uint32_t*)(vrow + vb0 + 4 * x) = vo[x];
         if (nb & 2) *(uint16_t*)(vrow + vb0 + 4 * (nb / 4)) = (uint16_t)vo[nb / 4];
       }
-      uint8_t* mrow = A.meta + i * A.mld;
-      const int64_t mb0 = s0 / 8;                             // 4 bits per group
-      if (groups_here == CT_GROUPS) *(uint32_t*)(mrow + mb0) = mw;
-      else for (int x = 0; x < groups_here / 2 + (groups_here & 1); x++) mrow[mb0 + x] = (uint8_t)(mw >> (8 * x));
+      if (!staged) {
+        if (groups_here == CT_GROUPS) *(uint32_t*)(mrow + mb0) = mw;
+        else for (int x = 0; x < groups_here / 2 + (groups_here & 1); x++) mrow[mb0 + x] = (uint8_t)(mw >> (8 * x));
+      }
       if (last_kb) {                                          // zero padding of both compressed rows
         const int64_t vend = vb0 + groups_here * 2 * ESZ;
         for (int64_t b = vend; b < A.vld * ESZ; b++) vrow[b] = 0;
         const int64_t mend = mb0 + (groups_here + 1) / 2;
         for (int64_t b = mend; b < A.mld; b++) mrow[b] = 0;
+      }
+    }
+    if (staged) {                                             // uniform over the block (depends on its index only)
+      __syncthreads();
+      const int64_t i0 = cg * LR;                             // the block's first logical row
+      const int64_t vbb = (kg * 4 * CT_ROWS / 4) * 2 * ESZ;  // its first value byte in a row (2 kept per group)
+      const int64_t mbb = kg * 4 * CT_ROWS / 8;               // its first offset byte in a row
+      constexpr int CH = 4 * VBYTES / 16;                     // 16-byte chunks of a logical row in the block
+#pragma unroll
+      for (int j = 0; j < LR * CH / 256; j++) {
+        const int q = threadIdx.x + 256 * j;
+        const int row = q / CH, ch = q % CH;
+        *(u32x4*)(A.vals + (i0 + row) * A.vld * ESZ + vbb + 16 * ch) = *(const u32x4*)(s_vals + row * VP + 16 * ch);
+      }
+#pragma unroll
+      for (int j = 0; j < LR * 4 / 256; j++) {
+        const int q = threadIdx.x + 256 * j;
+        *(uint32_t*)(A.meta + (i0 + q / 4) * A.mld + mbb + 4 * (q % 4)) = s_meta[q];
       }
     }
   } else {  // decompress
@@ -833,8 +872,8 @@ static hipError_t launch_colT(const nm_plan& pl, ColTArgs A, hipStream_t s) {
   const int cpl = 4 / pl.esz_ab;
   A.m = pl.p.m; A.k = pl.p.k; A.lda = pl.p.lda; A.vld = pl.vld; A.mld = pl.mld;
   A.col_lanes = (A.m + cpl - 1) / cpl;
-  const int64_t threads = A.col_lanes * ((A.k + CT_ROWS - 1) / CT_ROWS);
-  const int64_t blocks = (threads + 255) / 256;
+  const int64_t row_blocks = (A.k + CT_ROWS - 1) / CT_ROWS;
+  const int64_t blocks = ((A.col_lanes + 63) / 64) * ((row_blocks + 3) / 4);
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
   switch (pl.p.type_ab) {
     case NM_F16: NM_LAUNCH((colT24_kernel<DT_F16, 2, OP>), dim3((unsigned)blocks), dim3(256), 0, s, A); break;
