@@ -699,12 +699,18 @@ __global__ void __launch_bounds__(256) colT24_kernel(ColTArgs A) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t cl = cg * 64 + lane, kb = kg * 4 + wv;        // column lane, 32-row block
   const int64_t c0 = cl * CPL, s0 = kb * CT_ROWS;             // first stored column, first stored row
-  // compress, 16-bit types, every lane of the block with whole columns and 8
-  // whole groups: the kept values and offsets go through LDS so that each
-  // store instruction writes whole 128-byte pieces of 8 compressed rows
-  // (a lane owns logical rows, so its own stores would touch 64 rows each)
+  // 16-bit types, every lane of the block with whole columns and 8 whole
+  // groups: the kept values and offsets go through LDS so that each global
+  // store (compress) or load (decompress) instruction covers whole 128-byte
+  // pieces of 8 compressed rows (a lane owns logical rows, so its own
+  // accesses would touch 64 rows each)
   constexpr int LR = 64 * CPL;                                // logical rows per block
-  const bool staged = OP == R_COMPRESS && ESZ == 2 && (kg * 4 + 4) * CT_ROWS <= A.k && (cg + 1) * LR <= A.m;
+  constexpr int VP = 4 * VBYTES + 16;                         // LDS pitch of a logical row's values (padded)
+  constexpr int CH = 4 * VBYTES / 16;                         // 16-byte chunks of a logical row in the block
+  const bool staged = ESZ == 2 && (kg * 4 + 4) * CT_ROWS <= A.k && (cg + 1) * LR <= A.m;
+  const int64_t i0 = cg * LR;                                 // the block's first logical row
+  const int64_t vbb = (kg * 4 * CT_ROWS / 4) * 2 * ESZ;      // its first value byte in a row (2 kept per group)
+  const int64_t mbb = kg * 4 * CT_ROWS / 8;                   // its first offset byte in a row
   if (s0 >= A.k) return;
   const int groups_here = (int)min((int64_t)CT_GROUPS, (A.k - s0) / 4);
   const int cols_here = (int)min((int64_t)CPL, A.m - c0);
@@ -715,7 +721,6 @@ __global__ void __launch_bounds__(256) colT24_kernel(ColTArgs A) {
     return ESZ == 2 ? (w >> (16 * c)) & 0xFFFFu : (w >> (8 * c)) & 0xFFu;
   };
   if constexpr (OP == R_COMPRESS) {
-    constexpr int VP = 4 * VBYTES + 16;                       // LDS pitch of a logical row's values (padded)
     __shared__ __attribute__((aligned(16))) uint8_t s_vals[ESZ == 2 ? LR * VP : 16];
     __shared__ __attribute__((aligned(16))) uint32_t s_meta[ESZ == 2 ? LR * 4 : 4];
     uint32_t w[CT_ROWS];
@@ -787,10 +792,6 @@ __global__ void __launch_bounds__(256) colT24_kernel(ColTArgs A) {
     }
     if (staged) {                                             // uniform over the block (depends on its index only)
       __syncthreads();
-      const int64_t i0 = cg * LR;                             // the block's first logical row
-      const int64_t vbb = (kg * 4 * CT_ROWS / 4) * 2 * ESZ;  // its first value byte in a row (2 kept per group)
-      const int64_t mbb = kg * 4 * CT_ROWS / 8;               // its first offset byte in a row
-      constexpr int CH = 4 * VBYTES / 16;                     // 16-byte chunks of a logical row in the block
 #pragma unroll
       for (int j = 0; j < LR * CH / 256; j++) {
         const int q = threadIdx.x + 256 * j;
@@ -804,6 +805,22 @@ __global__ void __launch_bounds__(256) colT24_kernel(ColTArgs A) {
       }
     }
   } else {  // decompress
+    __shared__ __attribute__((aligned(16))) uint8_t s_vals[ESZ == 2 ? LR * VP : 16];
+    __shared__ __attribute__((aligned(16))) uint32_t s_meta[ESZ == 2 ? LR * 4 : 4];
+    if (staged) {                                             // uniform over the block (depends on its index only)
+#pragma unroll
+      for (int j = 0; j < LR * CH / 256; j++) {
+        const int q = threadIdx.x + 256 * j;
+        const int row = q / CH, ch = q % CH;
+        *(u32x4*)(s_vals + row * VP + 16 * ch) = *(const u32x4*)(A.vals + (i0 + row) * A.vld * ESZ + vbb + 16 * ch);
+      }
+#pragma unroll
+      for (int j = 0; j < LR * 4 / 256; j++) {
+        const int q = threadIdx.x + 256 * j;
+        s_meta[q] = *(const uint32_t*)(A.meta + (i0 + q / 4) * A.mld + mbb + 4 * (q % 4));
+      }
+      __syncthreads();
+    }
     uint32_t w[CT_ROWS];
 #pragma unroll
     for (int r = 0; r < CT_ROWS; r++) w[r] = 0;
@@ -814,23 +831,33 @@ __global__ void __launch_bounds__(256) colT24_kernel(ColTArgs A) {
       const uint8_t* vrow = A.vals + i * A.vld * ESZ;
       const int64_t vb0 = (s0 / 4) * 2 * ESZ;
       uint32_t vo[VBYTES / 4];
-      if (groups_here == CT_GROUPS) {
+      uint32_t mw = 0;
+      if (staged) {
+        const int lr = lane * CPL + c;                        // logical row in the block
 #pragma unroll
         for (int x = 0; x < VBYTES / 16; x++) {
-          const u32x4 v = *(const u32x4*)(vrow + vb0 + 16 * x);
+          const u32x4 v = *(const u32x4*)(s_vals + lr * VP + wv * VBYTES + 16 * x);
           vo[4 * x] = v[0]; vo[4 * x + 1] = v[1]; vo[4 * x + 2] = v[2]; vo[4 * x + 3] = v[3];
         }
+        mw = s_meta[lr * 4 + wv];
       } else {
-        const int nb = groups_here * 2 * ESZ;                 // value bytes present (even)
+        if (groups_here == CT_GROUPS) {
 #pragma unroll
-        for (int x = 0; x < VBYTES / 4; x++) vo[x] = x < nb / 4 ? *(const uint32_t*)(vrow + vb0 + 4 * x) : 0u;
-        if (nb & 2) vo[nb / 4] = *(const uint16_t*)(vrow + vb0 + 4 * (nb / 4));
+          for (int x = 0; x < VBYTES / 16; x++) {
+            const u32x4 v = *(const u32x4*)(vrow + vb0 + 16 * x);
+            vo[4 * x] = v[0]; vo[4 * x + 1] = v[1]; vo[4 * x + 2] = v[2]; vo[4 * x + 3] = v[3];
+          }
+        } else {
+          const int nb = groups_here * 2 * ESZ;               // value bytes present (even)
+#pragma unroll
+          for (int x = 0; x < VBYTES / 4; x++) vo[x] = x < nb / 4 ? *(const uint32_t*)(vrow + vb0 + 4 * x) : 0u;
+          if (nb & 2) vo[nb / 4] = *(const uint16_t*)(vrow + vb0 + 4 * (nb / 4));
+        }
+        const uint8_t* mrow = A.meta + i * A.mld;
+        const int64_t mb0 = s0 / 8;
+        if (groups_here == CT_GROUPS) mw = *(const uint32_t*)(mrow + mb0);
+        else for (int x = 0; x < (groups_here + 1) / 2; x++) mw |= (uint32_t)mrow[mb0 + x] << (8 * x);
       }
-      const uint8_t* mrow = A.meta + i * A.mld;
-      const int64_t mb0 = s0 / 8;
-      uint32_t mw = 0;
-      if (groups_here == CT_GROUPS) mw = *(const uint32_t*)(mrow + mb0);
-      else for (int x = 0; x < (groups_here + 1) / 2; x++) mw |= (uint32_t)mrow[mb0 + x] << (8 * x);
 #pragma unroll
       for (int g = 0; g < CT_GROUPS; g++) {
         if (g >= groups_here) break;
