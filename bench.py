@@ -1,19 +1,24 @@
 """Benchmark: N:M structured-sparse GEMM hot path on one MI355X.
 
-A step is one pass of the whole hot path over the BERT-Large GEMM shapes of
-the cuSPARSELt blog's Table 1 (FC1 4096x1024, FC2 1024x4096, PROJ 1024x1024
-weights; 4096 tokens = batch 32 x seq 128): for each weight, 2:4 prune,
-conformance check, compress, the SpMM against the activations in both
-layouts (NT: tokens x features as stored; NN: its transpose), and decompress.
-Weights are re-sparsified every step, as in runtime-sparsified training where
-the weights change between steps (the blog: compress again when A changes).
+A step is one pass of the whole hot path over one workload's weights and
+activations: for each weight, prune (1-D top-N, or the transposable 4x4-tile
+2:4 mask), conformance check, compress, the SpMM (in every B layout the
+workload names) and decompress. Weights are re-sparsified every step, as in
+runtime-sparsified training where the weights change between steps (the
+cuSPARSELt blog: compress again whenever A changes).
+
+Default workload (x1): the training pair at its largest shapes in fp16, W
+11008 x 4096 pruned to transposable 2:4, X 8192 x 4096 and dY 8192 x 11008:
+the forward Y^T = W X^T (11008 x 8192 x 4096) and the input gradient
+dX^T = W^T dY^T (4096 x 8192 x 11008). Other workloads: --workload NAME.
 
 value  = dense-equivalent TFLOP/s of the step's SpMMs (2*m*n*k each) over the
          whole step time (prune/check/compress/decompress included).
 Also reported: the SpMM kernels alone, the same-shape dense MFMA GEMM written
-in this library, the speed-up, the roofline of the dominant kernel (measured
-with HIP events on the launch stream over the timed region), and the CPU
-oracle timed on one step of the same workload.
+in this library (with its fraction of the dense peak), the speed-up, the
+roofline of the dominant kernel (measured with HIP events on the launch
+stream over the timed region), and the CPU oracle timed on a bounded sample
+of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -66,7 +71,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="bert", choices=sorted(WORKLOAD_SETS))
+    ap.add_argument("--workload", default="x1", choices=sorted(WORKLOAD_SETS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -292,43 +297,71 @@ def main():
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     spmm_total_ms = sum(spmm_ms[(g["label"], ob)] for g in gemms for ob in g["layouts"])
     spmm_only_tflops = step_flops / (spmm_total_ms * 1e-3) / 1e12
-    dom_launch_ms = max(float(np.median([e0.elapsed_time(e1) for _, e0, e1 in events])) - event_ms, 1e-6)
 
-    # dominant kernel: the device kernel (as the profiler names it) with the most SpMM time
-    kern = {}
-    for g in gemms:
-        for ob in g["layouts"]:
-            kk = g["plans"][ob].spmm_kernel
-            d = kern.setdefault(kk, dict(flops=0.0, bytes=0.0, launches=0, dtype=g["dtype"]))
-            d["launches"] += 1
-            keep = g["N"] / g["M"]
-            d["flops"] += 2.0 * g["m"] * g["n"] * g["k"] * keep            # multiply-adds actually required
-            d["bytes"] += spmm_bytes(g)
-    dom = kern[dom_key]
-    avg_ms = dom_launch_ms
-    avg_flops = dom["flops"] / dom["launches"]
-    avg_bytes = dom["bytes"] / dom["launches"]
-    ai = avg_flops / avg_bytes
-    peak_f = PEAK_TFLOPS[dom["dtype"]]
+    # Roofline of the dominant kernel (the device kernel, as the profiler names
+    # it, with the most SpMM time). Its launches in the timed region may cover
+    # several GEMM shapes (the same kernel serves several weights): each launch
+    # is priced with the work of its own shape, and the kernel's figure is the
+    # sum of that work over the sum of the launch times (a mean, so that it
+    # compares with the profiler's average duration over the same launches).
+    gemm_of = {g["label"]: g for g in gemms}
+    by_label = {}
+    for key, e0, e1 in events:
+        by_label.setdefault(key, []).append(max(e0.elapsed_time(e1) - event_ms, 1e-6))
+    dtype_dom = gemm_of[next(iter(by_label))[0]]["dtype"]
+    kname = gemm_of[next(iter(by_label))[0]]["plans"][next(iter(by_label))[1]].kernel_name
+    peak_f = PEAK_TFLOPS[dtype_dom]
     ridge = peak_f * 1e12 / (HBM_PEAK_GBS * 1e9)
-    if ai >= ridge:
-        achieved = avg_flops / (avg_ms * 1e-3) / 1e12
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_f, "unit": "TFLOP/s",
-                    "frac": round(achieved / peak_f, 4), "traffic": None}
-    else:
-        achieved = avg_bytes / (avg_ms * 1e-3) / 1e9
+
+    def kernel_work(g):
+        """(flops per launch as this kernel executes them, algorithmic bytes per launch)."""
+        keep = g["N"] / g["M"]
+        if kname == "spmm_gather_mfma":
+            # element-wise N:M: each k-step's kept values are expanded into a dense
+            # tile and run on the dense matrix instructions, so the executed
+            # matrix work is the dense product's
+            return 2.0 * g["m"] * g["n"] * g["k"], spmm_bytes(g)
+        return 2.0 * g["m"] * g["n"] * g["k"] * keep, spmm_bytes(g)    # multiply-adds of the kept values
+
+    tot_ms = tot_flops = tot_bytes = 0.0
+    n_launch = 0
+    per_shape = []
+    for key, ts in sorted(by_label.items()):
+        g = gemm_of[key[0]]
+        f, by = kernel_work(g)
+        tot_ms += sum(ts); tot_flops += f * len(ts); tot_bytes += by * len(ts); n_launch += len(ts)
+        mean = float(np.mean(ts))
+        per_shape.append({"gemm": key[0], "layout": "N" + key[1], "m": g["m"], "n": g["n"], "k": g["k"],
+                          "launches": len(ts), "mean_ms": round(mean, 5),
+                          "tflops": round(f / (mean * 1e-3) / 1e12, 2), "gbs": round(by / (mean * 1e-3) / 1e9, 1)})
+    avg_ms = tot_ms / n_launch
+    avg_bytes = tot_bytes / n_launch
+    ai = tot_flops / tot_bytes
+    if kname == "spmm_skinny" or (kname == "spmm_smfmac_2of4" and ai < ridge):
+        achieved = tot_bytes / (tot_ms * 1e-3) / 1e9
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None}
+    else:
+        achieved = tot_flops / (tot_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak_f, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak_f, 4), "traffic": None}
     roofline["kernel"] = dom_key
+    roofline["work_counted"] = ("dense multiply-adds of the expanded tile (2 m n k), executed on the dense matrix "
+                                "instructions" if kname == "spmm_gather_mfma" else
+                                "multiply-adds of the kept values (2 m n k N/M) against the dense matrix peak, the same "
+                                "ratio as dense-equivalent flops against the 2:4 peak" if roofline["bound"] == "mfma"
+                                else "compressed A + metadata + B + D (+ C) bytes per launch")
+    roofline["per_shape"] = per_shape
     # operands of one launch against the 256 MB Infinity Cache: below it, repeated
     # steps can find them there (cache-warm); above it, every launch streams from HBM
     roofline["working_set_mb"] = round(avg_bytes / 1e6, 1)
     roofline["cache"] = "warm (below the 256 MB Infinity Cache)" if avg_bytes < 256e6 else "cold (beyond the 256 MB Infinity Cache)"
     roofline["launch_ms"] = round(avg_ms, 5)
-    roofline["launch_ms_method"] = ("median over the timed steps of the HIP-event interval around each launch of this "
+    roofline["launch_ms_method"] = ("mean over the timed steps of the HIP-event interval around each launch of this "
                                     "kernel (the only events in the timed region), less the median interval of an empty "
-                                    "event pair (%.5f ms)" % event_ms)
-    roofline["launches_per_step"] = dom["launches"]
+                                    "event pair (%.5f ms); achieved = the launches' summed work / their summed time"
+                                    % event_ms)
+    roofline["launches_per_step"] = n_launch // args.steps
     traffic = load_traffic(args.workload, dom_key)
     if traffic is not None:
         roofline["traffic"] = traffic["bytes_per_launch"]
@@ -370,9 +403,11 @@ def main():
             row = {"gemm": g["label"], "layout": "N" + ob, "m": g["m"], "n": g["n"], "k": g["k"],
                    "kernel": g["plans"][ob].kernel_name, "spmm_ms": round(t_s, 5),
                    "spmm_tflops": round(flops_dense_eq(g) / (t_s * 1e-3) / 1e12, 2)}
+            row["spmm_frac_of_sparse_peak"] = round(row["spmm_tflops"] / (2 * PEAK_TFLOPS[g["dtype"]]), 4)
             if key in dense:
                 row["dense_ms"] = round(dense[key], 5)
                 row["dense_tflops"] = round(flops_dense_eq(g) / (dense[key] * 1e-3) / 1e12, 2)
+                row["dense_frac_of_dense_peak"] = round(row["dense_tflops"] / PEAK_TFLOPS[g["dtype"]], 4)
                 row["speedup"] = round(dense[key] / t_s, 3)
             per_gemm.append(row)
     speedup = None
@@ -380,7 +415,7 @@ def main():
         speedup = round(sum(dense.values()) / spmm_total_ms, 3)
 
     # measured achievable peaks (calibration loops, outside the timed region)
-    cal = calibrate(torch, stream, dom["dtype"])
+    cal = calibrate(torch, stream, dtype_dom)
     if cal is not None:
         roofline["achievable"] = cal
         if roofline["bound"] == "mfma" and cal["sparse_matrix"] > 0:

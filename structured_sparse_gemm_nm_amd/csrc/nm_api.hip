@@ -124,20 +124,12 @@ nm_status_t nm_plan_init(nm_plan_t* plan, const nm_problem_t* p) {
   pl->vld = (nvals + per16 - 1) / per16 * per16;
   const int64_t mbytes = (p->k / M * N * b + 7) / 8;
   pl->mld = (mbytes + 15) / 16 * 16;
-  // benchmark-sweep overrides (read once here, not per launch)
   pl->force_tile = -1;
   pl->algorithm = NM_ALG_AUTO;
-  if (const char* f = getenv("NM_FORCE_TILE")) {
-    if (!strcmp(f, "128")) pl->force_tile = nm::T128;
-    else if (!strcmp(f, "256x128")) pl->force_tile = nm::T256x128;
-    else if (!strcmp(f, "256")) pl->force_tile = nm::T256;
-  }
-  pl->no_dma = getenv("NM_NO_DMA") != nullptr;
-  pl->no_dma_nn = getenv("NM_NO_DMA_NN") != nullptr;
-  pl->no_deep_ring = getenv("NM_NO_DEEP_RING") != nullptr;
-  pl->old_skinny = getenv("NM_OLD_SKINNY") != nullptr;
+  // the one environment switch: the LDS tile kernels for prune / check /
+  // compress / decompress even where the register path applies (read once
+  // here; the parity tests use it to run both paths on the same inputs)
   pl->tile_elemwise = getenv("NM_TILE_ELEMWISE") != nullptr;
-  pl->sp128_w8 = getenv("NM_SP128_W8") != nullptr;
   // kernel choice
   if (p->n <= 16) pl->kernel = K_SKINNY;
   else if (N == 2 && M == 4) pl->kernel = K_SMFMAC_24;

@@ -142,7 +142,7 @@ static bool skinny2_ok(const nm_plan& pl, bool dense_a) {
 
 template <bool DENSE_A>
 static hipError_t launch_skinny_dt(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
-  if (skinny2_ok(pl, DENSE_A) && !pl.old_skinny) {
+  if (skinny2_ok(pl, DENSE_A)) {
     switch (pl.p.type_ab) {
       case NM_F16: return launch_skinny2_f16(pl, A, s, DENSE_A);
       case NM_BF16: return launch_skinny2_bf16(pl, A, s, DENSE_A);

@@ -615,226 +615,6 @@ __global__ void __launch_bounds__(NTH) gemm_kernel(GemmArgs A) {
     }
 }
 
-// ---------------------------------------------------------------- full-tile kernel
-
-// The same product for problems made of whole tiles (m % BM == 0, n % BN == 0,
-// k a multiple of the k-step, 16-byte rows, every operand below 2 GiB): no
-// bounds checks; each thread keeps 32-bit byte offsets of its chunks from
-// block-uniform bases, advanced by a uniform step offset. Fragments for the
-// next instruction group are read from LDS while the current group's matrix
-// instructions run.
-template <int DT, int AMODE, int BKC, int AKC, int BM, int BN>
-__global__ void __launch_bounds__(NTH) gemm_fast_kernel(GemmArgs A) {
-  constexpr int ESZ = DT == DT_I8 ? 1 : 2;
-  constexpr int EPC = 16 / ESZ;
-  constexpr int KL = KBYTES / ESZ;
-  constexpr int WM = BM / 2, WN = BN / 2, FM = WM / 32, FN = WN / 32;
-  constexpr int LDS_A = AMODE == A_SPARSE24 ? BM * ASTRIDE_SP : BM * BSTRIDE;
-  constexpr int LDS_B = BN * BSTRIDE;
-  constexpr int MB = ESZ == 2 ? 8 : 16;           // metadata bytes per row per step
-  __shared__ __attribute__((aligned(16))) uint8_t s_a[2][LDS_A];
-  __shared__ __attribute__((aligned(16))) uint8_t s_b[2][LDS_B];
-
-  typedef typename Acc<DT>::t acc_t;
-  typedef typename Frag<DT>::ab ab_t;
-  typedef typename Frag<DT>::b2 b2_t;
-
-  const int64_t tiles_m = A.m / BM, tiles_n = A.n / BN;
-  int64_t tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
-  const int64_t r0 = tm * BM, c0 = tn * BN;
-  const int t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
-  const int wm0 = (wave >> 1) * WM, wn0 = (wave & 1) * WN;
-  const int l32 = lane & 31, q = lane >> 5;
-  const int ksteps = (int)(A.k / KL);
-
-  // ---- per-thread chunk offsets (bytes) ----
-  const uint8_t* bbase = A.b + (size_t)(BKC ? c0 * A.ldb : c0) * ESZ;
-  const uint32_t bstep = BKC ? (uint32_t)KBYTES : (uint32_t)(KL * A.ldb * ESZ);
-  uint32_t boff[BN / 32];
-  if (BKC) {
-#pragma unroll
-    for (int i = 0; i < BN / 32; i++) {
-      const int id = t + NTH * i, r = id / 8, part = id % 8;
-      boff[i] = (uint32_t)((r * A.ldb + part * EPC) * ESZ);
-    }
-  } else {
-    constexpr int CPR = BN / EPC;
-#pragma unroll
-    for (int j = 0; j < BN / 128; j++) {
-      const int pid = t + NTH * j, cc = pid % CPR, kq = pid / CPR;
-#pragma unroll
-      for (int i = 0; i < 4; i++) boff[j * 4 + i] = (uint32_t)(((kq * 4 + i) * A.ldb + cc * EPC) * ESZ);
-    }
-  }
-  const uint8_t* abase;
-  uint32_t astep;
-  uint32_t aoff[AMODE == A_DENSE ? BM / 32 : BM / 64];
-  uint32_t moff = 0;
-  if constexpr (AMODE == A_DENSE) {
-    abase = A.a + (size_t)(AKC ? r0 * A.lda : r0) * ESZ;
-    astep = AKC ? (uint32_t)KBYTES : (uint32_t)(KL * A.lda * ESZ);
-    if (AKC) {
-#pragma unroll
-      for (int i = 0; i < BM / 32; i++) {
-        const int id = t + NTH * i, r = id / 8, part = id % 8;
-        aoff[i] = (uint32_t)((r * A.lda + part * EPC) * ESZ);
-      }
-    } else {
-      constexpr int CPR = BM / EPC;
-#pragma unroll
-      for (int j = 0; j < BM / 128; j++) {
-        const int pid = t + NTH * j, cc = pid % CPR, kq = pid / CPR;
-#pragma unroll
-        for (int i = 0; i < 4; i++) aoff[j * 4 + i] = (uint32_t)(((kq * 4 + i) * A.lda + cc * EPC) * ESZ);
-      }
-    }
-  } else {
-    abase = A.a + (size_t)(r0 * A.lda) * ESZ;
-    astep = 64;
-#pragma unroll
-    for (int i = 0; i < BM / 64; i++) {
-      const int id = t + NTH * i, r = id / 4, part = id % 4;
-      aoff[i] = (uint32_t)((r * A.lda + part * EPC) * ESZ);
-    }
-    moff = (uint32_t)(t * A.mld);
-  }
-  const uint8_t* mbase = A.meta + (size_t)(r0 * A.mld);
-
-  KChunks<BN> rb;
-  KChunks<BM> ra;
-  SpChunks<BM> rs;
-  auto load_step = [&](int ks) {
-    const uint8_t* bp = bbase + (size_t)ks * bstep;
-#pragma unroll
-    for (int i = 0; i < BN / 32; i++) rb.v[i] = *(const u32x4*)(bp + boff[i]);
-    const uint8_t* ap = abase + (size_t)ks * astep;
-    if constexpr (AMODE == A_DENSE) {
-#pragma unroll
-      for (int i = 0; i < BM / 32; i++) ra.v[i] = *(const u32x4*)(ap + aoff[i]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < BM / 64; i++) rs.v[i] = *(const u32x4*)(ap + aoff[i]);
-      if (t < BM) {
-        const uint8_t* mp = mbase + (size_t)ks * MB + moff;
-        if (MB == 8) {
-          const u32x2 w = *(const u32x2*)mp;
-          rs.meta = u32x4{w[0], w[1], 0, 0};
-        } else {
-          rs.meta = *(const u32x4*)mp;
-        }
-      }
-    }
-  };
-  auto store_step = [&](int buf) {
-    if (BKC) store_kcontig<BN>(s_b[buf], rb);
-    else store_mncontig<ESZ, BN>(s_b[buf], rb);
-    if constexpr (AMODE == A_DENSE) {
-      if (AKC) store_kcontig<BM>(s_a[buf], ra);
-      else store_mncontig<ESZ, BM>(s_a[buf], ra);
-    } else {
-      store_sp24<ESZ, BM>(s_a[buf], rs);
-    }
-  };
-
-  acc_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; i++)
-#pragma unroll
-    for (int j = 0; j < FN; j++)
-#pragma unroll
-      for (int r = 0; r < 16; r++) acc[i][j][r] = 0;
-
-  // ---- fragments ----
-  struct SpFrag { ab_t a[FM]; int idx[FM]; b2_t b[FN]; };
-  struct DnFrag { ab_t a[FM]; ab_t b[FN]; };
-  auto load_sp = [&](SpFrag& F, const uint8_t* la, const uint8_t* lb, int h) {
-#pragma unroll
-    for (int fm = 0; fm < FM; fm++) {
-      const uint8_t* p = la + (wm0 + fm * 32 + l32) * ASTRIDE_SP;
-      F.a[fm] = *(const ab_t*)(p + 32 * h + 16 * q);
-      F.idx[fm] = ESZ == 2 ? (int)*(const uint16_t*)(p + 64 + h * (MB / 2) + 2 * q)
-                           : (int)*(const uint32_t*)(p + 64 + h * (MB / 2) + 4 * q);
-    }
-#pragma unroll
-    for (int fn = 0; fn < FN; fn++) {
-      const uint8_t* p = lb + (wn0 + fn * 32 + l32) * BSTRIDE + 64 * h;
-      F.b[fn] = concat<DT>(*(const ab_t*)(p + 16 * q), *(const ab_t*)(p + 32 + 16 * q));
-    }
-  };
-  auto mma_sp = [&](const SpFrag& F) {
-#pragma unroll
-    for (int fn = 0; fn < FN; fn++)
-#pragma unroll
-      for (int fm = 0; fm < FM; fm++) acc[fm][fn] = smfmac32<DT>(F.a[fm], F.b[fn], acc[fm][fn], F.idx[fm]);
-  };
-  auto load_dn = [&](DnFrag& F, const uint8_t* la, const uint8_t* lb, int i) {
-#pragma unroll
-    for (int fm = 0; fm < FM; fm++) F.a[fm] = *(const ab_t*)(la + (wm0 + fm * 32 + l32) * BSTRIDE + 32 * i + 16 * q);
-#pragma unroll
-    for (int fn = 0; fn < FN; fn++) F.b[fn] = *(const ab_t*)(lb + (wn0 + fn * 32 + l32) * BSTRIDE + 32 * i + 16 * q);
-  };
-  auto mma_dn = [&](const DnFrag& F) {
-#pragma unroll
-    for (int fn = 0; fn < FN; fn++)
-#pragma unroll
-      for (int fm = 0; fm < FM; fm++) acc[fm][fn] = mfma32<DT>(F.a[fm], F.b[fn], acc[fm][fn]);
-  };
-  auto compute = [&](int buf) {
-    const uint8_t* la = s_a[buf];
-    const uint8_t* lb = s_b[buf];
-    if constexpr (AMODE == A_SPARSE24) {
-      SpFrag F0, F1;
-      load_sp(F0, la, lb, 0);
-      load_sp(F1, la, lb, 1);
-      mma_sp(F0);
-      mma_sp(F1);
-    } else {
-      DnFrag F0, F1;
-      load_dn(F0, la, lb, 0);
-      load_dn(F1, la, lb, 1);
-      mma_dn(F0);
-      load_dn(F0, la, lb, 2);
-      mma_dn(F1);
-      load_dn(F1, la, lb, 3);
-      mma_dn(F0);
-      mma_dn(F1);
-    }
-  };
-
-  load_step(0);
-  store_step(0);
-  if (ksteps > 1) load_step(1);
-  __syncthreads();
-  for (int ks = 0; ks < ksteps; ks++) {
-    const int buf = ks & 1;
-    compute(buf);
-    if (ks + 1 < ksteps) store_step(buf ^ 1);
-    if (ks + 2 < ksteps) load_step(ks + 2);
-    __syncthreads();
-  }
-
-  // ---- epilogue: D = alpha * acc + beta * C ----
-#pragma unroll
-  for (int fm = 0; fm < FM; fm++)
-#pragma unroll
-    for (int fn = 0; fn < FN; fn++) {
-      const int64_t col = c0 + wn0 + fn * 32 + l32;
-#pragma unroll
-      for (int r = 0; r < 16; r++) {
-        const int64_t row = r0 + wm0 + fm * 32 + 8 * (r / 4) + 4 * q + (r % 4);
-        if constexpr (DT == DT_I8) {
-          int_store(A, row * A.d_rs + col * A.d_cs, int_epilogue(A, acc[fm][fn][r], row * A.c_rs + col * A.c_cs));
-        } else {
-          float v = A.alpha * acc[fm][fn][r];
-          if (A.beta != 0.0f) v += A.beta * from_bits16<DT>(((const uint16_t*)A.c)[row * A.c_rs + col * A.c_cs]);
-          ((uint16_t*)A.d)[row * A.d_rs + col * A.d_cs] = to_bits16<DT>(v);
-        }
-      }
-    }
-}
-
 // ---------------------------------------------------------------- LDS-DMA ring kernel (NT)
 
 // For op_b = T (B stored n x k, k contiguous) and operands made of whole tiles:
@@ -1471,8 +1251,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
 // Block tile: 256 x 256 when that still gives most CUs a tile, 256 x 128 or
 // 128 x 128 otherwise (the dense comparator stops at 256 x 128, whose ring of
 // three stages fits LDS). The general N:M gather path always uses 128 x 128 (its
-// staging needs LDS). NM_FORCE_TILE=128|256x128|256 pins the choice and
-// NM_NO_DMA=1 disables the LDS-DMA kernel (benchmark sweeps only).
+// staging needs LDS). An algorithm id on the plan pins the choice.
 inline int pick_tile(const nm_plan& pl, int amode) {
   if (amode == A_GATHER) return T128;
   if (pl.force_tile == T128 || pl.force_tile == T256x128) return pl.force_tile;   // -1: automatic
@@ -1518,8 +1297,7 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
   const bool bkc = pl.p.op_b == NM_OP_T;
   const bool akc = pl.p.op_a == NM_OP_N || AMODE != A_DENSE;
   if constexpr (AMODE != A_GATHER) {
-    const bool dma_nn = !bkc && !pl.no_dma_nn;
-    if (full_tiles(pl, A, TM, TN, AMODE) && (bkc || dma_nn) && (akc || AMODE == A_DENSE) && !pl.no_dma) {
+    if (full_tiles(pl, A, TM, TN, AMODE)) {
       // 256-row tiles run eight waves (two per SIMD, 128 x 64 or 64 x 64 each);
       // 128 x 128 tiles run four waves with two blocks per CU.
       constexpr int WGM = TM == 256 ? (TN == 256 ? 2 : 4) : 2;
@@ -1528,7 +1306,7 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
       constexpr int SD = dma_stages<DT, AMODE, TM, TN, true>();
       // measured: the deep ring lifts the dense 128 x 128 kernel (BERT FC2: 545 ->
       // 700 TFLOP/s) but not the 2:4 one, which stays on the shallow ring
-      const bool deep = AMODE == A_DENSE && TM == 128 && TN == 128 && tiles <= NUM_CU && !pl.no_deep_ring;
+      const bool deep = AMODE == A_DENSE && TM == 128 && TN == 128 && tiles <= NUM_CU;
       if constexpr (AMODE == A_DENSE) {
         // dense A stored k x m (op_a = T): its stored k-rows are staged like
         // those of B stored k x n and read with the transposing LDS reads
@@ -1548,8 +1326,8 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
         // eight waves (2 x 4 of 64 x 32) instead of four: measured faster for B
         // stored k x n when every CU has at most one tile (BERT FC2 NN 41.2 ->
         // 38.4 us, PROJ NN 12.5 -> 11.7 us) and slower for B stored n x k
-        // (FC2 NT 37 -> 39.5 us); NM_SP128_W8 forces it for both
-        if (pl.sp128_w8 || (!bkc && tiles <= NUM_CU)) {
+        // (FC2 NT 37 -> 39.5 us)
+        if (!bkc && tiles <= NUM_CU) {
           if (bkc) NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, S1, 2, 4, 1>), grid, dim3(512), 0, s, A);
           else NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, S1, 2, 4, 0>), grid, dim3(512), 0, s, A);
           return launch_status();
@@ -1565,18 +1343,11 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
         NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, S1, WGM, WGN, 0>), grid, dim3(64 * WGM * WGN), 0, s, A);
       return launch_status();
     }
-    if (full_tiles(pl, A, TM, TN, AMODE)) {
-      if (bkc && akc) NM_LAUNCH((gemm_fast_kernel<DT, AMODE, 1, 1, TM, TN>), grid, dim3(NTH), 0, s, A);
-      else if (!bkc && akc) NM_LAUNCH((gemm_fast_kernel<DT, AMODE, 0, 1, TM, TN>), grid, dim3(NTH), 0, s, A);
-      else if (AMODE == A_DENSE && bkc) NM_LAUNCH((gemm_fast_kernel<DT, A_DENSE, 1, 0, TM, TN>), grid, dim3(NTH), 0, s, A);
-      else if (AMODE == A_DENSE) NM_LAUNCH((gemm_fast_kernel<DT, A_DENSE, 0, 0, TM, TN>), grid, dim3(NTH), 0, s, A);
-      return launch_status();
-    }
   }
   if constexpr (AMODE == A_GATHER) {
     // M = 32 with 4-, 8- or 16-byte groups: expanded from registers, pipelined
     const int gv = (int)(A.N * pl.esz_ab);
-    if (A.M == 32 && !pl.old_skinny && (gv == 4 || gv == 8 || gv == 16)) {
+    if (A.M == 32 && (gv == 4 || gv == 8 || gv == 16)) {
       if (gv == 4 && bkc) NM_LAUNCH((gemm_kernel<DT, AMODE, 1, 1, TM, TN, 4>), grid, dim3(NTH), 0, s, A);
       else if (gv == 4) NM_LAUNCH((gemm_kernel<DT, AMODE, 0, 1, TM, TN, 4>), grid, dim3(NTH), 0, s, A);
       else if (gv == 8 && bkc) NM_LAUNCH((gemm_kernel<DT, AMODE, 1, 1, TM, TN, 8>), grid, dim3(NTH), 0, s, A);

@@ -18,15 +18,10 @@ struct nm_plan {
   int64_t mld;          // metadata row stride (bytes)
   int kernel;           // SpMM kernel id (nm::KernelId)
   std::string spmm_symbol;  // device kernel nm_spmm launches (filled on first query)
-  // kernel-selection overrides for benchmark sweeps, read from the environment
-  // once at plan creation (NM_FORCE_TILE = 128 | 256x128 | 256, NM_NO_DMA,
-  // NM_NO_DMA_NN, NM_NO_DEEP_RING, NM_OLD_SKINNY, NM_TILE_ELEMWISE, NM_SP128_W8), so
-  // launches do not scan the environment
-  int force_tile;           // -1 = automatic, else nm::TileCfg
+  int force_tile;           // -1 = automatic, else nm::TileCfg (set through the algorithm id)
   int algorithm;            // nm_plan_set_algorithm id (NM_ALG_AUTO unless set)
-  bool no_dma, no_dma_nn, no_deep_ring, old_skinny;
-  bool tile_elemwise;       // prune/check/compress/decompress on the older kernels even where the row path applies
-  bool sp128_w8;            // NM_SP128_W8: 2:4 128 x 128 tiles with eight waves for every B layout (sweep)
+  bool tile_elemwise;       // NM_TILE_ELEMWISE (read once at plan creation): prune/check/compress/decompress
+                            // on the LDS tile kernels even where the register path applies
 };
 
 namespace nm {

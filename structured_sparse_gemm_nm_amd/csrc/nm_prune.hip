@@ -284,6 +284,28 @@ constexpr int count_tile_patterns() {
 }
 static_assert(count_tile_patterns() == 90, "4x4 tiles with two per row and column: 90 patterns");
 
+// Row masks (4 bits per tile row, row 0 lowest) of the first pattern in the
+// scan order: the winner when no candidate's score compares greater than the
+// start value, which happens only when every candidate keeps a NaN.
+constexpr uint32_t first_tile_pattern() {
+  constexpr int pa[6] = {0, 0, 0, 1, 1, 2}, pb[6] = {1, 2, 3, 2, 3, 3};
+  for (int p0 = 0; p0 < 6; p0++)
+    for (int p1 = 0; p1 < 6; p1++)
+      for (int p2 = 0; p2 < 6; p2++)
+        for (int p3 = 0; p3 < 6; p3++) {
+          const int p[4] = {p0, p1, p2, p3};
+          int c[4] = {0, 0, 0, 0};
+          uint32_t bits = 0;
+          for (int r = 0; r < 4; r++) {
+            c[pa[p[r]]]++; c[pb[p[r]]]++;
+            bits |= ((1u << pa[p[r]]) | (1u << pb[p[r]])) << (4 * r);
+          }
+          if (c[0] == 2 && c[1] == 2 && c[2] == 2 && c[3] == 2) return bits;
+        }
+  return 0;
+}
+static_assert(first_tile_pattern() == 0xCC33u, "first pattern keeps (0,1), (0,1), (2,3), (2,3)");
+
 template <int DT, int ESZ>
 __device__ __forceinline__ uint32_t load_raw(const uint8_t* p, int64_t idx) {
   return ESZ == 2 ? (uint32_t)((const uint16_t*)p)[idx] : (uint32_t)p[idx];
@@ -315,10 +337,10 @@ __global__ void __launch_bounds__(TPB) tile4_prune_kernel(const uint8_t* a, uint
   // scan candidates in order (p0 outermost); replace only on a strictly larger
   // score. The winner is kept as its four row masks packed in one constant (one
   // select per candidate), and the best score as a running maximum (the same
-  // value the strict replacement keeps; a NaN score changes neither).
+  // value the strict replacement keeps; a NaN score changes neither). It starts
+  // at the first pattern, which stays when every candidate keeps a NaN.
   double best = -1.0;
-  uint32_t bmask = (1u << PA[0]) | (1u << PB[0]);
-  bmask |= bmask << 4 | bmask << 8 | bmask << 12;
+  uint32_t bmask = first_tile_pattern();
 #pragma unroll
   for (int p0 = 0; p0 < 6; p0++)
 #pragma unroll

@@ -53,11 +53,29 @@ def _plans(out_f, in_f, tokens, dtype):
     return p
 
 
+def _check_operands(x2d, weight):
+    """The library takes raw device addresses: refuse host tensors, mixed devices
+    and dtype mismatches before anything is launched."""
+    if weight.dtype not in _DTYPE_NAMES:
+        raise ValueError("weight must be torch.float16 or torch.bfloat16, got %s" % weight.dtype)
+    if x2d.dtype != weight.dtype:
+        raise ValueError("input dtype %s differs from the weight dtype %s" % (x2d.dtype, weight.dtype))
+    if not (x2d.is_cuda and weight.is_cuda):
+        raise ValueError("input and weight must be GPU tensors")
+    if x2d.device != weight.device:
+        raise ValueError("input (%s) and weight (%s) are on different devices" % (x2d.device, weight.device))
+    if x2d.dim() != 2 or weight.dim() != 2 or x2d.shape[1] != weight.shape[1]:
+        raise ValueError("expected x (tokens x in) and weight (out x in)")
+    if not (x2d.is_contiguous() and weight.is_contiguous()):
+        raise ValueError("input and weight must be contiguous")
+
+
 class SparseLinearFunction(torch.autograd.Function):
     """Y = X W_hat^T with W_hat the transposable 2:4 pruning of W (see the module docstring)."""
 
     @staticmethod
     def forward(ctx, x2d, weight):
+        _check_operands(x2d, weight)
         out_f, in_f = weight.shape
         tokens = x2d.shape[0]
         plans = _plans(out_f, in_f, tokens, _DTYPE_NAMES[weight.dtype])
@@ -78,6 +96,8 @@ class SparseLinearFunction(torch.autograd.Function):
     def backward(ctx, dy):
         x2d, v_bwd, m_bwd = ctx.saved_tensors
         tokens, out_f, in_f = ctx.shape
+        if dy.dtype != x2d.dtype or not dy.is_cuda or dy.device != x2d.device or tuple(dy.shape) != (tokens, out_f):
+            raise ValueError("output gradient must be a (tokens x out) GPU tensor of the layer's dtype and device")
         dy = dy.contiguous()
         dx = dw = None
         if ctx.needs_input_grad[0]:
@@ -98,6 +118,8 @@ class SemiStructuredSparseLinear(torch.nn.Module):
         super().__init__()
         if dtype not in _DTYPE_NAMES:
             raise ValueError("dtype must be torch.float16 or torch.bfloat16")
+        if weight is None and torch.device(device).type != "cuda":
+            raise ValueError("the layer runs on the GPU: device must be a cuda device")
         if in_features % 8 or out_features % 8:
             raise ValueError("in_features and out_features must be multiples of 8")
         self.in_features, self.out_features = in_features, out_features
@@ -106,6 +128,8 @@ class SemiStructuredSparseLinear(torch.nn.Module):
             torch.nn.init.normal_(weight, std=0.02)
         elif tuple(weight.shape) != (out_features, in_features) or weight.dtype != dtype:
             raise ValueError("weight must be (out_features, in_features) of the layer's dtype")
+        if not weight.is_cuda:
+            raise ValueError("the weight must live on the GPU (the library's kernels read it in place)")
         self.weight = torch.nn.Parameter(weight.contiguous())
 
     def forward(self, x):
@@ -114,5 +138,6 @@ class SemiStructuredSparseLinear(torch.nn.Module):
         x2d = x.reshape(-1, self.in_features).contiguous()
         if x2d.shape[0] % 4:
             raise ValueError("the number of tokens must be a multiple of 4")
+        _check_operands(x2d, self.weight)
         y = SparseLinearFunction.apply(x2d, self.weight)
         return y.reshape(*x.shape[:-1], self.out_features)

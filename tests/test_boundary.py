@@ -175,6 +175,32 @@ def test_sparse_linear_validates_on_host():
         SemiStructuredSparseLinear(64, 64, dtype=torch.float32)
 
 
+def test_sparse_linear_refuses_host_tensors_and_dtype_mismatch(monkeypatch):
+    """Host tensors, mixed devices and mixed dtypes are refused before any
+    library call (the library would read a host address as device memory)."""
+    import torch
+    import structured_sparse_gemm_nm_amd.linear as lin
+    from structured_sparse_gemm_nm_amd.linear import SemiStructuredSparseLinear, SparseLinearFunction
+
+    def no_call(*a, **k):
+        raise AssertionError("a library call was made")
+    for name in ("nm_prune", "nm_compress", "nm_spmm", "nm_dense_gemm", "nm_plan_init"):
+        monkeypatch.setattr(lin, name, no_call)
+    w = torch.zeros((16, 32), dtype=torch.float16)
+    with pytest.raises(ValueError, match="GPU"):
+        SparseLinearFunction.apply(torch.zeros((8, 32), dtype=torch.float16), w)
+    with pytest.raises(ValueError, match="dtype"):
+        SparseLinearFunction.apply(torch.zeros((8, 32), dtype=torch.float32), w)
+    with pytest.raises(ValueError, match="dtype"):
+        SparseLinearFunction.apply(torch.zeros((8, 32), dtype=torch.bfloat16), w)
+    with pytest.raises(ValueError):
+        SparseLinearFunction.apply(torch.zeros((8, 32), dtype=torch.float32), w.float())
+    with pytest.raises(ValueError, match="cuda"):
+        SemiStructuredSparseLinear(32, 16, device="cpu")
+    with pytest.raises(ValueError, match="GPU"):
+        SemiStructuredSparseLinear(32, 16, weight=w)
+
+
 def test_algorithm_ids_validate_on_host():
     plan = _init()
     assert nm.nm_plan_algorithm_count(plan) == nm.NM_ALG_COUNT == 4

@@ -29,8 +29,15 @@ def stored(op, rows, cols):
     return (rows, cols) if op == "N" else (cols, rows)
 
 
-def plan_for(dtype, m, n, k, N, M, op_a="N", op_b="N", **kw):
-    return nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=op_b, dtype=dtype, **kw)
+TILE_ALG = {None: nm.NM_ALG_AUTO, "auto": nm.NM_ALG_AUTO, "128": nm.NM_ALG_TILE128,
+            "256x128": nm.NM_ALG_TILE256X128, "256": nm.NM_ALG_TILE256}
+
+
+def plan_for(dtype, m, n, k, N, M, op_a="N", op_b="N", tile=None, **kw):
+    """A plan; `tile` pins the block tile through the plan's algorithm id."""
+    plan = nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=op_b, dtype=dtype, **kw)
+    nm.nm_plan_set_algorithm(plan, TILE_ALG[tile])
+    return plan
 
 
 # ------------------------------------------------------------------ prune / check / compress
@@ -254,6 +261,105 @@ def test_row_path_ragged(dtype, N, M, path, monkeypatch):
         assert np.array_equal(got[:, k:], sentinel[:, k:]), (m, k)
 
 
+# ------------------------------------------------------------------ ties, signed zeros, NaN
+
+def tie_values(dtype, shape, seed):
+    """Tie-heavy inputs: fp16/bf16 drawn from {0, -0, +-0.5, +-1, 2}, int8 from
+    [-3, 3], so equal magnitudes (and +0 against -0) meet in most groups."""
+    rng = np.random.default_rng(seed)
+    if dtype == "i8":
+        return rng.integers(-3, 4, size=shape).astype(np.int8)
+    x = rng.choice(np.array([0.0, -0.0, 0.5, -0.5, 1.0, -1.0, 2.0], np.float32), size=shape)
+    if dtype == "f16":
+        return x.astype(np.float16).view(np.uint16)
+    return inputs._fp32_to_bf16_bits(x).reshape(shape)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("N,M", NM_CASES)
+@pytest.mark.parametrize("op", ["N", "T"])
+def test_ties_prune_check_compress_1d(dtype, N, M, op):
+    """1-D prune, check and compress on tie-heavy inputs with signed zeros, bit for
+    bit: ties go to the lower offset (select_topn for M <= 16, the selection
+    network for M = 32 on the register path), +0 and -0 weigh the same."""
+    m, k = 208, 544
+    a = tie_values(dtype, stored(op, m, k), 31 + N * M)
+    ref, keep = oracle.prune_1d(a, dtype, N, M, op)
+    plan = plan_for(dtype, m, 8, k, N, M, op_a=op)
+    out = Guarded(a.shape, TRAW[dtype])
+    mask = Guarded((plan.mask_bytes // 4,), torch.int32)
+    nm.nm_prune(plan, dev(a), out.t, "1d", mask.t)
+    sync()
+    out.check(); mask.check()
+    assert np.array_equal(host(out.t, RAW[dtype]), ref)
+    assert np.array_equal(host(mask.t, np.uint32).reshape(ref.shape[0], -1), oracle.mask_bits(keep))
+    cnt = torch.full((1,), 777, dtype=torch.int32, device="cuda")
+    nm.nm_prune_check(plan, dev(a), "1d", cnt)
+    sync()
+    assert int(cnt.item()) == oracle.check_1d(a, dtype, N, M, op)
+    vref, mref = oracle.compress(a, dtype, N, M, op)
+    vals = Guarded((m, plan.values_ld), TRAW[dtype])
+    meta = Guarded((m, plan.meta_ld), torch.uint8)
+    nm.nm_compress(plan, dev(a), vals.t, meta.t)
+    sync()
+    vals.check(); meta.check()
+    assert np.array_equal(host(vals.t, RAW[dtype]), vref)
+    assert np.array_equal(host(meta.t, np.uint8), mref)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+def test_ties_prune_tile(dtype):
+    """Transposable tile prune on tie-heavy tiles, all-equal tiles (the first
+    pattern must win), all-zero tiles and tiles of +0 / -0 only."""
+    rows, cols = 64, 96
+    a = tie_values(dtype, (rows, cols), 55)
+    one = {"f16": 0x3C00, "bf16": 0x3F80, "i8": 1}[dtype]
+    neg_zero = {"f16": 0x8000, "bf16": 0x8000, "i8": 0}[dtype]
+    a[0:4, 0:4] = one                                   # all-equal magnitudes
+    a[4:8, 4:8] = 0                                     # all zero
+    a[8:12, 8:12] = neg_zero                            # all -0
+    a[12:16, 12:16] = np.where(np.arange(16).reshape(4, 4) % 3 == 0, neg_zero, 0)   # +0 / -0 mix
+    a[16:20, 16:20] = one
+    a[17, 17] = a[19, 18] = (one | 0x8000) if dtype != "i8" else -1                 # equal magnitudes, signs differ
+    ref, keep = oracle.prune_tile(a, dtype)
+    first = [[1, 1, 0, 0], [1, 1, 0, 0], [0, 0, 1, 1], [0, 0, 1, 1]]
+    for t in range(5):
+        assert keep[4 * t:4 * t + 4, 4 * t:4 * t + 4].tolist() == first, t
+    plan = plan_for(dtype, rows, 16, cols, 2, 4)
+    out = Guarded(a.shape, TRAW[dtype])
+    mask = Guarded((plan.mask_bytes // 4,), torch.int32)
+    nm.nm_prune(plan, dev(a), out.t, "tile", mask.t)
+    sync()
+    out.check(); mask.check()
+    assert np.array_equal(host(out.t, RAW[dtype]), ref)
+    assert np.array_equal(host(mask.t, np.uint32).reshape(rows, -1), oracle.mask_bits(keep))
+    cnt = torch.full((1,), 777, dtype=torch.int32, device="cuda")
+    nm.nm_prune_check(plan, dev(a), "tile", cnt)
+    sync()
+    assert int(cnt.item()) == oracle.check_tile(a, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prune_tile_nan_and_inf(dtype):
+    """Tiles holding NaN or Inf: a NaN-keeping candidate never wins, and with no
+    ordered candidate (a NaN row, column or tile) the first pattern stays."""
+    from tests.test_oracle_pins import nan_inf_tiles
+    a = nan_inf_tiles(dtype)
+    ref, keep = oracle.prune_tile(a, dtype)
+    plan = plan_for(dtype, a.shape[0], 16, a.shape[1], 2, 4)
+    out = Guarded(a.shape, TRAW[dtype])
+    mask = Guarded((plan.mask_bytes // 4,), torch.int32)
+    nm.nm_prune(plan, dev(a), out.t, "tile", mask.t)
+    sync()
+    out.check(); mask.check()
+    assert np.array_equal(host(out.t, RAW[dtype]), ref)
+    assert np.array_equal(host(mask.t, np.uint32).reshape(a.shape[0], -1), oracle.mask_bits(keep))
+    cnt = torch.full((1,), 777, dtype=torch.int32, device="cuda")
+    nm.nm_prune_check(plan, out.t, "tile", cnt)
+    sync()
+    assert int(cnt.item()) == 0
+
+
 # ------------------------------------------------------------------ products
 
 def ref_product(dtype, ahat_logical, b_logical, alpha, beta, c):
@@ -278,7 +384,7 @@ def assert_close(dtype, got_raw, ref, tol):
     assert not bad.any(), (np.argwhere(bad)[:5], err[bad][:5], tol[bad][:5])
 
 
-def run_spmm(dtype, N, M, m, n, k, op_b, alpha, beta, seed, op_a="N"):
+def run_spmm(dtype, N, M, m, n, k, op_b, alpha, beta, seed, op_a="N", tile=None):
     a = rand(dtype, stored(op_a, m, k), seed)
     ahat_stored, _ = oracle.prune_1d(a, dtype, N, M, op_a)
     ahat = ahat_stored if op_a == "N" else np.ascontiguousarray(ahat_stored.T)
@@ -289,7 +395,7 @@ def run_spmm(dtype, N, M, m, n, k, op_b, alpha, beta, seed, op_a="N"):
     if beta != 0:
         c = (inputs.uniform_int((m, n), seed + 2, -2**20, 2**20, np.int32) if dtype == "i8"
              else rand(dtype, (m, n), seed + 2))
-    plan = plan_for(dtype, m, n, k, N, M, op_a=op_a, op_b=op_b)
+    plan = plan_for(dtype, m, n, k, N, M, op_a=op_a, op_b=op_b, tile=tile)
     odt = torch.int32 if dtype == "i8" else torch.int16
     d = Guarded((m, n), odt)
     nm.nm_spmm(plan, alpha, dev(vref), dev(mref), dev(b_st), beta, dev(c) if c is not None else None, d.t)
@@ -306,13 +412,11 @@ def run_spmm(dtype, N, M, m, n, k, op_b, alpha, beta, seed, op_a="N"):
                                    (256, 512, 640)])
 @pytest.mark.parametrize("ab", [(1.0, 0.0), (2.0, -3.0)])
 @pytest.mark.parametrize("tile", ["auto", "128", "256"])
-def test_spmm_2of4(dtype, op_b, m, n, k, ab, tile, monkeypatch):
-    if tile != "auto":
-        monkeypatch.setenv("NM_FORCE_TILE", tile)
+def test_spmm_2of4(dtype, op_b, m, n, k, ab, tile):
     alpha, beta = ab
     if dtype != "i8":
         alpha, beta = (0.75, -1.25) if beta != 0 else (1.0, 0.0)
-    plan = run_spmm(dtype, 2, 4, m, n, k, op_b, alpha, beta, 1000 + m + n + k)
+    plan = run_spmm(dtype, 2, 4, m, n, k, op_b, alpha, beta, 1000 + m + n + k, tile=tile)
     assert plan.kernel_name == "spmm_smfmac_2of4"
 
 
@@ -428,14 +532,12 @@ def test_dense_skinny_tall(dtype, n, k):
 @pytest.mark.parametrize("m,n,k", [(272, 8, 208), (272, 144, 208), (272, 304, 208), (256, 256, 320), (512, 384, 192),
                                    (256, 512, 640)])
 @pytest.mark.parametrize("tile", ["auto", "128", "256"])
-def test_dense_gemm(dtype, op_a, op_b, m, n, k, tile, monkeypatch):
-    if tile != "auto":
-        monkeypatch.setenv("NM_FORCE_TILE", tile)
+def test_dense_gemm(dtype, op_a, op_b, m, n, k, tile):
     a_log = rand(dtype, (m, k), 41)
     a_st = a_log if op_a == "N" else np.ascontiguousarray(a_log.T)
     b_log = rand(dtype, (k, n), 42)
     b_st = b_log if op_b == "N" else np.ascontiguousarray(b_log.T)
-    plan = plan_for(dtype, m, n, k, 2, 4, op_a=op_a, op_b=op_b)
+    plan = plan_for(dtype, m, n, k, 2, 4, op_a=op_a, op_b=op_b, tile=tile)
     odt = torch.int32 if dtype == "i8" else torch.int16
     d = Guarded((m, n), odt)
     nm.nm_dense_gemm(plan, 1.0, dev(a_st), dev(b_st), 0.0, None, d.t)
@@ -449,12 +551,11 @@ def test_dense_gemm(dtype, op_a, op_b, m, n, k, tile, monkeypatch):
 @pytest.mark.parametrize("op_b", ["N", "T"])
 @pytest.mark.parametrize("m,n,k,pad,tile", [(256, 256, 256, 64, "256"), (384, 256, 512, 32, "128"),
                                             (2304, 2048, 256, 0, "128"), (2304, 256, 256, 16, "256")])
-def test_dense_op_a_t_full_tiles(dtype, op_b, m, n, k, pad, tile, monkeypatch):
+def test_dense_op_a_t_full_tiles(dtype, op_b, m, n, k, pad, tile):
     """A stored k x m (op_a = T) with a padded leading dimension and beta != 0 on
     whole tiles: the copy-ring kernel's transposed-A staging, on both tile shapes
     and both ring depths (more 128 x 128 tiles than compute units takes the
     shallow ring)."""
-    monkeypatch.setenv("NM_FORCE_TILE", tile)
     a_log = rand(dtype, (m, k), 51)
     lda = m + pad
     a_st = np.zeros((k, lda), dtype=a_log.dtype)
@@ -463,7 +564,7 @@ def test_dense_op_a_t_full_tiles(dtype, op_b, m, n, k, pad, tile, monkeypatch):
     b_st = b_log if op_b == "N" else np.ascontiguousarray(b_log.T)
     c = (inputs.uniform_int((m, n), 53, -2**20, 2**20, np.int32) if dtype == "i8" else rand(dtype, (m, n), 53))
     alpha, beta = (2.0, -1.0) if dtype == "i8" else (0.75, 0.5)
-    plan = plan_for(dtype, m, n, k, 2, 4, op_a="T", op_b=op_b, lda=lda)
+    plan = plan_for(dtype, m, n, k, 2, 4, op_a="T", op_b=op_b, lda=lda, tile=tile)
     odt = torch.int32 if dtype == "i8" else torch.int16
     d = Guarded((m, n), odt)
     nm.nm_dense_gemm(plan, alpha, dev(a_st), dev(b_st), beta, dev(c), d.t)
@@ -509,13 +610,11 @@ COL_CASES = [
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
 @pytest.mark.parametrize("case", COL_CASES, ids=[c[0] for c in COL_CASES])
 @pytest.mark.parametrize("beta", [0.0, 1.0])
-def test_col_major_cd(dtype, case, beta, monkeypatch):
+def test_col_major_cd(dtype, case, beta):
     """Column-major C and D (the blog's column-major output): D element (i, j) at
     j * ldd + i, with ldd > m so that the rows past m of every column (the caller's
     bytes) must stay untouched; C read column-major the same way."""
     label, N, M, m, n, k, op_b, tile = case
-    if tile:
-        monkeypatch.setenv("NM_FORCE_TILE", tile)
     es_cd = 4 if dtype == "i8" else 2
     ld = -(-m // (16 // es_cd)) * (16 // es_cd) + 16 // es_cd      # 16-byte columns, padded past m
     seed = 7000 + m + n + k
@@ -527,7 +626,7 @@ def test_col_major_cd(dtype, case, beta, monkeypatch):
     if beta != 0:
         c = (inputs.uniform_int((m, n), seed + 2, -2**20, 2**20, np.int32) if dtype == "i8"
              else rand(dtype, (m, n), seed + 2))
-    plan = plan_for(dtype, m, n, k, N or 2, M or 4, op_b=op_b, ldc=ld, ldd=ld, order_cd="col")
+    plan = plan_for(dtype, m, n, k, N or 2, M or 4, op_b=op_b, ldc=ld, ldd=ld, order_cd="col", tile=tile)
     raw = np.int32 if dtype == "i8" else np.uint16
     sentinel = np.full((n, ld), 0x3C3C if es_cd == 2 else 0x3C3C3C3C, dtype=raw)
     d = Guarded((n, ld), torch.int32 if dtype == "i8" else torch.int16, fill=dev(sentinel))

@@ -60,3 +60,27 @@ def test_planted_mistake_is_caught(name, old, new, pin, tmp_path, monkeypatch):
     with pytest.raises(AssertionError):
         pin()
     monkeypatch.setattr(orc, "_lib", None)
+
+
+# Mistakes planted in the Python side of the oracle (the keep-mask packing):
+# the mutated function replaces oracle.mask_bits for the duration of the pin.
+PY_MUTATIONS = [
+    ("mask bits packed most-significant bit first", 'bitorder="little"', 'bitorder="big"'),
+    ("mask rows padded to 64-bit words", "words = (cols + 31) // 32", "words = (cols + 63) // 64 * 2"),
+    ("mask rows run on without a fresh word", "padded[:, :cols] = keep",
+     "padded = np.zeros((rows, words * 32), np.uint8); padded.reshape(-1)[:rows * cols] = keep.reshape(-1)"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", PY_MUTATIONS, ids=[m[0] for m in PY_MUTATIONS])
+def test_planted_mask_mistake_is_caught(name, old, new, monkeypatch):
+    import inspect
+    import numpy as np
+    src = inspect.getsource(orc.mask_bits)
+    assert src.count(old) == 1, name
+    ns = {"np": np}
+    exec(src.replace(old, new), ns)
+    monkeypatch.setattr(orc, "mask_bits", ns["mask_bits"])
+    monkeypatch.setattr(oracle, "mask_bits", ns["mask_bits"])
+    with pytest.raises(AssertionError):
+        pins.test_mask_bits_hand_cases()

@@ -237,6 +237,89 @@ def test_prune_tile_invariants(dtype):
     assert np.allclose(st[transposable], sr[transposable], rtol=0, atol=1e-12)
 
 
+def _tile_first_max_float(w):
+    """First maximiser over the 90 patterns when magnitudes may be NaN or Inf: a
+    candidate keeping a NaN has a NaN score, which never compares greater, so it
+    can never replace the current winner; when no candidate has an ordered score
+    the first pattern (rows (0,1), (0,1), (2,3), (2,3)) stays."""
+    best, best_p = None, (0, 0, 5, 5)
+    for p in itertools.product(range(6), repeat=4):
+        cols = [0] * 4
+        for r in range(4):
+            for c in PAIRS[p[r]]:
+                cols[c] += 1
+        if cols != [2, 2, 2, 2]:
+            continue
+        kept = [w[r][c] for r in range(4) for c in PAIRS[p[r]]]
+        if any(np.isnan(x) for x in kept):
+            continue
+        if any(np.isinf(x) for x in kept):
+            s = float("inf")
+        else:
+            s = sum((Fraction(float(x)) for x in kept), Fraction(0))
+        if best is None or s > best:
+            best, best_p = s, p
+    keep = np.zeros((4, 4), np.uint8)
+    for r in range(4):
+        keep[r, list(PAIRS[best_p[r]])] = 1
+    return keep
+
+
+def nan_inf_tiles(dtype):
+    """4x4 tiles (stacked vertically) holding NaN and Inf: one NaN element, a NaN
+    row, a NaN column, NaN everywhere, one +Inf, two -Inf in different rows."""
+    nan_bits = 0x7E00 if dtype == "f16" else 0x7FC0
+    inf_bits = 0x7C00 if dtype == "f16" else 0x7F80
+    base = _groups(dtype, 4, 24, seed=404, ties=False)
+    t = base.copy()
+    t[0, 0] = nan_bits
+    t[4 + 2, :] = nan_bits
+    t[8:12, 1] = nan_bits
+    t[12:16, :] = nan_bits | 0x8000
+    t[16 + 1, 2] = inf_bits
+    t[20 + 0, 3] = inf_bits | 0x8000
+    t[20 + 3, 0] = inf_bits | 0x8000
+    return t
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_prune_tile_nan_and_inf(dtype):
+    t = nan_inf_tiles(dtype)
+    _, keep = oracle.prune_tile(t, dtype)
+    mags = np.abs(oracle.decode(t, dtype))
+    for i in range(t.shape[0] // 4):
+        ref = _tile_first_max_float(mags[4 * i:4 * i + 4])
+        assert np.array_equal(keep[4 * i:4 * i + 4], ref), i
+    # a NaN row, a NaN column and an all-NaN tile leave no ordered candidate: first pattern
+    first = [[1, 1, 0, 0], [1, 1, 0, 0], [0, 0, 1, 1], [0, 0, 1, 1]]
+    for i in (1, 2, 3):
+        assert keep[4 * i:4 * i + 4].tolist() == first, i
+    # every tile still keeps two per row and per column
+    kt = keep.reshape(-1, 4, 4)
+    assert (kt.sum(1) == 2).all() and (kt.sum(2) == 2).all()
+
+
+# ------------------------------------------------------------------ keep-mask packing
+
+def test_mask_bits_hand_cases():
+    """Keep masks pack into uint32 words least significant bit first, each row
+    starting a new word (ceil(cols / 32) words per row)."""
+    k = np.array([[1, 0, 1, 1]], np.uint8)                       # bits 0, 2, 3
+    assert oracle.mask_bits(k).tolist() == [[0b1101]]
+    k = np.zeros((2, 33), np.uint8)
+    k[0, 0] = k[0, 5] = k[0, 32] = 1                              # word 0 = 1 + 32, word 1 = 1 (column 32)
+    k[1, 31] = 1                                                  # a new row starts a new word
+    assert oracle.mask_bits(k).tolist() == [[33, 1], [0x80000000, 0]]
+    k = np.zeros((1, 64), np.uint8)
+    k[0, 31] = k[0, 63] = k[0, 40] = 1
+    assert oracle.mask_bits(k).tolist() == [[0x80000000, 0x80000100]]
+    k = np.zeros((3, 4), np.uint8)
+    k[2, 1] = 1
+    assert oracle.mask_bits(k).tolist() == [[0], [0], [2]]
+    k = np.ones((1, 70), np.uint8)                                # ragged last word: 6 low bits
+    assert oracle.mask_bits(k).tolist() == [[0xFFFFFFFF, 0xFFFFFFFF, 0x3F]]
+
+
 # ------------------------------------------------------------------ prune check
 
 def test_check_counts_injected_violations():
