@@ -74,6 +74,8 @@ def parse():
     ap.add_argument("--workload", default="x1", choices=sorted(WORKLOAD_SETS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-autotune", action="store_true",
+                    help="keep every SpMM plan on its default block tile and no split-k (no timing-based choice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain %d MiB elementwise copy (y = -x) %d times (for counter calibration)" % (CAL_MIB, CAL_REPS))
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -171,6 +173,29 @@ def main():
         g["host"] = dict(a=a, b=bs, c=c)
         gemms.append(g)
 
+    # Algorithm selection, once per plan and outside every timed region (the
+    # blog's plan-time choice): each SpMM plan tries every block tile and split-k
+    # in {1, 2, 4} on the workload's own operands and keeps the fastest; a
+    # split-k choice gets its workspace here, allocated by the caller.
+    tuned = {}
+    if not args.no_autotune and args.workload != "linear":
+        from structured_sparse_gemm_nm_amd.tuning import autotune_spmm
+        for g in gemms:
+            nm.nm_prune(g["plan"], g["A"], g["Ap"], g["mode"])
+            nm.nm_compress(g["plan"], g["Ap"], g["vals"], g["meta"])
+            for ob in g["layouts"]:
+                pl = g["plans"][ob]
+                if pl.kernel_name != "spmm_smfmac_2of4":
+                    continue
+                # twice: the first pass brings the clocks up, the second decides
+                for _ in range(2):
+                    autotune_spmm(pl, g["w"]["alpha"], g["vals"], g["meta"], g["B"][ob], g["w"]["beta"], g["C"],
+                                  g["D"][ob], reps=10, warmup=3, split_ks=(1, 2, 4))
+                tuned[(g["label"], ob)] = (nm.nm_plan_get_algorithm(pl), nm.nm_plan_get_split_k(pl)[1])
+        torch.cuda.synchronize()
+    for g in gemms:
+        g["WS"] = {ob: g["plans"][ob].empty_workspace() for ob in g["layouts"]}
+
     # The step calls the C ABI with arguments marshalled once, so that the host
     # enqueues well ahead of the GPU and the events around a SpMM launch
     # (recorded on the stream the kernels run on) time the kernel, not host gaps.
@@ -188,7 +213,8 @@ def main():
         calls.append((L.nm_compress, (h, P(g["Ap"]), P(g["vals"]), P(g["meta"]), sp), None))
         for ob in g["layouts"]:
             calls.append((L.nm_spmm, (g["plans"][ob].handle, ctypes.byref(g["_ab"][0]), P(g["vals"]), P(g["meta"]),
-                                      P(g["B"][ob]), ctypes.byref(g["_ab"][1]), P(g["C"]), P(g["D"][ob]), None, sp),
+                                      P(g["B"][ob]), ctypes.byref(g["_ab"][1]), P(g["C"]), P(g["D"][ob]),
+                                      P(g["WS"][ob]), sp),
                           (g["label"], ob)))
         calls.append((L.nm_decompress, (h, P(g["vals"]), P(g["meta"]), P(g["Ad"]), sp), None))
 
@@ -380,28 +406,34 @@ def main():
             if g["op_a"] == "T":
                 a_dense = g["Ap"].t().contiguous()
             for ob in g["layouts"]:
-                pl = g["plans"][ob]
-                if g["op_a"] == "T":
-                    pl = nm.nm_plan_init(g["m"], g["n"], g["k"], g["N"], g["M"], op_a="N", op_b=ob, dtype=g["dtype"],
-                                         order_cd=g["w"].get("order_cd", "row"))
+                # its own plan, every block tile timed, the fastest kept (the
+                # comparator gets the same plan-time choice as the SpMM)
+                pl = nm.nm_plan_init(g["m"], g["n"], g["k"], g["N"], g["M"], op_a="N", op_b=ob, dtype=g["dtype"],
+                                     order_cd=g["w"].get("order_cd", "row"))
                 f = lambda: nm.nm_dense_gemm(pl, g["w"]["alpha"], a_dense, g["B"][ob], g["w"]["beta"], g["C"], g["D"][ob])
-                for _ in range(max(2, args.warmup)):
-                    f()
-                e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)
-                reps = max(5, args.steps)
-                e0.record(stream)
-                for _ in range(reps):
-                    f()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                dense[(g["label"], ob)] = e0.elapsed_time(e1) / reps
+                best = None
+                for alg in range(nm.NM_ALG_COUNT if not args.no_autotune else 1):
+                    nm.nm_plan_set_algorithm(pl, alg)
+                    for _ in range(max(2, args.warmup)):
+                        f()
+                    e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)
+                    reps = max(5, args.steps)
+                    e0.record(stream)
+                    for _ in range(reps):
+                        f()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    t = e0.elapsed_time(e1) / reps
+                    best = t if best is None else min(best, t)
+                dense[(g["label"], ob)] = best
     per_gemm = []
     for g in gemms:
         for ob in g["layouts"]:
             key = (g["label"], ob)
             t_s = spmm_ms[key]
             row = {"gemm": g["label"], "layout": "N" + ob, "m": g["m"], "n": g["n"], "k": g["k"],
-                   "kernel": g["plans"][ob].kernel_name, "spmm_ms": round(t_s, 5),
+                   "kernel": g["plans"][ob].kernel_name, "algorithm": nm.nm_plan_get_algorithm(g["plans"][ob]),
+                   "split_k": nm.nm_plan_get_split_k(g["plans"][ob])[1], "spmm_ms": round(t_s, 5),
                    "spmm_tflops": round(flops_dense_eq(g) / (t_s * 1e-3) / 1e12, 2)}
             row["spmm_frac_of_sparse_peak"] = round(row["spmm_tflops"] / (2 * PEAK_TFLOPS[g["dtype"]]), 4)
             if key in dense:

@@ -170,7 +170,13 @@ nm_status_t nm_decompress(nm_plan_t plan, const void* d_values, const void* d_me
  * on the int8 path both must be integers. dC may be NULL when *beta == 0 and
  * may equal dD. C and D are stored in the plan's order_cd (row- or
  * column-major). fp16/bf16 outputs are alpha*acc + beta*C evaluated in fp32
- * and rounded to nearest even. d_workspace must be NULL (no workspace needed). */
+ * and rounded to nearest even.
+ * d_workspace: device memory of at least nm_spmm_workspace_size bytes, 16-byte
+ * aligned, when that size is non-zero (a split-k plan); it must not overlap
+ * any operand, its contents on entry do not matter, and it is scratch after
+ * the call (the blog's matmul takes its workspace the same way). When the size
+ * is zero d_workspace is not read and may be NULL. A missing workspace is
+ * NM_ERR_INVALID_ARG, returned before anything is enqueued. */
 nm_status_t nm_spmm(nm_plan_t plan, const float* alpha, const void* d_values, const void* d_meta,
                     const void* dB, const float* beta, const void* dC, void* dD, void* d_workspace,
                     void* stream);
@@ -196,6 +202,28 @@ enum { NM_ALG_AUTO = 0, NM_ALG_TILE128 = 1, NM_ALG_TILE256X128 = 2, NM_ALG_TILE2
 int32_t nm_plan_algorithm_count(nm_plan_t plan);   /* NM_ALG_COUNT (0 for a NULL plan) */
 nm_status_t nm_plan_set_algorithm(nm_plan_t plan, int32_t alg);
 nm_status_t nm_plan_get_algorithm(nm_plan_t plan, int32_t* alg);
+
+/* Split-k: the blog's split-k setting of the algorithm selection, with the
+ * workspace its matmul call takes (the workspace-size query and the
+ * d_workspace argument of the code example). With splits S > 1, the 2:4
+ * product on whole tiles (m and n multiples of the block tile, k a multiple of
+ * 64 fp16/bf16 or 128 int8 elements, 16-byte rows) runs S blocks per output
+ * tile, each over one contiguous range of the k-steps (range z covers steps
+ * [z T / S, (z + 1) T / S) of the T = k / 64 (128 for int8) steps), writes its
+ * raw fp32 (int32) partial sums to plane z of the workspace, and a second
+ * kernel adds the planes in the order z = 0, 1, ..., applies alpha and beta
+ * and rounds once. int8 results are bit-identical to the unsplit product;
+ * fp16/bf16 differ only by fp32 summation order. Shapes the split does not
+ * apply to (other tiles, general N:M, small n) run unsplit and need no
+ * workspace. Host-only.
+ *   nm_plan_set_split_k: S in [1, 16] (1 = no split, the default); invalid
+ *     values give NM_ERR_INVALID_ARG and leave the plan unchanged.
+ *   nm_plan_get_split_k: the requested S and the S nm_spmm will launch
+ *     (min(S, T) where the split applies, else 1); either pointer may be NULL.
+ *   nm_spmm_workspace_size: S_eff * m * n * 4 bytes when S_eff > 1, else 0. */
+nm_status_t nm_plan_set_split_k(nm_plan_t plan, int32_t splits);
+nm_status_t nm_plan_get_split_k(nm_plan_t plan, int32_t* requested, int32_t* effective);
+nm_status_t nm_spmm_workspace_size(nm_plan_t plan, size_t* bytes);
 
 /* Name of the SpMM kernel the plan dispatches to (static string). */
 const char* nm_plan_kernel_name(nm_plan_t plan);

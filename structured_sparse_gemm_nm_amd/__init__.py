@@ -71,6 +71,10 @@ def lib():
         L.nm_plan_set_algorithm.restype = st; L.nm_plan_set_algorithm.argtypes = [P, I32]
         L.nm_plan_get_algorithm.restype = st; L.nm_plan_get_algorithm.argtypes = [P, ctypes.POINTER(I32)]
         L.nm_plan_spmm_kernel.restype = ctypes.c_char_p; L.nm_plan_spmm_kernel.argtypes = [P]
+        L.nm_plan_set_split_k.restype = st; L.nm_plan_set_split_k.argtypes = [P, I32]
+        L.nm_plan_get_split_k.restype = st
+        L.nm_plan_get_split_k.argtypes = [P, ctypes.POINTER(I32), ctypes.POINTER(I32)]
+        L.nm_spmm_workspace_size.restype = st; L.nm_spmm_workspace_size.argtypes = [P, ctypes.POINTER(S)]
         L.nm_status_string.restype = ctypes.c_char_p; L.nm_status_string.argtypes = [st]
         L.nm_last_error.restype = ctypes.c_char_p; L.nm_last_error.argtypes = []
         L.nm_version.restype = I32; L.nm_version.argtypes = []
@@ -160,6 +164,11 @@ class Plan:
     def empty_meta(self, device="cuda"):
         return torch.empty((self.m, self.meta_ld), dtype=torch.uint8, device=device)
 
+    def empty_workspace(self, device="cuda"):
+        """Workspace nm_spmm needs for this plan's split-k setting (None when it needs none)."""
+        n = nm_spmm_workspace_size(self)
+        return torch.empty((n,), dtype=torch.uint8, device=device) if n else None
+
     def empty_mask(self, device="cuda"):
         rows = self.problem.m if self.problem.op_a == NM_OP_N else self.problem.k
         return torch.empty((rows, self.mask_ld_words), dtype=torch.int32, device=device)
@@ -220,10 +229,28 @@ def nm_decompress(plan, d_values, d_meta, dA_out, stream=None):
     _check(lib().nm_decompress(plan.handle, _ptr(d_values), _ptr(d_meta), _ptr(dA_out), _stream(stream)))
 
 
-def nm_spmm(plan, alpha, d_values, d_meta, dB, beta, dC, dD, stream=None):
+def nm_spmm(plan, alpha, d_values, d_meta, dB, beta, dC, dD, stream=None, workspace=None):
+    """workspace: device buffer of at least nm_spmm_workspace_size(plan) bytes (split-k plans)."""
     a, b = ctypes.c_float(alpha), ctypes.c_float(beta)
     _check(lib().nm_spmm(plan.handle, ctypes.byref(a), _ptr(d_values), _ptr(d_meta), _ptr(dB), ctypes.byref(b),
-                         _ptr(dC), _ptr(dD), None, _stream(stream)))
+                         _ptr(dC), _ptr(dD), _ptr(workspace), _stream(stream)))
+
+
+def nm_plan_set_split_k(plan, splits):
+    _check(lib().nm_plan_set_split_k(plan.handle, int(splits)))
+
+
+def nm_plan_get_split_k(plan):
+    """(requested, effective) split-k of the plan."""
+    r, e = ctypes.c_int32(), ctypes.c_int32()
+    _check(lib().nm_plan_get_split_k(plan.handle, ctypes.byref(r), ctypes.byref(e)))
+    return r.value, e.value
+
+
+def nm_spmm_workspace_size(plan):
+    n = ctypes.c_size_t()
+    _check(lib().nm_spmm_workspace_size(plan.handle, ctypes.byref(n)))
+    return n.value
 
 
 def nm_dense_gemm(plan, alpha, dA, dB, beta, dC, dD, stream=None):

@@ -126,6 +126,7 @@ nm_status_t nm_plan_init(nm_plan_t* plan, const nm_problem_t* p) {
   pl->mld = (mbytes + 15) / 16 * 16;
   pl->force_tile = -1;
   pl->algorithm = NM_ALG_AUTO;
+  pl->split_k = 1;
   // the one environment switch: the LDS tile kernels for prune / check /
   // compress / decompress even where the register path applies (read once
   // here; the parity tests use it to run both paths on the same inputs)
@@ -151,7 +152,7 @@ const char* nm_plan_spmm_kernel(nm_plan_t plan) {
     pr.armed = true;
     pr.kernel = nullptr;
     switch (plan->kernel) {
-      case K_SMFMAC_24: (void)launch_spmm_smfmac(*plan, 1.0f, nullptr, nullptr, nullptr, 0.0f, nullptr, nullptr, 0); break;
+      case K_SMFMAC_24: (void)launch_spmm_smfmac(*plan, 1.0f, nullptr, nullptr, nullptr, 0.0f, nullptr, nullptr, nullptr, 0); break;
       case K_GATHER_MFMA: (void)launch_spmm_gather(*plan, 1.0f, nullptr, nullptr, nullptr, 0.0f, nullptr, nullptr, 0); break;
       default: (void)launch_spmm_skinny(*plan, 1.0f, nullptr, nullptr, nullptr, 0.0f, nullptr, nullptr, 0); break;
     }
@@ -185,6 +186,28 @@ nm_status_t nm_plan_set_algorithm(nm_plan_t plan, int32_t alg) {
 nm_status_t nm_plan_get_algorithm(nm_plan_t plan, int32_t* alg) {
   if (!plan || !alg) return fail(NM_ERR_INVALID_ARG, "plan / alg is NULL");
   *alg = plan->algorithm;
+  return NM_OK;
+}
+
+nm_status_t nm_plan_set_split_k(nm_plan_t plan, int32_t splits) {
+  if (!plan) return fail(NM_ERR_INVALID_ARG, "plan is NULL");
+  if (splits < 1 || splits > nm::MAX_SPLIT_K) return fail(NM_ERR_INVALID_ARG, "split-k must be in [1, 16]");
+  plan->split_k = splits;
+  plan->spmm_symbol.clear();
+  set_error("");
+  return NM_OK;
+}
+
+nm_status_t nm_plan_get_split_k(nm_plan_t plan, int32_t* requested, int32_t* effective) {
+  if (!plan) return fail(NM_ERR_INVALID_ARG, "plan is NULL");
+  if (requested) *requested = plan->split_k;
+  if (effective) *effective = nm::spmm_splits(*plan);
+  return NM_OK;
+}
+
+nm_status_t nm_spmm_workspace_size(nm_plan_t plan, size_t* bytes) {
+  if (!plan || !bytes) return fail(NM_ERR_INVALID_ARG, "plan / bytes is NULL");
+  *bytes = nm::spmm_workspace_bytes(*plan);
   return NM_OK;
 }
 
@@ -299,14 +322,20 @@ nm_status_t nm_spmm(nm_plan_t plan, const float* alpha, const void* d_values, co
   if (!plan) return fail(NM_ERR_INVALID_ARG, "plan is NULL");
   nm_status_t st = check_scalars(plan, alpha, beta);
   if (st != NM_OK) return st;
-  if (d_workspace) return fail(NM_ERR_INVALID_ARG, "d_workspace must be NULL");
   st = check_product_ptrs(plan, d_values, d_meta, dB, *beta, dC, dD);
   if (st != NM_OK) return st;
+  const size_t ws_bytes = nm::spmm_workspace_bytes(*plan);
+  if (ws_bytes > 0 && !d_workspace)
+    return fail(NM_ERR_INVALID_ARG, "this plan's split-k product needs a workspace of " + std::to_string(ws_bytes) +
+                                        " bytes (nm_spmm_workspace_size); d_workspace is NULL");
+  if (!aligned16(d_workspace)) return fail(NM_ERR_ALIGN, "d_workspace must be 16-byte aligned");
   if (plan->p.m == 0 || plan->p.n == 0) return NM_OK;
   hipStream_t s = (hipStream_t)stream;
   hipError_t e;
   switch (plan->kernel) {
-    case K_SMFMAC_24: e = launch_spmm_smfmac(*plan, *alpha, d_values, d_meta, dB, *beta, dC, dD, s); break;
+    case K_SMFMAC_24:
+      e = launch_spmm_smfmac(*plan, *alpha, d_values, d_meta, dB, *beta, dC, dD, ws_bytes ? d_workspace : nullptr, s);
+      break;
     case K_GATHER_MFMA: e = launch_spmm_gather(*plan, *alpha, d_values, d_meta, dB, *beta, dC, dD, s); break;
     default: e = launch_spmm_skinny(*plan, *alpha, d_values, d_meta, dB, *beta, dC, dD, s); break;
   }

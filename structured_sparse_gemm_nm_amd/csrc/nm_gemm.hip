@@ -118,7 +118,29 @@ static GemmArgs make_gemm_args(const nm_plan& pl, float alpha, const void* a, co
   A.N = pl.p.nm_n; A.M = pl.p.nm_m; A.bits = pl.bits;
   A.a_vec = (A.lda * pl.esz_ab) % 16 == 0;
   A.b_vec = (A.ldb * pl.esz_ab) % 16 == 0;
+  A.splits = 1;
+  A.ws = nullptr;
   return A;
+}
+
+int spmm_splits(const nm_plan& pl) {
+  if (pl.split_k <= 1 || pl.kernel != K_SMFMAC_24 || pl.p.m == 0 || pl.p.n == 0) return 1;
+  const GemmArgs A = make_gemm_args(pl, 1.0f, nullptr, nullptr, nullptr, 0.0f, nullptr, nullptr, false);
+  int tm = 128, tn = 128;
+  switch (pick_tile(pl, A_SPARSE24)) {
+    case T256: tm = 256; tn = 256; break;
+    case T256x128: tm = 256; tn = 128; break;
+    default: break;
+  }
+  if (!full_tiles(pl, A, tm, tn, A_SPARSE24)) return 1;
+  const int64_t ksteps = pl.p.k / (KBYTES / pl.esz_ab);
+  const int64_t sp = pl.split_k < ksteps ? pl.split_k : ksteps;
+  return (int)(sp > 1 ? sp : 1);
+}
+
+size_t spmm_workspace_bytes(const nm_plan& pl) {
+  const int sp = spmm_splits(pl);
+  return sp > 1 ? (size_t)sp * (size_t)pl.p.m * (size_t)pl.p.n * 4u : 0u;
 }
 
 static hipError_t launch_tiles_any(const nm_plan& pl, int amode, const GemmArgs& A, hipStream_t s) {
@@ -160,8 +182,11 @@ static hipError_t launch_skinny_dt(const nm_plan& pl, const GemmArgs& A, hipStre
 }
 
 hipError_t launch_spmm_smfmac(const nm_plan& pl, float alpha, const void* vals, const void* meta, const void* b,
-                              float beta, const void* c, void* d, hipStream_t s) {
-  return launch_tiles_any(pl, A_SPARSE24, make_gemm_args(pl, alpha, vals, meta, b, beta, c, d, false), s);
+                              float beta, const void* c, void* d, void* ws, hipStream_t s) {
+  GemmArgs A = make_gemm_args(pl, alpha, vals, meta, b, beta, c, d, false);
+  A.splits = spmm_splits(pl);
+  A.ws = (uint8_t*)ws;
+  return launch_tiles_any(pl, A_SPARSE24, A, s);
 }
 
 hipError_t launch_spmm_gather(const nm_plan& pl, float alpha, const void* vals, const void* meta, const void* b,

@@ -68,6 +68,8 @@ struct GemmArgs {
   float alpha, beta;
   int N, M, bits;
   int a_vec, b_vec;     // 16-byte vector loads allowed on A / B rows
+  int splits;           // split-k: k ranges (1 = none); with more, each block writes raw partial sums to ws
+  uint8_t* ws;          // splits planes of m x n fp32 (int32 for int8) partial sums, in D's storage order
 };
 
 // Integer-path epilogue: v = alpha * acc + beta * C exactly in int64, stored as
@@ -439,13 +441,15 @@ __device__ __forceinline__ typename Acc<DT>::t mfma32(const typename Frag<DT>::a
 // patch and share both A row tiles and B column tiles in that XCD's L2.
 constexpr int NUM_XCD = 8;
 constexpr int NUM_CU = 256;
-__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
-  constexpr int GROUP = 8;
+__device__ __forceinline__ int64_t xcd_logical_id() {
   const int64_t nb = gridDim.x;
   const int64_t hw = blockIdx.x;
   const int64_t per = nb / NUM_XCD, rem = nb % NUM_XCD;
   const int64_t x = hw % NUM_XCD, local = hw / NUM_XCD;
-  const int64_t id = (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + local;
+  return (x < rem ? x * (per + 1) : rem * (per + 1) + (x - rem) * per) + local;
+}
+__device__ __forceinline__ void band_coords(int64_t id, int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
+  constexpr int GROUP = 8;
   const int64_t per_band = GROUP * tiles_n;
   const int64_t band = id / per_band;
   const int64_t first = band * GROUP;
@@ -453,6 +457,18 @@ __device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, in
   const int64_t in = id % per_band;
   tm = first + in % rows_in_band;
   tn = in / rows_in_band;
+}
+__device__ __forceinline__ void tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn) {
+  band_coords(xcd_logical_id(), tiles_m, tiles_n, tm, tn);
+}
+// With split-k the grid is splits x tiles: logical ids run through every tile
+// of k range 0, then of range 1, ..., so the blocks one XCD holds at a time
+// work on the same k range of neighbouring tiles, as without a split.
+__device__ __forceinline__ void split_tile_coords(int64_t tiles_m, int64_t tiles_n, int64_t& tm, int64_t& tn,
+                                                  int& z) {
+  const int64_t id = xcd_logical_id(), tiles = tiles_m * tiles_n;
+  z = (int)(id / tiles);
+  band_coords(id % tiles, tiles_m, tiles_n, tm, tn);
 }
 
 // ---------------------------------------------------------------- the tiled kernel
@@ -723,23 +739,28 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
 
   const int64_t tiles_m = A.m / BM, tiles_n = A.n / BN;
   int64_t tm, tn;
-  tile_coords(tiles_m, tiles_n, tm, tn);
+  int z = 0;                                             // k range of this block (split-k)
+  split_tile_coords(tiles_m, tiles_n, tm, tn, z);
   const int64_t r0 = tm * BM, c0 = tn * BN;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);   // uniform: keeps LDS/M0 math scalar
   const int wm0 = (wave / WGN) * WM, wn0 = (wave % WGN) * WN;
   const int l32 = lane & 31, q = lane >> 5;
-  const int ksteps = (int)(A.k / KL);
+  // k-steps [kb, kb + ksteps) of the A.k / KL; the host keeps splits <= k-steps,
+  // so every range holds at least one step
+  const int ktotal = (int)(A.k / KL);
+  const int kb = (int)((int64_t)z * ktotal / A.splits);
+  const int ksteps = (int)((int64_t)(z + 1) * ktotal / A.splits) - kb;
 
   // ---- DMA: block-uniform bases (advanced per step in scalar registers) and
   // per-lane byte offsets computed once ----
-  const uint8_t* bbase = A.b + (size_t)(BKC ? c0 * A.ldb : c0) * ESZ;
   const size_t bstep = BKC ? (size_t)KBYTES : (size_t)KL * A.ldb * ESZ;
-  const uint8_t* abase = A.a + (size_t)(AT ? r0 : r0 * A.lda) * ESZ;
+  const uint8_t* bbase = A.b + (size_t)(BKC ? c0 * A.ldb : c0) * ESZ + (size_t)kb * bstep;
   const size_t astep = AT ? (size_t)KL * A.lda * ESZ : (size_t)(SP ? 64 : KBYTES);
+  const uint8_t* abase = A.a + (size_t)(AT ? r0 : r0 * A.lda) * ESZ + (size_t)kb * astep;
   constexpr int ASLOTS = BM * ESZ / 16;                  // 16-byte slots per stored k-row of A (AT)
-  const uint8_t* mbase = A.meta + (size_t)(r0 * A.mld);
+  const uint8_t* mbase = A.meta + (size_t)(r0 * A.mld) + (size_t)kb * MB;
   uint32_t ob[NB], oa[NA], om[NMT > 0 ? NMT : 1];
 #pragma unroll
   for (int j = 0; j < NB; j++) {
@@ -990,6 +1011,34 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
       __builtin_amdgcn_sched_barrier(0);
       compute_group(g);
     }
+  }
+
+  // ---- split-k: this block's partial sums go to plane z of the workspace, in
+  // D's storage order, raw (alpha, beta and rounding are applied once, by the
+  // reduction over the planes) ----
+  if (A.splits > 1) {
+    typedef typename std::conditional<DT == DT_I8, int32_t, float>::type raw_t;
+    typedef typename std::conditional<DT == DT_I8, intx4, floatx4>::type raw4_t;
+    raw_t* plane = (raw_t*)A.ws + (size_t)z * (size_t)(A.m * A.n);
+#pragma unroll
+    for (int fm = 0; fm < FM; fm++)
+#pragma unroll
+      for (int fn = 0; fn < FN; fn++) {
+        const int64_t col = c0 + wn0 + fn * 32 + l32;
+#pragma unroll
+        for (int r4 = 0; r4 < 4; r4++) {
+          const int64_t row = r0 + wm0 + fm * 32 + 8 * r4 + 4 * q;
+          if (A.cd_col) {
+            // four consecutive rows of one column: one 16-byte store
+            *(raw4_t*)(plane + col * A.m + row) = raw4_t{(raw_t)acc[fm][fn][4 * r4], (raw_t)acc[fm][fn][4 * r4 + 1],
+                                                          (raw_t)acc[fm][fn][4 * r4 + 2], (raw_t)acc[fm][fn][4 * r4 + 3]};
+          } else {
+#pragma unroll
+            for (int t4 = 0; t4 < 4; t4++) plane[(row + t4) * A.n + col] = (raw_t)acc[fm][fn][4 * r4 + t4];
+          }
+        }
+      }
+    return;
   }
 
   // ---- epilogue: D = alpha * acc + beta * C ----
@@ -1246,6 +1295,70 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
     }
 }
 
+// ---------------------------------------------------------------- split-k reduction
+
+// D = alpha * (sum over the planes of the partial sums) + beta * C, four
+// consecutive elements of D's storage order per thread: planes added in order
+// z = 0, 1, ... in fp32 (exactly in int32 for int8, then alpha and beta in
+// int64 as in every integer epilogue), rounded to nearest even once. The
+// split-k shapes are whole tiles, so every line (row of row-major D, column of
+// column-major D) is a multiple of 128 elements long.
+template <int DT>
+__global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs A) {
+  typedef typename std::conditional<DT == DT_I8, intx4, floatx4>::type raw4_t;
+  const int64_t len = A.cd_col ? A.m : A.n;             // elements per stored line
+  const int64_t quads = A.m * A.n / 4;
+  const int64_t qid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (qid >= quads) return;
+  const int64_t line = qid / (len / 4), off = (qid % (len / 4)) * 4;
+  const int64_t plane = A.m * A.n;
+  raw4_t sum = *(const raw4_t*)((const uint8_t*)A.ws + (size_t)(qid * 4) * 4);
+  for (int z = 1; z < A.splits; z++) {
+    const raw4_t p = *(const raw4_t*)((const uint8_t*)A.ws + (size_t)(z * plane + qid * 4) * 4);
+    sum += p;
+  }
+  const int64_t cld = A.cd_col ? A.c_cs : A.c_rs, dld = A.cd_col ? A.d_cs : A.d_rs;
+  const int64_t cidx = line * cld + off, didx = line * dld + off;
+  if constexpr (DT == DT_I8) {
+    int64_t v[4];
+#pragma unroll
+    for (int t = 0; t < 4; t++) v[t] = (int64_t)A.alpha * sum[t];
+    if (A.beta != 0.0f) {
+      if (A.cd_i8) {
+        const uint32_t cv = *(const uint32_t*)((const int8_t*)A.c + cidx);
+#pragma unroll
+        for (int t = 0; t < 4; t++) v[t] += (int64_t)A.beta * (int64_t)(int8_t)(cv >> (8 * t));
+      } else {
+        const intx4 cv = *(const intx4*)((const int32_t*)A.c + cidx);
+#pragma unroll
+        for (int t = 0; t < 4; t++) v[t] += (int64_t)A.beta * cv[t];
+      }
+    }
+    if (A.cd_i8) {
+      uint32_t o = 0;
+#pragma unroll
+      for (int t = 0; t < 4; t++) o |= ((uint32_t)sat_i8(v[t]) & 0xFFu) << (8 * t);
+      *(uint32_t*)((int8_t*)A.d + didx) = o;
+    } else {
+      *(intx4*)((int32_t*)A.d + didx) = intx4{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
+    }
+  } else {
+    float v[4];
+#pragma unroll
+    for (int t = 0; t < 4; t++) v[t] = A.alpha * sum[t];
+    if (A.beta != 0.0f) {
+      const u32x2 cv = *(const u32x2*)((const uint16_t*)A.c + cidx);
+      v[0] += A.beta * from_bits16<DT>((uint16_t)(cv[0] & 0xFFFFu));
+      v[1] += A.beta * from_bits16<DT>((uint16_t)(cv[0] >> 16));
+      v[2] += A.beta * from_bits16<DT>((uint16_t)(cv[1] & 0xFFFFu));
+      v[3] += A.beta * from_bits16<DT>((uint16_t)(cv[1] >> 16));
+    }
+    const uint32_t lo = (uint32_t)to_bits16<DT>(v[0]) | ((uint32_t)to_bits16<DT>(v[1]) << 16);
+    const uint32_t hi = (uint32_t)to_bits16<DT>(v[2]) | ((uint32_t)to_bits16<DT>(v[3]) << 16);
+    *(u32x2*)((uint16_t*)A.d + didx) = u32x2{lo, hi};
+  }
+}
+
 // ---------------------------------------------------------------- tile launch (per element type)
 
 // Block tile: 256 x 256 when that still gives most CUs a tile, 256 x 128 or
@@ -1277,6 +1390,20 @@ inline bool full_tiles(const nm_plan& pl, const GemmArgs& A, int TM, int TN, int
   return b_rows * A.ldb * es < lim && a_rows * A.lda * es < lim && A.m * A.mld < lim;
 }
 
+// After a split-k product: the reduction over the partial-sum planes (nothing
+// to do without a split).
+template <int DT>
+hipError_t launch_reduce(const GemmArgs& A, hipStream_t s) {
+  if (A.splits <= 1) return launch_status();
+  if (!launch_probe().armed) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int64_t quads = A.m * A.n / 4;
+  NM_LAUNCH((splitk_reduce_kernel<DT>), dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, s, A);
+  return launch_status();
+}
+
 // Stages of the LDS-DMA ring: as many as fit (at most 4), keeping two blocks
 // per CU for 128 x 128 tiles; DEEP: one block per CU (grids of at most one
 // block per CU), so the ring takes the whole LDS (up to 6 stages): the copies
@@ -1293,9 +1420,12 @@ constexpr int dma_stages() {
 template <int DT, int AMODE, int TM, int TN>
 hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
   const int64_t tiles = ((A.m + TM - 1) / TM) * ((A.n + TN - 1) / TN);
-  const dim3 grid((unsigned)tiles);
   const bool bkc = pl.p.op_b == NM_OP_T;
   const bool akc = pl.p.op_a == NM_OP_N || AMODE != A_DENSE;
+  // split-k: only the whole-tile copy-ring kernel of the 2:4 product takes it
+  // (spmm_splits decides with the same tile choice and whole-tile test)
+  if (A.splits > 1 && (AMODE != A_SPARSE24 || !full_tiles(pl, A, TM, TN, AMODE))) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)(tiles * A.splits));
   if constexpr (AMODE != A_GATHER) {
     if (full_tiles(pl, A, TM, TN, AMODE)) {
       // 256-row tiles run eight waves (two per SIMD, 128 x 64 or 64 x 64 each);
@@ -1327,10 +1457,9 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
         // stored k x n when every CU has at most one tile (BERT FC2 NN 41.2 ->
         // 38.4 us, PROJ NN 12.5 -> 11.7 us) and slower for B stored n x k
         // (FC2 NT 37 -> 39.5 us)
-        if (!bkc && tiles <= NUM_CU) {
-          if (bkc) NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, S1, 2, 4, 1>), grid, dim3(512), 0, s, A);
-          else NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, S1, 2, 4, 0>), grid, dim3(512), 0, s, A);
-          return launch_status();
+        if (!bkc && tiles * A.splits <= NUM_CU) {
+          NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, S1, 2, 4, 0>), grid, dim3(512), 0, s, A);
+          return launch_reduce<DT>(A, s);
         }
       }
       if (bkc && deep)
@@ -1341,7 +1470,7 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
         NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, SD, WGM, WGN, 0>), grid, dim3(64 * WGM * WGN), 0, s, A);
       else
         NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, S1, WGM, WGN, 0>), grid, dim3(64 * WGM * WGN), 0, s, A);
-      return launch_status();
+      return launch_reduce<DT>(A, s);
     }
   }
   if constexpr (AMODE == A_GATHER) {

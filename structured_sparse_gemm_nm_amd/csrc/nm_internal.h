@@ -20,6 +20,7 @@ struct nm_plan {
   std::string spmm_symbol;  // device kernel nm_spmm launches (filled on first query)
   int force_tile;           // -1 = automatic, else nm::TileCfg (set through the algorithm id)
   int algorithm;            // nm_plan_set_algorithm id (NM_ALG_AUTO unless set)
+  int split_k;              // nm_plan_set_split_k: requested k ranges of the 2:4 product (1 = none)
   bool tile_elemwise;       // NM_TILE_ELEMWISE (read once at plan creation): prune/check/compress/decompress
                             // on the LDS tile kernels even where the register path applies
 };
@@ -41,6 +42,8 @@ void set_error(const std::string& msg);
 // Dry run of a launch: while the calling thread's probe is armed, NM_LAUNCH
 // records the kernel's host stub instead of launching it, so the same host
 // logic that picks a kernel can also name it.
+// The first kernel recorded is the product's main kernel (a split-k product
+// launches its reduction afterwards).
 struct LaunchProbe {
   bool armed = false;
   const void* kernel = nullptr;
@@ -49,9 +52,20 @@ LaunchProbe& launch_probe();
 inline hipError_t launch_status() { return launch_probe().armed ? hipSuccess : hipGetLastError(); }
 #define NM_LAUNCH(KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                              \
   do {                                                                                  \
-    if (::nm::launch_probe().armed) ::nm::launch_probe().kernel = (const void*)(KERNEL); \
-    else hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);           \
+    if (::nm::launch_probe().armed) {                                                   \
+      if (!::nm::launch_probe().kernel) ::nm::launch_probe().kernel = (const void*)(KERNEL); \
+    } else {                                                                            \
+      hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);              \
+    }                                                                                   \
   } while (0)
+
+// Split-k of the 2:4 product: the k ranges nm_spmm launches for this plan (1
+// when the plan asks for none or its shape does not take the whole-tile
+// copy-ring kernel), and the workspace bytes they need: one m x n plane of
+// fp32 / int32 partial sums per range.
+int spmm_splits(const nm_plan& pl);
+size_t spmm_workspace_bytes(const nm_plan& pl);
+constexpr int MAX_SPLIT_K = 16;
 
 // ---- launchers (return hipError_t from the launch) ----
 hipError_t launch_prune_1d(const nm_plan& pl, const void* a, void* out, uint32_t* mask, hipStream_t s);
@@ -72,7 +86,7 @@ hipError_t launch_check(const nm_plan& pl, const void* a, int mode, int32_t* cou
 hipError_t launch_compress(const nm_plan& pl, const void* a, void* vals, void* meta, hipStream_t s);
 hipError_t launch_decompress(const nm_plan& pl, const void* vals, const void* meta, void* out, hipStream_t s);
 hipError_t launch_spmm_smfmac(const nm_plan& pl, float alpha, const void* vals, const void* meta,
-                              const void* b, float beta, const void* c, void* d, hipStream_t s);
+                              const void* b, float beta, const void* c, void* d, void* ws, hipStream_t s);
 hipError_t launch_spmm_gather(const nm_plan& pl, float alpha, const void* vals, const void* meta,
                               const void* b, float beta, const void* c, void* d, hipStream_t s);
 hipError_t launch_spmm_skinny(const nm_plan& pl, float alpha, const void* vals, const void* meta,

@@ -142,7 +142,12 @@ def test_calls_reject_bad_arguments_before_launching():
     spmm = L.nm_spmm
     assert spmm(plan.handle, None, fake, fake, fake, ctypes.byref(one), None, fake, None, None) == nm.NM_ERR_INVALID_ARG
     assert spmm(plan.handle, ctypes.byref(one), fake, fake, fake, ctypes.byref(one), None, fake, None, None) == nm.NM_ERR_INVALID_ARG  # beta != 0, C NULL
-    assert spmm(plan.handle, ctypes.byref(one), fake, fake, fake, ctypes.byref(ctypes.c_float(0.0)), None, fake, fake, None) == nm.NM_ERR_INVALID_ARG  # workspace
+    splan = _init(m=256, n=256, k=1024, op_b="T")
+    nm.nm_plan_set_split_k(splan, 2)
+    zero = ctypes.byref(ctypes.c_float(0.0))
+    assert spmm(splan.handle, ctypes.byref(one), fake, fake, fake, zero, None, fake, None, None) == nm.NM_ERR_INVALID_ARG  # workspace missing
+    assert "workspace" in nm.nm_last_error()
+    assert spmm(splan.handle, ctypes.byref(one), fake, fake, fake, zero, None, fake, odd, None) == nm.NM_ERR_ALIGN
     assert spmm(plan.handle, ctypes.byref(one), fake, odd, fake, ctypes.byref(ctypes.c_float(0.0)), None, fake, None, None) == nm.NM_ERR_ALIGN
     assert spmm(plan.handle, ctypes.byref(ctypes.c_float(float("nan"))), fake, fake, fake, ctypes.byref(one), fake, fake, None, None) == nm.NM_ERR_INVALID_ARG
     iplan = _init(dtype="i8")
@@ -213,3 +218,33 @@ def test_algorithm_ids_validate_on_host():
             nm.nm_plan_set_algorithm(plan, bad)
         assert e.value.status == nm.NM_ERR_INVALID_ARG
     assert nm.nm_plan_get_algorithm(plan) == nm.NM_ALG_COUNT - 1     # unchanged by the rejected ids
+
+
+def test_split_k_settings_and_workspace_size():
+    """Split-k is a host-side plan setting; the workspace size is one m x n plane
+    of 4-byte partial sums per k range, only where the whole-tile 2:4 kernel runs."""
+    plan = _init(m=256, n=256, k=1024, op_b="T")            # 16 k-steps of 64
+    assert nm.nm_plan_get_split_k(plan) == (1, 1)
+    assert nm.nm_spmm_workspace_size(plan) == 0
+    nm.nm_plan_set_split_k(plan, 4)
+    assert nm.nm_plan_get_split_k(plan) == (4, 4)
+    assert nm.nm_spmm_workspace_size(plan) == 4 * 256 * 256 * 4
+    nm.nm_plan_set_split_k(plan, 16)
+    assert nm.nm_plan_get_split_k(plan) == (16, 16)
+    for bad in (0, -1, 17):
+        with pytest.raises(nm.NmError) as e:
+            nm.nm_plan_set_split_k(plan, bad)
+        assert e.value.status == nm.NM_ERR_INVALID_ARG
+    assert nm.nm_plan_get_split_k(plan) == (16, 16)         # unchanged by the rejected values
+    short = _init(m=256, n=256, k=192, op_b="T")            # 3 k-steps: the split is clamped
+    nm.nm_plan_set_split_k(short, 8)
+    assert nm.nm_plan_get_split_k(short) == (8, 3)
+    assert nm.nm_spmm_workspace_size(short) == 3 * 256 * 256 * 4
+    i8 = _init(m=256, n=256, k=1024, dtype="i8")            # int8 k-steps are 128 long: 8 of them
+    nm.nm_plan_set_split_k(i8, 16)
+    assert nm.nm_plan_get_split_k(i8) == (16, 8)
+    # shapes the split does not apply to need no workspace
+    for kw in (dict(m=200, n=144, k=336), dict(m=256, n=256, k=1024, nm_n=4, nm_m=32), dict(m=256, n=8, k=1024)):
+        p = _init(**kw)
+        nm.nm_plan_set_split_k(p, 4)
+        assert nm.nm_plan_get_split_k(p)[1] == 1 and nm.nm_spmm_workspace_size(p) == 0, kw

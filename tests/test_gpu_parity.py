@@ -730,11 +730,17 @@ def test_algorithm_ids_pin_the_tile_and_autotune(dtype):
         d.check()
         assert_close(dtype, host(d.t, raw), ref, tol)
     d = Guarded((m, n), odt)
-    times = autotune_spmm(plan, 1.0, dv, dm, db, 0.0, None, d.t, reps=3)
-    best = nm.nm_plan_get_algorithm(plan)
-    assert set(times) == set(range(nm.NM_ALG_COUNT)) and times[best][0] == min(t for t, _ in times.values())
+    times = autotune_spmm(plan, 1.0, dv, dm, db, 0.0, None, d.t, reps=3, split_ks=(1, 2))
+    best = (nm.nm_plan_get_algorithm(plan), nm.nm_plan_get_split_k(plan)[0])
+    assert set(times) == {(a, s) for a in range(nm.NM_ALG_COUNT) for s in (1, 2)}
+    assert times[best][0] == min(t for t, _ in times.values())
     sync()
     assert_close(dtype, host(d.t, raw), ref, tol)
+    # the pinned setting runs with the workspace it asks for
+    d2 = Guarded((m, n), odt)
+    nm.nm_spmm(plan, 1.0, dv, dm, db, 0.0, None, d2.t, workspace=plan.empty_workspace())
+    sync()
+    assert_close(dtype, host(d2.t, raw), ref, tol)
 
 
 @pytest.mark.parametrize("dtype", ["f16", "i8"])
@@ -796,3 +802,116 @@ def test_c_may_alias_d():
     sync()
     ref, tol = ref_product("f16", ahat, b, 1.0, 1.0, c)
     assert_close("f16", host(dc, np.uint16), ref, tol)
+
+
+# ------------------------------------------------------------------ split-k with a workspace
+
+SPLIT_CASES = [
+    # (label, m, n, k, op_b, tile, splits, beta, order_cd): even and uneven k ranges, the
+    # clamp to the number of k-steps, both B layouts, all three block tiles, beta and
+    # column-major C/D, and the eight-wave 128 x 128 kernel (B stored k x n, few tiles)
+    ("128-NT-2", 256, 256, 1024, "T", "128", 2, 0.0, "row"),
+    ("128-NN-4-beta", 256, 256, 1024, "N", "128", 4, 1.0, "row"),
+    ("256-NT-3-col", 512, 512, 640, "T", "256", 3, 1.0, "col"),
+    ("128-NN-clamped-col", 256, 384, 384, "N", "128", 16, 0.0, "col"),
+    ("256x128-NT-5", 1024, 256, 2048, "T", "256x128", 5, -0.5, "row"),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("case", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_split_k(dtype, case):
+    """Split-k on the whole-tile 2:4 kernel: each k range writes its partial sums
+    to its own workspace plane and the reduction adds them in order. int8 is
+    bit-exact (and equal to the unsplit product); fp16/bf16 within tolerance.
+    The workspace is guarded on both sides and its size is the documented one."""
+    label, m, n, k, op_b, tile, splits, beta, order = case
+    seed = 9100 + m + n + k
+    a = rand(dtype, (m, k), seed)
+    ahat, _ = oracle.prune_1d(a, dtype, 2, 4)
+    vref, mref = oracle.compress(a, dtype, 2, 4)
+    b_log = rand(dtype, (k, n), seed + 1)
+    b_st = b_log if op_b == "N" else np.ascontiguousarray(b_log.T)
+    c = None
+    if beta != 0:
+        c = (inputs.uniform_int((m, n), seed + 2, -2**20, 2**20, np.int32) if dtype == "i8"
+             else rand(dtype, (m, n), seed + 2))
+    alpha = 1.0 if dtype == "i8" else 0.75
+    if dtype == "i8" and beta != 0:
+        beta = 1.0
+    plan = plan_for(dtype, m, n, k, 2, 4, op_b=op_b, tile=tile, order_cd=order)
+    nm.nm_plan_set_split_k(plan, splits)
+    kl = 128 if dtype == "i8" else 64
+    eff = min(splits, k // kl)
+    assert nm.nm_plan_get_split_k(plan) == (splits, eff)
+    assert nm.nm_spmm_workspace_size(plan) == (eff * m * n * 4 if eff > 1 else 0)
+    raw = np.int32 if dtype == "i8" else np.uint16
+    odt = torch.int32 if dtype == "i8" else torch.int16
+    dshape = (n, m) if order == "col" else (m, n)
+    dc = None
+    if c is not None:
+        dc = dev(np.ascontiguousarray(c.T) if order == "col" else c)
+    ws = Guarded((max(1, nm.nm_spmm_workspace_size(plan)),), torch.uint8)
+    d = Guarded(dshape, odt)
+    nm.nm_spmm(plan, alpha, dev(vref), dev(mref), dev(b_st), beta, dc, d.t, workspace=ws.t)
+    sync()
+    d.check(); ws.check()
+    got = host(d.t, raw)
+    got = np.ascontiguousarray(got.T) if order == "col" else got
+    ref, tol = ref_product(dtype, ahat, b_log, alpha, beta, c)
+    assert_close(dtype, got, ref, tol)
+    # a second call on the same workspace (its old contents must not leak in)
+    d2 = Guarded(dshape, odt)
+    nm.nm_spmm(plan, alpha, dev(vref), dev(mref), dev(b_st), beta, dc, d2.t, workspace=ws.t)
+    sync()
+    assert np.array_equal(host(d2.t, raw), host(d.t, raw))
+    if dtype == "i8":
+        unsplit = plan_for(dtype, m, n, k, 2, 4, op_b=op_b, tile=tile, order_cd=order)
+        d3 = Guarded(dshape, odt)
+        nm.nm_spmm(unsplit, alpha, dev(vref), dev(mref), dev(b_st), beta, dc, d3.t)
+        sync()
+        assert np.array_equal(host(d3.t, raw), host(d.t, raw))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "i8"])
+def test_split_k_c_aliases_d_and_kernel_name(dtype):
+    """C == D through the reduction (each quad is read and written by one thread),
+    and the plan still names the product kernel, not the reduction."""
+    m, n, k = 256, 256, 512
+    a = rand(dtype, (m, k), 71)
+    ahat, _ = oracle.prune_1d(a, dtype, 2, 4)
+    v, meta = oracle.compress(a, dtype, 2, 4)
+    b = rand(dtype, (n, k), 72)
+    if dtype == "i8":
+        c = inputs.uniform_int((m, n), 73, -2**20, 2**20, np.int32)
+        alpha, beta, raw = 2.0, -1.0, np.int32
+    else:
+        c = rand(dtype, (m, n), 73)
+        alpha, beta, raw = 0.5, 1.5, np.uint16
+    plan = plan_for(dtype, m, n, k, 2, 4, op_b="T", tile="128")
+    nm.nm_plan_set_split_k(plan, 3)
+    assert "gemm_dma_kernel" in plan.spmm_kernel
+    ws = plan.empty_workspace()
+    dc = dev(c)
+    nm.nm_spmm(plan, alpha, dev(v), dev(meta), dev(b), beta, dc, dc, workspace=ws)
+    sync()
+    ref, tol = ref_product(dtype, ahat, np.ascontiguousarray(b.T), alpha, beta, c)
+    assert_close(dtype, host(dc, raw), ref, tol)
+
+
+def test_split_k_not_applicable_runs_unsplit():
+    """Ragged shapes, general N:M and small n ignore the split and need no workspace."""
+    for (N, M, m, n, k) in [(2, 4, 200, 144, 336), (4, 32, 150, 80, 544), (2, 4, 100, 8, 1088)]:
+        a = rand("f16", (m, k), 5 + m)
+        ahat, _ = oracle.prune_1d(a, "f16", N, M)
+        v, meta = oracle.compress(a, "f16", N, M)
+        b = rand("f16", (k, n), 6 + m)
+        plan = plan_for("f16", m, n, k, N, M)
+        nm.nm_plan_set_split_k(plan, 4)
+        assert nm.nm_spmm_workspace_size(plan) == 0
+        d = Guarded((m, n), torch.int16)
+        nm.nm_spmm(plan, 1.0, dev(v), dev(meta), dev(b), 0.0, None, d.t)
+        sync()
+        d.check()
+        ref, tol = ref_product("f16", ahat, b, 1.0, 0.0, None)
+        assert_close("f16", host(d.t, np.uint16), ref, tol)
