@@ -181,6 +181,25 @@ nm_status_t nm_spmm(nm_plan_t plan, const float* alpha, const void* d_values, co
                     const void* dB, const float* beta, const void* dC, void* dD, void* d_workspace,
                     void* stream);
 
+/* nm_spmm without a workspace argument and without any device allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. A split-k
+ * plan's partial sums go to a static device array of the library,
+ * NM_NOALLOC_SCRATCH_BYTES (32 MiB) on every GPU the library runs on, held
+ * until the process ends; its address is looked up once per device on the
+ * first call that needs it (the device of `stream`, the current device for
+ * the null stream). Plans whose workspace (nm_spmm_workspace_size) exceeds
+ * that size get NM_ERR_SHAPE before anything is enqueued; plans that need no
+ * workspace run exactly as nm_spmm. All calls on one GPU share that GPU's
+ * array, which keeps the last call's contents (every element a call reads
+ * was written earlier in the same call, so nothing has to be cleared): calls
+ * that may overlap on one GPU (different streams, no ordering between them)
+ * race on it and must be serialised by the caller. Arguments and results
+ * otherwise as nm_spmm. */
+#define NM_NOALLOC_SCRATCH_BYTES (32u << 20)
+nm_status_t nm_spmm_noalloc(nm_plan_t plan, const float* alpha, const void* d_values, const void* d_meta,
+                            const void* dB, const float* beta, const void* dC, void* dD, void* stream);
+
 /* Same-shape dense product D = alpha * op(A) * op(B) + beta * C with A dense
  * (stored with lda and op_a as in the plan). This is the in-library
  * comparator for the sparse speed-up (the blog's dense-vs-sparse table); it

@@ -75,6 +75,7 @@ def lib():
         L.nm_plan_get_split_k.restype = st
         L.nm_plan_get_split_k.argtypes = [P, ctypes.POINTER(I32), ctypes.POINTER(I32)]
         L.nm_spmm_workspace_size.restype = st; L.nm_spmm_workspace_size.argtypes = [P, ctypes.POINTER(S)]
+        L.nm_spmm_noalloc.restype = st; L.nm_spmm_noalloc.argtypes = [P, FP, P, P, P, FP, P, P, P]
         L.nm_status_string.restype = ctypes.c_char_p; L.nm_status_string.argtypes = [st]
         L.nm_last_error.restype = ctypes.c_char_p; L.nm_last_error.argtypes = []
         L.nm_version.restype = I32; L.nm_version.argtypes = []
@@ -234,6 +235,16 @@ def nm_spmm(plan, alpha, d_values, d_meta, dB, beta, dC, dD, stream=None, worksp
     a, b = ctypes.c_float(alpha), ctypes.c_float(beta)
     _check(lib().nm_spmm(plan.handle, ctypes.byref(a), _ptr(d_values), _ptr(d_meta), _ptr(dB), ctypes.byref(b),
                          _ptr(dC), _ptr(dD), _ptr(workspace), _stream(stream)))
+
+
+NM_NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def nm_spmm_noalloc(plan, alpha, d_values, d_meta, dB, beta, dC, dD, stream=None):
+    """nm_spmm with the split-k partial sums in the library's static device scratch (no workspace)."""
+    a, b = ctypes.c_float(alpha), ctypes.c_float(beta)
+    _check(lib().nm_spmm_noalloc(plan.handle, ctypes.byref(a), _ptr(d_values), _ptr(d_meta), _ptr(dB),
+                                 ctypes.byref(b), _ptr(dC), _ptr(dD), _stream(stream)))
 
 
 def nm_plan_set_split_k(plan, splits):

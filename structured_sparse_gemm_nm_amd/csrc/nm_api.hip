@@ -11,6 +11,7 @@
 #include <cxxabi.h>
 #include <stdlib.h>
 
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -340,6 +341,76 @@ nm_status_t nm_spmm(nm_plan_t plan, const float* alpha, const void* d_values, co
     default: e = launch_spmm_skinny(*plan, *alpha, d_values, d_meta, dB, *beta, dC, dD, s); break;
   }
   return hip_status(e, "spmm");
+}
+
+}  // extern "C"
+
+// ---- allocation-free product: split-k partial sums in a static device array ----
+
+namespace nm {
+
+// Device memory of the library itself (every GPU the library runs on holds
+// its own copy until the process ends). In host code `scratch` names a host
+// stand-in, not device memory: host code uses the address
+// hipGetSymbolAddress returns for the current device, never the name.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[NM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// The scratch address on the device `stream` belongs to, looked up once per
+// device with that device current.
+static nm_status_t scratch_address(hipStream_t stream, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  int dev = cur;
+  if (stream) {
+    hipDevice_t sd;
+    e = hipStreamGetDevice(stream, &sd);
+    if (e != hipSuccess) return hip_status(e, "hipStreamGetDevice");
+    dev = (int)sd;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(NM_ERR_INVALID_ARG, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_status(e, "hipSetDevice");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) (void)hipSetDevice(cur);
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(NM_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return NM_OK;
+}
+
+}  // namespace nm
+
+extern "C" {
+
+nm_status_t nm_spmm_noalloc(nm_plan_t plan, const float* alpha, const void* d_values, const void* d_meta,
+                            const void* dB, const float* beta, const void* dC, void* dD, void* stream) {
+  if (!plan) return fail(NM_ERR_INVALID_ARG, "plan is NULL");
+  const size_t need = nm::spmm_workspace_bytes(*plan);
+  if (need > (size_t)NM_NOALLOC_SCRATCH_BYTES)
+    return fail(NM_ERR_SHAPE, "this plan's split-k product needs " + std::to_string(need) +
+                                  " bytes of partial sums, more than the " +
+                                  std::to_string((size_t)NM_NOALLOC_SCRATCH_BYTES) +
+                                  "-byte static scratch of nm_spmm_noalloc (lower the split-k or use nm_spmm)");
+  void* ws = nullptr;
+  if (need > 0 && plan->p.m > 0 && plan->p.n > 0) {
+    // validate everything nm_spmm checks before touching the device
+    nm_status_t st = check_scalars(plan, alpha, beta);
+    if (st != NM_OK) return st;
+    st = check_product_ptrs(plan, d_values, d_meta, dB, *beta, dC, dD);
+    if (st != NM_OK) return st;
+    st = nm::scratch_address((hipStream_t)stream, &ws);
+    if (st != NM_OK) return st;
+  }
+  return nm_spmm(plan, alpha, d_values, d_meta, dB, beta, dC, dD, ws, stream);
 }
 
 nm_status_t nm_dense_gemm(nm_plan_t plan, const float* alpha, const void* dA, const void* dB, const float* beta,

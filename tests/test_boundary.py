@@ -248,3 +248,19 @@ def test_split_k_settings_and_workspace_size():
         p = _init(**kw)
         nm.nm_plan_set_split_k(p, 4)
         assert nm.nm_plan_get_split_k(p)[1] == 1 and nm.nm_spmm_workspace_size(p) == 0, kw
+
+
+def test_noalloc_refuses_splits_beyond_its_scratch():
+    """nm_spmm_noalloc checks the split-k workspace against its static scratch
+    before any device call (the fake pointers below are never touched)."""
+    L = nm.lib()
+    big = _init(m=2048, n=2048, k=4096, op_b="T")
+    nm.nm_plan_set_split_k(big, 4)                            # 64 MiB of partial sums
+    assert nm.nm_spmm_workspace_size(big) == 4 * 2048 * 2048 * 4 > nm.NM_NOALLOC_SCRATCH_BYTES
+    fake = ctypes.c_void_p(0x10000)
+    one, zero = ctypes.c_float(1.0), ctypes.c_float(0.0)
+    st = L.nm_spmm_noalloc(big.handle, ctypes.byref(one), fake, fake, fake, ctypes.byref(zero), None, fake, None)
+    assert st == nm.NM_ERR_SHAPE
+    assert "scratch" in nm.nm_last_error()
+    assert L.nm_spmm_noalloc(None, ctypes.byref(one), fake, fake, fake, ctypes.byref(zero), None, fake, None) \
+        == nm.NM_ERR_INVALID_ARG
