@@ -8,7 +8,9 @@
  * Sources for what is computed (titles of the web pages the method is taken from):
  *  - "[sparse] update support for arbitrary N:M settings sparse" (NVIDIA apex
  *    pull request 1631), extension 1, the mn_1d_greedy mask calculator:
- *    magnitude top-N per group of M consecutive elements along the last dim.
+ *    magnitude top-N per group of M consecutive elements along the last dim;
+ *    extension 2, vector-wise N:M for nmSPARSE, with its vector score (the
+ *    absolute value of the sum of the vector's elements).
  *  - "backpropagation for sparse semi-structured" (pytorch issue 126420), the
  *    maintainer reply: 4x4 tiles that are 2:4 sparse in both directions, so the
  *    same weight serves the forward (W x) and backward (W^T dy) products.
@@ -276,6 +278,126 @@ void or_decompress(const void* vals, int64_t vals_ld, const uint8_t* meta, int64
   }
 }
 
+/* ---------- vector-wise N:M: V consecutive rows share one kept-offset set ---------- */
+
+/* The apex pull request (extension 2) extends the mask calculators to
+ * vector-wise (VW) and block-wise N:M for nmSPARSE. Its vector-wise routine
+ * scores a vector by the absolute value of the SUM of its elements (signed
+ * values added first, abs taken last), unlike the block-wise routine, which
+ * sums absolute values; the VW reading here keeps that score. A vector is V
+ * consecutive rows of op(A) at one column; within every group of M columns the
+ * N vectors of largest score are kept for all V rows, ties to the lower
+ * in-group offset. The score is accumulated in fp64 in increasing row order;
+ * scores are compared through the bit pattern of the (non-negative) fp64
+ * value as an unsigned integer, which orders them numerically with NaN above
+ * +Inf. */
+static double vw_score(const void* a, int dt, int64_t cols, int64_t r0, int V, int64_t c) {
+  double s = 0.0;
+  for (int v = 0; v < V; v++) s += elem_f64(a, dt, (size_t)((r0 + v) * cols + c));
+  return fabs(s);
+}
+
+static uint64_t score_key(double x) {
+  uint64_t u;
+  memcpy(&u, &x, sizeof u);
+  return u & 0x7FFFFFFFFFFFFFFFull;
+}
+
+/* keep[j] = 1 for the N offsets kept in group g of the V-row block starting at r0. */
+static void select_vw_group(const void* a, int dt, int64_t cols, int64_t r0, int V, int64_t g, int N, int M,
+                            uint8_t* keep) {
+  int order[32];
+  uint64_t key[32];
+  for (int j = 0; j < M; j++) { order[j] = j; key[j] = score_key(vw_score(a, dt, cols, r0, V, g * M + j)); }
+  for (int x = 1; x < M; x++) {                 /* stable insertion sort, descending */
+    int o = order[x];
+    int y = x - 1;
+    while (y >= 0 && key[order[y]] < key[o]) { order[y + 1] = order[y]; y--; }
+    order[y + 1] = o;
+  }
+  memset(keep, 0, (size_t)M);
+  for (int s = 0; s < N; s++) keep[order[s]] = 1;
+}
+
+/* a: logical op(A), rows x cols (rows a multiple of V). out / keep as or_prune_1d. */
+void or_prune_vw(const void* a, int dt, int64_t rows, int64_t cols, int V, int N, int M, void* out, uint8_t* keep) {
+  uint8_t k[32];
+  for (int64_t b = 0; b < rows / V; b++)
+    for (int64_t g = 0; g < cols / M; g++) {
+      select_vw_group(a, dt, cols, b * V, V, g, N, M, k);
+      for (int v = 0; v < V; v++)
+        for (int j = 0; j < M; j++) {
+          size_t idx = (size_t)((b * V + v) * cols + g * M + j);
+          if (keep) keep[idx] = k[j];
+          if (k[j]) { if (out != a) copy_elem(out, idx, a, idx, dt); }
+          else zero_elem(out, idx, dt);
+        }
+    }
+}
+
+/* Groups of V-row blocks whose rows hold non-zeros at more than N offsets
+ * (the union over the block's rows), i.e. blocks that do not conform. */
+int64_t or_check_vw(const void* a, int dt, int64_t rows, int64_t cols, int V, int N, int M) {
+  int64_t bad = 0;
+  for (int64_t b = 0; b < rows / V; b++)
+    for (int64_t g = 0; g < cols / M; g++) {
+      int used = 0;
+      for (int j = 0; j < M; j++) {
+        int any = 0;
+        for (int v = 0; v < V; v++) any |= is_nonzero(a, dt, (size_t)((b * V + v) * cols + g * M + j));
+        used += any;
+      }
+      if (used > N) bad++;
+    }
+  return bad;
+}
+
+/* VW compressed form: values exactly as the element-wise layout (row r keeps
+ * its own values, in increasing offset order, at the offsets its block
+ * selected); metadata has one row per block of V rows, with the element-wise
+ * bit-stream layout: field (g*N + s) of block row b holds the s-th kept offset
+ * of group g. All padding is zero. */
+void or_compress_vw(const void* a, int dt, int64_t rows, int64_t cols, int V, int N, int M,
+                    void* vals, int64_t vals_ld, uint8_t* meta, int64_t meta_ld) {
+  int b = or_meta_bits(M);
+  uint8_t keep[32];
+  memset(vals, 0, (size_t)(rows * vals_ld) * esize(dt));
+  memset(meta, 0, (size_t)((rows / V) * meta_ld));
+  for (int64_t blk = 0; blk < rows / V; blk++) {
+    uint8_t* mrow = meta + blk * meta_ld;
+    for (int64_t g = 0; g < cols / M; g++) {
+      select_vw_group(a, dt, cols, blk * V, V, g, N, M, keep);
+      int s = 0;
+      for (int j = 0; j < M; j++) {
+        if (!keep[j]) continue;
+        for (int v = 0; v < V; v++) {
+          int64_t r = blk * V + v;
+          copy_elem(vals, (size_t)(r * vals_ld + g * N + s), a, (size_t)(r * cols + g * M + j), dt);
+        }
+        int64_t t0 = (g * N + s) * (int64_t)b;
+        for (int q = 0; q < b; q++) put_bit(mrow, t0 + q, (j >> q) & 1);
+        s++;
+      }
+    }
+  }
+}
+
+void or_decompress_vw(const void* vals, int64_t vals_ld, const uint8_t* meta, int64_t meta_ld, int dt,
+                      int64_t rows, int64_t cols, int V, int N, int M, void* out) {
+  int b = or_meta_bits(M);
+  memset(out, 0, (size_t)(rows * cols) * esize(dt));
+  for (int64_t r = 0; r < rows; r++) {
+    const uint8_t* mrow = meta + (r / V) * meta_ld;
+    for (int64_t g = 0; g < cols / M; g++)
+      for (int s = 0; s < N; s++) {
+        int64_t t0 = (g * N + s) * (int64_t)b;
+        int j = 0;
+        for (int q = 0; q < b; q++) j |= get_bit(mrow, t0 + q) << q;
+        copy_elem(out, (size_t)(r * cols + g * M + j), vals, (size_t)(r * vals_ld + g * N + s), dt);
+      }
+  }
+}
+
 /* ---------- the product D = alpha * op(A) * op(B) + beta * C ---------- */
 
 /* Dense triple loop in fp64, k ascending for every output. A: m x k, B: k x n,
@@ -352,6 +474,29 @@ void or_spmm_compressed_f64(const void* vals, int64_t vals_ld, const uint8_t* me
         for (int64_t c = 0; c < n; c++) acc[c] += a * brow[c];
       }
     for (int64_t c = 0; c < n; c++) D[i * n + c] = alpha * acc[c] + (beta != 0.0 ? beta * C[i * n + c] : 0.0);
+    free(acc);
+  }
+}
+
+/* The sparse loop for the vector-wise form: row i reads metadata row i / V. */
+void or_spmm_compressed_vw_f64(const void* vals, int64_t vals_ld, const uint8_t* meta, int64_t meta_ld,
+                               int dt, int64_t m, int64_t k, int V, int N, int M,
+                               const double* B, int64_t n, double* D) {
+  int b = or_meta_bits(M);
+  #pragma omp parallel for schedule(static)
+  for (int64_t i = 0; i < m; i++) {
+    double* acc = (double*)calloc((size_t)n, sizeof(double));
+    const uint8_t* mrow = meta + (i / V) * meta_ld;
+    for (int64_t g = 0; g < k / M; g++)
+      for (int s = 0; s < N; s++) {
+        int64_t t0 = (g * N + s) * (int64_t)b;
+        int j = 0;
+        for (int q = 0; q < b; q++) j |= get_bit(mrow, t0 + q) << q;
+        double a = elem_f64(vals, dt, (size_t)(i * vals_ld + g * N + s));
+        const double* brow = B + (g * M + j) * n;
+        for (int64_t c = 0; c < n; c++) acc[c] += a * brow[c];
+      }
+    for (int64_t c = 0; c < n; c++) D[i * n + c] = acc[c];
     free(acc);
   }
 }

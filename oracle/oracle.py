@@ -8,6 +8,8 @@ groups along k); for op_a == 'T' the stored k x m matrix is transposed here
 What is computed, and from which page:
   prune_1d      -- apex PR "[sparse] update support for arbitrary N:M settings
                    sparse", extension 1 (mn_1d_greedy): top-N |w| per group of M.
+  *_vw          -- the same PR, extension 2: vector-wise N:M (V rows share the
+                   kept offsets; vector score |sum of its values|).
   prune_tile    -- pytorch issue "backpropagation for sparse semi-structured",
                    maintainer reply: 2:4 in both directions on 4x4 tiles.
   check_*       -- cuSPARSELt blog, the prune-check snippet (non-zero = invalid).
@@ -64,6 +66,11 @@ def lib():
         L.or_gemm_i64.argtypes = [P, P, P, P, I64, I64, I64, I64, I64]
         L.or_threads.restype = I; L.or_threads.argtypes = []
         L.or_spmm_compressed_f64.argtypes = [P, I64, P, I64, I, I64, I64, I, I, P, I64, P, P, D, D]
+        L.or_prune_vw.argtypes = [P, I, I64, I64, I, I, I, P, P]
+        L.or_check_vw.restype = I64; L.or_check_vw.argtypes = [P, I, I64, I64, I, I, I]
+        L.or_compress_vw.argtypes = [P, I, I64, I64, I, I, I, P, I64, P, I64]
+        L.or_decompress_vw.argtypes = [P, I64, P, I64, I, I64, I64, I, I, I, P]
+        L.or_spmm_compressed_vw_f64.argtypes = [P, I64, P, I64, I, I64, I64, I, I, I, P, I64, P]
         _lib = L
     return _lib
 
@@ -191,6 +198,56 @@ def decompress(vals, meta, dtype, m, k, N, M, op="N"):
     out = np.empty((m, k), NP_RAW[dtype])
     lib().or_decompress(_ptr(vals), vals.shape[1], _ptr(meta), meta.shape[1], DT[dtype], m, k, N, M, _ptr(out))
     return _stored(out, op)
+
+
+# ---------------------------------------------------------------- vector-wise N:M
+
+def prune_vw(a, dtype, V, N, M):
+    """Vector-wise N:M on logical op(A) (m x k, m a multiple of V): every block of
+    V consecutive rows keeps, in each group of M columns, the N columns whose
+    score |sum of the V values| is largest (apex PR extension 2's vector score),
+    ties to the lower offset. Returns (pruned, keep mask as uint8)."""
+    x = _c(a, NP_RAW[dtype])
+    rows, cols = x.shape
+    assert rows % V == 0 and cols % M == 0
+    out = np.empty_like(x)
+    keep = np.empty(x.shape, np.uint8)
+    lib().or_prune_vw(_ptr(x), DT[dtype], rows, cols, V, N, M, _ptr(out), _ptr(keep))
+    return out, keep
+
+
+def check_vw(a, dtype, V, N, M):
+    """Number of (V-row block, group) pairs whose rows use more than N offsets."""
+    x = _c(a, NP_RAW[dtype])
+    return int(lib().or_check_vw(_ptr(x), DT[dtype], x.shape[0], x.shape[1], V, N, M))
+
+
+def compress_vw(a, dtype, V, N, M):
+    """Returns (values rows x values_ld, meta (rows / V) x meta_ld)."""
+    x = _c(a, NP_RAW[dtype])
+    rows, cols = x.shape
+    vld, mld = values_ld(cols, N, M, dtype), meta_ld(cols, N, M)
+    vals = np.empty((rows, vld), NP_RAW[dtype])
+    meta = np.empty((rows // V, mld), np.uint8)
+    lib().or_compress_vw(_ptr(x), DT[dtype], rows, cols, V, N, M, _ptr(vals), vld, _ptr(meta), mld)
+    return vals, meta
+
+
+def decompress_vw(vals, meta, dtype, m, k, V, N, M):
+    vals = _c(vals, NP_RAW[dtype]); meta = _c(meta, np.uint8)
+    out = np.empty((m, k), NP_RAW[dtype])
+    lib().or_decompress_vw(_ptr(vals), vals.shape[1], _ptr(meta), meta.shape[1], DT[dtype], m, k, V, N, M, _ptr(out))
+    return out
+
+
+def spmm_compressed_vw_f64(vals, meta, dtype, m, k, V, N, M, B):
+    """The sparse loop on the vector-wise form: D = A_hat @ B in fp64, reading (values, metadata)."""
+    vals = _c(vals, NP_RAW[dtype]); meta = _c(meta, np.uint8); B = _c(B, np.float64)
+    n = B.shape[1]
+    D = np.empty((m, n), np.float64)
+    lib().or_spmm_compressed_vw_f64(_ptr(vals), vals.shape[1], _ptr(meta), meta.shape[1], DT[dtype], m, k, V, N, M,
+                                    _ptr(B), n, _ptr(D))
+    return D
 
 
 # ---------------------------------------------------------------- products

@@ -16,7 +16,8 @@ MUTATIONS = [
      "while (b >= 0 && key[order[b]] < key[o])", "while (b >= 0 && key[order[b]] <= key[o])",
      lambda: pins.test_prune_1d_exhaustive_int8_small_values(2)),
     ("keeps the smallest magnitudes",
-     "for (int s = 0; s < N; s++) keep[order[s]] = 1;", "for (int s = 0; s < N; s++) keep[order[M - 1 - s]] = 1;",
+     "order[b + 1] = o;\n  }\n  memset(keep, 0, (size_t)M);\n  for (int s = 0; s < N; s++) keep[order[s]] = 1;",
+     "order[b + 1] = o;\n  }\n  memset(keep, 0, (size_t)M);\n  for (int s = 0; s < N; s++) keep[order[M - 1 - s]] = 1;",
      lambda: pins.test_prune_1d_equals_brute_force("f16", 4, (2,), 50, False)),
     ("tile score drops its last row",
      "double score = ((s[0] + s[1]) + s[2]) + s[3];", "double score = ((s[0] + s[1]) + s[2]);",
@@ -26,8 +27,8 @@ MUTATIONS = [
      "if (col[0] == 2 && col[1] == 2 && col[2] == 2 && col[3] == 2 && p0 <= p3) {",
      pins.test_exactly_90_transposable_patterns),
     ("metadata fields written most-significant bit first",
-     "for (int q = 0; q < b; q++) put_bit(mrow, t0 + q, (j >> q) & 1);",
-     "for (int q = 0; q < b; q++) put_bit(mrow, t0 + (b - 1 - q), (j >> q) & 1);",
+     "row, (size_t)(g * M + j), dt);\n        int64_t t0 = (g * N + s) * (int64_t)b;\n        for (int q = 0; q < b; q++) put_bit(mrow, t0 + q, (j >> q) & 1);",
+     "row, (size_t)(g * M + j), dt);\n        int64_t t0 = (g * N + s) * (int64_t)b;\n        for (int q = 0; q < b; q++) put_bit(mrow, t0 + (b - 1 - q), (j >> q) & 1);",
      lambda: pins.test_round_trips("f16", 2, 4, "N")),
     ("fp16 exponent bias off by one",
      "else v = ldexp((double)(f + 1024), e - 25);", "else v = ldexp((double)(f + 1024), e - 24);",
@@ -39,9 +40,24 @@ MUTATIONS = [
      "return (((const uint16_t*)p)[i] & 0x7FFFu) != 0;", "return ((const uint16_t*)p)[i] != 0;",
      pins.test_check_counts_injected_violations),
     ("decompress drops the last kept value of each group",
-     "for (int s = 0; s < N; s++) {\n        int64_t t0 = (g * N + s) * (int64_t)b;\n        int j = 0;\n        for (int q = 0; q < b; q++) j |= get_bit(mrow, t0 + q) << q;\n        copy_elem(",
-     "for (int s = 0; s < N - 1; s++) {\n        int64_t t0 = (g * N + s) * (int64_t)b;\n        int j = 0;\n        for (int q = 0; q < b; q++) j |= get_bit(mrow, t0 + q) << q;\n        copy_elem(",
+     "meta + r * meta_ld;\n    for (int64_t g = 0; g < cols / M; g++)\n      for (int s = 0; s < N; s++) {",
+     "meta + r * meta_ld;\n    for (int64_t g = 0; g < cols / M; g++)\n      for (int s = 0; s < N - 1; s++) {",
      lambda: pins.test_round_trips("bf16", 2, 4, "T")),
+    ("vector score sums magnitudes",
+     "for (int v = 0; v < V; v++) s += elem_f64(a, dt, (size_t)((r0 + v) * cols + c));",
+     "for (int v = 0; v < V; v++) s += fabs(elem_f64(a, dt, (size_t)((r0 + v) * cols + c)));",
+     pins.test_prune_vw_scores_the_signed_sum),
+    ("vector score skips the block's last row",
+     "for (int v = 0; v < V; v++) s += elem_f64(a, dt, (size_t)((r0 + v) * cols + c));",
+     "for (int v = 0; v < V - 1; v++) s += elem_f64(a, dt, (size_t)((r0 + v) * cols + c));",
+     lambda: pins.test_prune_vw_equals_brute_force("f16", 2, 4, (1, 2, 3), 60, False)),
+    ("vector ties go to the higher offset",
+     "while (y >= 0 && key[order[y]] < key[o])", "while (y >= 0 && key[order[y]] <= key[o])",
+     lambda: pins.test_prune_vw_equals_brute_force("i8", 2, 4, (1, 2, 3), 60, True)),
+    ("vector-wise compress writes the block's offsets into the wrong metadata field",
+     "        int64_t t0 = (g * N + s) * (int64_t)b;\n        for (int q = 0; q < b; q++) put_bit(mrow, t0 + q, (j >> q) & 1);\n        s++;\n      }\n    }\n  }\n}\n\nvoid or_decompress_vw",
+     "        int64_t t0 = (g * N + (N - 1 - s)) * (int64_t)b;\n        for (int q = 0; q < b; q++) put_bit(mrow, t0 + q, (j >> q) & 1);\n        s++;\n      }\n    }\n  }\n}\n\nvoid or_decompress_vw",
+     pins.test_compress_vw_hand_case),
 ]
 
 

@@ -488,3 +488,132 @@ def test_int8_output_saturates_the_exact_integer():
     c = np.array([[-100]], np.int8)
     assert oracle.gemm_i8_saturated(small, ones, 2, 1, c)[0, 0] == -90
     assert oracle.gemm_i8_saturated(small, ones, 1, 3, c)[0, 0] == -128
+
+
+# ------------------------------------------------------------------ vector-wise N:M
+
+def _vw_scores_exact(block, dtype):
+    """Exact |sum over the block's rows| per column (Fractions)."""
+    vals = oracle.decode(block, dtype)
+    return [abs(sum((Fraction(float(vals[r, j])) for r in range(vals.shape[0])), Fraction(0)))
+            for j in range(vals.shape[1])]
+
+
+def _vw_brute_force(block, dtype, N):
+    """argmax over all N-subsets of the exact summed vector scores; among equal
+    sums the lexicographically smallest index tuple (ties to the lower offset)."""
+    sc = _vw_scores_exact(block, dtype)
+    best, best_set = None, None
+    for sub in itertools.combinations(range(len(sc)), N):
+        s = sum((sc[i] for i in sub), Fraction(0))
+        if best is None or s > best:
+            best, best_set = s, sub
+    keep = np.zeros(len(sc), np.uint8)
+    keep[list(best_set)] = 1
+    return keep
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("V,M,Ns,blocks", [(2, 4, (1, 2, 3), 60), (4, 8, (1, 3, 5), 20), (16, 32, (1, 2, 4), 2),
+                                           (16, 4, (2,), 20)])
+@pytest.mark.parametrize("ties", [False, True])
+def test_prune_vw_equals_brute_force(dtype, V, M, Ns, blocks, ties):
+    g = _groups(dtype, M, V * blocks, seed=V * 13 + M + ties, ties=ties)       # (V*blocks) x M
+    for N in Ns:
+        _, keep = oracle.prune_vw(g, dtype, V, N, M)
+        for b in range(blocks):
+            blk = g[b * V:(b + 1) * V]
+            ref = _vw_brute_force(blk, dtype, N)
+            for r in range(V):
+                assert np.array_equal(keep[b * V + r], ref), (dtype, V, M, N, b, blk)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("N,M", [(2, 4), (4, 32), (3, 8)])
+def test_prune_vw_with_one_row_is_the_1d_rule(dtype, N, M):
+    """A vector of one element scores |w|: V = 1 is the element-wise rule."""
+    a = _groups(dtype, M, 40, seed=N + M, ties=True).reshape(10, 4 * M)
+    p1, k1 = oracle.prune_1d(a, dtype, N, M)
+    pv, kv = oracle.prune_vw(a, dtype, 1, N, M)
+    assert np.array_equal(k1, kv) and np.array_equal(p1, pv)
+
+
+def test_prune_vw_scores_the_signed_sum():
+    """The page's vector score is |sum|, not sum of |.|: a vector whose values
+    cancel scores zero. Rows (1, 3, -2, 0.5) and (-1, 0, 2, 0.5): scores 0, 3,
+    0, 1 keep offsets 1 and 3 (the sum of magnitudes 2, 3, 4, 1 would keep 1, 2)."""
+    a = np.array([[1, 3, -2, 0.5], [-1, 0, 2, 0.5]], np.float16).view(np.uint16)
+    p, keep = oracle.prune_vw(a, "f16", 2, 2, 4)
+    assert keep.tolist() == [[0, 1, 0, 1], [0, 1, 0, 1]]
+    assert p.view(np.float16).tolist() == [[0, 3, 0, 0.5], [0, 0, 0, 0.5]]
+
+
+@pytest.mark.parametrize("dtype,V,N,M", [("f16", 16, 4, 32), ("bf16", 16, 8, 32), ("i8", 32, 2, 4), ("f16", 64, 2, 8)])
+def test_prune_vw_invariants(dtype, V, N, M):
+    rows, k = 2 * V, 4 * M
+    a = (_groups(dtype, k, rows, seed=77, ties=False) if dtype != "i8"
+         else inputs.uniform_int((rows, k), 9, -127, 127))
+    p, keep = oracle.prune_vw(a, dtype, V, N, M)
+    kb = keep.reshape(rows // V, V, k)
+    assert (kb == kb[:, :1, :]).all()                               # a block's rows share the offsets
+    assert (keep.reshape(-1, M).sum(1) == N).all()
+    assert np.array_equal(p[keep == 1], a[keep == 1])
+    assert (p[keep == 0].view(np.uint8 if dtype == "i8" else np.uint16) == 0).all()
+    assert oracle.check_vw(p, dtype, V, N, M) == 0
+    p2, _ = oracle.prune_vw(p, dtype, V, N, M)
+    assert np.array_equal(p2, p)
+
+
+def test_check_vw_counts_blocks_using_too_many_offsets():
+    a = inputs.normal((32, 64), 5, 1.0, "f16")
+    p, keep = oracle.prune_vw(a, "f16", 16, 4, 32)
+    assert oracle.check_vw(p, "f16", 16, 4, 32) == 0
+    q = p.copy()
+    j = int(np.flatnonzero(keep[3, :32] == 0)[0])
+    q[3, j] = np.float16(0.25).view(np.uint16)                     # one row uses a fifth offset
+    assert oracle.check_vw(q, "f16", 16, 4, 32) == 1
+    q[20, 32 + int(np.flatnonzero(keep[20, 32:] == 0)[0])] = np.float16(1).view(np.uint16)
+    assert oracle.check_vw(q, "f16", 16, 4, 32) == 2
+    z = p.copy(); z[keep == 0] = np.float16(-0.0).view(np.uint16)   # -0 is zero
+    assert oracle.check_vw(z, "f16", 16, 4, 32) == 0
+
+
+def test_compress_vw_hand_case():
+    # V = 2, 2:4, k = 8, fp16. Block rows (1, 3, -2, 0.5 | 0, 0, 4, -4) and
+    # (-1, 0, 2, 0.5 | 0, 0, 4, 4): group 0 scores 0, 3, 0, 1 -> offsets 1, 3;
+    # group 1 scores 0, 0, 8, 0 -> offsets 2 and, among the tied zeros, 0.
+    a = np.array([[1, 3, -2, 0.5, 0, 0, 4, -4], [-1, 0, 2, 0.5, 0, 0, 4, 4]], np.float16).view(np.uint16)
+    v, meta = oracle.compress_vw(a, "f16", 2, 2, 4)
+    assert v.shape == (2, 8) and meta.shape == (1, 16)
+    assert v.view(np.float16)[:, :4].tolist() == [[3, 0.5, 0, 4], [0, 0.5, 0, 4]]
+    assert (v[:, 4:] == 0).all()
+    # one metadata row for the block: nibbles 1 | 3 << 2 = 0xD, then 0 | 2 << 2 = 0x8
+    assert meta[0, 0] == 0x8D and (meta[0, 1:] == 0).all()
+
+
+@pytest.mark.parametrize("dtype,V,N,M", [("f16", 16, 4, 32), ("bf16", 16, 2, 4), ("i8", 32, 8, 32), ("f16", 16, 3, 8)])
+def test_vw_round_trips(dtype, V, N, M):
+    rows, k = 2 * V, 3 * M * 2
+    a = (_groups(dtype, k, rows, seed=3, ties=True) if dtype != "i8"
+         else inputs.uniform_int((rows, k), 4, -3, 3))
+    p, _ = oracle.prune_vw(a, dtype, V, N, M)
+    v, meta = oracle.compress_vw(a, dtype, V, N, M)
+    assert np.array_equal(oracle.decompress_vw(v, meta, dtype, rows, k, V, N, M), p)
+    v2, m2 = oracle.compress_vw(oracle.decompress_vw(v, meta, dtype, rows, k, V, N, M), dtype, V, N, M)
+    assert np.array_equal(v2, v) and np.array_equal(m2, meta)
+    # compress(A) == compress(prune(A))
+    v3, m3 = oracle.compress_vw(p, dtype, V, N, M)
+    assert np.array_equal(v3, v) and np.array_equal(m3, meta)
+
+
+@pytest.mark.parametrize("dtype,V,N,M", [("f16", 16, 4, 32), ("bf16", 16, 8, 32), ("f16", 32, 2, 4)])
+def test_vw_sparse_loop_equals_dense_loop(dtype, V, N, M):
+    m, k, n = 2 * V, 4 * M, 24
+    a = inputs.normal((m, k), 8, 1.0, dtype)
+    b = inputs.normal((k, n), 9, 1.0, dtype)
+    p, _ = oracle.prune_vw(a, dtype, V, N, M)
+    v, meta = oracle.compress_vw(a, dtype, V, N, M)
+    B = oracle.decode(b, dtype)
+    dense = oracle.gemm_f64(oracle.decode(p, dtype), B)
+    sparse = oracle.spmm_compressed_vw_f64(v, meta, dtype, m, k, V, N, M, B)
+    assert np.array_equal(dense, sparse)
