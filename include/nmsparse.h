@@ -66,6 +66,22 @@
  * among equal magnitudes the lower offset wins (for fp16/bf16 the magnitude
  * order is the order of the bit pattern with the sign cleared, so +0 and -0
  * are equal). Exactly N slots are kept per group even when some are zero.
+ *
+ * Vector-wise N:M (vector_rows = V > 1; the apex pull request's extension 2,
+ * vector-wise N:M for nmSPARSE): the V consecutive rows bV .. bV+V-1 of op(A)
+ * share one set of kept offsets in every group. A vector is the V values of
+ * one column of such a block; its score is |v_0 + v_1 + ... + v_{V-1}| (the
+ * signed values summed first, as the pull request's vector-wise calculator
+ * does), accumulated in fp64 in increasing row order. In every group the N
+ * vectors of largest score are kept for all V rows, ties to the lower offset
+ * (scores compare as the bit patterns of the non-negative fp64 values, so a
+ * NaN score ranks above +Inf). The compressed values keep the element-wise
+ * layout (row r holds its own kept values); the metadata has one row per
+ * block: m / V rows of meta_ld bytes, block row b holding the element-wise
+ * bit stream of its offsets. Requires op_a = NM_OP_N (NM_ERR_UNSUPPORTED
+ * otherwise) and m % V == 0 (NM_ERR_SHAPE); the prune check counts the
+ * (block, group) pairs whose V rows hold non-zeros at more than N offsets;
+ * NM_PRUNE_TILE4X4 does not apply (NM_ERR_INVALID_ARG).
  */
 #ifndef NMSPARSE_H
 #define NMSPARSE_H
@@ -82,7 +98,7 @@ typedef enum {
   NM_ERR_INVALID_ARG = 1, /* null pointer, unknown enum, bad N:M, non-integral alpha/beta on the int path */
   NM_ERR_SHAPE = 2,       /* k % M != 0, tile mode on dims not divisible by 4, ld too small, size overflow */
   NM_ERR_ALIGN = 3,       /* pointer or leading dimension breaks the 16-byte rule */
-  NM_ERR_UNSUPPORTED = 4, /* valid request this build does not implement (reserved: no call returns it today) */
+  NM_ERR_UNSUPPORTED = 4, /* valid request this build does not implement (vector-wise N:M with op_a = T) */
   NM_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
 } nm_status_t;
 
@@ -105,7 +121,8 @@ typedef struct {
   int32_t type_ab, type_cd; /* nm_dtype_t pair, see above */
   int64_t lda, ldb, ldc, ldd;
   int32_t order_cd;         /* nm_order_t of C and D (both the same order) */
-  int32_t reserved;         /* must be 0 */
+  int32_t vector_rows;      /* V: 0 or 1 = element-wise N:M (every row of op(A) has its own kept offsets);
+                               V in {2, 4, ..., 256} (a power of two) = vector-wise N:M (see below) */
 } nm_problem_t;
 
 typedef struct nm_plan* nm_plan_t;
@@ -119,7 +136,8 @@ nm_status_t nm_plan_init(nm_plan_t* plan, const nm_problem_t* problem);
 nm_status_t nm_plan_destroy(nm_plan_t plan);
 
 /* Sizes of the compressed form of op(A) (the blog's compressed-size query):
- * values_bytes = m * values_ld * sizeof(type_ab); meta_bytes = m * meta_ld.
+ * values_bytes = m * values_ld * sizeof(type_ab); meta_bytes = (m / V) *
+ * meta_ld (V = vector_rows, 1 for element-wise N:M).
  * Any output pointer may be NULL. */
 nm_status_t nm_compressed_size(nm_plan_t plan, size_t* values_bytes, size_t* meta_bytes,
                                int64_t* values_ld_elems, int64_t* meta_ld_bytes);

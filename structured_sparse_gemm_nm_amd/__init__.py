@@ -38,7 +38,7 @@ class nm_problem_t(ctypes.Structure):
                 ("op_a", ctypes.c_int32), ("op_b", ctypes.c_int32),
                 ("type_ab", ctypes.c_int32), ("type_cd", ctypes.c_int32),
                 ("lda", ctypes.c_int64), ("ldb", ctypes.c_int64), ("ldc", ctypes.c_int64), ("ldd", ctypes.c_int64),
-                ("order_cd", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("order_cd", ctypes.c_int32), ("vector_rows", ctypes.c_int32)]
 
 
 _lib = None
@@ -162,8 +162,12 @@ class Plan:
         dt = TORCH_DTYPES[self.dtype]
         return torch.empty((self.m, self.values_ld), dtype=dt, device=device)
 
+    @property
+    def vector_rows(self):
+        return max(1, self.problem.vector_rows)
+
     def empty_meta(self, device="cuda"):
-        return torch.empty((self.m, self.meta_ld), dtype=torch.uint8, device=device)
+        return torch.empty((self.m // self.vector_rows, self.meta_ld), dtype=torch.uint8, device=device)
 
     def empty_workspace(self, device="cuda"):
         """Workspace nm_spmm needs for this plan's split-k setting (None when it needs none)."""
@@ -176,9 +180,10 @@ class Plan:
 
 
 def nm_plan_init(m, n, k, nm_n=2, nm_m=4, op_a="N", op_b="N", dtype="f16", lda=None, ldb=None, ldc=None, ldd=None,
-                 order_cd="row", out_dtype=None):
+                 order_cd="row", out_dtype=None, vector_rows=0):
     """Validate a problem and return a Plan (host only). order_cd: "row" or "col" (C and D storage).
-    out_dtype: C/D type when it differs from the default of `dtype` ("i8" with dtype "i8": saturated int8 D)."""
+    out_dtype: C/D type when it differs from the default of `dtype` ("i8" with dtype "i8": saturated int8 D).
+    vector_rows: V > 1 for vector-wise N:M (V consecutive rows share their kept offsets)."""
     ta, tc = DTYPES[dtype]
     if out_dtype is not None:
         tc = {"f16": NM_F16, "bf16": NM_BF16, "i8": NM_I8, "i32": NM_I32}[out_dtype]
@@ -196,7 +201,7 @@ def nm_plan_init(m, n, k, nm_n=2, nm_m=4, op_a="N", op_b="N", dtype="f16", lda=N
     cd_len = m if order_cd == "col" else n
     p.ldc = ldc if ldc is not None else max(1, cd_len)
     p.ldd = ldd if ldd is not None else max(1, cd_len)
-    p.order_cd, p.reserved = (1 if order_cd == "col" else 0), 0
+    p.order_cd, p.vector_rows = (1 if order_cd == "col" else 0), int(vector_rows)
     h = ctypes.c_void_p()
     _check(lib().nm_plan_init(ctypes.byref(h), ctypes.byref(p)))
     return Plan(h, p, dtype)

@@ -17,7 +17,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libnmsparse.so")
 CAL_LIB = os.path.join(HERE, "libnmcal.so")       # calibration loops for the benchmark (not the ABI)
-SOURCES = ["nm_api.hip", "nm_prune.hip", "nm_rows.hip", "nm_gemm.hip", "nm_gemm_f16.hip", "nm_gemm_bf16.hip", "nm_gemm_i8.hip",
+SOURCES = ["nm_api.hip", "nm_prune.hip", "nm_rows.hip", "nm_vw.hip", "nm_gemm.hip", "nm_gemm_f16.hip", "nm_gemm_bf16.hip",
+           "nm_gemm_i8.hip",
            "nm_skinny_f16.hip", "nm_skinny_bf16.hip", "nm_skinny_i8.hip"]
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")

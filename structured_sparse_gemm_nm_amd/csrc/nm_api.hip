@@ -88,8 +88,13 @@ nm_status_t nm_plan_init(nm_plan_t* plan, const nm_problem_t* p) {
   if (!pair_ok) return fail(NM_ERR_INVALID_ARG, "type pair must be (F16,F16), (BF16,BF16), (I8,I32) or (I8,I8)");
   if (p->order_cd != NM_ROW_MAJOR && p->order_cd != NM_COL_MAJOR)
     return fail(NM_ERR_INVALID_ARG, "order_cd must be NM_ROW_MAJOR or NM_COL_MAJOR");
-  if (p->reserved != 0) return fail(NM_ERR_INVALID_ARG, "reserved must be 0");
+  const int V = p->vector_rows <= 1 ? 1 : p->vector_rows;
+  if (p->vector_rows < 0 || p->vector_rows > 256 || (V & (V - 1)) != 0)
+    return fail(NM_ERR_INVALID_ARG, "vector_rows must be 0, 1 or a power of two up to 256");
   if (p->k % M != 0) return fail(NM_ERR_SHAPE, "k must be a multiple of M");
+  if (V > 1 && p->op_a != NM_OP_N)
+    return fail(NM_ERR_UNSUPPORTED, "vector-wise N:M takes op_a = NM_OP_N (blocks of rows of the stored A)");
+  if (V > 1 && p->m % V != 0) return fail(NM_ERR_SHAPE, "vector-wise N:M needs m to be a multiple of vector_rows");
   const int ea = esize(p->type_ab), ec = esize(p->type_cd);
   const int64_t a_rows = p->op_a == NM_OP_N ? p->m : p->k;
   const int64_t a_cols = p->op_a == NM_OP_N ? p->k : p->m;
@@ -120,6 +125,9 @@ nm_status_t nm_plan_init(nm_plan_t* plan, const nm_problem_t* p) {
   int b = 0;
   while ((1 << b) < M) b++;
   pl->bits = b;
+  pl->vrows = V;
+  pl->vshift = 0;
+  while ((1 << pl->vshift) < V) pl->vshift++;
   const int64_t per16 = 16 / ea;
   const int64_t nvals = p->k / M * N;
   pl->vld = (nvals + per16 - 1) / per16 * per16;
@@ -134,6 +142,7 @@ nm_status_t nm_plan_init(nm_plan_t* plan, const nm_problem_t* p) {
   pl->tile_elemwise = getenv("NM_TILE_ELEMWISE") != nullptr;
   // kernel choice
   if (p->n <= 16) pl->kernel = K_SKINNY;
+  else if (V > 1) pl->kernel = nm::vw_mfma_ok(*pl) ? K_VW_MFMA : K_GATHER_MFMA;
   else if (N == 2 && M == 4) pl->kernel = K_SMFMAC_24;
   else pl->kernel = K_GATHER_MFMA;
   *plan = pl;
@@ -155,6 +164,7 @@ const char* nm_plan_spmm_kernel(nm_plan_t plan) {
     switch (plan->kernel) {
       case K_SMFMAC_24: (void)launch_spmm_smfmac(*plan, 1.0f, nullptr, nullptr, nullptr, 0.0f, nullptr, nullptr, nullptr, 0); break;
       case K_GATHER_MFMA: (void)launch_spmm_gather(*plan, 1.0f, nullptr, nullptr, nullptr, 0.0f, nullptr, nullptr, 0); break;
+      case K_VW_MFMA: (void)launch_spmm_vw(*plan, 1.0f, nullptr, nullptr, nullptr, 0.0f, nullptr, nullptr, 0); break;
       default: (void)launch_spmm_skinny(*plan, 1.0f, nullptr, nullptr, nullptr, 0.0f, nullptr, nullptr, 0); break;
     }
     pr.armed = false;
@@ -217,6 +227,7 @@ const char* nm_plan_kernel_name(nm_plan_t plan) {
   switch (plan->kernel) {
     case K_SMFMAC_24: return "spmm_smfmac_2of4";
     case K_GATHER_MFMA: return "spmm_gather_mfma";
+    case K_VW_MFMA: return "spmm_vw_mfma";
     case K_SKINNY: return "spmm_skinny";
   }
   return "none";
@@ -226,7 +237,7 @@ nm_status_t nm_compressed_size(nm_plan_t plan, size_t* values_bytes, size_t* met
                                int64_t* meta_ld) {
   if (!plan) return fail(NM_ERR_INVALID_ARG, "plan is NULL");
   if (values_bytes) *values_bytes = (size_t)(plan->p.m * plan->vld * plan->esz_ab);
-  if (meta_bytes) *meta_bytes = (size_t)(plan->p.m * plan->mld);
+  if (meta_bytes) *meta_bytes = (size_t)((plan->p.m / plan->vrows) * plan->mld);
   if (values_ld) *values_ld = plan->vld;
   if (meta_ld) *meta_ld = plan->mld;
   return NM_OK;
@@ -243,6 +254,7 @@ nm_status_t nm_mask_size(nm_plan_t plan, size_t* mask_bytes, int64_t* mask_ld_wo
 static nm_status_t check_mode(const nm_plan* plan, int32_t mode) {
   if (mode != NM_PRUNE_1D && mode != NM_PRUNE_TILE4X4) return fail(NM_ERR_INVALID_ARG, "unknown prune mode");
   if (mode == NM_PRUNE_TILE4X4) {
+    if (plan->vrows > 1) return fail(NM_ERR_INVALID_ARG, "tile mode is element-wise (vector_rows must be 0 or 1)");
     if (!(plan->p.nm_n == 2 && plan->p.nm_m == 4)) return fail(NM_ERR_INVALID_ARG, "tile mode needs N:M = 2:4");
     if (plan->a_rows % 4 || plan->a_cols % 4) return fail(NM_ERR_SHAPE, "tile mode needs both stored dims % 4 == 0");
   }
@@ -260,6 +272,7 @@ nm_status_t nm_prune(nm_plan_t plan, const void* dA, void* dA_pruned, int32_t mo
   if (empty) return NM_OK;
   hipStream_t s = (hipStream_t)stream;
   if (mode == NM_PRUNE_TILE4X4) return hip_status(launch_prune_tile(*plan, dA, dA_pruned, d_mask, s), "prune (tile)");
+  if (plan->vrows > 1) return hip_status(launch_vw_prune(*plan, dA, dA_pruned, d_mask, s), "prune (vector-wise)");
   return hip_status(launch_prune_1d(*plan, dA, dA_pruned, d_mask, s), "prune (1-D)");
 }
 
@@ -272,6 +285,7 @@ nm_status_t nm_prune_check(nm_plan_t plan, const void* dA, int32_t mode, int32_t
   if (!empty && !dA) return fail(NM_ERR_INVALID_ARG, "dA is NULL");
   if (!aligned16(dA)) return fail(NM_ERR_ALIGN, "dA must be 16-byte aligned");
   if (((uintptr_t)d_violations & 3u) != 0) return fail(NM_ERR_ALIGN, "d_violations must be 4-byte aligned");
+  if (plan->vrows > 1) return hip_status(launch_vw_check(*plan, dA, d_violations, (hipStream_t)stream), "prune check");
   return hip_status(launch_check(*plan, dA, mode, d_violations, (hipStream_t)stream), "prune check");
 }
 
@@ -282,6 +296,7 @@ nm_status_t nm_compress(nm_plan_t plan, const void* dA, void* d_values, void* d_
   if (!aligned16(dA) || !aligned16(d_values) || !aligned16(d_meta))
     return fail(NM_ERR_ALIGN, "device pointers must be 16-byte aligned");
   if (empty) return NM_OK;
+  if (plan->vrows > 1) return hip_status(launch_vw_compress(*plan, dA, d_values, d_meta, (hipStream_t)stream), "compress");
   return hip_status(launch_compress(*plan, dA, d_values, d_meta, (hipStream_t)stream), "compress");
 }
 
@@ -292,6 +307,8 @@ nm_status_t nm_decompress(nm_plan_t plan, const void* d_values, const void* d_me
   if (!aligned16(dA_out) || !aligned16(d_values) || !aligned16(d_meta))
     return fail(NM_ERR_ALIGN, "device pointers must be 16-byte aligned");
   if (empty) return NM_OK;
+  if (plan->vrows > 1)
+    return hip_status(launch_vw_decompress(*plan, d_values, d_meta, dA_out, (hipStream_t)stream), "decompress");
   return hip_status(launch_decompress(*plan, d_values, d_meta, dA_out, (hipStream_t)stream), "decompress");
 }
 
@@ -338,6 +355,7 @@ nm_status_t nm_spmm(nm_plan_t plan, const float* alpha, const void* d_values, co
       e = launch_spmm_smfmac(*plan, *alpha, d_values, d_meta, dB, *beta, dC, dD, ws_bytes ? d_workspace : nullptr, s);
       break;
     case K_GATHER_MFMA: e = launch_spmm_gather(*plan, *alpha, d_values, d_meta, dB, *beta, dC, dD, s); break;
+    case K_VW_MFMA: e = launch_spmm_vw(*plan, *alpha, d_values, d_meta, dB, *beta, dC, dD, s); break;
     default: e = launch_spmm_skinny(*plan, *alpha, d_values, d_meta, dB, *beta, dC, dD, s); break;
   }
   return hip_status(e, "spmm");

@@ -4,6 +4,7 @@
 // element type in nm_gemm_{f16,bf16,i8}.hip and nm_skinny_{f16,bf16,i8}.hip.
 #include "nm_gemm_kernels.h"
 #include "nm_skinny_kernels.h"
+#include "nm_vw_kernels.h"
 
 namespace nm {
 
@@ -60,7 +61,7 @@ __global__ void __launch_bounds__(NTH) skinny_kernel(GemmArgs A, int b_op_t, int
       } else {
         const int gps = kn / A.M;
         const int64_t g0 = kc / A.M;
-        const uint8_t* mrow = A.meta + row * A.mld;
+        const uint8_t* mrow = A.meta + (row >> A.vshift) * A.mld;
         for (int g = lane; g < gps; g += 64) {
           for (int s = 0; s < A.N; s++) {
             const int64_t slot = (g0 + g) * A.N + s;
@@ -118,6 +119,7 @@ static GemmArgs make_gemm_args(const nm_plan& pl, float alpha, const void* a, co
   A.N = pl.p.nm_n; A.M = pl.p.nm_m; A.bits = pl.bits;
   A.a_vec = (A.lda * pl.esz_ab) % 16 == 0;
   A.b_vec = (A.ldb * pl.esz_ab) % 16 == 0;
+  A.vshift = pl.vshift;
   A.splits = 1;
   A.ws = nullptr;
   return A;
@@ -187,6 +189,30 @@ hipError_t launch_spmm_smfmac(const nm_plan& pl, float alpha, const void* vals, 
   A.splits = spmm_splits(pl);
   A.ws = (uint8_t*)ws;
   return launch_tiles_any(pl, A_SPARSE24, A, s);
+}
+
+// The vector-wise matrix-core kernel: blocks of 16 rows share their offsets
+// (vrows a multiple of 16), B stored k x n, whole 256 x 128 tiles and k-steps,
+// N a power of two with k-step x N / M kept k per step in its instantiated set,
+// 16-byte rows, operands addressable with 32-bit offsets.
+bool vw_mfma_ok(const nm_plan& pl) {
+  const nm_problem_t& p = pl.p;
+  if (pl.vrows < 16 || pl.vrows % 16 || p.op_a != NM_OP_N || p.op_b != NM_OP_N || vw_kp(pl) == 0) return false;
+  const int64_t ks = 256 / pl.esz_ab;
+  if (p.m % VW_BM || p.n % VW_BN || p.k % ks || p.k == 0 || (p.ldb * pl.esz_ab) % 16) return false;
+  const int64_t lim = (int64_t)1 << 31;
+  return p.k * p.ldb * pl.esz_ab < lim && p.m * pl.vld * pl.esz_ab < lim && (p.m / pl.vrows) * pl.mld < lim;
+}
+
+hipError_t launch_spmm_vw(const nm_plan& pl, float alpha, const void* vals, const void* meta, const void* b,
+                          float beta, const void* c, void* d, hipStream_t s) {
+  const GemmArgs A = make_gemm_args(pl, alpha, vals, meta, b, beta, c, d, false);
+  if (!vw_mfma_ok(pl)) return hipErrorInvalidValue;
+  switch (pl.p.type_ab) {
+    case NM_F16: return launch_vw_f16(pl, A, s);
+    case NM_BF16: return launch_vw_bf16(pl, A, s);
+    default: return launch_vw_i8(pl, A, s);
+  }
 }
 
 hipError_t launch_spmm_gather(const nm_plan& pl, float alpha, const void* vals, const void* meta, const void* b,

@@ -68,6 +68,7 @@ struct GemmArgs {
   float alpha, beta;
   int N, M, bits;
   int a_vec, b_vec;     // 16-byte vector loads allowed on A / B rows
+  int vshift;           // metadata row of op(A) row r: r >> vshift (0: element-wise; vector-wise N:M shares a row per 2^vshift rows)
   int splits;           // split-k: k ranges (1 = none); with more, each block writes raw partial sums to ws
   uint8_t* ws;          // splits planes of m x n fp32 (int32 for int8) partial sums, in D's storage order
 };
@@ -289,7 +290,7 @@ __device__ __forceinline__ void stage_gather(uint8_t* stg, const GemmArgs& A, in
       *(uint32_t*)(stg + r * STG_V + c * 4) = val;
     } else {
       const int64_t w = w0 + (c - vw);
-      if (gr < A.m && w < row_mwords) val = *(const uint32_t*)(A.meta + gr * A.mld + w * 4);
+      if (gr < A.m && w < row_mwords) val = *(const uint32_t*)(A.meta + (gr >> A.vshift) * A.mld + w * 4);
       *(uint32_t*)(stg + ROWS * STG_V + r * STG_M + (c - vw) * 4) = val;
     }
   }
@@ -360,7 +361,7 @@ __device__ __forceinline__ void load_g32(G32Regs<ESZ, ROWS, GV>& R, const GemmAr
       R.v[i][0] = *(const uint32_t*)pv;
     }
     const int64_t w0 = (gg * G::NV * 5) >> 5;                  // the group's bits end inside the row
-    const uint32_t* mr = (const uint32_t*)(A.meta + row * A.mld);
+    const uint32_t* mr = (const uint32_t*)(A.meta + (row >> A.vshift) * A.mld);
 #pragma unroll
     for (int x = 0; x < G::MW; x++) R.m[i][x] = mr[w0 + x < mwords ? w0 + x : mwords - 1];
   }

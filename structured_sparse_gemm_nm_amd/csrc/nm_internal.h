@@ -14,6 +14,8 @@ struct nm_plan {
   int64_t a_rows;       // stored A rows  (m for op N, k for op T)
   int64_t a_cols;       // stored A cols  (k for op N, m for op T)
   int bits;             // metadata bits per kept element: ceil(log2 M)
+  int vrows;            // rows of op(A) sharing one kept-offset set (1: element-wise N:M; >1: vector-wise)
+  int vshift;           // log2(vrows): metadata row of op(A) row r is r >> vshift
   int64_t vld;          // values row stride (elements)
   int64_t mld;          // metadata row stride (bytes)
   int kernel;           // SpMM kernel id (nm::KernelId)
@@ -35,6 +37,7 @@ enum KernelId {
   K_SMFMAC_24 = 1,      // 2:4 on the sparse matrix instructions
   K_GATHER_MFMA = 2,    // general N:M: A expanded in registers, dense MFMA
   K_SKINNY = 3,         // small n: streamed A, B in LDS, VALU gather
+  K_VW_MFMA = 4,        // vector-wise N:M: B rows gathered per 16-row block, dense MFMA on the kept k
 };
 
 void set_error(const std::string& msg);
@@ -87,6 +90,15 @@ hipError_t launch_compress(const nm_plan& pl, const void* a, void* vals, void* m
 hipError_t launch_decompress(const nm_plan& pl, const void* vals, const void* meta, void* out, hipStream_t s);
 hipError_t launch_spmm_smfmac(const nm_plan& pl, float alpha, const void* vals, const void* meta,
                               const void* b, float beta, const void* c, void* d, void* ws, hipStream_t s);
+// vector-wise N:M (vrows > 1, op_a = N): prune, check, compress, decompress
+hipError_t launch_vw_prune(const nm_plan& pl, const void* a, void* out, uint32_t* mask, hipStream_t s);
+hipError_t launch_vw_check(const nm_plan& pl, const void* a, int32_t* count, hipStream_t s);
+hipError_t launch_vw_compress(const nm_plan& pl, const void* a, void* vals, void* meta, hipStream_t s);
+hipError_t launch_vw_decompress(const nm_plan& pl, const void* vals, const void* meta, void* out, hipStream_t s);
+// whether the vector-wise matrix-core product takes this plan (whole tiles, B stored k x n, ...)
+bool vw_mfma_ok(const nm_plan& pl);
+hipError_t launch_spmm_vw(const nm_plan& pl, float alpha, const void* vals, const void* meta, const void* b,
+                          float beta, const void* c, void* d, hipStream_t s);
 hipError_t launch_spmm_gather(const nm_plan& pl, float alpha, const void* vals, const void* meta,
                               const void* b, float beta, const void* c, void* d, hipStream_t s);
 hipError_t launch_spmm_skinny(const nm_plan& pl, float alpha, const void* vals, const void* meta,

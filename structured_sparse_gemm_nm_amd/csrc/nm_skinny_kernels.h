@@ -116,7 +116,7 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
       // the group's bits end inside the row's stream, so clamping the word
       // index only ever replaces words that are not used
       const int64_t w0 = (gg * NV * b) >> 5;
-      const uint32_t* mr = (const uint32_t*)(A.meta + row * A.mld);
+      const uint32_t* mr = (const uint32_t*)(A.meta + (row >> A.vshift) * A.mld);
 #pragma unroll
       for (int x = 0; x < MW; x++) pc.m[x] = mr[w0 + x < mwords ? w0 + x : mwords - 1];
     }

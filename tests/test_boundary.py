@@ -71,8 +71,15 @@ def test_plan_init_rejects_bad_type_pair_and_order():
     p.order_cd = 2
     assert nm.lib().nm_plan_init(ctypes.byref(h), ctypes.byref(p)) == nm.NM_ERR_INVALID_ARG
     p.order_cd = 0
-    p.reserved = 7
+    p.vector_rows = 7                                        # not a power of two
     assert nm.lib().nm_plan_init(ctypes.byref(h), ctypes.byref(p)) == nm.NM_ERR_INVALID_ARG
+    p.vector_rows = 512                                      # above 256
+    assert nm.lib().nm_plan_init(ctypes.byref(h), ctypes.byref(p)) == nm.NM_ERR_INVALID_ARG
+    p.vector_rows = 32                                       # m = 16 is not a multiple of 32
+    assert nm.lib().nm_plan_init(ctypes.byref(h), ctypes.byref(p)) == nm.NM_ERR_SHAPE
+    p.vector_rows, p.op_a, p.lda = 16, nm.NM_OP_T, 16        # vector-wise needs op_a = N
+    assert nm.lib().nm_plan_init(ctypes.byref(h), ctypes.byref(p)) == nm.NM_ERR_UNSUPPORTED
+    p.vector_rows, p.op_a = 0, nm.NM_OP_N
     assert nm.lib().nm_plan_init(None, ctypes.byref(p)) == nm.NM_ERR_INVALID_ARG
     assert nm.lib().nm_plan_init(ctypes.byref(h), None) == nm.NM_ERR_INVALID_ARG
 
