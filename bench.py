@@ -48,6 +48,8 @@ WORKLOAD_SETS = {
     "x2": [("n1", "x2_4of32_n1"), ("n8", "x2_4of32_n8")],
     "c5_4of32": [("n1", "c5_4of32_n1"), ("n8", "c5_4of32_n8"), ("n4096", "c5_4of32_n4096")],
     "c5_8of32": [("n1", "c5_8of32_n1"), ("n8", "c5_8of32_n8"), ("n4096", "c5_8of32_n4096")],
+    "vw_4of32": [("n1", "c5vw_4of32_n1"), ("n8", "c5vw_4of32_n8"), ("n4096", "c5vw_4of32_n4096")],
+    "vw_8of32": [("n1", "c5vw_8of32_n1"), ("n8", "c5vw_8of32_n8"), ("n4096", "c5vw_8of32_n4096")],
 }
 WORKLOAD_DESC = {
     "bert": "BERT-Large GEMMs (FC1 4096x1024, FC2 1024x4096, PROJ 1024x1024 weights, 4096 tokens), fp16 2:4, NT+NN",
@@ -63,6 +65,8 @@ WORKLOAD_DESC = {
           "weights, 16384 tokens, fp16 2:4, NT, D column-major as in the blog",
     "c5_4of32": "fp16 4:32, A 4096x4096, B 4096 x {1, 8, 4096}, NN",
     "c5_8of32": "fp16 8:32, A 4096x4096, B 4096 x {1, 8, 4096}, NN",
+    "vw_4of32": "fp16 vector-wise 4:32 (16 rows share each group's offsets), A 4096x4096, B 4096 x {1, 8, 4096}, NN",
+    "vw_8of32": "fp16 vector-wise 8:32 (16 rows share each group's offsets), A 4096x4096, B 4096 x {1, 8, 4096}, NN",
 }
 
 
@@ -155,9 +159,12 @@ def main():
         mode = "tile" if w.get("tile") else "1d"
         g = dict(label=label, name=wname, w=w, dtype=dtype, m=m, n=n, k=k, N=N, M=M, mode=mode, op_a=op_a)
         order = "col" if args.workload == "linear" else w.get("order_cd", "row")
-        g["plan"] = nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=layouts[0], dtype=dtype, order_cd=order)
-        g["plans"] = {ob: nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=ob, dtype=dtype, order_cd=order)
-                      for ob in layouts}
+        vr = w.get("vector_rows", 0)
+        g["vrows"] = max(1, vr)
+        g["plan"] = nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=layouts[0], dtype=dtype, order_cd=order,
+                                    vector_rows=vr)
+        g["plans"] = {ob: nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=ob, dtype=dtype, order_cd=order,
+                                          vector_rows=vr) for ob in layouts}
         g["A"] = to_dev(a)
         g["Ap"] = torch.empty_like(g["A"])
         g["Ad"] = torch.empty_like(g["A"])
@@ -374,6 +381,9 @@ def main():
     roofline["kernel"] = dom_key
     roofline["work_counted"] = ("dense multiply-adds of the expanded tile (2 m n k), executed on the dense matrix "
                                 "instructions" if kname == "spmm_gather_mfma" else
+                                "multiply-adds of the kept values (2 m n k N/M), executed on the dense matrix "
+                                "instructions over the gathered rows of B, against the dense matrix peak"
+                                if kname == "spmm_vw_mfma" else
                                 "multiply-adds of the kept values (2 m n k N/M) against the dense matrix peak, the same "
                                 "ratio as dense-equivalent flops against the 2:4 peak" if roofline["bound"] == "mfma"
                                 else "compressed A + metadata + B + D (+ C) bytes per launch")
@@ -762,13 +772,21 @@ def cpu_baseline(gemms):
         for g in gemms:
             dtype, N, M = g["dtype"], g["N"], g["M"]
             a = g["host"]["a"]
+            V = g["vrows"]
             if g["mode"] == "tile":
                 p, _ = oracle.prune_tile(a, dtype)
+            elif V > 1:
+                p, _ = oracle.prune_vw(a, dtype, V, N, M)
             else:
                 p, _ = oracle.prune_1d(a, dtype, N, M, g["op_a"])
-            oracle.check_1d(p, dtype, N, M, g["op_a"])
-            v, meta = oracle.compress(p, dtype, N, M, g["op_a"])
-            ahat = oracle.decompress(v, meta, dtype, g["m"], g["k"], N, M, g["op_a"])
+            if V > 1:
+                oracle.check_vw(p, dtype, V, N, M)
+                v, meta = oracle.compress_vw(p, dtype, V, N, M)
+                ahat = oracle.decompress_vw(v, meta, dtype, g["m"], g["k"], V, N, M)
+            else:
+                oracle.check_1d(p, dtype, N, M, g["op_a"])
+                v, meta = oracle.compress(p, dtype, N, M, g["op_a"])
+                ahat = oracle.decompress(v, meta, dtype, g["m"], g["k"], N, M, g["op_a"])
             ahat_log = ahat if g["op_a"] == "N" else np.ascontiguousarray(ahat.T)
             rows = max(1, int(round(g["m"] * frac)))      # the product on the first rows only
             for ob in g["layouts"]:

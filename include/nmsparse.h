@@ -164,6 +164,13 @@ nm_status_t nm_mask_size(nm_plan_t plan, size_t* mask_bytes, int64_t* mask_ld_wo
 nm_status_t nm_prune(nm_plan_t plan, const void* dA, void* dA_pruned, int32_t mode,
                      uint32_t* d_mask, void* stream);
 
+/* Apply a keep mask written by nm_prune to another matrix of the stored A's
+ * shape and leading dimension (lda): elements whose bit is clear become +0,
+ * the others are left as they are. This masks a gradient with the sparsity
+ * pattern of the weight it belongs to (the pytorch issue's sparse training
+ * setting: the masked weight gradient keeps the pruned weights at zero). */
+nm_status_t nm_mask_apply(nm_plan_t plan, const uint32_t* d_mask, void* dX, void* stream);
+
 /* Conformance check (the blog's prune check, with its flag made a count):
  * writes to *d_violations (device int32) the number of groups of op(A) that
  * hold more than N non-zeros (1-D), or the number of 4x4-tile rows plus
@@ -239,6 +246,19 @@ enum { NM_ALG_AUTO = 0, NM_ALG_TILE128 = 1, NM_ALG_TILE256X128 = 2, NM_ALG_TILE2
 int32_t nm_plan_algorithm_count(nm_plan_t plan);   /* NM_ALG_COUNT (0 for a NULL plan) */
 nm_status_t nm_plan_set_algorithm(nm_plan_t plan, int32_t alg);
 nm_status_t nm_plan_get_algorithm(nm_plan_t plan, int32_t* alg);
+
+/* nm_spmm over several streams (the blog's matmul takes an array of streams):
+ * the rows of D are split into at most num_streams blocks of whole 256-row
+ * multiples, and block i is enqueued on streams[i] as its own product (the
+ * same kernels nm_spmm picks for a problem of that many rows; a split-k
+ * plan's workspace is shared out between the blocks, so the workspace size is
+ * the plan's). The caller orders the streams after the call (each stream's
+ * work is independent). num_streams in [1, 64]; 1 is nm_spmm on streams[0].
+ * Results equal nm_spmm's up to fp32 summation order (bit-identical for int8).
+ * Errors and arguments as nm_spmm. */
+nm_status_t nm_spmm_streams(nm_plan_t plan, const float* alpha, const void* d_values, const void* d_meta,
+                            const void* dB, const float* beta, const void* dC, void* dD, void* d_workspace,
+                            void* const* streams, int32_t num_streams);
 
 /* Split-k: the blog's split-k setting of the algorithm selection, with the
  * workspace its matmul call takes (the workspace-size query and the

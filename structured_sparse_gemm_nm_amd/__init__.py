@@ -61,6 +61,7 @@ def lib():
         L.nm_mask_size.restype = st; L.nm_mask_size.argtypes = [P, ctypes.POINTER(S), ctypes.POINTER(I64)]
         L.nm_prune.restype = st; L.nm_prune.argtypes = [P, P, P, I32, P, P]
         L.nm_prune_check.restype = st; L.nm_prune_check.argtypes = [P, P, I32, P, P]
+        L.nm_mask_apply.restype = st; L.nm_mask_apply.argtypes = [P, P, P, P]
         L.nm_compress.restype = st; L.nm_compress.argtypes = [P, P, P, P, P]
         L.nm_decompress.restype = st; L.nm_decompress.argtypes = [P, P, P, P, P]
         FP = ctypes.POINTER(ctypes.c_float)
@@ -76,6 +77,8 @@ def lib():
         L.nm_plan_get_split_k.argtypes = [P, ctypes.POINTER(I32), ctypes.POINTER(I32)]
         L.nm_spmm_workspace_size.restype = st; L.nm_spmm_workspace_size.argtypes = [P, ctypes.POINTER(S)]
         L.nm_spmm_noalloc.restype = st; L.nm_spmm_noalloc.argtypes = [P, FP, P, P, P, FP, P, P, P]
+        L.nm_spmm_streams.restype = st
+        L.nm_spmm_streams.argtypes = [P, FP, P, P, P, FP, P, P, P, ctypes.POINTER(P), I32]
         L.nm_status_string.restype = ctypes.c_char_p; L.nm_status_string.argtypes = [st]
         L.nm_last_error.restype = ctypes.c_char_p; L.nm_last_error.argtypes = []
         L.nm_version.restype = I32; L.nm_version.argtypes = []
@@ -223,6 +226,10 @@ def nm_prune(plan, dA, dA_pruned, mode="1d", d_mask=None, stream=None):
     _check(lib().nm_prune(plan.handle, _ptr(dA), _ptr(dA_pruned), MODES[mode], _ptr(d_mask), _stream(stream)))
 
 
+def nm_mask_apply(plan, d_mask, dX, stream=None):
+    _check(lib().nm_mask_apply(plan.handle, _ptr(d_mask), _ptr(dX), _stream(stream)))
+
+
 def nm_prune_check(plan, dA, mode, d_violations, stream=None):
     _check(lib().nm_prune_check(plan.handle, _ptr(dA), MODES[mode], _ptr(d_violations), _stream(stream)))
 
@@ -240,6 +247,14 @@ def nm_spmm(plan, alpha, d_values, d_meta, dB, beta, dC, dD, stream=None, worksp
     a, b = ctypes.c_float(alpha), ctypes.c_float(beta)
     _check(lib().nm_spmm(plan.handle, ctypes.byref(a), _ptr(d_values), _ptr(d_meta), _ptr(dB), ctypes.byref(b),
                          _ptr(dC), _ptr(dD), _ptr(workspace), _stream(stream)))
+
+
+def nm_spmm_streams(plan, alpha, d_values, d_meta, dB, beta, dC, dD, streams, workspace=None):
+    """nm_spmm with the rows of D split over `streams` (torch streams or raw handles)."""
+    a, b = ctypes.c_float(alpha), ctypes.c_float(beta)
+    arr = (ctypes.c_void_p * len(streams))(*[_stream(s_).value for s_ in streams])
+    _check(lib().nm_spmm_streams(plan.handle, ctypes.byref(a), _ptr(d_values), _ptr(d_meta), _ptr(dB), ctypes.byref(b),
+                                 _ptr(dC), _ptr(dD), _ptr(workspace), arr, len(streams)))
 
 
 NM_NOALLOC_SCRATCH_BYTES = 32 << 20

@@ -49,6 +49,15 @@ static bool ld_ok(int64_t row_elems, int64_t ld, int es) {
 
 static const int64_t kMaxElems = (int64_t)1 << 46;
 
+// The SpMM path a plan takes (from its shape alone).
+static void choose_kernel(nm_plan& pl) {
+  const nm_problem_t& p = pl.p;
+  if (p.n <= 16) pl.kernel = K_SKINNY;
+  else if (pl.vrows > 1) pl.kernel = vw_mfma_ok(pl) ? K_VW_MFMA : K_GATHER_MFMA;
+  else if (p.nm_n == 2 && p.nm_m == 4) pl.kernel = K_SMFMAC_24;
+  else pl.kernel = K_GATHER_MFMA;
+}
+
 }  // namespace nm
 
 using namespace nm;
@@ -140,11 +149,7 @@ nm_status_t nm_plan_init(nm_plan_t* plan, const nm_problem_t* p) {
   // compress / decompress even where the register path applies (read once
   // here; the parity tests use it to run both paths on the same inputs)
   pl->tile_elemwise = getenv("NM_TILE_ELEMWISE") != nullptr;
-  // kernel choice
-  if (p->n <= 16) pl->kernel = K_SKINNY;
-  else if (V > 1) pl->kernel = nm::vw_mfma_ok(*pl) ? K_VW_MFMA : K_GATHER_MFMA;
-  else if (N == 2 && M == 4) pl->kernel = K_SMFMAC_24;
-  else pl->kernel = K_GATHER_MFMA;
+  choose_kernel(*pl);
   *plan = pl;
   set_error("");
   return NM_OK;
@@ -276,6 +281,15 @@ nm_status_t nm_prune(nm_plan_t plan, const void* dA, void* dA_pruned, int32_t mo
   return hip_status(launch_prune_1d(*plan, dA, dA_pruned, d_mask, s), "prune (1-D)");
 }
 
+nm_status_t nm_mask_apply(nm_plan_t plan, const uint32_t* d_mask, void* dX, void* stream) {
+  if (!plan) return fail(NM_ERR_INVALID_ARG, "plan is NULL");
+  const bool empty = plan->a_rows == 0 || plan->a_cols == 0;
+  if (!empty && (!d_mask || !dX)) return fail(NM_ERR_INVALID_ARG, "d_mask / dX is NULL");
+  if (!aligned16(d_mask) || !aligned16(dX)) return fail(NM_ERR_ALIGN, "device pointers must be 16-byte aligned");
+  if (empty) return NM_OK;
+  return hip_status(launch_mask_apply(*plan, d_mask, dX, (hipStream_t)stream), "mask apply");
+}
+
 nm_status_t nm_prune_check(nm_plan_t plan, const void* dA, int32_t mode, int32_t* d_violations, void* stream) {
   if (!plan) return fail(NM_ERR_INVALID_ARG, "plan is NULL");
   nm_status_t st = check_mode(plan, mode);
@@ -359,6 +373,61 @@ nm_status_t nm_spmm(nm_plan_t plan, const float* alpha, const void* d_values, co
     default: e = launch_spmm_skinny(*plan, *alpha, d_values, d_meta, dB, *beta, dC, dD, s); break;
   }
   return hip_status(e, "spmm");
+}
+
+nm_status_t nm_spmm_streams(nm_plan_t plan, const float* alpha, const void* d_values, const void* d_meta,
+                            const void* dB, const float* beta, const void* dC, void* dD, void* d_workspace,
+                            void* const* streams, int32_t num_streams) {
+  if (!plan) return fail(NM_ERR_INVALID_ARG, "plan is NULL");
+  if (num_streams < 1 || num_streams > 64 || !streams)
+    return fail(NM_ERR_INVALID_ARG, "num_streams must be in [1, 64] with a streams array");
+  nm_status_t st = check_scalars(plan, alpha, beta);
+  if (st != NM_OK) return st;
+  st = check_product_ptrs(plan, d_values, d_meta, dB, *beta, dC, dD);
+  if (st != NM_OK) return st;
+  const size_t ws_bytes = nm::spmm_workspace_bytes(*plan);
+  if (ws_bytes > 0 && !d_workspace)
+    return fail(NM_ERR_INVALID_ARG, "this plan's split-k product needs a workspace of " + std::to_string(ws_bytes) +
+                                        " bytes (nm_spmm_workspace_size); d_workspace is NULL");
+  if (!aligned16(d_workspace)) return fail(NM_ERR_ALIGN, "d_workspace must be 16-byte aligned");
+  const int64_t m = plan->p.m;
+  if (m == 0 || plan->p.n == 0) return NM_OK;
+  // row blocks of whole 256-row multiples, one per stream (fewer when m is small)
+  const int64_t units = (m + 255) / 256;
+  const int64_t parts = num_streams < units ? num_streams : units;
+  const int64_t rows_per = (units + parts - 1) / parts * 256;
+  const bool col = plan->p.order_cd == NM_COL_MAJOR;
+  size_t ws_off = 0;
+  for (int64_t i = 0; i * rows_per < m; i++) {
+    const int64_t r0 = i * rows_per;
+    const int64_t rows = m - r0 < rows_per ? m - r0 : rows_per;
+    nm_plan sub = *plan;                                   // host copy: the row block as its own problem
+    sub.p.m = rows;
+    sub.spmm_symbol.clear();
+    choose_kernel(sub);
+    const size_t vb = (size_t)r0 * (size_t)plan->vld * (size_t)plan->esz_ab;
+    const size_t mb = (size_t)(r0 >> plan->vshift) * (size_t)plan->mld;
+    const size_t cd_elem = col ? (size_t)r0 : (size_t)r0 * (size_t)plan->p.ldd;
+    const size_t c_elem = col ? (size_t)r0 : (size_t)r0 * (size_t)plan->p.ldc;
+    const void* v = (const uint8_t*)d_values + vb;
+    const void* mt = (const uint8_t*)d_meta + mb;
+    const void* c = dC ? (const void*)((const uint8_t*)dC + c_elem * plan->esz_cd) : nullptr;
+    void* d = (uint8_t*)dD + cd_elem * plan->esz_cd;
+    const size_t sub_ws = nm::spmm_workspace_bytes(sub);
+    void* ws = sub_ws ? (uint8_t*)d_workspace + ws_off : nullptr;
+    ws_off += sub_ws;
+    hipStream_t s = (hipStream_t)streams[i % num_streams];
+    hipError_t e;
+    switch (sub.kernel) {
+      case K_SMFMAC_24: e = launch_spmm_smfmac(sub, *alpha, v, mt, dB, *beta, c, d, ws, s); break;
+      case K_GATHER_MFMA: e = launch_spmm_gather(sub, *alpha, v, mt, dB, *beta, c, d, s); break;
+      case K_VW_MFMA: e = launch_spmm_vw(sub, *alpha, v, mt, dB, *beta, c, d, s); break;
+      default: e = launch_spmm_skinny(sub, *alpha, v, mt, dB, *beta, c, d, s); break;
+    }
+    st = hip_status(e, "spmm (multi-stream)");
+    if (st != NM_OK) return st;
+  }
+  return NM_OK;
 }
 
 }  // extern "C"

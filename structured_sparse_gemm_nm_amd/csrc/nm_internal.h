@@ -85,6 +85,7 @@ hipError_t launch_colT_decompress(const nm_plan& pl, const void* vals, const voi
 bool check_row_ok(const nm_plan& pl);
 hipError_t launch_check_row(const nm_plan& pl, const void* a, int32_t* count, hipStream_t s);
 hipError_t launch_prune_tile(const nm_plan& pl, const void* a, void* out, uint32_t* mask, hipStream_t s);
+hipError_t launch_mask_apply(const nm_plan& pl, const uint32_t* mask, void* x, hipStream_t s);
 hipError_t launch_check(const nm_plan& pl, const void* a, int mode, int32_t* count, hipStream_t s);
 hipError_t launch_compress(const nm_plan& pl, const void* a, void* vals, void* meta, hipStream_t s);
 hipError_t launch_decompress(const nm_plan& pl, const void* vals, const void* meta, void* out, hipStream_t s);

@@ -529,6 +529,37 @@ hipError_t launch_decompress(const nm_plan& pl, const void* vals, const void* me
   return dispatch_tile<T_DECOMPRESS>(pl, A, s);
 }
 
+// X (the stored shape of A, lda) keeps the elements whose keep-mask bit is set
+// and gets +0 elsewhere: one thread per mask word (32 consecutive elements of
+// a stored row).
+template <int ESZ>
+__global__ void __launch_bounds__(TPB) mask_apply_kernel(const uint32_t* mask, uint8_t* x, int64_t rows, int64_t cols,
+                                                         int64_t ld, int64_t mask_ld) {
+  const int64_t wid = (int64_t)blockIdx.x * TPB + threadIdx.x;
+  if (wid >= rows * mask_ld) return;
+  const int64_t r = wid / mask_ld, w = wid % mask_ld;
+  const uint32_t bits = mask[r * mask_ld + w];
+  const int64_t c0 = w * 32;
+  const int n = cols - c0 < 32 ? (int)(cols - c0) : 32;
+  for (int e = 0; e < n; e++)
+    if (!((bits >> e) & 1u)) {
+      if (ESZ == 2) ((uint16_t*)x)[r * ld + c0 + e] = 0;
+      else x[r * ld + c0 + e] = 0;
+    }
+}
+
+hipError_t launch_mask_apply(const nm_plan& pl, const uint32_t* mask, void* x, hipStream_t s) {
+  const int64_t rows = pl.a_rows, cols = pl.a_cols;
+  if (rows == 0 || cols == 0) return hipSuccess;
+  const int64_t mld = (cols + 31) / 32;
+  const dim3 grid((unsigned)((rows * mld + TPB - 1) / TPB));
+  if (pl.esz_ab == 2)
+    hipLaunchKernelGGL((mask_apply_kernel<2>), grid, dim3(TPB), 0, s, mask, (uint8_t*)x, rows, cols, pl.p.lda, mld);
+  else
+    hipLaunchKernelGGL((mask_apply_kernel<1>), grid, dim3(TPB), 0, s, mask, (uint8_t*)x, rows, cols, pl.p.lda, mld);
+  return hipGetLastError();
+}
+
 hipError_t launch_prune_tile(const nm_plan& pl, const void* a, void* out, uint32_t* mask, hipStream_t s) {
   const int64_t rows = pl.a_rows, cols = pl.a_cols;
   if (rows == 0 || cols == 0) return hipSuccess;

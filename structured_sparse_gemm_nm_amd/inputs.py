@@ -122,6 +122,20 @@ WORKLOADS = {
                         a=("normal", 5001, 1.0), b=("normal", 5003, 1.0), alpha=1.0, beta=0.0),
     "c5_8of32_n4096": dict(dtype="f16", N=8, M=32, m=4096, n=4096, k=4096, op_a="N", op_b="N",
                            a=("normal", 5001, 1.0), b=("normal", 5004, 1.0), alpha=1.0, beta=0.0),
+    # vector-wise N:M (16 consecutive rows share each group's kept offsets) on the
+    # M = 32 shapes: the variant whose gather of B rows is shared by a row block
+    "c5vw_4of32_n1": dict(dtype="f16", N=4, M=32, m=4096, n=1, k=4096, op_a="N", op_b="N", vector_rows=16,
+                          a=("normal", 5001, 1.0), b=("normal", 5002, 1.0), alpha=1.0, beta=0.0),
+    "c5vw_4of32_n8": dict(dtype="f16", N=4, M=32, m=4096, n=8, k=4096, op_a="N", op_b="N", vector_rows=16,
+                          a=("normal", 5001, 1.0), b=("normal", 5003, 1.0), alpha=1.0, beta=0.0),
+    "c5vw_4of32_n4096": dict(dtype="f16", N=4, M=32, m=4096, n=4096, k=4096, op_a="N", op_b="N", vector_rows=16,
+                             a=("normal", 5001, 1.0), b=("normal", 5004, 1.0), alpha=1.0, beta=0.0),
+    "c5vw_8of32_n1": dict(dtype="f16", N=8, M=32, m=4096, n=1, k=4096, op_a="N", op_b="N", vector_rows=16,
+                          a=("normal", 5001, 1.0), b=("normal", 5002, 1.0), alpha=1.0, beta=0.0),
+    "c5vw_8of32_n8": dict(dtype="f16", N=8, M=32, m=4096, n=8, k=4096, op_a="N", op_b="N", vector_rows=16,
+                          a=("normal", 5001, 1.0), b=("normal", 5003, 1.0), alpha=1.0, beta=0.0),
+    "c5vw_8of32_n4096": dict(dtype="f16", N=8, M=32, m=4096, n=4096, k=4096, op_a="N", op_b="N", vector_rows=16,
+                             a=("normal", 5001, 1.0), b=("normal", 5004, 1.0), alpha=1.0, beta=0.0),
 }
 
 

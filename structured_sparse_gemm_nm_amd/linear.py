@@ -19,7 +19,9 @@ Backward, with dY the (tokens x out) output gradient:
 - nm_spmm: dX^T = W_hat^T dY^T written column-major, i.e. dX row-major;
 - nm_dense_gemm: dW = dY^T X, the dense gradient of the pruned product, handed
   to the dense weight as it is (the pages describe no masking of the weight
-  gradient; the next forward prunes again).
+  gradient; the next forward prunes again), or, with mask_weight_grad=True,
+  masked with the forward's keep mask (nm_mask_apply), so that pruned weights
+  receive no gradient.
 
 Every step runs in the library's kernels; this module only allocates the
 outputs with torch and marshals pointers. Shapes: in and out multiples of 8
@@ -28,7 +30,7 @@ reduction length of the weight-gradient product).
 """
 import torch
 
-from . import nm_compress, nm_dense_gemm, nm_plan_init, nm_prune, nm_spmm
+from . import nm_compress, nm_dense_gemm, nm_mask_apply, nm_plan_init, nm_prune, nm_spmm
 
 _DTYPE_NAMES = {torch.float16: "f16", torch.bfloat16: "bf16"}
 
@@ -74,27 +76,29 @@ class SparseLinearFunction(torch.autograd.Function):
     """Y = X W_hat^T with W_hat the transposable 2:4 pruning of W (see the module docstring)."""
 
     @staticmethod
-    def forward(ctx, x2d, weight):
+    def forward(ctx, x2d, weight, mask_weight_grad=False):
         _check_operands(x2d, weight)
         out_f, in_f = weight.shape
         tokens = x2d.shape[0]
         plans = _plans(out_f, in_f, tokens, _DTYPE_NAMES[weight.dtype])
         w_hat = torch.empty_like(weight)
-        nm_prune(plans.fwd, weight, w_hat, "tile")
+        keep = plans.fwd.empty_mask() if mask_weight_grad else None
+        nm_prune(plans.fwd, weight, w_hat, "tile", keep)
         v_fwd, m_fwd = plans.fwd.empty_values(), plans.fwd.empty_meta()
         nm_compress(plans.fwd, w_hat, v_fwd, m_fwd)
         v_bwd, m_bwd = plans.bwd.empty_values(), plans.bwd.empty_meta()
         nm_compress(plans.bwd, w_hat, v_bwd, m_bwd)
         y = torch.empty((tokens, out_f), dtype=weight.dtype, device=weight.device)
         nm_spmm(plans.fwd, 1.0, v_fwd, m_fwd, x2d, 0.0, None, y)
-        ctx.save_for_backward(x2d, v_bwd, m_bwd)
+        ctx.save_for_backward(x2d, v_bwd, m_bwd, keep if keep is not None else torch.empty(0, device=x2d.device))
         ctx.plans = plans
         ctx.shape = (tokens, out_f, in_f)
+        ctx.mask_weight_grad = mask_weight_grad
         return y
 
     @staticmethod
     def backward(ctx, dy):
-        x2d, v_bwd, m_bwd = ctx.saved_tensors
+        x2d, v_bwd, m_bwd, keep = ctx.saved_tensors
         tokens, out_f, in_f = ctx.shape
         if dy.dtype != x2d.dtype or not dy.is_cuda or dy.device != x2d.device or tuple(dy.shape) != (tokens, out_f):
             raise ValueError("output gradient must be a (tokens x out) GPU tensor of the layer's dtype and device")
@@ -106,7 +110,9 @@ class SparseLinearFunction(torch.autograd.Function):
         if ctx.needs_input_grad[1]:
             dw = torch.empty((out_f, in_f), dtype=dy.dtype, device=dy.device)
             nm_dense_gemm(ctx.plans.dw, 1.0, dy, x2d, 0.0, None, dw)
-        return dx, dw
+            if ctx.mask_weight_grad:
+                nm_mask_apply(ctx.plans.fwd, keep, dw)
+        return dx, dw, None
 
 
 class SemiStructuredSparseLinear(torch.nn.Module):
@@ -114,8 +120,10 @@ class SemiStructuredSparseLinear(torch.nn.Module):
     and compressed at every forward; forward and input-gradient products run on
     the 2:4 SpMM, the weight gradient on the dense product."""
 
-    def __init__(self, in_features, out_features, dtype=torch.float16, device="cuda", weight=None):
+    def __init__(self, in_features, out_features, dtype=torch.float16, device="cuda", weight=None,
+                 mask_weight_grad=False):
         super().__init__()
+        self.mask_weight_grad = bool(mask_weight_grad)
         if dtype not in _DTYPE_NAMES:
             raise ValueError("dtype must be torch.float16 or torch.bfloat16")
         if weight is None and torch.device(device).type != "cuda":
@@ -139,5 +147,5 @@ class SemiStructuredSparseLinear(torch.nn.Module):
         if x2d.shape[0] % 4:
             raise ValueError("the number of tokens must be a multiple of 4")
         _check_operands(x2d, self.weight)
-        y = SparseLinearFunction.apply(x2d, self.weight)
+        y = SparseLinearFunction.apply(x2d, self.weight, self.mask_weight_grad)
         return y.reshape(*x.shape[:-1], self.out_features)

@@ -102,3 +102,47 @@ def test_sparse_linear_rejects_bad_shapes():
     layer = SemiStructuredSparseLinear(64, 64)
     with pytest.raises(ValueError):
         layer(torch.zeros((6, 64), dtype=torch.float16, device="cuda"))
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_sparse_linear_masked_weight_gradient(dtype):
+    """mask_weight_grad=True: dW is the dense dY^T X with the pruned positions of
+    the weight set to +0 (the forward's keep mask applied by nm_mask_apply)."""
+    tokens, in_f, out_f = 64, 136, 96
+    w = inputs.normal((out_f, in_f), 9101, 0.02, dtype)
+    x = inputs.normal((tokens, in_f), 9102, 1.0, dtype)
+    dy = inputs.normal((tokens, out_f), 9103, 1.0, dtype)
+    layer = SemiStructuredSparseLinear(in_f, out_f, dtype=TORCH[dtype], weight=to_torch(w, dtype),
+                                       mask_weight_grad=True)
+    xt = to_torch(x, dtype).requires_grad_(True)
+    layer(xt).backward(to_torch(dy, dtype))
+    sync()
+    _, keep = oracle.prune_tile(w, dtype)
+    g_raw = host(layer.weight.grad.contiguous().view(torch.int16), np.uint16)
+    assert (g_raw[keep == 0] == 0).all()                     # pruned positions: exactly +0
+    DY = oracle.decode(dy, dtype); X = oracle.decode(x, dtype)
+    ref = oracle.gemm_f64(np.ascontiguousarray(DY.T), X) * keep
+    tol = oracle.tolerance(np.abs(np.ascontiguousarray(DY.T)), np.abs(X))
+    g = oracle.decode(g_raw, dtype)
+    assert (np.abs(g - ref) <= tol).all()
+
+
+def test_mask_apply_matches_keep_mask():
+    """nm_mask_apply keeps the elements whose bit is set, +0 elsewhere, on padded
+    rows of any width (ragged last mask word), leaving the padding alone."""
+    import structured_sparse_gemm_nm_amd as nm
+    from tests.gpu_helpers import dev
+    rows, cols, ld = 12, 70, 80
+    a = inputs.normal((rows, ld), 77, 1.0, "f16")
+    p, keep = oracle.prune_1d(np.ascontiguousarray(a[:, :68]), "f16", 2, 4)   # a keep mask of 68 columns
+    keep70 = np.zeros((rows, cols), np.uint8); keep70[:, :68] = keep; keep70[:, 68] = 1
+    plan = nm.nm_plan_init(rows, 16, 72, 2, 4, dtype="f16", lda=ld)
+    # the plan's stored shape is rows x 72: build a 72-column mask (columns 70, 71 cleared)
+    keep72 = np.zeros((rows, 72), np.uint8); keep72[:, :cols] = keep70
+    x = a.copy()
+    dx = dev(x)
+    nm.nm_mask_apply(plan, dev(oracle.mask_bits(keep72)), dx)
+    sync()
+    got = host(dx, np.uint16)
+    exp = x.copy(); exp[:, :72][keep72 == 0] = 0
+    assert np.array_equal(got, exp)

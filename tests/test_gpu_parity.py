@@ -915,3 +915,55 @@ def test_split_k_not_applicable_runs_unsplit():
         d.check()
         ref, tol = ref_product("f16", ahat, b, 1.0, 0.0, None)
         assert_close("f16", host(d.t, np.uint16), ref, tol)
+
+
+# ------------------------------------------------------------------ several streams
+
+STREAM_CASES = [
+    # (label, N, M, V, m, n, k, op_b, splits, order): whole tiles on both B layouts, a ragged last
+    # row block, vector-wise rows, a split-k plan sharing its workspace, column-major D
+    ("24-NT", 2, 4, 0, 1024, 256, 512, "T", 1, "row"),
+    ("24-NN-ragged", 2, 4, 0, 600, 144, 336, "N", 1, "row"),
+    ("vw16-4of32", 4, 32, 16, 768, 256, 512, "N", 1, "row"),
+    ("24-split", 2, 4, 0, 768, 256, 1024, "T", 2, "col"),
+]
+
+
+@pytest.mark.parametrize("dtype", ["f16", "i8"])
+@pytest.mark.parametrize("case", STREAM_CASES, ids=[c[0] for c in STREAM_CASES])
+def test_spmm_streams(dtype, case):
+    """nm_spmm_streams splits D's rows over three streams; the result matches the
+    oracle (int8 bit-exact) and, for int8, nm_spmm's single-stream result."""
+    label, N, M, V, m, n, k, op_b, splits, order = case
+    seed = 9900 + m + n
+    a = rand(dtype, (m, k), seed)
+    if V:
+        ahat, _ = oracle.prune_vw(a, dtype, V, N, M)
+        v, meta = oracle.compress_vw(a, dtype, V, N, M)
+    else:
+        ahat, _ = oracle.prune_1d(a, dtype, N, M)
+        v, meta = oracle.compress(a, dtype, N, M)
+    b_log = rand(dtype, (k, n), seed + 1)
+    b_st = b_log if op_b == "N" else np.ascontiguousarray(b_log.T)
+    plan = plan_for(dtype, m, n, k, N, M, op_b=op_b, order_cd=order, vector_rows=V)
+    nm.nm_plan_set_split_k(plan, splits)
+    ws = plan.empty_workspace()
+    raw, odt = (np.int32, torch.int32) if dtype == "i8" else (np.uint16, torch.int16)
+    dshape = (n, m) if order == "col" else (m, n)
+    streams = [torch.cuda.Stream() for _ in range(3)]
+    dv, dm, db = dev(v), dev(meta), dev(b_st)
+    sync()
+    d = Guarded(dshape, odt)
+    nm.nm_spmm_streams(plan, 1.0, dv, dm, db, 0.0, None, d.t, streams, workspace=ws)
+    for s_ in streams:
+        s_.synchronize()
+    d.check()
+    got = host(d.t, raw)
+    got = np.ascontiguousarray(got.T) if order == "col" else got
+    ref, tol = ref_product(dtype, ahat, b_log, 1.0, 0.0, None)
+    assert_close(dtype, got, ref, tol)
+    if dtype == "i8":
+        d1 = Guarded(dshape, odt)
+        nm.nm_spmm(plan, 1.0, dv, dm, db, 0.0, None, d1.t, workspace=ws)
+        sync()
+        assert np.array_equal(host(d1.t, raw), host(d.t, raw))

@@ -55,7 +55,9 @@ CASES = [("c1_fp16_256", "N"), ("c2_fc1", "T"), ("c2_fc1", "N"), ("c2_fc2", "T")
          ("c4_int8", "T"), ("c5_4of32_n1", "N"), ("c5_4of32_n8", "N"), ("c5_4of32_n4096", "N"),
          ("c5_8of32_n1", "N"), ("c5_8of32_n8", "N"), ("c5_8of32_n4096", "N"),
          ("x1_fwd", "T"), ("x1_bwd", "T"), ("x3_qkv", "T"), ("x3_proj", "T"), ("x3_fc1", "T"), ("x3_fc2", "T"),
-         ("x2_4of32_n1", "N"), ("x2_4of32_n8", "N")]
+         ("x2_4of32_n1", "N"), ("x2_4of32_n8", "N"),
+         ("c5vw_4of32_n1", "N"), ("c5vw_4of32_n8", "N"), ("c5vw_4of32_n4096", "N"),
+         ("c5vw_8of32_n1", "N"), ("c5vw_8of32_n8", "N"), ("c5vw_8of32_n4096", "N")]
 
 
 @pytest.mark.parametrize("name,op_b", CASES, ids=["%s-%s" % c for c in CASES])
@@ -66,11 +68,14 @@ def test_workload(name, op_b):
     print("workload", name, "op_b", op_b, flush=True)
     a, b, c = inputs.workload_inputs(name, op_b)
     order = w.get("order_cd", "row")
-    plan = nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=op_b, dtype=dtype, order_cd=order)
+    V = w.get("vector_rows", 0)
+    plan = nm.nm_plan_init(m, n, k, N, M, op_a=op_a, op_b=op_b, dtype=dtype, order_cd=order, vector_rows=V)
     mode = "tile" if w.get("tile") else "1d"
     # prune on the GPU, bit-exact against the oracle
     if mode == "tile":
         ref_p, _ = oracle.prune_tile(a, dtype)
+    elif V > 1:
+        ref_p, _ = oracle.prune_vw(a, dtype, V, N, M)
     else:
         ref_p, _ = oracle.prune_1d(a, dtype, N, M, op_a)
     da = dev(a)
@@ -82,7 +87,7 @@ def test_workload(name, op_b):
     assert np.array_equal(host(dp, RAW[dtype]), ref_p)
     assert int(cnt.item()) == 0
     # compress the pruned matrix
-    vref, mref = oracle.compress(ref_p, dtype, N, M, op_a)
+    vref, mref = (oracle.compress_vw(ref_p, dtype, V, N, M) if V > 1 else oracle.compress(ref_p, dtype, N, M, op_a))
     vals, meta = plan.empty_values(), plan.empty_meta()
     vals = vals.view(TRAW[dtype]) if dtype != "i8" else vals
     nm.nm_compress(plan, dp, vals, meta)
@@ -96,7 +101,8 @@ def test_workload(name, op_b):
     nm.nm_decompress(plan, vals, meta, back)
     sync()
     got_back = host(back, RAW[dtype])
-    ref_back = oracle.decompress(vref, mref, dtype, m, k, N, M, op_a)
+    ref_back = (oracle.decompress_vw(vref, mref, dtype, m, k, V, N, M) if V > 1
+                else oracle.decompress(vref, mref, dtype, m, k, N, M, op_a))
     assert np.array_equal(got_back, ref_back)
     if dtype == "i8":
         assert np.array_equal(got_back, ref_p)
