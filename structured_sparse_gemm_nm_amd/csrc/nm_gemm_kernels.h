@@ -696,11 +696,15 @@ __device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* lds_wave_base) {
 // k = base .. base + 3, i.e. four consecutive k of its own column, which is
 // what the matrix instructions' B operand holds. 16-bit types only.
 // LAYOUT bit 0: B stored n x k (k-contiguous rows); bit 1: dense A stored k x m
-// (op_a = T), staged and read like B stored k x n.
+// (op_a = T), staged and read like B stored k x n; bit 2 (2:4, 16-bit types):
+// metadata staged four k-steps at a time (32 bytes per row) in a double-buffered
+// slot outside the ring, so that a copy instruction moves 32 contiguous bytes of
+// a row instead of 8 (a quarter of the cache-line requests per metadata byte).
 template <int DT, int AMODE, int BM, int BN, int S, int WGM, int WGN, int LAYOUT>
 __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   constexpr int BKC = LAYOUT & 1;
   constexpr bool AT = (LAYOUT & 2) != 0;
+  constexpr bool M4 = (LAYOUT & 4) != 0;
   static_assert(!AT || AMODE == A_DENSE, "transposed A is dense only");
   constexpr int NW = WGM * WGN;                          // waves per block
   constexpr int ESZ = DT == DT_I8 ? 1 : 2;
@@ -710,12 +714,16 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   constexpr int MDW = MB / 4;
   constexpr bool SP = AMODE == A_SPARSE24;
   constexpr int A_VAL = SP ? BM * 64 : BM * 128;         // values (2:4) or dense A rows
-  constexpr int A_META = SP ? BM * MB : 0;
+  static_assert(!M4 || (SP && ESZ == 2), "batched metadata: 2:4 with 16-bit types");
+  constexpr int A_META = SP && !M4 ? BM * MB : 0;
   constexpr int B_ST = BN * 128;
   constexpr int STAGE = A_VAL + A_META + B_ST;
-  static_assert(S * STAGE <= 160 * 1024, "LDS ring too large");
+  constexpr int MSLOT = M4 ? BM * 4 * MB : 0;            // one metadata slot: 4 k-steps of every row
+  static_assert(S * STAGE + 2 * MSLOT <= 160 * 1024, "LDS ring too large");
   // DMA wave instructions per stage (64 lanes x 16 or 4 bytes), split evenly over the waves
-  constexpr int TB = BN / 8, TA = SP ? BM / 16 : BM / 8, TMT = SP ? BM * MDW / 64 : 0;
+  constexpr int TB = BN / 8, TA = SP ? BM / 16 : BM / 8, TMT = SP && !M4 ? BM * MDW / 64 : 0;
+  constexpr int NMG = M4 ? BM * 2 / 64 / (WGM * WGN) : 0;  // 16-byte metadata copies per wave and slot fill
+  static_assert(!M4 || NMG * 64 * WGM * WGN == BM * 2, "metadata slot split");
   // HALF_META: twice as many waves as metadata instructions; each wave then
   // copies its share with the lower 32 lanes (one instruction, so every wave
   // still issues the same number of copies per stage)
@@ -732,7 +740,8 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
     else return c ^ (2 * ((r / (256 / W)) % (W * ESZ / 16 / 2)));
   };
   auto nn_slot = [&](int r, int c) -> int { return nn_slot_w(r, c, BN); };
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[S * STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[S * STAGE + 2 * MSLOT];
+  uint8_t* const mslots = ring + S * STAGE;
 
   typedef typename Acc<DT>::t acc_t;
   typedef typename Frag<DT>::ab ab_t;
@@ -818,6 +827,29 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
     }
   };
   auto issue = [&](int st) { issue_part(st, 0, 1); };
+  // Metadata slot fill: k-steps 4 mg .. 4 mg + 3 of every row (32 bytes) into
+  // slot mg % 2; lane p of the fill copies 16-byte chunk p % 2 of row p / 2,
+  // stored at chunk (p % 2) ^ bit 3 of the row (two rows 8 apart then read
+  // different banks). The launch takes this path only without split-k (the
+  // block's metadata then starts on a 16-byte boundary); chunks past the row's
+  // padded end are clamped into the row and never read.
+  uint32_t omr[NMG > 0 ? NMG : 1], omc[NMG > 0 ? NMG : 1];   // row byte offset, chunk byte offset
+#pragma unroll
+  for (int j = 0; j < NMG; j++) {
+    const int p = 64 * (wave * NMG + j) + lane;
+    const int row = p / 2;
+    omr[j] = (uint32_t)(row * A.mld);
+    omc[j] = (uint32_t)((((p % 2) ^ ((row >> 3) & 1))) * 16);
+  }
+  auto issue_meta = [&](int mg) {
+    uint8_t* base = mslots + (mg % 2) * MSLOT;
+#pragma unroll
+    for (int j = 0; j < NMG; j++) {
+      int64_t o = (int64_t)mg * 32 + omc[j];
+      if (o + 16 > A.mld) o = A.mld - 16;
+      dma16(A.meta + (size_t)r0 * A.mld + omr[j] + (size_t)o, base + (wave * NMG + j) * 1024);
+    }
+  };
 
   acc_t acc[FM][FN];
 #pragma unroll
@@ -871,7 +903,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   b2_t bv[2];
   ab_t bw[2][FN];
   const int qshift = 16 * q;
-  auto load_group = [&](const uint8_t* st, int g) {
+  auto load_group = [&](const uint8_t* st, int g, int ks) {
     if constexpr (SP) {
       const uint8_t* la = st;
       const uint8_t* lm = st + A_VAL;
@@ -888,7 +920,13 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
             // halves; the lane's 16 bits are selected at use (shift by 16 q)
             if (h == 0) {
               typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-              const u32x2_t mw = *(const u32x2_t*)(lm + row * MB);
+              const uint8_t* mp = lm + row * MB;
+              if constexpr (M4) {
+                // step ks: slot (ks / 4) % 2, 8-byte piece ks % 4 of the row's 32 bytes
+                const int sub = ks & 3;
+                mp = mslots + ((ks >> 2) & 1) * MSLOT + row * 32 + ((((sub >> 1) ^ (row >> 3)) & 1) << 4) + (sub & 1) * 8;
+              }
+              const u32x2_t mw = *(const u32x2_t*)mp;
               iv[0][fm] = (int)mw[0];
               ivn[fm] = (int)mw[1];
             } else {
@@ -986,28 +1024,47 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
     else wait_vmcnt<0>();
   };
   // every slot is filled up front; stage 0 is complete once at most stages
-  // 1 .. min(S-1, ksteps-1) are outstanding
+  // 1 .. min(S-1, ksteps-1) are outstanding (the first metadata slot is
+  // filled before stage 0)
+  if constexpr (M4) issue_meta(0);
 #pragma unroll
   for (int st = 0; st < S; st++)
     if (st < ksteps) issue(st);
   wait_stages(min(S - 1, ksteps - 1));
   lds_barrier();
-  load_group(ring, 0);
+  load_group(ring, 0, 0);
   for (int ks = 0; ks < ksteps; ks++) {
     const uint8_t* st = ring + (ks % S) * STAGE;
+    // batched metadata: the slot for k-steps ks + 4 .. ks + 7 is filled at the
+    // start of every fourth step (the slot it overwrites was last read at the
+    // start of step ks - 1), before that step's ring refill
+    const bool meta_fill = M4 && (ks & 3) == 0 && ks + 4 < ksteps;
 #pragma unroll
     for (int g = 0; g < G; g++) {
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (M4) {
+        if (g == 0 && meta_fill) issue_meta((ks >> 2) + 1);
+      }
       // stage ks+S-1 goes into the slot freed at the end of step ks-1
       if (ks >= 1 && ks + S - 1 < ksteps) issue_part(ks + S - 1, g, G);
       if (g + 1 < G) {
-        load_group(st, g + 1);
+        load_group(st, g + 1, ks);
       } else if (ks + 1 < ksteps) {
         // issued so far: stages up to min(ks+S-1, ksteps-1); stage ks+1 is
-        // complete once at most stages ks+2 .. min(ks+S-1, ksteps-1) are outstanding
-        wait_stages(min(S - 2, ksteps - ks - 2));
+        // complete once at most stages ks+2 .. min(ks+S-1, ksteps-1) (and
+        // this step's metadata fill, issued after stage ks+1) are outstanding
+        if constexpr (M4) {
+          static_assert(S == 3, "batched metadata runs with a three-stage ring");
+          const bool next_stage = ks + 2 < ksteps;
+          if (next_stage && meta_fill) wait_vmcnt<L + NMG>();
+          else if (next_stage) wait_vmcnt<L>();
+          else if (meta_fill) wait_vmcnt<NMG>();
+          else wait_vmcnt<0>();
+        } else {
+          wait_stages(min(S - 2, ksteps - ks - 2));
+        }
         lds_barrier();                                   // every wave is done reading stage ks
-        load_group(ring + ((ks + 1) % S) * STAGE, 0);
+        load_group(ring + ((ks + 1) % S) * STAGE, 0, ks + 1);
       }
       __builtin_amdgcn_sched_barrier(0);
       compute_group(g);
@@ -1451,6 +1508,15 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
           else
             NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, S1, WGM, WGN, 2>), grid, dim3(64 * WGM * WGN), 0, s, A);
           return launch_status();
+        }
+      }
+      if constexpr (AMODE == A_SPARSE24 && TM == 256 && TN == 256 && DT != DT_I8 && S1 == 3) {
+        // 2:4, 16-bit, 256 x 256: metadata staged four k-steps at a time (not
+        // with split-k, whose k ranges may start half-way into a 16-byte piece)
+        if (A.splits == 1) {
+          if (bkc) NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, 3, WGM, WGN, 5>), grid, dim3(64 * WGM * WGN), 0, s, A);
+          else NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, 3, WGM, WGN, 4>), grid, dim3(64 * WGM * WGN), 0, s, A);
+          return launch_reduce<DT>(A, s);
         }
       }
       if constexpr (AMODE == A_SPARSE24 && TM == 128 && TN == 128) {
