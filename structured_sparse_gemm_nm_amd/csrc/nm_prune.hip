@@ -304,43 +304,202 @@ constexpr uint32_t first_tile_pattern() {
         }
   return 0;
 }
-static_assert(first_tile_pattern() == 0xCC33u, "first pattern keeps (0,1), (0,1), (2,3), (2,3)");
+constexpr uint32_t kFirstTilePattern = first_tile_pattern();   // folded here, not evaluated per tile
+static_assert(kFirstTilePattern == 0xCC33u, "first pattern keeps (0,1), (0,1), (2,3), (2,3)");
 
 template <int DT, int ESZ>
 __device__ __forceinline__ uint32_t load_raw(const uint8_t* p, int64_t idx) {
   return ESZ == 2 ? (uint32_t)((const uint16_t*)p)[idx] : (uint32_t)p[idx];
 }
 
-// One thread per 4x4 tile of the stored matrix; lanes run along tile columns so
-// each of the four row loads is contiguous across the wave.
-template <int DT, int ESZ>
-__global__ void __launch_bounds__(TPB) tile4_prune_kernel(const uint8_t* a, uint8_t* out, uint32_t* mask,
-                                                          int64_t rows, int64_t cols, int64_t ld,
-                                                          int64_t mask_ld) {
-  const int64_t tj = (int64_t)blockIdx.x * TPB + threadIdx.x;
-  const int64_t ti = blockIdx.y;
-  const bool active = tj < cols / 4;
-  uint32_t raw[4][4];
-  double w[4][4];
+// One row of a 4x4 tile (four elements from idx on). With vec the four are
+// one naturally aligned 8-byte (16-bit types) or 4-byte (int8) word: one load,
+// one store per row instead of four.
+template <int ESZ>
+__device__ __forceinline__ void load_row4(const uint8_t* p, int64_t idx, bool vec, uint32_t (&v)[4]) {
+  if (vec) {
+    if constexpr (ESZ == 2) {
+      const u32x2 w = *(const u32x2*)(p + idx * 2);
+      v[0] = w[0] & 0xFFFFu; v[1] = w[0] >> 16; v[2] = w[1] & 0xFFFFu; v[3] = w[1] >> 16;
+    } else {
+      const uint32_t w = *(const uint32_t*)(p + idx);
 #pragma unroll
-  for (int r = 0; r < 4; r++)
+      for (int c = 0; c < 4; c++) v[c] = (w >> (8 * c)) & 0xFFu;
+    }
+  } else {
+#pragma unroll
+    for (int c = 0; c < 4; c++) v[c] = load_raw<0, ESZ>(p, idx + c);
+  }
+}
+template <int ESZ>
+__device__ __forceinline__ void store_row4(uint8_t* p, int64_t idx, bool vec, const uint32_t (&v)[4]) {
+  if (vec) {
+    if constexpr (ESZ == 2) *(u32x2*)(p + idx * 2) = u32x2{v[0] | v[1] << 16, v[2] | v[3] << 16};
+    else *(uint32_t*)(p + idx) = v[0] | v[1] << 8 | v[2] << 16 | v[3] << 24;
+  } else {
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-      raw[r][c] = active ? load_raw<DT, ESZ>(a, (ti * 4 + r) * ld + tj * 4 + c) : 0u;
-      w[r][c] = absval64<DT>(raw[r][c]);
+      if (ESZ == 2) ((uint16_t*)p)[idx + c] = (uint16_t)v[c];
+      else p[idx + c] = (uint8_t)v[c];
     }
+  }
+}
+
+// Row-pair decomposition of the 90 patterns. After tile rows 0 and 1 keep
+// pairs p0 and p1, rows 2 and 3 must keep what each column still needs: a
+// need vector with entries in {0, 1, 2} summing to 4 (19 such vectors). Each
+// (p0, p1) leads to one need state, and each state has 1, 2 or 6 completions
+// (p2, p3). In order of increasing p2 the completions of a state, and in
+// lexicographic order the (p0, p1), enumerate the 90 patterns in the scan's
+// order.
+struct TilePairTables {
+  int nstates;
+  int state_of[36];       // (p0 * 6 + p1) -> need state
+  int ncomp[19];
+  int comp_p2[19][6], comp_p3[19][6];
+};
+constexpr TilePairTables make_pair_tables() {
+  constexpr int pa[6] = {0, 0, 0, 1, 1, 2}, pb[6] = {1, 2, 3, 2, 3, 3};
+  TilePairTables t{};
+  int need[19][4] = {};
+  for (int p0 = 0; p0 < 6; p0++)
+    for (int p1 = 0; p1 < 6; p1++) {
+      int nd[4] = {2, 2, 2, 2};
+      nd[pa[p0]]--; nd[pb[p0]]--; nd[pa[p1]]--; nd[pb[p1]]--;
+      int st = -1;
+      for (int x = 0; x < t.nstates; x++)
+        if (need[x][0] == nd[0] && need[x][1] == nd[1] && need[x][2] == nd[2] && need[x][3] == nd[3]) st = x;
+      if (st < 0) {
+        st = t.nstates++;
+        for (int c = 0; c < 4; c++) need[st][c] = nd[c];
+        t.ncomp[st] = 0;
+        for (int p2 = 0; p2 < 6; p2++) {
+          int rest[4] = {nd[0], nd[1], nd[2], nd[3]};
+          rest[pa[p2]]--; rest[pb[p2]]--;
+          bool ok = true;
+          for (int c = 0; c < 4; c++) ok = ok && rest[c] >= 0 && rest[c] <= 1;
+          if (!ok) continue;
+          for (int p3 = 0; p3 < 6; p3++)
+            if (rest[pa[p3]] == 1 && rest[pb[p3]] == 1) {
+              t.comp_p2[st][t.ncomp[st]] = p2;
+              t.comp_p3[st][t.ncomp[st]] = p3;
+              t.ncomp[st]++;
+            }
+        }
+      }
+      t.state_of[p0 * 6 + p1] = st;
+    }
+  return t;
+}
+constexpr TilePairTables kPairTab = make_pair_tables();
+constexpr int count_pair_patterns() {
+  int n = 0;
+  for (int i = 0; i < 36; i++) n += kPairTab.ncomp[kPairTab.state_of[i]];
+  return n;
+}
+static_assert(kPairTab.nstates == 19 && count_pair_patterns() == 90, "19 need states, 90 patterns");
+
+// Tie ranks. With column offsets o = (4, 2, 1, 0), pair p of a row gets
+// f(p) = o[PA[p]] + o[PB[p]] = 6 - p, and a candidate gets the rank
+// 49 f(p0) + 7 f(p1) + f(p2) (p3 follows from the other three): base-7 digits in
+// 1..6, so increasing rank is decreasing (p0, p1, p2) in lexicographic order,
+// the scan's order reversed. Ranks lie in [57, 342]; the table gives each used
+// rank's pattern as four row masks (row 0 lowest).
+struct TilePatternTable {
+  uint16_t pat[343];
+};
+constexpr TilePatternTable make_pattern_table() {
+  constexpr int pa[6] = {0, 0, 0, 1, 1, 2}, pb[6] = {1, 2, 3, 2, 3, 3};
+  TilePatternTable t{};
+  for (int i = 0; i < 36; i++) {
+    const int st = kPairTab.state_of[i], p0 = i / 6, p1 = i % 6;
+    const int m0 = (1 << pa[p0]) | (1 << pb[p0]), m1 = (1 << pa[p1]) | (1 << pb[p1]);
+    for (int c = 0; c < kPairTab.ncomp[st]; c++) {
+      const int p2 = kPairTab.comp_p2[st][c], p3 = kPairTab.comp_p3[st][c];
+      t.pat[49 * (6 - p0) + 7 * (6 - p1) + (6 - p2)] =
+          (uint16_t)(m0 | m1 << 4 | ((1 << pa[p2]) | (1 << pb[p2])) << 8 | ((1 << pa[p3]) | (1 << pb[p3])) << 12);
+    }
+  }
+  return t;
+}
+__constant__ TilePatternTable kTilePatterns = make_pattern_table();
+static_assert(make_pattern_table().pat[49 * 6 + 7 * 6 + 1] == kFirstTilePattern,
+              "the highest rank (p0 = p1 = 0, p2 = 5) is the scan's first pattern");
+constexpr int kRowWeight[4] = {49, 7, 1, 0};
+constexpr int kColOffset[4] = {4, 2, 1, 0};
+
+// The key of a candidate is its score plus its rank in units uu. When every
+// score is a multiple of 512 uu and every key lies below 2^53 uu (fp64) or 2^31
+// (int32), all sums are exact, the largest key has the largest score, and among
+// equal scores it has the highest rank: the scan's first maximum. Adding
+// kRowWeight[r] * kColOffset[c] * uu to element (r, c) puts the rank into the
+// row-pair sums t[r][p], so a key is a plain sum of four row terms and its
+// maximum is taken in stages: per need state over rows 2 and 3, then per p0
+// over p1, then over p0.
+__device__ __forceinline__ double kmax(double x, double y) { return fmax(x, y); }
+__device__ __forceinline__ int32_t kmax(int32_t x, int32_t y) { return x > y ? x : y; }
+
+template <typename K, int ST, int C>
+__device__ __forceinline__ void best_completion(const K (&s2)[6], const K (&s3)[6], K& b) {
+  if constexpr (C < kPairTab.ncomp[ST]) {
+    const K v = s2[kPairTab.comp_p2[ST][C]] + s3[kPairTab.comp_p3[ST][C]];
+    if constexpr (C == 0) b = v;
+    else b = kmax(b, v);
+    best_completion<K, ST, C + 1>(s2, s3, b);
+  }
+}
+template <typename K, int ST>
+__device__ __forceinline__ void best_completions(const K (&s2)[6], const K (&s3)[6], K (&b)[19]) {
+  best_completion<K, ST, 0>(s2, s3, b[ST]);
+  if constexpr (ST + 1 < 19) best_completions<K, ST + 1>(s2, s3, b);
+}
+template <typename K, int P0, int P1>
+__device__ __forceinline__ void best_row1(const K (&s1)[6], const K (&b)[19], K& m) {
+  const K v = s1[P1] + b[kPairTab.state_of[P0 * 6 + P1]];
+  if constexpr (P1 == 0) m = v;
+  else m = kmax(m, v);
+  if constexpr (P1 + 1 < 6) best_row1<K, P0, P1 + 1>(s1, b, m);
+}
+template <typename K, int P0>
+__device__ __forceinline__ void best_key(const K (&s0)[6], const K (&s1)[6], const K (&b)[19], K& key) {
+  K m;
+  best_row1<K, P0, 0>(s1, b, m);
+  const K v = s0[P0] + m;
+  if constexpr (P0 == 0) key = v;
+  else key = kmax(key, v);
+  if constexpr (P0 + 1 < 6) best_key<K, P0 + 1>(s0, s1, b, key);
+}
+// The largest key over all 90 candidates, from the row-pair terms.
+template <typename K>
+__device__ __forceinline__ K max_key(const K (&t)[4][6]) {
+  K b[19], key;
+  best_completions<K, 0>(t[2], t[3], b);
+  best_key<K, 0>(t[0], t[1], b, key);
+  return key;
+}
+
+// The fixed-order scan of all 90 candidates, for tiles whose keys could round
+// (a NaN or Inf, or bf16 magnitudes spread over more than 32 binades). Kept out
+// of line: it is rare, and its registers would otherwise bound the occupancy of
+// the common path.
+struct TileRaw {
+  uint32_t v[16];
+};
+template <int DT>
+__device__ __attribute__((noinline)) uint32_t scan_tile(TileRaw raw) {
   double s[4][6];
 #pragma unroll
   for (int r = 0; r < 4; r++)
 #pragma unroll
-    for (int p = 0; p < 6; p++) s[r][p] = w[r][PA[p]] + w[r][PB[p]];
+    for (int p = 0; p < 6; p++) s[r][p] = absval64<DT>(raw.v[4 * r + PA[p]]) + absval64<DT>(raw.v[4 * r + PB[p]]);
+  constexpr auto bits = [](int p) { return (1u << PA[p]) | (1u << PB[p]); };
+  uint32_t bmask = kFirstTilePattern;
   // scan candidates in order (p0 outermost); replace only on a strictly larger
   // score. The winner is kept as its four row masks packed in one constant (one
   // select per candidate), and the best score as a running maximum (the same
   // value the strict replacement keeps; a NaN score changes neither). It starts
   // at the first pattern, which stays when every candidate keeps a NaN.
   double best = -1.0;
-  uint32_t bmask = first_tile_pattern();
 #pragma unroll
   for (int p0 = 0; p0 < 6; p0++)
 #pragma unroll
@@ -360,36 +519,216 @@ __global__ void __launch_bounds__(TPB) tile4_prune_kernel(const uint8_t* a, uint
 #pragma unroll
         for (int p = 0; p < 6; p++) if (PA[p] == lo && PB[p] == hi) p3 = p;
         const double score = ((s[0][p0] + s[1][p1]) + s[2][p2]) + s[3][p3];
-        constexpr auto bits = [](int p) { return (1u << PA[p]) | (1u << PB[p]); };
         const uint32_t cand = bits(p0) | bits(p1) << 4 | bits(p2) << 8 | bits(p3) << 12;
         bmask = score > best ? cand : bmask;
         best = fmax(best, score);
       }
-  uint32_t rowbits[4];
+  return bmask;
+}
+
+// The transposable pattern of one 4x4 tile (raw element bits, row-major; for
+// 16-bit types also the tile's eight 32-bit words, row r in words 2r, 2r + 1):
+// its four row masks, row 0 lowest.
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+template <int DT>
+__device__ __forceinline__ uint32_t select_tile(const uint32_t (&raw)[4][4], const uint32_t (&wd)[8]) {
+  if constexpr (DT == DT_I8) {
+    // magnitudes are integers up to 128, u = 1: int32 keys 512 s + rank, below 2^20
+    int32_t w[4][4], t[4][6];
 #pragma unroll
-  for (int r = 0; r < 4; r++) {
-    rowbits[r] = (bmask >> (4 * r)) & 15u;
-    if (active) {
+    for (int r = 0; r < 4; r++)
 #pragma unroll
       for (int c = 0; c < 4; c++) {
-        const uint32_t v = ((rowbits[r] >> c) & 1u) ? raw[r][c] : 0u;
-        const int64_t idx = (ti * 4 + r) * ld + tj * 4 + c;
-        if (ESZ == 2) ((uint16_t*)out)[idx] = (uint16_t)v;
-        else out[idx] = (uint8_t)v;
+        const int32_t v = (int32_t)(int8_t)(uint8_t)raw[r][c];
+        w[r][c] = ((v < 0 ? -v : v) << 9) + kRowWeight[r] * kColOffset[c];
+      }
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+#pragma unroll
+      for (int p = 0; p < 6; p++) t[r][p] = w[r][PA[p]] + w[r][PB[p]];
+    return kTilePatterns.pat[max_key<int32_t>(t) & 511];
+  } else {
+    // The unit u that every magnitude is a multiple of, and the key unit
+    // uu = u / 512: fp16 u = 2^-24 (scores below 2^19); bf16 u = the unit of
+    // the smallest non-zero exponent field E (at least 1), 2^(E - 134), with
+    // scores below 2^(Emax - 123). Keys are exact for every finite fp16 tile
+    // and for bf16 tiles with Emax - E <= 32; others (a NaN or Inf, or bf16
+    // magnitudes spread further) take the scan of all 90 in the fixed order.
+    double w[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; r++)
+#pragma unroll
+      for (int c = 0; c < 4; c++) {
+        if constexpr (DT == DT_F16)
+          w[r][c] = (double)fabsf((float)__builtin_bit_cast(_Float16, (uint16_t)raw[r][c]));
+        else
+          w[r][c] = absval64<DT>(raw[r][c]);
+      }
+    bool exact;
+    int uexp = -33;                                          // log2 uu
+    if constexpr (DT == DT_F16) {
+      // no NaN or Inf: the sum of all sixteen finite magnitudes is finite
+      double total = 0.0;
+#pragma unroll
+      for (int r = 0; r < 4; r++) total += (w[r][0] + w[r][1]) + (w[r][2] + w[r][3]);
+      exact = total < __builtin_huge_val();
+    } else {
+      // largest magnitude, and smallest non-zero one minus 1 (0xFFFF when all are zero)
+      u16x2 mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
+#pragma unroll
+      for (int i = 0; i < 8; i++) {
+        const u16x2 m = __builtin_bit_cast(u16x2, wd[i] & 0x7FFF7FFFu);
+        mx = __builtin_elementwise_max(mx, m);
+        mn = __builtin_elementwise_min(mn, m - (u16x2){1, 1});
+      }
+      const int emax = (int)((mx[0] > mx[1] ? mx[0] : mx[1]) >> 7);
+      const uint32_t mn1 = mn[0] < mn[1] ? mn[0] : mn[1];
+      const int emin = mn1 == 0xFFFFu ? 1 : (int)((mn1 + 1u) >> 7);
+      const int e1 = emin > 1 ? emin : 1;
+      exact = emax != 0xFF && emax - e1 <= 32;
+      uexp = e1 - 143;
+    }
+    uint32_t bmask;
+    if (exact) {
+      const double uu = __longlong_as_double((long long)(1023 + uexp) << 52);
+      double t[4][6];
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+#pragma unroll
+        for (int c = 0; c < 4; c++)
+          if (kRowWeight[r] * kColOffset[c] != 0) w[r][c] = fma((double)(kRowWeight[r] * kColOffset[c]), uu, w[r][c]);
+#pragma unroll
+        for (int p = 0; p < 6; p++) t[r][p] = w[r][PA[p]] + w[r][PB[p]];
+      }
+      const double x = max_key<double>(t) * __longlong_as_double((long long)(1023 - uexp) << 52);   // key / uu
+      const double hi = floor(x * (1.0 / 512.0));
+      bmask = kTilePatterns.pat[(int)fma(hi, -512.0, x)];
+    } else {
+      bmask = scan_tile<DT>(TileRaw{{raw[0][0], raw[0][1], raw[0][2], raw[0][3], raw[1][0], raw[1][1], raw[1][2], raw[1][3],
+                                     raw[2][0], raw[2][1], raw[2][2], raw[2][3], raw[3][0], raw[3][1], raw[3][2], raw[3][3]}});
+    }
+    return bmask;
+  }
+}
+
+// Each thread takes TPT horizontally adjacent tiles, one 16-byte word per tile
+// row (one load, one store per row when rows are 16-byte aligned); lanes run
+// along tile columns so each row access is contiguous across the wave. Blocks
+// stride down the tile rows, loading the next tile row while selecting the
+// current one.
+template <int ESZ>
+__device__ __forceinline__ void load_tile_rows(const uint8_t* a, int64_t ti, int64_t ld, int64_t tj0,
+                                               int64_t ntiles, bool full, u32x4 (&pk)[4]) {
+  constexpr int TPT = 16 / (4 * ESZ);
+#pragma unroll
+  for (int r = 0; r < 4; r++) {
+    const int64_t idx = (ti * 4 + r) * ld + tj0 * 4;
+    if (full) {
+      pk[r] = *(const u32x4*)(a + idx * ESZ);
+    } else {
+      uint32_t v[TPT][4];
+#pragma unroll
+      for (int t = 0; t < TPT; t++) {
+        if (tj0 + t < ntiles) load_row4<ESZ>(a, idx + 4 * t, false, v[t]);
+        else v[t][0] = v[t][1] = v[t][2] = v[t][3] = 0u;
+      }
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        uint32_t word = 0;
+#pragma unroll
+        for (int x = 0; x < 4 / ESZ; x++) {
+          const int e = d * (4 / ESZ) + x;
+          word |= v[e / 4][e % 4] << (8 * ESZ * x);
+        }
+        pk[r][d] = word;
       }
     }
   }
-  if (mask) {
-    // 8 consecutive tiles share a 32-bit mask word per row: OR them across lanes.
-    const int sub = (int)(tj % 8);
+}
+
+template <int DT, int ESZ>
+__global__ void __launch_bounds__(TPB) tile4_prune_kernel(const uint8_t* a, uint8_t* out, uint32_t* mask,
+                                                          int64_t rows, int64_t cols, int64_t ld,
+                                                          int64_t mask_ld, int vec) {
+  constexpr int TPT = 16 / (4 * ESZ);
+  const int64_t ntiles = cols / 4, ntr = rows / 4;
+  const int64_t tj0 = ((int64_t)blockIdx.x * TPB + threadIdx.x) * TPT;
+  const bool full = vec && tj0 + TPT <= ntiles;
+  const bool any = tj0 < ntiles;
+  u32x4 pk[4];
+  int64_t ti = blockIdx.y;
+  if (any && ti < ntr) load_tile_rows<ESZ>(a, ti, ld, tj0, ntiles, full, pk);
+  for (; ti < ntr; ti += gridDim.y) {
+    u32x4 nx[4];
+    const int64_t tn = ti + gridDim.y;
+    if (any && tn < ntr) load_tile_rows<ESZ>(a, tn, ld, tj0, ntiles, full, nx);
+    uint32_t rowbits[4] = {0u, 0u, 0u, 0u};   // TPT * 4 bits per row, tile t at bit 4 t
+#pragma unroll
+    for (int t = 0; t < TPT; t++) {
+      uint32_t raw[4][4];
+#pragma unroll
+      for (int r = 0; r < 4; r++)
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          const int e = 4 * t + c;
+          const uint32_t word = pk[r][e * ESZ / 4];
+          raw[r][c] = ESZ == 2 ? (word >> (16 * (e & 1))) & 0xFFFFu : (word >> (8 * (e & 3))) & 0xFFu;
+        }
+      uint32_t wd[8];
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        wd[2 * r] = pk[r][(2 * t) & 3];
+        wd[2 * r + 1] = pk[r][(2 * t + 1) & 3];
+      }
+      const uint32_t bm = tj0 + t < ntiles ? select_tile<DT>(raw, wd) : 0u;   // no bits past the last tile
+#pragma unroll
+      for (int r = 0; r < 4; r++) rowbits[r] |= ((bm >> (4 * r)) & 15u) << (4 * t);
+      __builtin_amdgcn_sched_barrier(0);   // one tile's selection at a time: bounds live registers
+    }
 #pragma unroll
     for (int r = 0; r < 4; r++) {
-      uint32_t v = active ? (rowbits[r] << (4 * sub)) : 0u;
-      v |= __shfl_xor(v, 1);
-      v |= __shfl_xor(v, 2);
-      v |= __shfl_xor(v, 4);
-      if (active && sub == 0) mask[(ti * 4 + r) * mask_ld + tj / 8] = v;
+      // keep mask of the row's 4 TPT elements, element e at bits [8 ESZ e, 8 ESZ (e + 1))
+      u32x4 wv;
+#pragma unroll
+      for (int d = 0; d < 4; d++) {
+        uint32_t m = 0;
+#pragma unroll
+        for (int x = 0; x < 4 / ESZ; x++) {
+          const int e = d * (4 / ESZ) + x;
+          m |= ((rowbits[r] >> e) & 1u) ? (ESZ == 2 ? 0xFFFFu : 0xFFu) << (8 * ESZ * x) : 0u;
+        }
+        wv[d] = pk[r][d] & m;
+      }
+      const int64_t idx = (ti * 4 + r) * ld + tj0 * 4;
+      if (full) {
+        *(u32x4*)(out + idx * ESZ) = wv;
+      } else {
+#pragma unroll
+        for (int t = 0; t < TPT; t++) {
+          if (tj0 + t >= ntiles) continue;
+          uint32_t v[4];
+#pragma unroll
+          for (int c = 0; c < 4; c++) {
+            const int e = 4 * t + c;
+            v[c] = ESZ == 2 ? (wv[e / 2] >> (16 * (e & 1))) & 0xFFFFu : (wv[e / 4] >> (8 * (e & 3))) & 0xFFu;
+          }
+          store_row4<ESZ>(out, idx + 4 * t, false, v);
+        }
+      }
     }
+    if (mask) {
+      // 8 consecutive tiles share a 32-bit mask word per row: OR the 8 / TPT lanes holding them.
+      const int sub = (int)(tj0 % 8);
+#pragma unroll
+      for (int r = 0; r < 4; r++) {
+        uint32_t v = rowbits[r] << (4 * sub);
+#pragma unroll
+        for (int off = 1; off < 8 / TPT; off <<= 1) v |= __shfl_xor(v, off);
+        if (any && sub == 0) mask[(ti * 4 + r) * mask_ld + tj0 / 8] = v;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; r++) pk[r] = nx[r];
   }
 }
 
@@ -441,17 +780,19 @@ __global__ void __launch_bounds__(TPB) check1d_kernel(const uint8_t* a, int64_t 
 
 template <int DT, int ESZ>
 __global__ void __launch_bounds__(TPB) check_tile_kernel(const uint8_t* a, int64_t rows, int64_t cols, int64_t ld,
-                                                         int32_t* count) {
+                                                         int vec, int32_t* count) {
   const int64_t tj = (int64_t)blockIdx.x * TPB + threadIdx.x;
   const int64_t ti = blockIdx.y;
   int bad = 0;
   if (tj < cols / 4) {
     uint32_t nzm = 0;   // bit r*4+c set when element (r, c) is non-zero
 #pragma unroll
-    for (int r = 0; r < 4; r++)
+    for (int r = 0; r < 4; r++) {
+      uint32_t v[4];
+      load_row4<ESZ>(a, (ti * 4 + r) * ld + tj * 4, vec, v);
 #pragma unroll
-      for (int c = 0; c < 4; c++)
-        nzm |= (magkey<DT>(load_raw<DT, ESZ>(a, (ti * 4 + r) * ld + tj * 4 + c)) != 0u ? 1u : 0u) << (r * 4 + c);
+      for (int c = 0; c < 4; c++) nzm |= (magkey<DT>(v[c]) != 0u ? 1u : 0u) << (r * 4 + c);
+    }
 #pragma unroll
     for (int x = 0; x < 4; x++) {
       bad += __builtin_popcount((nzm >> (4 * x)) & 0xFu) > 2;
@@ -560,17 +901,32 @@ hipError_t launch_mask_apply(const nm_plan& pl, const uint32_t* mask, void* x, h
   return hipGetLastError();
 }
 
+// Every tile row is one naturally aligned word: the base and the leading
+// dimension are multiples of four elements.
+static bool tile_rows_aligned(const nm_plan& pl, const void* p) {
+  return ((uintptr_t)p % (4 * (uintptr_t)pl.esz_ab)) == 0 && pl.p.lda % 4 == 0;
+}
+// Every row starts on a 16-byte boundary.
+static bool rows_aligned16(const nm_plan& pl, const void* p) {
+  return ((uintptr_t)p % 16) == 0 && (pl.p.lda * pl.esz_ab) % 16 == 0;
+}
+
 hipError_t launch_prune_tile(const nm_plan& pl, const void* a, void* out, uint32_t* mask, hipStream_t s) {
   const int64_t rows = pl.a_rows, cols = pl.a_cols;
   if (rows == 0 || cols == 0) return hipSuccess;
-  const dim3 grid((unsigned)((cols / 4 + TPB - 1) / TPB), (unsigned)(rows / 4));
+  const int64_t tpt = 16 / (4 * pl.esz_ab);   // tiles per thread
+  // about 1024 blocks (four resident per compute unit), each striding down the tile rows
+  const int64_t gx = (cols / 4 + tpt * TPB - 1) / (tpt * TPB);
+  const int64_t gy = std::min<int64_t>(rows / 4, std::max<int64_t>(1, 1024 / gx));
+  const dim3 grid((unsigned)gx, (unsigned)gy);
   const int64_t mld = (cols + 31) / 32;
   const uint8_t* ap = (const uint8_t*)a;
   uint8_t* op = (uint8_t*)out;
+  const int vec = rows_aligned16(pl, a) && rows_aligned16(pl, out);
   switch (pl.p.type_ab) {
-    case NM_F16: hipLaunchKernelGGL((tile4_prune_kernel<DT_F16, 2>), grid, dim3(TPB), 0, s, ap, op, mask, rows, cols, pl.p.lda, mld); break;
-    case NM_BF16: hipLaunchKernelGGL((tile4_prune_kernel<DT_BF16, 2>), grid, dim3(TPB), 0, s, ap, op, mask, rows, cols, pl.p.lda, mld); break;
-    default: hipLaunchKernelGGL((tile4_prune_kernel<DT_I8, 1>), grid, dim3(TPB), 0, s, ap, op, mask, rows, cols, pl.p.lda, mld); break;
+    case NM_F16: hipLaunchKernelGGL((tile4_prune_kernel<DT_F16, 2>), grid, dim3(TPB), 0, s, ap, op, mask, rows, cols, pl.p.lda, mld, vec); break;
+    case NM_BF16: hipLaunchKernelGGL((tile4_prune_kernel<DT_BF16, 2>), grid, dim3(TPB), 0, s, ap, op, mask, rows, cols, pl.p.lda, mld, vec); break;
+    default: hipLaunchKernelGGL((tile4_prune_kernel<DT_I8, 1>), grid, dim3(TPB), 0, s, ap, op, mask, rows, cols, pl.p.lda, mld, vec); break;
   }
   return hipGetLastError();
 }
@@ -584,10 +940,11 @@ hipError_t launch_check(const nm_plan& pl, const void* a, int mode, int32_t* cou
     const int64_t rows = pl.a_rows, cols = pl.a_cols;
     if (rows == 0 || cols == 0) return hipSuccess;
     const dim3 grid((unsigned)((cols / 4 + TPB - 1) / TPB), (unsigned)(rows / 4));
+    const int vec = tile_rows_aligned(pl, a);
     switch (pl.p.type_ab) {
-      case NM_F16: hipLaunchKernelGGL((check_tile_kernel<DT_F16, 2>), grid, dim3(TPB), 0, s, ap, rows, cols, pl.p.lda, count); break;
-      case NM_BF16: hipLaunchKernelGGL((check_tile_kernel<DT_BF16, 2>), grid, dim3(TPB), 0, s, ap, rows, cols, pl.p.lda, count); break;
-      default: hipLaunchKernelGGL((check_tile_kernel<DT_I8, 1>), grid, dim3(TPB), 0, s, ap, rows, cols, pl.p.lda, count); break;
+      case NM_F16: hipLaunchKernelGGL((check_tile_kernel<DT_F16, 2>), grid, dim3(TPB), 0, s, ap, rows, cols, pl.p.lda, vec, count); break;
+      case NM_BF16: hipLaunchKernelGGL((check_tile_kernel<DT_BF16, 2>), grid, dim3(TPB), 0, s, ap, rows, cols, pl.p.lda, vec, count); break;
+      default: hipLaunchKernelGGL((check_tile_kernel<DT_I8, 1>), grid, dim3(TPB), 0, s, ap, rows, cols, pl.p.lda, vec, count); break;
     }
     return hipGetLastError();
   }

@@ -360,6 +360,47 @@ def test_prune_tile_nan_and_inf(dtype):
     assert int(cnt.item()) == 0
 
 
+def wide_bf16_tiles(seed):
+    """bf16 tiles whose magnitudes span up to the whole exponent range, so that
+    fp64 sums of kept magnitudes round: random exponents over all finite values
+    (subnormals included), tiles with one huge element that absorbs the rest (every
+    candidate keeping it ties after rounding), and tiles whose exponent fields
+    span 32 and 33 binades (the edge of the exactly keyed case)."""
+    rng = np.random.default_rng(seed)
+    rows, cols = 64, 128
+    sign = rng.integers(0, 2, (rows, cols)).astype(np.uint16) << 15
+    expo = rng.integers(0, 255, (rows, cols)).astype(np.uint16) << 7
+    mant = rng.integers(0, 128, (rows, cols)).astype(np.uint16)
+    a = sign | expo | mant
+    small = (0x3F80 + rng.integers(0, 128, (16, 128))).astype(np.uint16)   # [1, 2)
+    a[16:32] = small
+    for t in range(32):
+        r, c = 16 + 4 * (t % 4), 4 * (t // 4)
+        a[r + (t % 3), c + (t % 4)] = 0x7180 + (t % 7)                         # about 2^100
+    edge = (0x3F80 + rng.integers(0, 128, (32, 128))).astype(np.uint16)
+    a[32:64] = edge
+    for t in range(64):
+        r, c = 32 + 4 * (t % 8), 4 * (t // 8)
+        spread = 32 if t % 2 == 0 else 33
+        a[r + (t % 4), c + ((t // 2) % 4)] = (0x3F80 + (spread << 7)) | (t % 128)
+    return a
+
+
+def test_prune_tile_wide_bf16_exponents():
+    """Exponent spreads where fp64 sums round: the fixed-order score and its
+    first maximum decide, as in the definition."""
+    a = wide_bf16_tiles(31)
+    ref, keep = oracle.prune_tile(a, "bf16")
+    plan = plan_for("bf16", a.shape[0], 16, a.shape[1], 2, 4)
+    out = Guarded(a.shape, TRAW["bf16"])
+    mask = Guarded((plan.mask_bytes // 4,), torch.int32)
+    nm.nm_prune(plan, dev(a), out.t, "tile", mask.t)
+    sync()
+    out.check(); mask.check()
+    assert np.array_equal(host(out.t, RAW["bf16"]), ref)
+    assert np.array_equal(host(mask.t, np.uint32).reshape(a.shape[0], -1), oracle.mask_bits(keep))
+
+
 # ------------------------------------------------------------------ products
 
 def ref_product(dtype, ahat_logical, b_logical, alpha, beta, c):
