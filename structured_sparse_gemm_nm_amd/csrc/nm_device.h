@@ -20,6 +20,24 @@ enum Dt { DT_F16 = 0, DT_BF16 = 1, DT_I8 = 2 };
 
 // Magnitude key: unsigned, ordered like |x|. 16-bit floats: bits with the sign
 // cleared (+0 and -0 both give 0). int8: |x|.
+// Violation counting. Counting kernels stride over their work with at most
+// kCheckBlocks blocks (about four per compute unit) and add each block's total
+// to the caller's counter with one atomic, none when it is zero: atomics on a
+// single address serialize, so one per wave over a large matrix would dominate
+// the kernel. Every thread of the block must reach the call.
+constexpr int64_t kCheckBlocks = 1024;
+__device__ __forceinline__ void block_add_count(int32_t* count, int v) {
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+  __shared__ int32_t part[16];
+  if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = v;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int32_t t = 0;
+    for (int i = 0; i < (int)(blockDim.x >> 6); i++) t += part[i];
+    if (t) atomicAdd(count, t);
+  }
+}
+
 template <int DT> __device__ __forceinline__ uint32_t magkey(uint32_t raw);
 template <> __device__ __forceinline__ uint32_t magkey<DT_F16>(uint32_t raw) { return raw & 0x7FFFu; }
 template <> __device__ __forceinline__ uint32_t magkey<DT_BF16>(uint32_t raw) { return raw & 0x7FFFu; }

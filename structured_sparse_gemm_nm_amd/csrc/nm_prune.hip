@@ -312,36 +312,19 @@ __device__ __forceinline__ uint32_t load_raw(const uint8_t* p, int64_t idx) {
   return ESZ == 2 ? (uint32_t)((const uint16_t*)p)[idx] : (uint32_t)p[idx];
 }
 
-// One row of a 4x4 tile (four elements from idx on). With vec the four are
-// one naturally aligned 8-byte (16-bit types) or 4-byte (int8) word: one load,
-// one store per row instead of four.
+// One row of a 4x4 tile, element by element (four elements from idx on): the
+// ragged last tiles of a row and rows that are not 16-byte aligned.
 template <int ESZ>
-__device__ __forceinline__ void load_row4(const uint8_t* p, int64_t idx, bool vec, uint32_t (&v)[4]) {
-  if (vec) {
-    if constexpr (ESZ == 2) {
-      const u32x2 w = *(const u32x2*)(p + idx * 2);
-      v[0] = w[0] & 0xFFFFu; v[1] = w[0] >> 16; v[2] = w[1] & 0xFFFFu; v[3] = w[1] >> 16;
-    } else {
-      const uint32_t w = *(const uint32_t*)(p + idx);
+__device__ __forceinline__ void load_row4(const uint8_t* p, int64_t idx, uint32_t (&v)[4]) {
 #pragma unroll
-      for (int c = 0; c < 4; c++) v[c] = (w >> (8 * c)) & 0xFFu;
-    }
-  } else {
-#pragma unroll
-    for (int c = 0; c < 4; c++) v[c] = load_raw<0, ESZ>(p, idx + c);
-  }
+  for (int c = 0; c < 4; c++) v[c] = load_raw<0, ESZ>(p, idx + c);
 }
 template <int ESZ>
-__device__ __forceinline__ void store_row4(uint8_t* p, int64_t idx, bool vec, const uint32_t (&v)[4]) {
-  if (vec) {
-    if constexpr (ESZ == 2) *(u32x2*)(p + idx * 2) = u32x2{v[0] | v[1] << 16, v[2] | v[3] << 16};
-    else *(uint32_t*)(p + idx) = v[0] | v[1] << 8 | v[2] << 16 | v[3] << 24;
-  } else {
+__device__ __forceinline__ void store_row4(uint8_t* p, int64_t idx, const uint32_t (&v)[4]) {
 #pragma unroll
-    for (int c = 0; c < 4; c++) {
-      if (ESZ == 2) ((uint16_t*)p)[idx + c] = (uint16_t)v[c];
-      else p[idx + c] = (uint8_t)v[c];
-    }
+  for (int c = 0; c < 4; c++) {
+    if (ESZ == 2) ((uint16_t*)p)[idx + c] = (uint16_t)v[c];
+    else p[idx + c] = (uint8_t)v[c];
   }
 }
 
@@ -629,7 +612,7 @@ __device__ __forceinline__ void load_tile_rows(const uint8_t* a, int64_t ti, int
       uint32_t v[TPT][4];
 #pragma unroll
       for (int t = 0; t < TPT; t++) {
-        if (tj0 + t < ntiles) load_row4<ESZ>(a, idx + 4 * t, false, v[t]);
+        if (tj0 + t < ntiles) load_row4<ESZ>(a, idx + 4 * t, v[t]);
         else v[t][0] = v[t][1] = v[t][2] = v[t][3] = 0u;
       }
 #pragma unroll
@@ -712,7 +695,7 @@ __global__ void __launch_bounds__(TPB) tile4_prune_kernel(const uint8_t* a, uint
             const int e = 4 * t + c;
             v[c] = ESZ == 2 ? (wv[e / 2] >> (16 * (e & 1))) & 0xFFFFu : (wv[e / 4] >> (8 * (e & 3))) & 0xFFu;
           }
-          store_row4<ESZ>(out, idx + 4 * t, false, v);
+          store_row4<ESZ>(out, idx + 4 * t, v);
         }
       }
     }
@@ -734,19 +717,12 @@ __global__ void __launch_bounds__(TPB) tile4_prune_kernel(const uint8_t* a, uint
 
 // ------------------------------------------------------------------ checks
 
-__device__ __forceinline__ void add_count(int32_t* count, int v) {
-  // wave reduction, then one atomic per wave
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  if ((threadIdx.x & 63) == 0 && v) atomicAdd(count, v);
-}
-
 template <int DT, int ESZ>
 __global__ void __launch_bounds__(TPB) check1d_kernel(const uint8_t* a, int64_t m, int64_t k, int64_t lda,
                                                       int N, int M, int op_t, int vec_ok, int32_t* count) {
   const int64_t groups = k / M;
-  const int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x;
   int bad = 0;
-  if (t < m * groups) {
+  for (int64_t t = (int64_t)blockIdx.x * TPB + threadIdx.x; t < m * groups; t += (int64_t)gridDim.x * TPB) {
     int64_t i, g;
     if (op_t) { i = t % m; g = t / m; }        // lanes along stored columns
     else { i = t / groups; g = t % groups; }   // lanes along a stored row
@@ -773,33 +749,43 @@ __global__ void __launch_bounds__(TPB) check1d_kernel(const uint8_t* a, int64_t 
         nz += magkey<DT>(load_raw<DT, ESZ>(a, idx)) != 0u;
       }
     }
-    bad = nz > N;
+    bad += nz > N;
   }
-  add_count(count, bad);
+  block_add_count(count, bad);
 }
 
 template <int DT, int ESZ>
 __global__ void __launch_bounds__(TPB) check_tile_kernel(const uint8_t* a, int64_t rows, int64_t cols, int64_t ld,
                                                          int vec, int32_t* count) {
-  const int64_t tj = (int64_t)blockIdx.x * TPB + threadIdx.x;
-  const int64_t ti = blockIdx.y;
+  // the tile prune's geometry: TPT adjacent tiles per thread, 16-byte rows when aligned
+  constexpr int TPT = 16 / (4 * ESZ);
+  const int64_t ntiles = cols / 4;
+  const int64_t tj0 = ((int64_t)blockIdx.x * TPB + threadIdx.x) * TPT;
+  const bool full = vec && tj0 + TPT <= ntiles;
   int bad = 0;
-  if (tj < cols / 4) {
-    uint32_t nzm = 0;   // bit r*4+c set when element (r, c) is non-zero
+  for (int64_t ti = blockIdx.y; tj0 < ntiles && ti < rows / 4; ti += gridDim.y) {
+    u32x4 pk[4];
+    load_tile_rows<ESZ>(a, ti, ld, tj0, ntiles, full, pk);
 #pragma unroll
-    for (int r = 0; r < 4; r++) {
-      uint32_t v[4];
-      load_row4<ESZ>(a, (ti * 4 + r) * ld + tj * 4, vec, v);
+    for (int t = 0; t < TPT; t++) {
+      uint32_t nzm = 0;   // bit r*4+c set when element (r, c) of tile t is non-zero
 #pragma unroll
-      for (int c = 0; c < 4; c++) nzm |= (magkey<DT>(v[c]) != 0u ? 1u : 0u) << (r * 4 + c);
-    }
+      for (int r = 0; r < 4; r++)
 #pragma unroll
-    for (int x = 0; x < 4; x++) {
-      bad += __builtin_popcount((nzm >> (4 * x)) & 0xFu) > 2;
-      bad += __builtin_popcount(nzm & (0x1111u << x)) > 2;
+        for (int c = 0; c < 4; c++) {
+          const int e = 4 * t + c;
+          const uint32_t word = pk[r][e * ESZ / 4];
+          const uint32_t raw = ESZ == 2 ? (word >> (16 * (e & 1))) & 0xFFFFu : (word >> (8 * (e & 3))) & 0xFFu;
+          nzm |= (magkey<DT>(raw) != 0u ? 1u : 0u) << (r * 4 + c);
+        }
+#pragma unroll
+      for (int x = 0; x < 4; x++) {
+        bad += __builtin_popcount((nzm >> (4 * x)) & 0xFu) > 2;
+        bad += __builtin_popcount(nzm & (0x1111u << x)) > 2;
+      }
     }
   }
-  add_count(count, bad);
+  block_add_count(count, bad);
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int32_t v) { *p = v; }
@@ -901,11 +887,6 @@ hipError_t launch_mask_apply(const nm_plan& pl, const uint32_t* mask, void* x, h
   return hipGetLastError();
 }
 
-// Every tile row is one naturally aligned word: the base and the leading
-// dimension are multiples of four elements.
-static bool tile_rows_aligned(const nm_plan& pl, const void* p) {
-  return ((uintptr_t)p % (4 * (uintptr_t)pl.esz_ab)) == 0 && pl.p.lda % 4 == 0;
-}
 // Every row starts on a 16-byte boundary.
 static bool rows_aligned16(const nm_plan& pl, const void* p) {
   return ((uintptr_t)p % 16) == 0 && (pl.p.lda * pl.esz_ab) % 16 == 0;
@@ -939,8 +920,10 @@ hipError_t launch_check(const nm_plan& pl, const void* a, int mode, int32_t* cou
   if (mode == NM_PRUNE_TILE4X4) {
     const int64_t rows = pl.a_rows, cols = pl.a_cols;
     if (rows == 0 || cols == 0) return hipSuccess;
-    const dim3 grid((unsigned)((cols / 4 + TPB - 1) / TPB), (unsigned)(rows / 4));
-    const int vec = tile_rows_aligned(pl, a);
+    const int64_t tpt = 16 / (4 * pl.esz_ab);
+    const int64_t gx = (cols / 4 + tpt * TPB - 1) / (tpt * TPB);
+    const dim3 grid((unsigned)gx, (unsigned)std::min<int64_t>(rows / 4, std::max<int64_t>(1, kCheckBlocks / gx)));
+    const int vec = rows_aligned16(pl, a);
     switch (pl.p.type_ab) {
       case NM_F16: hipLaunchKernelGGL((check_tile_kernel<DT_F16, 2>), grid, dim3(TPB), 0, s, ap, rows, cols, pl.p.lda, vec, count); break;
       case NM_BF16: hipLaunchKernelGGL((check_tile_kernel<DT_BF16, 2>), grid, dim3(TPB), 0, s, ap, rows, cols, pl.p.lda, vec, count); break;
@@ -951,7 +934,7 @@ hipError_t launch_check(const nm_plan& pl, const void* a, int mode, int32_t* cou
   const int64_t total = pl.p.m * (pl.p.k / pl.p.nm_m);
   if (total == 0) return hipSuccess;
   if (check_row_ok(pl) && !pl.tile_elemwise) return launch_check_row(pl, a, count, s);
-  const dim3 grid((unsigned)((total + TPB - 1) / TPB));
+  const dim3 grid((unsigned)std::min<int64_t>((total + TPB - 1) / TPB, kCheckBlocks));
   const int opt = pl.p.op_a == NM_OP_T;
   const int vec = (pl.p.lda * pl.esz_ab) % 16 == 0;
   switch (pl.p.type_ab) {

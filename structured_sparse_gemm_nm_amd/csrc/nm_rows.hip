@@ -520,9 +520,11 @@ __global__ void __launch_bounds__(256) check_row_kernel(const uint8_t* a, int64_
   constexpr int PPU = GB > 16 ? GB / 16 : 1;            // chunks per group
   constexpr int GPC = GB >= 16 ? 1 : 16 / GB;           // groups per chunk
   const int lane = threadIdx.x & 63;
-  const int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int64_t total = m * chunks_row;
+  const int64_t nwaves = (total + 64 * CHECK_CHUNKS_PER_LANE - 1) / (64 * CHECK_CHUNKS_PER_LANE);
   const int64_t row_bytes = k * ESZ;
+  int bad = 0;
+  for (int64_t wave = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); wave < nwaves; wave += (int64_t)gridDim.x * 4) {
   u32x4 v[CHECK_CHUNKS_PER_LANE];
 #pragma unroll
   for (int i = 0; i < CHECK_CHUNKS_PER_LANE; i++) {
@@ -540,7 +542,6 @@ __global__ void __launch_bounds__(256) check_row_kernel(const uint8_t* a, int64_
       }
     }
   }
-  int bad = 0;
 #pragma unroll
   for (int i = 0; i < CHECK_CHUNKS_PER_LANE; i++) {
     const int64_t t = (wave * CHECK_CHUNKS_PER_LANE + i) * 64 + lane;
@@ -565,8 +566,8 @@ __global__ void __launch_bounds__(256) check_row_kernel(const uint8_t* a, int64_
       for (int g = 0; g < GPC; g++) bad += nz[g] > N;     // zero-filled groups past k count 0
     }
   }
-  for (int off = 32; off > 0; off >>= 1) bad += __shfl_xor(bad, off);
-  if (lane == 0 && bad) atomicAdd(count, bad);
+  }
+  block_add_count(count, bad);
 }
 
 bool check_row_ok(const nm_plan& pl) {
@@ -576,8 +577,7 @@ bool check_row_ok(const nm_plan& pl) {
 hipError_t launch_check_row(const nm_plan& pl, const void* a, int32_t* count, hipStream_t s) {
   const int64_t chunks_row = (pl.p.k * pl.esz_ab + 15) / 16;
   const int64_t waves = (pl.p.m * chunks_row + 64 * CHECK_CHUNKS_PER_LANE - 1) / (64 * CHECK_CHUNKS_PER_LANE);
-  const int64_t blocks = (waves + 3) / 4;
-  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  const int64_t blocks = std::min<int64_t>((waves + 3) / 4, kCheckBlocks);
   const uint8_t* ap = (const uint8_t*)a;
   const dim3 grid((unsigned)blocks), block(256);
   const int64_t m = pl.p.m, k = pl.p.k, lda = pl.p.lda;

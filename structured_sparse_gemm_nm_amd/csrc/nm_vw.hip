@@ -84,12 +84,15 @@ __global__ void __launch_bounds__(VW_COLS) vw_elem_kernel(VwArgs A) {
   const int nbytes = (int)((chunk_groups * N * b + 7) / 8);
 
   if constexpr (OP == VW_CHECK) {
-    bool nz = false;
-    for (int v = 0; v < A.V; v++) nz |= in && nonzero<DT>(ld_raw<ESZ>(A.a, (r0 + v) * A.lda + c));
-    const uint64_t used = __ballot(nz) & group_lanes;
-    int bad = (j == 0 && in && __popcll(used) > N) ? 1 : 0;
-    for (int off = 32; off > 0; off >>= 1) bad += __shfl_xor(bad, off);
-    if (lane == 0 && bad) atomicAdd(A.count, bad);
+    // the grid strides down the row blocks
+    int bad = 0;
+    for (int64_t rb = blk; rb < A.m / A.V; rb += gridDim.y) {
+      bool nz = false;
+      for (int v = 0; v < A.V; v++) nz |= in && nonzero<DT>(ld_raw<ESZ>(A.a, (rb * A.V + v) * A.lda + c));
+      const uint64_t used = __ballot(nz) & group_lanes;
+      bad += (j == 0 && in && __popcll(used) > N) ? 1 : 0;
+    }
+    block_add_count(A.count, bad);
     return;
   }
 
@@ -187,7 +190,8 @@ static VwArgs make_vw_args(const nm_plan& pl) {
 template <int OP>
 static hipError_t launch_vw(const nm_plan& pl, const VwArgs& A, hipStream_t s) {
   if (A.m == 0 || A.k == 0) return hipSuccess;
-  const dim3 grid((unsigned)((A.k + VW_COLS - 1) / VW_COLS), (unsigned)(A.m / A.V));
+  const int64_t gx = (A.k + VW_COLS - 1) / VW_COLS, gy = A.m / A.V;
+  const dim3 grid((unsigned)gx, (unsigned)(OP == VW_CHECK ? std::min<int64_t>(gy, std::max<int64_t>(1, kCheckBlocks / gx)) : gy));
   switch (pl.p.type_ab) {
     case NM_F16: hipLaunchKernelGGL((vw_elem_kernel<DT_F16, OP>), grid, dim3(VW_COLS), 0, s, A); break;
     case NM_BF16: hipLaunchKernelGGL((vw_elem_kernel<DT_BF16, OP>), grid, dim3(VW_COLS), 0, s, A); break;
