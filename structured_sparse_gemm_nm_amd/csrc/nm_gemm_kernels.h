@@ -1041,7 +1041,6 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
     const bool meta_fill = M4 && (ks & 3) == 0 && ks + 4 < ksteps;
 #pragma unroll
     for (int g = 0; g < G; g++) {
-      __builtin_amdgcn_sched_barrier(0);
       if constexpr (M4) {
         if (g == 0 && meta_fill) issue_meta((ks >> 2) + 1);
       }
@@ -1066,7 +1065,6 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
         lds_barrier();                                   // every wave is done reading stage ks
         load_group(ring + ((ks + 1) % S) * STAGE, 0, ks + 1);
       }
-      __builtin_amdgcn_sched_barrier(0);
       compute_group(g);
     }
   }

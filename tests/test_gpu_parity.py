@@ -485,7 +485,8 @@ def test_spmm_identity_is_bit_exact(dtype):
 def test_spmm_kernel_names_the_launched_kernel():
     # the name comes from the same host logic that launches (dry run)
     big = plan_for("f16", 4096, 4096, 1024, 2, 4, op_b="T").spmm_kernel
-    assert big.startswith("void nm::gemm_dma_kernel<0, 0, 256, 256,") and big.endswith(", 1>(nm::GemmArgs)"), big
+    # op_b = T with metadata staged four k-steps at a time: layout bits 1 | 4
+    assert big.startswith("void nm::gemm_dma_kernel<0, 0, 256, 256,") and big.endswith(", 5>(nm::GemmArgs)"), big
     nn = plan_for("bf16", 1024, 4096, 4096, 2, 4, op_b="N").spmm_kernel
     assert nn.startswith("void nm::gemm_dma_kernel<1, 0, 128, 128,") and nn.endswith(", 2, 4, 0>(nm::GemmArgs)"), nn
     nt = plan_for("bf16", 1024, 4096, 4096, 2, 4, op_b="T").spmm_kernel
