@@ -436,6 +436,38 @@ def main():
                     t = e0.elapsed_time(e1) / reps
                     best = t if best is None else min(best, t)
                 dense[(g["label"], ob)] = best
+    # vendor dense GEMM (torch.matmul, hipBLASLt on this platform) on the same
+    # pruned A and B, as a reference for the in-library dense comparator: the
+    # plain product op(A) op(B) in the operand type (no alpha, beta or C), int8
+    # through torch._int_mm where the build supports it
+    vendor = {}
+    if not args.no_dense:
+        tdt = {"f16": torch.float16, "bf16": torch.bfloat16}
+        for g in gemms:
+            a_dense = g["Ap"] if g["op_a"] == "N" else g["Ap"].t().contiguous()
+            for ob in g["layouts"]:
+                bt = g["B"][ob]
+                try:
+                    if g["dtype"] == "i8":
+                        a8 = a_dense.view(torch.int8)
+                        b8 = (bt.view(torch.int8).t() if ob == "T" else bt.view(torch.int8))
+                        f = lambda: torch._int_mm(a8, b8)
+                    else:
+                        av = a_dense.view(tdt[g["dtype"]])
+                        bv = bt.view(tdt[g["dtype"]])
+                        f = (lambda: torch.matmul(av, bv.t())) if ob == "T" else (lambda: torch.matmul(av, bv))
+                    for _ in range(max(2, args.warmup)):
+                        f()
+                    e0 = torch.cuda.Event(enable_timing=True); e1 = torch.cuda.Event(enable_timing=True)
+                    reps = max(5, args.steps)
+                    e0.record(stream)
+                    for _ in range(reps):
+                        f()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    vendor[(g["label"], ob)] = e0.elapsed_time(e1) / reps
+                except (RuntimeError, NotImplementedError):
+                    pass
     per_gemm = []
     for g in gemms:
         for ob in g["layouts"]:
@@ -451,10 +483,17 @@ def main():
                 row["dense_tflops"] = round(flops_dense_eq(g) / (dense[key] * 1e-3) / 1e12, 2)
                 row["dense_frac_of_dense_peak"] = round(row["dense_tflops"] / PEAK_TFLOPS[g["dtype"]], 4)
                 row["speedup"] = round(dense[key] / t_s, 3)
+            if key in vendor:
+                row["vendor_dense_ms"] = round(vendor[key], 5)
+                row["vendor_dense_tflops"] = round(flops_dense_eq(g) / (vendor[key] * 1e-3) / 1e12, 2)
+                row["speedup_vs_vendor_dense"] = round(vendor[key] / t_s, 3)
             per_gemm.append(row)
     speedup = None
     if dense:
         speedup = round(sum(dense.values()) / spmm_total_ms, 3)
+    speedup_vendor = None
+    if vendor and len(vendor) == len(spmm_ms):
+        speedup_vendor = round(sum(vendor.values()) / spmm_total_ms, 3)
 
     # measured achievable peaks (calibration loops, outside the timed region)
     cal = calibrate(torch, stream, dtype_dom)
@@ -490,6 +529,7 @@ def main():
                    "step": "prune+check+compress+spmm(per layout)+decompress per weight"},
         "spmm_only_tflops": round(spmm_only_tflops, 2),
         "speedup_vs_dense": speedup,
+        "speedup_vs_vendor_dense": speedup_vendor,
         "per_gemm": per_gemm,
         "roofline": roofline,
         "cpu_baseline": cpu,
