@@ -156,8 +156,10 @@ static hipError_t launch_tiles_any(const nm_plan& pl, int amode, const GemmArgs&
 // The streamed small-n kernel needs each group's kept values to be one
 // naturally aligned load (N * esize a power of two <= 16 bytes) and its
 // offsets inside a 3-dword window (N * b <= 64); for the dense comparator,
-// op_a = N, 16-byte aligned rows and k a whole number of 16-byte chunks.
+// op_a = N, 16-byte aligned rows and k a whole number of 16-byte chunks. Its
+// row, k and group indices are 32-bit: m and k below 2^30.
 static bool skinny2_ok(const nm_plan& pl, bool dense_a) {
+  if (pl.p.m >= ((int64_t)1 << 30) || pl.p.k >= ((int64_t)1 << 30)) return false;
   if (dense_a)
     return pl.p.op_a == NM_OP_N && (pl.p.lda * pl.esz_ab) % 16 == 0 && (pl.p.k * pl.esz_ab) % 16 == 0;
   const int vb = pl.p.nm_n * pl.esz_ab;

@@ -65,9 +65,12 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
   const int lm = __builtin_ctz(M), lw = lm + 6;             // M and W are powers of two
   // B rows can be copied whole: op N, n equal to the record width, rows aligned to it
   const bool b_rowvec = RB <= 16 && !b_op_t && n == NP && ((A.ldb * ESZ) % RB) == 0;
-  const int64_t row_groups = (A.m + SK2_WAVES * RW - 1) / (SK2_WAVES * RW);
+  // the host launches this kernel only for m, k < 2^30, so row, k and group
+  // indices are 32-bit; byte offsets are formed in 64 bits
+  const int mm = (int)A.m;
+  const int row_groups = (mm + SK2_WAVES * RW - 1) / (SK2_WAVES * RW);
   const bool one_chunk = A.k <= KC;
-  const int64_t mwords = A.mld / 4;
+  const int mwords = (int)(A.mld / 4);
 
   auto elem = [&](uint32_t raw) __attribute__((always_inline)) -> acc_t {
     if constexpr (ESZ == 2) return from_bits16<FDT>((uint16_t)raw);
@@ -97,17 +100,17 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
   // Loads are unconditional (indices clamped into the operand) so that none
   // sits behind a branch: rows past m load row m - 1 and are never written;
   // groups past the chunk load its last group and are zeroed at use.
-  auto load_piece = [&](int64_t row, int64_t kc, int kn, int it, Piece& pc) __attribute__((always_inline)) {
-    row = row < A.m ? row : A.m - 1;
+  auto load_piece = [&](int row, int kc, int kn, int it, Piece& pc) __attribute__((always_inline)) {
+    row = row < mm ? row : mm - 1;
     const int g = it * 64 + lane;
     if constexpr (DENSE_A) {                                // k is a whole number of 16-byte chunks
       const int kk0 = g * EPC < kn - EPC ? g * EPC : kn - EPC;
-      const u32x4 v = *(const u32x4*)(A.a + (size_t)(row * A.lda + kc + kk0) * ESZ);
+      const u32x4 v = *(const u32x4*)(A.a + ((size_t)row * (size_t)A.lda + (size_t)(kc + kk0)) * ESZ);
       pc.v[0] = v[0]; pc.v[1] = v[1]; pc.v[2] = v[2]; pc.v[3] = v[3];
     } else {
       const int units = kn >> lm;
-      const int64_t gg = (kc >> lm) + (g < units ? g : units - 1);
-      const uint8_t* p = A.a + (size_t)(row * A.lda + gg * NV) * ESZ;
+      const int gg = (kc >> lm) + (g < units ? g : units - 1);
+      const uint8_t* p = A.a + ((size_t)row * (size_t)A.lda + (size_t)gg * NV) * ESZ;
       if constexpr (VB == 16) { const u32x4 v = *(const u32x4*)p; pc.v[0] = v[0]; pc.v[1] = v[1]; pc.v[2] = v[2]; pc.v[3] = v[3]; }
       else if constexpr (VB == 8) { const u32x2 v = *(const u32x2*)p; pc.v[0] = v[0]; pc.v[1] = v[1]; }
       else if constexpr (VB == 4) pc.v[0] = *(const uint32_t*)p;
@@ -115,20 +118,20 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
       else pc.v[0] = *p;
       // the group's bits end inside the row's stream, so clamping the word
       // index only ever replaces words that are not used
-      const int64_t w0 = (gg * NV * b) >> 5;
-      const uint32_t* mr = (const uint32_t*)(A.meta + (row >> A.vshift) * A.mld);
+      const int w0 = (int)(((int64_t)gg * NV * b) >> 5);
+      const uint32_t* mr = (const uint32_t*)(A.meta + (size_t)(row >> A.vshift) * (size_t)A.mld);
 #pragma unroll
       for (int x = 0; x < MW; x++) pc.m[x] = mr[w0 + x < mwords ? w0 + x : mwords - 1];
     }
   };
-  auto use_piece = [&](int64_t kc, int kn, int it, const Piece& pc, acc_t (&acc)[NP]) __attribute__((always_inline)) {
+  auto use_piece = [&](int kc, int kn, int it, const Piece& pc, acc_t (&acc)[NP]) __attribute__((always_inline)) {
     const int g = it * 64 + lane;
     const int rbase = it * W + lane;                        // record of offset 0 of this lane's group
     const bool valid = DENSE_A ? g * EPC < kn : g < (kn >> lm);
     uint64_t lo = 0, hi = 0;
     int off = 0;
     if constexpr (!DENSE_A) {
-      off = (int)((((kc >> lm) + g) * NV * b) & 31);
+      off = (int)((((int64_t)(kc >> lm) + g) * NV * b) & 31);
       lo = ((uint64_t)pc.m[1] << 32) | pc.m[0];
       if constexpr (MW == 3) hi = ((uint64_t)pc.m[2] << 32) | pc.m[1];
     }
@@ -273,8 +276,8 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
     }
   };
   // combine this wave's sums of row group grp, write them, clear them
-  auto flush = [&](int64_t grp, acc_t (&acc)[RW][NP]) __attribute__((always_inline)) {
-    const int64_t row0 = (grp * SK2_WAVES + wave) * RW;
+  auto flush = [&](int grp, acc_t (&acc)[RW][NP]) __attribute__((always_inline)) {
+    const int64_t row0 = ((int64_t)grp * SK2_WAVES + wave) * RW;
 #pragma unroll
     for (int rr = 0; rr < RW; rr++) {
       const int64_t row = row0 + rr;
@@ -304,31 +307,31 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
   for (int rr = 0; rr < RW; rr++)
 #pragma unroll
     for (int c = 0; c < NP; c++) acc[rr][c] = 0;
-  const int64_t gstride = gridDim.x;                        // blocks walk row groups blockIdx.x + j gridDim.x
+  const int gstride = gridDim.x;                            // blocks walk row groups blockIdx.x + j gridDim.x
   const int kcs = db ? KC / 2 : KC;                         // k per chunk (a multiple of every window)
   const int nchunks = (int)((A.k + kcs - 1) / kcs);
   if (nchunks == 0) {                                       // k = 0: D = beta C
-    for (int64_t grp = blockIdx.x; grp < row_groups; grp += gstride) flush(grp, acc);
+    for (int grp = blockIdx.x; grp < row_groups; grp += gstride) flush(grp, acc);
     return;
   }
   const int kn_last = (int)(A.k - (int64_t)(nchunks - 1) * kcs);
   const int nit_full = kcs / W;
   const int nit_last = DENSE_A ? ((kn_last + EPC - 1) / EPC + 63) / 64 : (kn_last / M + 63) / 64;
-  struct Cur { int64_t grp; int c, it; };
+  struct Cur { int grp, c, it; };
   auto advance = [&](Cur& q) __attribute__((always_inline)) {
     if (++q.it == (q.c == nchunks - 1 ? nit_last : nit_full)) {
       q.it = 0;
       if (++q.c == nchunks) { q.c = 0; q.grp += gstride; }
     }
   };
-  Cur ld{(int64_t)blockIdx.x, 0, 0}, us = ld;
+  Cur ld{(int)blockIdx.x, 0, 0}, us = ld;
   Piece pc[RW][DEPTH];
 #pragma unroll
   for (int u = 0; u < DEPTH; u++) {
-    const int64_t row0 = (ld.grp * SK2_WAVES + wave) * RW;
+    const int row0 = (ld.grp * SK2_WAVES + wave) * RW;
 #pragma unroll
     for (int rr = 0; rr < RW; rr++)
-      load_piece(row0 + rr, (int64_t)ld.c * kcs, ld.c == nchunks - 1 ? kn_last : kcs, ld.it, pc[rr][u]);
+      load_piece(row0 + rr, ld.c * kcs, ld.c == nchunks - 1 ? kn_last : kcs, ld.it, pc[rr][u]);
     advance(ld);
   }
   bool staged = false;
@@ -344,7 +347,7 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
 #pragma unroll
     for (int u = 0; u < DEPTH; u++) {
       if (us.grp >= row_groups) break;
-      const int64_t kc = (int64_t)us.c * kcs;
+      const int kc = us.c * kcs;
       const int kn = us.c == nchunks - 1 ? kn_last : kcs;
       if (us.it == 0) {
         if (us.c == 0 && us.grp != blockIdx.x) flush(us.grp - gstride, acc);
@@ -367,8 +370,8 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
           staged = true;
         }
       }
-      const int64_t lrow0 = (ld.grp * SK2_WAVES + wave) * RW;
-      const int64_t lkc = (int64_t)ld.c * kcs;
+      const int lrow0 = (ld.grp * SK2_WAVES + wave) * RW;
+      const int lkc = ld.c * kcs;
       const int lkn = ld.c == nchunks - 1 ? kn_last : kcs;
 #pragma unroll
       for (int rr = 0; rr < RW; rr++) {
