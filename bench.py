@@ -595,9 +595,10 @@ def _read_counter_csv(d, counter):
         for r in csv.DictReader(open(f)):
             if r.get("Counter_Name") != counter:
                 continue
-            out.setdefault(r["Kernel_Name"], {}).setdefault(r.get("Dispatch_Id", len(out)), 0.0)
-            out[r["Kernel_Name"]][r.get("Dispatch_Id")] += float(r["Counter_Value"])
-    return {k: list(v.values()) for k, v in out.items()}
+            did = int(r.get("Dispatch_Id", 0))
+            out.setdefault(r["Kernel_Name"], {}).setdefault(did, 0.0)
+            out[r["Kernel_Name"]][did] += float(r["Counter_Value"])
+    return {k: [v[d] for d in sorted(v)] for k, v in out.items()}     # in dispatch order
 
 
 def summarize_counters(args):
@@ -614,11 +615,21 @@ def summarize_counters(args):
     ck = copy_kernel(fetch)
     f_scale = cal_bytes / (np.median(fetch[ck]) * 1024)
     w_scale = cal_bytes / (np.median(write[copy_kernel(write)]) * 1024)
+    # the bench line of the fetch run names the dominant kernel; its timed launches are
+    # its last ones in the run (autotuning before them also runs split-k variants of
+    # the same kernel, whose partial-sum planes would inflate an average over all)
+    dom, n_timed = None, 0
+    if args.bench_log:
+        bl = json.loads([l for l in open(args.bench_log) if l.startswith("{")][-1])
+        dom, n_timed = bl["roofline"]["kernel"], bl["roofline"]["launches_per_step"] * bl["steps"]
     kernels = {}
     for k in fetch:
         if k in write and "nm::" in k:
-            kernels[k] = {"fetch_kib": round(float(np.mean(fetch[k])), 1), "write_kib": round(float(np.mean(write[k])), 1),
-                          "dispatches": len(fetch[k])}
+            fv, wv = fetch[k], write[k]
+            if k == dom and len(fv) >= n_timed and len(wv) >= n_timed:
+                fv, wv = fv[-n_timed:], wv[-n_timed:]
+            kernels[k] = {"fetch_kib": round(float(np.mean(fv)), 1), "write_kib": round(float(np.mean(wv)), 1),
+                          "dispatches": len(fv), "timed_only": k == dom}
     rec = {"workload": args.workload, "sources": source_fingerprint(), "fetch_scale": round(float(f_scale), 4),
            "write_scale": round(float(w_scale), 4), "copy_kernel": ck[:100], "kernels": kernels}
     os.makedirs(PROFILES, exist_ok=True)
@@ -635,6 +646,9 @@ def summarize_counters(args):
         for k, v in sorted(kernels.items(), key=lambda kv: -kv[1]["fetch_kib"]):
             mb = (v["fetch_kib"] * f_scale + v["write_kib"] * w_scale) * 1024 / 1e6
             fh.write("| `%s` | %d | %.1f | %.1f | %.2f |\n" % (k, v["dispatches"], v["fetch_kib"], v["write_kib"], mb))
+        if dom:
+            fh.write("\nThe dominant kernel of the bench line (`%s`) is averaged over its %d timed launches only (its "
+                     "last dispatches of the run); every other kernel over all its dispatches.\n" % (dom, n_timed))
         fh.write("\nSource fingerprint %s: bench.py reports these figures only while the library sources match.\n\n"
                  % rec["sources"])
         fh.write("record: %s\n" % json.dumps(rec))
@@ -770,13 +784,28 @@ def summarize_trace(args):
                                                           float(r["AverageNs"]) / 1e3, float(r["Percentage"])))
         if args.bench_log:
             line = [l for l in open(args.bench_log) if l.startswith("{")][-1]
-            roof = json.loads(line)["roofline"]
+            bl = json.loads(line)
+            roof = bl["roofline"]
             prof = {r["Name"]: float(r["AverageNs"]) / 1e3 for r in rows}
             avg = prof.get(roof["kernel"])
-            fh.write("\nThe bench line of this same run names `%s` as its dominant kernel: HIP-event median %.2f us "
-                     "per launch over the timed steps; rocprofv3 average over all its dispatches %s us%s.\n"
-                     % (roof["kernel"], roof["launch_ms"] * 1e3, "%.2f" % avg if avg else "n/a",
-                        " (ratio %.3f)" % (roof["launch_ms"] * 1e3 / avg) if avg else ""))
+            # the timed region's launches of that kernel are its last ones in the run (the
+            # dense comparator, the vendor GEMM and the calibration loops use other kernels)
+            n_timed = roof["launches_per_step"] * bl["steps"]
+            durs = []
+            for f in glob.glob(os.path.join(args.summarize_trace, "**", "*kernel_trace.csv"), recursive=True):
+                for r in csv.DictReader(open(f)):
+                    if r["Kernel_Name"] == roof["kernel"]:
+                        durs.append((int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+            durs.sort()
+            timed = [d for _, d in durs[-n_timed:]] if len(durs) >= n_timed else []
+            t_avg = sum(timed) / len(timed) if timed else None
+            fh.write("\nThe bench line of this same run names `%s` as its dominant kernel: HIP-event mean %.2f us per "
+                     "launch over the %d timed launches; rocprofv3 mean over those same launches (the kernel's last %d "
+                     "dispatches) %s us%s; over all %d of its dispatches (autotuning and warm-up included) %s us.\n"
+                     % (roof["kernel"], roof["launch_ms"] * 1e3, n_timed, n_timed,
+                        "%.2f" % t_avg if t_avg else "n/a",
+                        " (ratio %.3f)" % (roof["launch_ms"] * 1e3 / t_avg) if t_avg else "",
+                        len(durs), "%.2f" % avg if avg else "n/a"))
             fh.write("\nBench line: `%s`\n" % line.strip()[:600])
     print("wrote", path)
 
