@@ -601,6 +601,14 @@ def _read_counter_csv(d, counter):
     return {k: [v[d] for d in sorted(v)] for k, v in out.items()}     # in dispatch order
 
 
+def _dominant_from_log(bench_log):
+    """(dominant kernel name, its launches in the timed region) from a bench run's stdout, or (None, 0)."""
+    if not bench_log:
+        return None, 0
+    bl = json.loads([l for l in open(bench_log) if l.startswith("{")][-1])
+    return bl["roofline"]["kernel"], bl["roofline"]["launches_per_step"] * bl["steps"]
+
+
 def summarize_counters(args):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of every kernel, with the copy calibration."""
     fetch = _read_counter_csv(args.summarize_counters[0], "FETCH_SIZE")
@@ -618,10 +626,7 @@ def summarize_counters(args):
     # the bench line of the fetch run names the dominant kernel; its timed launches are
     # its last ones in the run (autotuning before them also runs split-k variants of
     # the same kernel, whose partial-sum planes would inflate an average over all)
-    dom, n_timed = None, 0
-    if args.bench_log:
-        bl = json.loads([l for l in open(args.bench_log) if l.startswith("{")][-1])
-        dom, n_timed = bl["roofline"]["kernel"], bl["roofline"]["launches_per_step"] * bl["steps"]
+    dom, n_timed = _dominant_from_log(args.bench_log)
     kernels = {}
     for k in fetch:
         if k in write and "nm::" in k:
@@ -678,10 +683,19 @@ def summarize_mfma(args):
             dur.setdefault(k, {})[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
     if not vals:
         raise SystemExit("no counter_collection.csv under %s" % args.summarize_mfma)
+    dom, n_timed = _dominant_from_log(args.bench_log)
     rows = []
     for k, d in vals.items():
+        keep = None
+        if k == dom:                      # its timed launches: its last dispatches of the run
+            ids = sorted({int(disp) for disp, _ in d}, key=int)
+            keep = set(str(i) for i in ids[-n_timed:]) if len(ids) >= n_timed else None
+            if keep is not None:
+                dur[k] = {i: t for i, t in dur[k].items() if i in keep}
         per = {}
         for (disp, cname), v in d.items():
+            if keep is not None and disp not in keep:
+                continue
             per.setdefault(cname, []).append(v)
         mops_name = sorted((c for c in per if c.startswith("SQ_INSTS_VALU_MFMA_MOPS_")),
                            key=lambda c: -float(np.mean(per[c])))          # the type this kernel runs
@@ -714,6 +728,10 @@ def summarize_mfma(args):
                  "those kernels; `of sparse peak` (dense-equivalent TFLOP/s / %.1f) uses time only.\n\n" % SPARSE_PEAK_F16)
         fh.write("| kernel | dispatches | us | dense-eq TFLOP/s | of sparse peak | clock GHz | MOPS/clk | of dense rate "
                  "| of sparse rate | of sparse loop | MFMA busy |\n|---|---|---|---|---|---|---|---|---|---|---|\n")
+        if dom:
+            fh.write("The dominant kernel of the bench line (`%s`) is averaged over its %d timed launches only (its last "
+                     "dispatches of the run; autotuning runs other splits of it first); every other kernel over all "
+                     "its dispatches.\n\n" % (dom, n_timed))
         for r in rows:
             sl = loops.get("sparse")
             fh.write("| `%s` | %d | %.1f | %.1f | %.3f | %.2f | %.0f | %.3f | %.3f | %s | %.3f |\n" % (
