@@ -107,4 +107,17 @@ __device__ __forceinline__ uint32_t select_topn(const uint32_t (&mag)[M], int N)
   return pick_kept ? picked : (full & ~picked);
 }
 
+// 2 of 4: the kept offsets j0 < j1 under the same rule, without a search. The
+// keys (mag << 2) | (3 - j) are unique and order the four exactly by it; with
+// a, b the smaller and larger of keys 0 and 1 and c, d those of keys 2 and 3,
+// the largest key is max(b, d) and the second largest max(min(b, d), a, c).
+// Magnitude keys are below 2^30.
+__device__ __forceinline__ void top2of4(const uint32_t (&mag)[4], int& j0, int& j1) {
+  const uint32_t k0 = (mag[0] << 2) | 3u, k1 = (mag[1] << 2) | 2u, k2 = (mag[2] << 2) | 1u, k3 = mag[3] << 2;
+  const uint32_t a = min(k0, k1), b = max(k0, k1), c = min(k2, k3), d = max(k2, k3);
+  const uint32_t t1 = max(b, d) & 3u, t2 = max(max(min(b, d), a), c) & 3u;   // 3 - offset of each
+  j0 = 3 - (int)max(t1, t2);
+  j1 = 3 - (int)min(t1, t2);
+}
+
 }  // namespace nm

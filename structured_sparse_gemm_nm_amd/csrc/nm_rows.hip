@@ -375,6 +375,7 @@ __global__ void __launch_bounds__(256) row_kernel(RowArgs A) {
       continue;
     }
     uint32_t keep[G::GU];
+    int j2[G::GU][2];                // 2:4: the kept offsets of each group, ascending
     uint32_t sel[N];                 // M = 32: the kept elements as by_offset() keys, offsets ascending
     if constexpr (M == 32) {
       uint32_t key[32];
@@ -406,7 +407,12 @@ __global__ void __launch_bounds__(256) row_kernel(RowArgs A) {
         uint32_t mag[M];
 #pragma unroll
         for (int j = 0; j < M; j++) mag[j] = magkey<DT>(elem_of<ESZ>(d[s], g * M + j));
-        keep[g] = g < vg ? select_topn<M>(mag, N) : 0u;
+        if constexpr (M == 4 && N == 2) {
+          top2of4(mag, j2[g][0], j2[g][1]);
+          keep[g] = g < vg ? (1u << j2[g][0]) | (1u << j2[g][1]) : 0u;
+        } else {
+          keep[g] = g < vg ? select_topn<M>(mag, N) : 0u;
+        }
       }
     }
     if (OP == R_PRUNE) {
@@ -457,6 +463,16 @@ __global__ void __launch_bounds__(256) row_kernel(RowArgs A) {
           f |= (uint64_t)(31u - (sel[sl] >> 16)) << (sl * G::B);
         }
       }
+    } else if constexpr (M == 4 && N == 2 && ESZ == 2) {
+      // the group's elements 0, 1 are dword 2g, elements 2, 3 dword 2g + 1: one
+      // byte permute takes elements j0 (low half) and j1 (high half)
+#pragma unroll
+      for (int g = 0; g < G::GU; g++) {
+        if (g >= vg) break;
+        const uint32_t jj = (uint32_t)j2[g][0] | ((uint32_t)j2[g][1] << 16);
+        vo[g] = __builtin_amdgcn_perm(d[s][2 * g + 1], d[s][2 * g], jj * 0x202u + 0x01000100u);
+        f |= (uint64_t)(j2[g][0] | (j2[g][1] << 2)) << (4 * g);
+      }
     } else
 #pragma unroll
     for (int g = 0; g < G::GU; g++) {
@@ -484,7 +500,20 @@ __global__ void __launch_bounds__(256) row_kernel(RowArgs A) {
     if (row_ok) {
       const int64_t mbyte0 = sr * 8 * G::FB;
       const int ndw = (int)((sr == A.segs - 1 ? A.mld - mbyte0 : 8 * (int64_t)G::FB) / 4);
-      store_seg_meta<G::FB>(A.meta + r * A.mld + mbyte0, f, ndw, lane);
+      if constexpr (G::FB == 8 || G::FB == 16) {
+        // a unit's field is a whole byte (short): each lane stores its own,
+        // contiguous across the wave. The segment's metadata never runs past
+        // its 64 units' bytes (the row's padded end is a multiple of 16 bytes
+        // and so is every segment start), and lanes past the row's end hold
+        // zero fields, which are that padding.
+        uint8_t* mp = A.meta + r * A.mld + mbyte0;
+        if (lane * (G::FB / 8) < 4 * ndw) {
+          if constexpr (G::FB == 8) mp[lane] = (uint8_t)f;
+          else *(uint16_t*)(mp + 2 * lane) = (uint16_t)f;
+        }
+      } else {
+        store_seg_meta<G::FB>(A.meta + r * A.mld + mbyte0, f, ndw, lane);
+      }
     }
   }
   if constexpr (STAGED && OP == R_PRUNE) {
@@ -751,8 +780,8 @@ __global__ void __launch_bounds__(256) colT24_kernel(ColTArgs A) {
         uint32_t mag[4], raw[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) { raw[j] = elem(w[4 * g + j], c); mag[j] = magkey<DT>(raw[j]); }
-        const uint32_t keep = select_topn<4>(mag, 2);
-        const int j0 = __builtin_ctz(keep), j1 = 31 - __builtin_clz(keep);
+        int j0, j1;
+        top2of4(mag, j0, j1);
         const uint32_t v0 = j0 == 0 ? raw[0] : j0 == 1 ? raw[1] : j0 == 2 ? raw[2] : raw[3];
         const uint32_t v1 = j1 == 0 ? raw[0] : j1 == 1 ? raw[1] : j1 == 2 ? raw[2] : raw[3];
         const int s = 2 * g;                                  // first slot of the group
