@@ -900,6 +900,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   ab_t av[2][FM];
   int iv[2][FM];
   int ivn[FM];                                           // 16-bit types: second half-step's metadata, staged
+  int ivo[M4 ? FM : 1][2];                               // batched metadata: the next (odd) step's two words
   b2_t bv[2];
   ab_t bw[2][FN];
   const int qshift = 16 * q;
@@ -919,16 +920,29 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
             // one 8-byte read per row serves both half-steps and both lane
             // halves; the lane's 16 bits are selected at use (shift by 16 q)
             if (h == 0) {
-              typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-              const uint8_t* mp = lm + row * MB;
               if constexpr (M4) {
-                // step ks: slot (ks / 4) % 2, 8-byte piece ks % 4 of the row's 32 bytes
-                const int sub = ks & 3;
-                mp = mslots + ((ks >> 2) & 1) * MSLOT + row * 32 + ((((sub >> 1) ^ (row >> 3)) & 1) << 4) + (sub & 1) * 8;
+                // steps ks and ks + 1 (ks even) sit in one 16-byte chunk of the
+                // row's 32 bytes in slot (ks / 4) % 2: one 16-byte read every
+                // other step, whose 16-lane passes (32 rows, two 16-byte
+                // chunks apart by bit 3 of the row) fall on distinct banks;
+                // the odd step's words wait in registers
+                if ((ks & 1) == 0) {
+                  const u32x4 mw = *(const u32x4*)(mslots + ((ks >> 2) & 1) * MSLOT + row * 32 +
+                                                   (((((ks & 3) >> 1) ^ (row >> 3)) & 1) << 4));
+                  iv[0][fm] = (int)mw[0];
+                  ivn[fm] = (int)mw[1];
+                  ivo[fm][0] = (int)mw[2];
+                  ivo[fm][1] = (int)mw[3];
+                } else {
+                  iv[0][fm] = ivo[fm][0];
+                  ivn[fm] = ivo[fm][1];
+                }
+              } else {
+                typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+                const u32x2_t mw = *(const u32x2_t*)(lm + row * MB);
+                iv[0][fm] = (int)mw[0];
+                ivn[fm] = (int)mw[1];
               }
-              const u32x2_t mw = *(const u32x2_t*)mp;
-              iv[0][fm] = (int)mw[0];
-              ivn[fm] = (int)mw[1];
             } else {
               iv[1][fm] = ivn[fm];
             }
