@@ -797,10 +797,14 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
       oa[j] = (uint32_t)(row * A.lda * ESZ + ((slot ^ swz8(row)) << 4));
     }
   }
+  // int8 (16 metadata bytes per row and step): stored dword d of row r holds
+  // the row's dword d ^ (2 * bit 4 of r), so that the 32 rows a wave reads at
+  // once (rows 16 apart otherwise share banks) fall on 64 distinct banks
+  auto meta_dw = [](int row, int d) -> int { return ESZ == 1 ? d ^ (((row >> 4) & 1) << 1) : d; };
 #pragma unroll
   for (int j = 0; j < NMT; j++) {                        // 4-byte pieces, MDW per row
     const int p = HALF_META ? 32 * wave + (lane & 31) : 64 * (wave * NMT + j) + lane;
-    om[j] = (uint32_t)((p / MDW) * A.mld + (p % MDW) * 4);
+    om[j] = (uint32_t)((p / MDW) * A.mld + meta_dw(p / MDW, p % MDW) * 4);
   }
   // Copies of stage st: the wave's L instructions in the order B, A values,
   // metadata; part `part` of `parts` issues those with index % parts == part,
@@ -947,7 +951,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
               iv[1][fm] = ivn[fm];
             }
           } else {
-            iv[h][fm] = (int)*(const uint32_t*)(lm + row * MB + h * (MB / 2) + 4 * q);
+            iv[h][fm] = (int)*(const uint32_t*)(lm + row * MB + 4 * meta_dw(row, 2 * h + q));
           }
         }
       }
