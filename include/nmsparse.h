@@ -237,7 +237,8 @@ nm_status_t nm_dense_gemm(nm_plan_t plan, const float* alpha, const void* dA, co
  * block tile of the matrix-core products (nm_spmm on the 2:4 and general N:M
  * paths and nm_dense_gemm): NM_ALG_AUTO (the default: the plan picks by shape),
  * NM_ALG_TILE128 (128 x 128), NM_ALG_TILE256X128 (256 x 128),
- * NM_ALG_TILE256 (256 x 256 for 2:4; 256 x 128 for the dense product). The
+ * NM_ALG_TILE256 (256 x 256; for the dense product on whole tiles a two-stage
+ * ring, which the automatic choice does not take). The
  * general N:M expansion always uses 128 x 128 and small n (n <= 16) its own
  * kernel; there the id has no effect. Results do not depend on the id beyond
  * fp32 summation order (bit-exact for int8). Host-only; invalid ids give

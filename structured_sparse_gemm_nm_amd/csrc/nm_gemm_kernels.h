@@ -1436,13 +1436,15 @@ __global__ void __launch_bounds__(256) splitk_reduce_kernel(GemmArgs A) {
 // ---------------------------------------------------------------- tile launch (per element type)
 
 // Block tile: 256 x 256 when that still gives most CUs a tile, 256 x 128 or
-// 128 x 128 otherwise (the dense comparator stops at 256 x 128, whose ring of
-// three stages fits LDS). The general N:M gather path always uses 128 x 128 (its
-// staging needs LDS). An algorithm id on the plan pins the choice.
+// 128 x 128 otherwise. The dense comparator chooses 256 x 128 automatically
+// (a ring of four stages fits LDS); its 256 x 256 tile (two stages) is taken
+// when an algorithm id asks for it, as the timing-based choice does where it
+// is faster (x1 shapes: 3-5%). The general N:M gather path always uses 128 x
+// 128 (its staging needs LDS). An algorithm id on the plan pins the choice.
 inline int pick_tile(const nm_plan& pl, int amode) {
   if (amode == A_GATHER) return T128;
   if (pl.force_tile == T128 || pl.force_tile == T256x128) return pl.force_tile;   // -1: automatic
-  if (pl.force_tile == T256) return amode == A_DENSE ? T256x128 : T256;
+  if (pl.force_tile == T256) return T256;
   const int64_t t256 = ((pl.p.m + 255) / 256) * ((pl.p.n + 255) / 256);
   const int64_t t256x128 = ((pl.p.m + 255) / 256) * ((pl.p.n + 127) / 128);
   if (t256 >= 192 && amode != A_DENSE) return T256;
@@ -1587,6 +1589,7 @@ hipError_t launch_tiles_dt(const nm_plan& pl, int amode, const GemmArgs& A, hipS
     }
   }
   switch (pick_tile(pl, A_DENSE)) {
+    case T256: return launch_tiles_t<DT, A_DENSE, 256, 256>(pl, A, s);
     case T256x128: return launch_tiles_t<DT, A_DENSE, 256, 128>(pl, A, s);
     default: return launch_tiles_t<DT, A_DENSE, 128, 128>(pl, A, s);
   }
