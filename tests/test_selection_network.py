@@ -1,5 +1,6 @@
 """CPU model of the per-group top-N selection network that the register path
-uses for M = 32 (N = 4 or 8), checked against brute force on tie-heavy groups.
+uses for M = 32 (N = 4 or 8), and of its search-free 2 of 4, checked against
+brute force on tie-heavy groups.
 
 The model performs the same compare-exchange sequence as the device code: runs
 of four sorted, (N = 8) pairs of runs merged into sorted runs of eight through
@@ -73,3 +74,41 @@ def test_selection_network_all_equal_and_zero_groups():
                 keys = [(mag << 6) | ((31 - j) << 1) | signs[j] for j in range(32)]
                 got = sorted(31 - ((x >> 1) & 31) for x in _network_top_n32(keys, N))
                 assert got == list(range(N))
+
+
+# ---- 2 of 4 without a search (the register path's 2:4 prune and compress)
+#
+# Keys (mag << 2) | (3 - j) are unique per group; with a, b the smaller and
+# larger key of elements 0 and 1 and c, d those of elements 2 and 3, the kernel
+# takes the largest key as max(b, d) and the second largest as
+# max(min(b, d), a, c), and reads the two kept offsets from their low bits.
+
+def _top2of4_model(mag):
+    k = [(mag[j] << 2) | (3 - j) for j in range(4)]
+    a, b, c, d = min(k[0], k[1]), max(k[0], k[1]), min(k[2], k[3]), max(k[2], k[3])
+    t1, t2 = max(b, d) & 3, max(min(b, d), a, c) & 3
+    return 3 - max(t1, t2), 3 - min(t1, t2)
+
+
+def _top2of4_brute(mag):
+    order = sorted(range(4), key=lambda j: (-mag[j], j))   # larger magnitude first, then lower offset
+    return tuple(sorted(order[:2]))
+
+
+def test_two_of_four_network_every_tie_pattern():
+    """Every group over a five-value magnitude alphabet (all tie patterns), and
+    the extremes of the 15-bit magnitude key."""
+    vals = [0, 1, 2, 3, 0x7FFF]
+    for m0 in vals:
+        for m1 in vals:
+            for m2 in vals:
+                for m3 in vals:
+                    mag = [m0, m1, m2, m3]
+                    assert _top2of4_model(mag) == _top2of4_brute(mag), mag
+
+
+def test_two_of_four_network_random():
+    rng = random.Random(2024)
+    for _ in range(20000):
+        mag = [rng.choice([rng.randrange(0x8000), rng.randrange(4)]) for _ in range(4)]
+        assert _top2of4_model(mag) == _top2of4_brute(mag), mag
