@@ -1178,11 +1178,15 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   }
   {
     // beta != 0 (any D type; 16-bit D with beta = 0 took the path above): the raw 4-byte
-    // accumulators go through the ring (in rounds of one wave row or column
-    // group when the whole tile does not fit), then each thread step takes four
-    // consecutive elements of a D row (column) with one 16-byte LDS read, reads
-    // the matching C elements as one vector, applies alpha and beta exactly as
-    // the direct path does and stores one vector
+    // accumulators go through the ring (when the whole tile does not fit, in
+    // rounds: row-major D one fragment column of every wave per round,
+    // column-major D one wave column group per round), then each thread step
+    // takes four consecutive elements of a D row (column) with one 16-byte LDS
+    // read, reads the matching C elements as one vector, applies alpha and beta
+    // exactly as the direct path does and stores one vector. In the row-major
+    // rounds the C loads of four thread steps are issued before any is waited
+    // for (one at a time, each load's latency was paid in full: int8 4096^3
+    // with int32 C, 74-77 -> 69-72 us)
     typedef typename std::conditional<DT == DT_I8, int32_t, float>::type raw_t;
     typedef typename std::conditional<DT == DT_I8, intx4, floatx4>::type raw4_t;
     constexpr int P4 = 4;                                    // pitch padding (elements)
@@ -1196,73 +1200,139 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
     if constexpr (FIT_R && FIT_C) if (A.beta != 0.0f) {
       raw_t* img = (raw_t*)ring;
       const int wr = wave / WGN, wc = wave % WGN;
-      auto finish4 = [&](const raw_t (&a4)[4], int64_t row, int64_t col, bool colmajor) {
-        // four consecutive elements of one D row (colmajor: one D column) from (row, col)
-        const int64_t cidx = colmajor ? col * A.c_cs + row : row * A.c_rs + col;
-        const int64_t didx = colmajor ? col * A.d_cs + row : row * A.d_rs + col;
+      // C of four consecutive elements of one D row (colmajor: one D column) at
+      // (row, col): 16 bytes of int32 C, 4 of int8 C, 8 of 16-bit C
+      struct C4 { uint32_t w[4]; };
+      auto cindex = [&](int64_t row, int64_t col, bool colmajor) -> int64_t {
+        return colmajor ? col * A.c_cs + row : row * A.c_rs + col;
+      };
+      // cd8: int8 C and D (the integer path's runtime flag, decided outside the
+      // batched loop below so that its loads are not split by branches)
+      auto load_c4t = [&](auto cd8, int64_t cidx, C4& c) {
+        if constexpr (DT == DT_I8) {
+          if constexpr (decltype(cd8)::value) {
+            c.w[0] = *(const uint32_t*)((const int8_t*)A.c + cidx);
+          } else {
+            const intx4 cv = *(const intx4*)((const int32_t*)A.c + cidx);
+            c.w[0] = (uint32_t)cv[0]; c.w[1] = (uint32_t)cv[1]; c.w[2] = (uint32_t)cv[2]; c.w[3] = (uint32_t)cv[3];
+          }
+        } else {
+          const u32x2 cv = *(const u32x2*)((const uint16_t*)A.c + cidx);
+          c.w[0] = cv[0]; c.w[1] = cv[1];
+        }
+      };
+      auto finish4c = [&](const raw_t (&a4)[4], const C4& c, int64_t didx) {
         if constexpr (DT == DT_I8) {
           int64_t v[4];
 #pragma unroll
           for (int t = 0; t < 4; t++) v[t] = (int64_t)A.alpha * a4[t];
-          if (A.beta != 0.0f) {
-            if (A.cd_i8) {
-              const uint32_t cv = *(const uint32_t*)((const int8_t*)A.c + cidx);
-#pragma unroll
-              for (int t = 0; t < 4; t++) v[t] += (int64_t)A.beta * (int64_t)(int8_t)(cv >> (8 * t));
-            } else {
-              const intx4 cv = *(const intx4*)((const int32_t*)A.c + cidx);
-#pragma unroll
-              for (int t = 0; t < 4; t++) v[t] += (int64_t)A.beta * cv[t];
-            }
-          }
           if (A.cd_i8) {
+#pragma unroll
+            for (int t = 0; t < 4; t++) v[t] += (int64_t)A.beta * (int64_t)(int8_t)(c.w[0] >> (8 * t));
             uint32_t o = 0;
 #pragma unroll
             for (int t = 0; t < 4; t++) o |= ((uint32_t)sat_i8(v[t]) & 0xFFu) << (8 * t);
             *(uint32_t*)((int8_t*)A.d + didx) = o;
           } else {
+#pragma unroll
+            for (int t = 0; t < 4; t++) v[t] += (int64_t)A.beta * (int64_t)(int32_t)c.w[t];
             *(intx4*)((int32_t*)A.d + didx) = intx4{(int)v[0], (int)v[1], (int)v[2], (int)v[3]};
           }
         } else {
           float v[4];
 #pragma unroll
           for (int t = 0; t < 4; t++) v[t] = A.alpha * a4[t];
-          if (A.beta != 0.0f) {
-            const u32x2 cv = *(const u32x2*)((const uint16_t*)A.c + cidx);
-            v[0] += A.beta * from_bits16<DT>((uint16_t)(cv[0] & 0xFFFFu));
-            v[1] += A.beta * from_bits16<DT>((uint16_t)(cv[0] >> 16));
-            v[2] += A.beta * from_bits16<DT>((uint16_t)(cv[1] & 0xFFFFu));
-            v[3] += A.beta * from_bits16<DT>((uint16_t)(cv[1] >> 16));
-          }
+          v[0] += A.beta * from_bits16<DT>((uint16_t)(c.w[0] & 0xFFFFu));
+          v[1] += A.beta * from_bits16<DT>((uint16_t)(c.w[0] >> 16));
+          v[2] += A.beta * from_bits16<DT>((uint16_t)(c.w[1] & 0xFFFFu));
+          v[3] += A.beta * from_bits16<DT>((uint16_t)(c.w[1] >> 16));
           const uint32_t lo = (uint32_t)to_bits16<DT>(v[0]) | ((uint32_t)to_bits16<DT>(v[1]) << 16);
           const uint32_t hi = (uint32_t)to_bits16<DT>(v[2]) | ((uint32_t)to_bits16<DT>(v[3]) << 16);
           *(u32x2*)((uint16_t*)A.d + didx) = u32x2{lo, hi};
         }
       };
-      if (!A.cd_col) {
-        constexpr int ROWS = BM / RR, QPR = BN / 4;
+      auto finish4 = [&](const raw_t (&a4)[4], int64_t row, int64_t col, bool colmajor) {
+        C4 c{{0u, 0u, 0u, 0u}};
+        if (DT == DT_I8 && A.cd_i8) load_c4t(std::true_type{}, cindex(row, col, colmajor), c);
+        else load_c4t(std::false_type{}, cindex(row, col, colmajor), c);
+        finish4c(a4, c, colmajor ? col * A.d_cs + row : row * A.d_rs + col);
+      };
+      // Row-major image drain, batched: the C loads of U thread steps are
+      // issued before any of them is waited for. The image holds W columns of
+      // the tile per row (BM rows); image column j maps to tile column colmap(j).
+      auto drain_rows_t = [&](auto cd8, int W, int LP, auto colmap) {
+        const int qpr = W / 4, steps = BM * qpr / (64 * NW);
+        constexpr int U = 4;
 #pragma unroll 1
-        for (int rd = 0; rd < RR; rd++) {
-          __syncthreads();                                   // the ring (or the previous round) is free
-          if (RR == 1 || wr == rd) {
+        for (int s0 = 0; s0 < steps; s0 += U) {
+          C4 cv[U];
 #pragma unroll
-            for (int fm = 0; fm < FM; fm++)
-#pragma unroll
-              for (int fn = 0; fn < FN; fn++)
-#pragma unroll
-                for (int r = 0; r < 16; r++) {
-                  const int rl = wm0 + fm * 32 + 8 * (r / 4) + 4 * q + (r % 4) - rd * ROWS;
-                  img[rl * LINE + wn0 + fn * 32 + l32] = (raw_t)acc[fm][fn][r];
-                }
+          for (int u = 0; u < U; u++) {
+            const int i = threadIdx.x + (s0 + u) * 64 * NW;
+            cv[u] = C4{{0u, 0u, 0u, 0u}};
+            if (s0 + u < steps) load_c4t(cd8, cindex(r0 + i / qpr, c0 + colmap(4 * (i % qpr)), false), cv[u]);
           }
-          __syncthreads();
-          for (int i = threadIdx.x; i < ROWS * QPR; i += 64 * NW) {
-            const int rr = i / QPR, qc = i % QPR;
-            const raw4_t w = *(const raw4_t*)(img + rr * LINE + 4 * qc);
+#pragma unroll
+          for (int u = 0; u < U; u++) {
+            if (s0 + u >= steps) break;
+            const int i = threadIdx.x + (s0 + u) * 64 * NW;
+            const int rr = i / qpr, j = 4 * (i % qpr);
+            const raw4_t w = *(const raw4_t*)(img + rr * LP + j);
             raw_t a4[4];
 #pragma unroll
             for (int t = 0; t < 4; t++) a4[t] = w[t];
-            finish4(a4, r0 + rd * ROWS + rr, c0 + 4 * qc, false);
+            finish4c(a4, cv[u], (r0 + rr) * A.d_rs + c0 + colmap(j));
+          }
+        }
+      };
+      auto drain_rows = [&](int W, int LP, auto colmap) {
+        if (DT == DT_I8 && A.cd_i8) drain_rows_t(std::true_type{}, W, LP, colmap);
+        else drain_rows_t(std::false_type{}, W, LP, colmap);
+      };
+      if (!A.cd_col) {
+        constexpr int LINEF = WGN * 32 + P4;               // one 32-column strip per wave column
+        if constexpr (RR > 1 && BM * LINEF * 4 <= S * STAGE) {
+          // the whole tile does not fit: round f takes every wave's fragment
+          // column f (all rows; a 32-column strip per wave column), so each
+          // round frees a share of every wave's accumulators
+#pragma unroll
+          for (int f = 0; f < FN; f++) {
+            __syncthreads();
+#pragma unroll
+            for (int fm = 0; fm < FM; fm++)
+#pragma unroll
+              for (int r = 0; r < 16; r++) {
+                const int rl = wm0 + fm * 32 + 8 * (r / 4) + 4 * q + (r % 4);
+                img[rl * LINEF + wc * 32 + l32] = (raw_t)acc[fm][f][r];
+              }
+            __syncthreads();
+            drain_rows(WGN * 32, LINEF, [f](int j) { return (j / 32) * WN + f * 32 + (j % 32); });
+          }
+        } else {
+          constexpr int ROWS = BM / RR, QPR = BN / 4;
+#pragma unroll 1
+          for (int rd = 0; rd < RR; rd++) {
+            __syncthreads();                                 // the ring (or the previous round) is free
+            if (RR == 1 || wr == rd) {
+#pragma unroll
+              for (int fm = 0; fm < FM; fm++)
+#pragma unroll
+                for (int fn = 0; fn < FN; fn++)
+#pragma unroll
+                  for (int r = 0; r < 16; r++) {
+                    const int rl = wm0 + fm * 32 + 8 * (r / 4) + 4 * q + (r % 4) - rd * ROWS;
+                    img[rl * LINE + wn0 + fn * 32 + l32] = (raw_t)acc[fm][fn][r];
+                  }
+            }
+            __syncthreads();
+            for (int i = threadIdx.x; i < ROWS * QPR; i += 64 * NW) {
+              const int rr = i / QPR, qc = i % QPR;
+              const raw4_t w = *(const raw4_t*)(img + rr * LINE + 4 * qc);
+              raw_t a4[4];
+#pragma unroll
+              for (int t = 0; t < 4; t++) a4[t] = w[t];
+              finish4(a4, r0 + rd * ROWS + rr, c0 + 4 * qc, false);
+            }
           }
         }
       } else {
