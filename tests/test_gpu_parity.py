@@ -808,6 +808,42 @@ def test_c_may_alias_d_full_tiles(dtype):
     assert_close(dtype, host(dc, raw), ref, tol)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
+@pytest.mark.parametrize("op_b", ["N", "T"])
+@pytest.mark.parametrize("order", ["row", "col"])
+def test_beta_epilogue_on_256_tiles(dtype, op_b, order):
+    """beta != 0 on 256 x 256 tiles, whose raw 4-byte tile does not fit LDS at
+    once: row-major D drains in rounds of one fragment column of every wave
+    (C loads issued several thread steps ahead), column-major D in rounds of
+    one wave column group; then again with C aliasing D."""
+    m, n, k = 512, 768, 384
+    a = rand(dtype, (m, k), 91)
+    v, meta = oracle.compress(a, dtype, 2, 4)
+    ahat, _ = oracle.prune_1d(a, dtype, 2, 4)
+    b_log = rand(dtype, (k, n), 92)
+    b_st = b_log if op_b == "N" else np.ascontiguousarray(b_log.T)
+    if dtype == "i8":
+        c = inputs.uniform_int((m, n), 93, -2**20, 2**20, np.int32)
+        alpha, beta, raw, odt = 3.0, 2.0, np.int32, torch.int32
+    else:
+        c = rand(dtype, (m, n), 93)
+        alpha, beta, raw, odt = 0.75, -1.25, np.uint16, torch.int16
+    plan = plan_for(dtype, m, n, k, 2, 4, op_b=op_b, tile="256", order_cd=order)
+    assert "256, 256," in plan.spmm_kernel, plan.spmm_kernel
+    c_st = c if order == "row" else np.ascontiguousarray(c.T)
+    ref, tol = ref_product(dtype, ahat, b_log, alpha, beta, c)
+    logical = (lambda x: x) if order == "row" else (lambda x: np.ascontiguousarray(x.T))
+    d = Guarded(c_st.shape, odt)
+    nm.nm_spmm(plan, alpha, dev(v), dev(meta), dev(b_st), beta, dev(c_st), d.t)
+    sync()
+    d.check()
+    assert_close(dtype, logical(host(d.t, raw)), ref, tol)
+    dc = dev(c_st)
+    nm.nm_spmm(plan, alpha, dev(v), dev(meta), dev(b_st), beta, dc, dc)
+    sync()
+    assert_close(dtype, logical(host(dc, raw)), ref, tol)
+
+
 def test_col_major_k_zero_and_alias():
     m, n = 40, 24
     c = rand("f16", (m, n), 11)
