@@ -21,10 +21,16 @@ roofline of the dominant kernel (measured with HIP events on the launch
 stream over the timed region), and the CPU oracle timed on a bounded sample
 of the same workload.
 
+Order: W warm-up steps, a per-launch pass (K steps, every SpMM bracketed by
+events), then untimed settling steps (at least W, and enough for 60 ms of
+continuous work: after an idle gap the GPU's power management runs the next
+tens of milliseconds of work slower than steady state), then the K timed steps.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 import argparse
 import json
+import math
 import os
 import sys
 import time
@@ -98,6 +104,7 @@ def parse():
 
 
 CAL_MIB, CAL_REPS = 1024, 3
+SETTLE_MS, SETTLE_MAX_STEPS = 60.0, 2000   # continuous untimed work directly before the timed region
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -302,6 +309,12 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # W untimed warm-up steps precede the per-launch pass. After an idle gap
+    # (host-side set-up, the per-launch pass's bookkeeping) the GPU's power
+    # management runs the following tens of milliseconds of work up to 30%
+    # slower than steady state, so the timed region is preceded by untimed
+    # settling steps: at least W, and enough for SETTLE_MS of continuous work,
+    # with no host work between them and the timed region.
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -311,9 +324,11 @@ def main():
     # Per-launch pass (not the timed region): every SpMM launch bracketed by
     # events, to time each GEMM and find the device kernel with the most time.
     all_ev, empty = [], []
+    t_pl = time.perf_counter()
     for _ in range(args.steps):
         step(all_ev, None, empty)
     torch.cuda.synchronize()
+    pass_ms_per_step = (time.perf_counter() - t_pl) * 1e3 / args.steps
     event_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in empty]))
     per = {}
     for key, e0, e1 in all_ev:
@@ -327,6 +342,9 @@ def main():
     # Timed region: K steps; only the dominant kernel's launches carry events
     # (each event pair adds its own few microseconds to the queue).
     events = []
+    settle_steps = min(max(args.warmup, math.ceil(SETTLE_MS / max(pass_ms_per_step, 1e-3))), SETTLE_MAX_STEPS)
+    for _ in range(settle_steps):
+        step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -532,6 +550,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(ms_per_step, 4),
         "host_enqueue_ms_per_step": round(host_ms_per_step, 4),
         "higher_is_better": True,
