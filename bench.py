@@ -108,6 +108,44 @@ SETTLE_MS, SETTLE_MAX_STEPS = 60.0, 2000   # continuous untimed work directly be
 PROFILES = os.path.join(ROOT, "profiles")
 
 
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence:
+    recording it writes a timestamp without the system-scope cache writeback
+    and invalidation a default event performs at every record (which costs a
+    few microseconds on the queue and leaves the next kernel with cold
+    caches). It is read only after a device synchronisation, which orders it
+    with the work it brackets."""
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if TimingEvent._hip is None:
+            import torch
+            hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            TimingEvent._hip = hip
+        self._c = ctypes
+        self.h = ctypes.c_void_p()
+        st = self._hip.hipEventCreateWithFlags(ctypes.byref(self.h), self.DISABLE_SYSTEM_FENCE)
+        if st != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed (%d)" % st)
+
+    def record(self, stream):
+        st = self._hip.hipEventRecord(self.h, self._c.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError("hipEventRecord failed (%d)" % st)
+
+    def elapsed_time(self, end):
+        ms = self._c.c_float()
+        st = self._hip.hipEventElapsedTime(self._c.byref(ms), self.h, end.h)
+        if st != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % st)
+        return ms.value
+
+
 def source_fingerprint():
     """sha256 over the library's kernel and host sources: counters taken on other sources do not apply."""
     import hashlib
@@ -273,11 +311,9 @@ def main():
 
     n_spmm = sum(1 for c in calls if c[2] is not None)
     spmm_kernel = {(g["label"], ob): g["plans"][ob].spmm_kernel for g in gemms for ob in g["layouts"]}
-    # events are created before any timed pass
-    pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            for _ in range(n_spmm * args.steps)]
-    empty_pool = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(args.steps)]
+    # events (timing-only HIP events, see TimingEvent) are created before any timed pass
+    pool = [(TimingEvent(), TimingEvent()) for _ in range(n_spmm * args.steps)]
+    empty_pool = [(TimingEvent(), TimingEvent()) for _ in range(args.steps)]
 
     def step(ev=None, only=None, empty=None):
         """One pass of the hot path. With `ev`, the SpMM launches whose device
@@ -426,7 +462,8 @@ def main():
     roofline["cache"] = "warm (below the 256 MB Infinity Cache)" if avg_bytes < 256e6 else "cold (beyond the 256 MB Infinity Cache)"
     roofline["launch_ms"] = round(avg_ms, 5)
     roofline["launch_ms_method"] = ("mean over the timed steps of the HIP-event interval around each launch of this "
-                                    "kernel (the only events in the timed region), less the median interval of an empty "
+                                    "kernel (the only events in the timed region; timing-only events without the "
+                                    "system-scope fence), less the median interval of an empty "
                                     "event pair (%.5f ms); achieved = the launches' summed work / their summed time"
                                     % event_ms)
     roofline["launches_per_step"] = n_launch // args.steps
