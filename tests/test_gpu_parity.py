@@ -174,17 +174,34 @@ def test_prune_tile_unaligned_short_rows(dtype):
     assert np.array_equal(got[:, cols:], full[:, cols:])
 
 
+def _lda_op_t(m, es, align):
+    """A padded leading dimension: whole 16-byte rows plus one more piece, or rows
+    that are 4-byte but not 8-byte aligned (lda * esize = 4 mod 8; plans allow
+    that only for rows shorter than 16 bytes)."""
+    if align == 16:
+        return -(-m // (16 // es)) * (16 // es) + 16 // es
+    lda = m + 1
+    while (lda * es) % 8 != 4:
+        lda += 1
+    return lda
+
+
 @pytest.mark.parametrize("dtype", ["f16", "bf16", "i8"])
-@pytest.mark.parametrize("path", ["colT", "tile"])
-def test_compress_op_t_ragged_padded(dtype, path, monkeypatch):
+@pytest.mark.parametrize("path,align", [("colT", 16), ("colT", 4), ("tile", 16)])
+def test_compress_op_t_ragged_padded(dtype, path, align, monkeypatch):
     """2:4 compress and decompress with groups down stored columns (op_a = T), on
-    padded stored rows: ragged column counts for the dword-wide lanes, a ragged
-    last block of 32 stored rows (odd group counts), several blocks."""
+    padded stored rows: ragged column counts for the 8-byte lanes (rows 8-byte
+    aligned) and the 4-byte ones (short rows 4-byte aligned only), a ragged last
+    block of 32 stored rows (odd group counts), several blocks, and blocks
+    staged through LDS (m >= 256) next to a ragged one."""
     if path == "tile":
         monkeypatch.setenv("NM_TILE_ELEMWISE", "1")
     es = 1 if dtype == "i8" else 2
-    for m, k in [(7, 4), (33, 100), (130, 268), (5, 36), (64, 96)]:
-        lda = -(-m // (16 // es)) * (16 // es) + 16 // es
+    shapes = [(7, 4), (33, 100), (130, 268), (5, 36), (64, 96), (521, 268)]
+    if align == 4:
+        shapes = [(m, k) for m, k in [(7, 4), (5, 36), (3, 268), (7, 100), (13, 268)] if m * es < 16]
+    for m, k in shapes:
+        lda = _lda_op_t(m, es, align)
         full = rand(dtype, (k, lda), 700 + m + k)
         a = np.ascontiguousarray(full[:, :m])                  # stored k x m
         plan = plan_for(dtype, m, 8, k, 2, 4, op_a="T", lda=lda)
