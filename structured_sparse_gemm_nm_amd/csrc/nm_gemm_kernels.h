@@ -676,15 +676,11 @@ __device__ __forceinline__ int swz4(int r) { return (((r >> 2) & 1) << 1) | (((r
 // after M0 is written.
 __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_wave_base) {
   const uint32_t l = (uint32_t)(uintptr_t)(lds_ptr_t)lds_wave_base;
-  uint32_t save;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(save) : "v"(g), "s"(l) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(l) : "memory", "m0");
 }
 __device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* lds_wave_base) {
   const uint32_t l = (uint32_t)(uintptr_t)(lds_ptr_t)lds_wave_base;
-  uint32_t save;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
-               : "=&s"(save) : "v"(g), "s"(l) : "memory");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(l) : "memory", "m0");
 }
 
 // op_b = N (B stored k x n): the B stage keeps the 64 k-rows as stored, rows of
