@@ -36,6 +36,50 @@ def torch_lib_dir():
     return os.path.join(list(spec.submodule_search_locations)[0], "lib")
 
 
+# The GEMM kernels' global-to-LDS copies write M0 (the LDS address of each
+# copy) from inline asm without saving it. That is sound only while the
+# compiler leaves M0 unused in those kernels, so the build also compiles the
+# 16-bit GEMM unit to device assembly and fails if an instruction outside an
+# inline-asm block names M0 or is one of those that read it implicitly.
+M0_SOURCE = "nm_gemm_f16.hip"
+M0_IMPLICIT = ("global_load_lds", "s_movrel", "v_movrel", "s_sendmsg", "ds_append", "ds_consume", "ds_gws", "ds_ordered")
+
+
+def check_m0_unused(asm_path):
+    """Instructions outside inline asm that name or implicitly use M0 (empty list: sound)."""
+    import re
+    bad, inside = [], False
+    for line in open(asm_path):
+        t = line.split(";;")[0].strip() if not line.strip().startswith(";;#ASM") else line.strip()
+        if t.startswith(";;#ASMSTART"):
+            inside = True
+            continue
+        if t.startswith(";;#ASMEND"):
+            inside = False
+            continue
+        t = t.split(";")[0].strip()
+        if inside or not t or t.startswith(".") or t.endswith(":"):
+            continue
+        op = t.split()[0]
+        if (re.search(r"\bm0\b", t) or op.startswith(M0_IMPLICIT)
+                or (op.startswith("buffer_load") and re.search(r"\blds\b", t))):
+            bad.append(t)
+    return bad
+
+
+def _m0_check():
+    out = os.path.join(BUILD, "m0_check.s")
+    cmd = [HIPCC] + CFLAGS + ["--cuda-device-only", "-S", os.path.join(CSRC, M0_SOURCE), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("compile failed: %s\n%s%s" % (" ".join(cmd), r.stdout, r.stderr))
+    bad = check_m0_unused(out)
+    if bad:
+        raise RuntimeError("the compiler uses M0 in the GEMM kernels, which the copy asm overwrites: " +
+                           "; ".join(bad[:5]))
+    return out
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC] + CFLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
@@ -65,8 +109,10 @@ def _link(objs, out, soname):
 def build(verbose=True):
     """Compile every HIP source for gfx950 and link libnmsparse.so and libnmcal.so (always rebuilds)."""
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES) + 1) as ex:
+    with ThreadPoolExecutor(max_workers=len(SOURCES) + 2) as ex:
+        m0 = ex.submit(_m0_check)
         objs = list(ex.map(_compile, SOURCES + ["nm_calib.hip"]))
+        m0.result()
     _link(objs[-1:], CAL_LIB, "libnmcal.so")
     objs = objs[:-1]
     tl = torch_lib_dir()

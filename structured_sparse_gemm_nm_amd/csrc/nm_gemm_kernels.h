@@ -671,16 +671,19 @@ __device__ __forceinline__ int swz4(int r) { return (((r >> 2) & 1) << 1) | (((r
 // them: its own tracking cannot tell the LDS reads of other ring slots apart
 // from the copies in flight and would drain every copy before such a read.
 // The kernels order the copies themselves (per-wave vmcnt waits, then an LDS
-// barrier before a slot is read or refilled). M0 carries the LDS address; it
-// is saved and restored around the copy, with the one wait state a copy needs
-// after M0 is written.
+// barrier before a slot is read or refilled). M0 carries the LDS address,
+// written with the one wait state a copy needs after it. M0 is a reserved
+// register the compiler does not let asm declare clobbered, and it is not
+// saved here (two scalar instructions per copy, measured 1-8% on the products):
+// this is sound because nothing else in these kernels uses M0, which the build
+// checks on the compiled assembly of the 16-bit GEMM unit.
 __device__ __forceinline__ void dma16(const uint8_t* g, uint8_t* lds_wave_base) {
   const uint32_t l = (uint32_t)(uintptr_t)(lds_ptr_t)lds_wave_base;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(l) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(g), "s"(l) : "memory");
 }
 __device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* lds_wave_base) {
   const uint32_t l = (uint32_t)(uintptr_t)(lds_ptr_t)lds_wave_base;
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(l) : "memory", "m0");
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(l) : "memory");
 }
 
 // op_b = N (B stored k x n): the B stage keeps the 64 k-rows as stored, rows of
@@ -805,8 +808,9 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   // Copies of stage st: the wave's L instructions in the order B, A values,
   // metadata; part `part` of `parts` issues those with index % parts == part,
   // so a refill can be spread over the fragment groups of a step.
-  auto issue_part = [&](int st, int part, int parts) {
-    uint8_t* base = ring + (st % S) * STAGE;
+  // (slot: st % S, passed in so that the steady loop keeps it in a register)
+  auto issue_part_at = [&](int st, int slot, int part, int parts) {
+    uint8_t* base = ring + slot * STAGE;
     const uint8_t* bp = bbase + (size_t)st * bstep;
     const uint8_t* ap = abase + (size_t)st * astep;
     const uint8_t* mp = mbase + (size_t)st * MB;
@@ -826,7 +830,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
       }
     }
   };
-  auto issue = [&](int st) { issue_part(st, 0, 1); };
+  auto issue = [&](int st) { issue_part_at(st, st % S, 0, 1); };
   // Metadata slot fill: k-steps 4 mg .. 4 mg + 3 of every row (32 bytes) into
   // slot mg % 2; lane p of the fill copies 16-byte chunk p % 2 of row p / 2,
   // stored at chunk (p % 2) ^ bit 3 of the row (two rows 8 apart then read
@@ -1047,8 +1051,16 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   wait_stages(min(S - 1, ksteps - 1));
   lds_barrier();
   load_group(ring, 0, 0);
-  for (int ks = 0; ks < ksteps; ks++) {
-    const uint8_t* st = ring + (ks % S) * STAGE;
+  // One k-step. REFILL (every step but the first and the last S - 1): stage
+  // ks + S - 1 goes into the slot freed at the end of step ks - 1, and stage
+  // ks + 1 exists; the two kinds of step are separate copies of the body, so
+  // the steady loop carries no per-group tests. cur = ks % S is kept in a
+  // register rather than recomputed.
+  auto kstep = [&](int ks, int cur, auto refill_t) {
+    constexpr bool REFILL = decltype(refill_t)::value;
+    const int nxt = cur + 1 == S ? 0 : cur + 1;          // (ks + 1) % S
+    const int fil = cur == 0 ? S - 1 : cur - 1;          // (ks + S - 1) % S
+    const uint8_t* st = ring + cur * STAGE;
     // batched metadata: the slot for k-steps ks + 4 .. ks + 7 is filled at the
     // start of every fourth step (the slot it overwrites was last read at the
     // start of step ks - 1), before that step's ring refill
@@ -1058,30 +1070,36 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
       if constexpr (M4) {
         if (g == 0 && meta_fill) issue_meta((ks >> 2) + 1);
       }
-      // stage ks+S-1 goes into the slot freed at the end of step ks-1
-      if (ks >= 1 && ks + S - 1 < ksteps) issue_part(ks + S - 1, g, G);
+      if constexpr (REFILL) issue_part_at(ks + S - 1, fil, g, G);
       if (g + 1 < G) {
         load_group(st, g + 1, ks);
-      } else if (ks + 1 < ksteps) {
+      } else if (REFILL || ks + 1 < ksteps) {
         // issued so far: stages up to min(ks+S-1, ksteps-1); stage ks+1 is
         // complete once at most stages ks+2 .. min(ks+S-1, ksteps-1) (and
         // this step's metadata fill, issued after stage ks+1) are outstanding
         if constexpr (M4) {
           static_assert(S == 3, "batched metadata runs with a three-stage ring");
-          const bool next_stage = ks + 2 < ksteps;
+          const bool next_stage = REFILL || ks + 2 < ksteps;
           if (next_stage && meta_fill) wait_vmcnt<L + NMG>();
           else if (next_stage) wait_vmcnt<L>();
           else if (meta_fill) wait_vmcnt<NMG>();
           else wait_vmcnt<0>();
+        } else if constexpr (REFILL) {
+          wait_stages(S - 2);
         } else {
           wait_stages(min(S - 2, ksteps - ks - 2));
         }
         lds_barrier();                                   // every wave is done reading stage ks
-        load_group(ring + ((ks + 1) % S) * STAGE, 0, ks + 1);
+        load_group(ring + nxt * STAGE, 0, ks + 1);
       }
       compute_group(g);
     }
-  }
+    return nxt;
+  };
+  int cur = kstep(0, 0, std::false_type{});
+  int ks = 1;
+  for (; ks + S - 1 < ksteps; ks++) cur = kstep(ks, cur, std::true_type{});
+  for (; ks < ksteps; ks++) cur = kstep(ks, cur, std::false_type{});
 
   // ---- split-k: this block's partial sums go to plane z of the workspace, in
   // D's storage order, raw (alpha, beta and rounding are applied once, by the
