@@ -908,7 +908,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   b2_t bv[2];
   ab_t bw[2][FN];
   const int qshift = 16 * q;
-  auto load_group = [&](const uint8_t* st, int g, int ks) {
+  // PAR: the parity of ks when the caller knows it statically (0 or 1), else -1
+  typedef std::integral_constant<int, -1> par_any;
+  auto load_group = [&](const uint8_t* st, int g, int ks, auto par_t) {
+    constexpr int PAR = decltype(par_t)::value;
     if constexpr (SP) {
       const uint8_t* la = st;
       const uint8_t* lm = st + A_VAL;
@@ -930,7 +933,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
                 // other step, whose 16-lane passes (32 rows, two 16-byte
                 // chunks apart by bit 3 of the row) fall on distinct banks;
                 // the odd step's words wait in registers
-                if ((ks & 1) == 0) {
+                if (PAR >= 0 ? PAR == 0 : (ks & 1) == 0) {
                   const u32x4 mw = *(const u32x4*)(mslots + ((ks >> 2) & 1) * MSLOT + row * 32 +
                                                    (((((ks & 3) >> 1) ^ (row >> 3)) & 1) << 4));
                   iv[0][fm] = (int)mw[0];
@@ -1050,13 +1053,14 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
     if (st < ksteps) issue(st);
   wait_stages(min(S - 1, ksteps - 1));
   lds_barrier();
-  load_group(ring, 0, 0);
+  load_group(ring, 0, 0, std::integral_constant<int, 0>{});
   // One k-step. REFILL (every step but the first and the last S - 1): stage
   // ks + S - 1 goes into the slot freed at the end of step ks - 1, and stage
   // ks + 1 exists; the two kinds of step are separate copies of the body, so
   // the steady loop carries no per-group tests. cur = ks % S is kept in a
   // register rather than recomputed.
-  auto kstep = [&](int ks, int cur, auto refill_t) {
+  // NEXT_PAR: the parity of ks + 1 when known statically (else par_any)
+  auto kstep = [&](int ks, int cur, auto refill_t, auto next_par_t) {
     constexpr bool REFILL = decltype(refill_t)::value;
     const int nxt = cur + 1 == S ? 0 : cur + 1;          // (ks + 1) % S
     const int fil = cur == 0 ? S - 1 : cur - 1;          // (ks + S - 1) % S
@@ -1072,7 +1076,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
       }
       if constexpr (REFILL) issue_part_at(ks + S - 1, fil, g, G);
       if (g + 1 < G) {
-        load_group(st, g + 1, ks);
+        load_group(st, g + 1, ks, par_any{});
       } else if (REFILL || ks + 1 < ksteps) {
         // issued so far: stages up to min(ks+S-1, ksteps-1); stage ks+1 is
         // complete once at most stages ks+2 .. min(ks+S-1, ksteps-1) (and
@@ -1090,16 +1094,24 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
           wait_stages(min(S - 2, ksteps - ks - 2));
         }
         lds_barrier();                                   // every wave is done reading stage ks
-        load_group(ring + nxt * STAGE, 0, ks + 1);
+        load_group(ring + nxt * STAGE, 0, ks + 1, next_par_t);
       }
       compute_group(g);
     }
     return nxt;
   };
-  int cur = kstep(0, 0, std::false_type{});
+  typedef std::integral_constant<int, 0> par_even;
+  typedef std::integral_constant<int, 1> par_odd;
+  int cur = kstep(0, 0, std::false_type{}, par_odd{});
   int ks = 1;
-  for (; ks + S - 1 < ksteps; ks++) cur = kstep(ks, cur, std::true_type{});
-  for (; ks < ksteps; ks++) cur = kstep(ks, cur, std::false_type{});
+  // steady steps in pairs (odd, even), so that the parity the batched metadata
+  // reads depend on is static
+  for (; ks + S < ksteps; ks += 2) {
+    cur = kstep(ks, cur, std::true_type{}, par_even{});
+    cur = kstep(ks + 1, cur, std::true_type{}, par_odd{});
+  }
+  for (; ks + S - 1 < ksteps; ks++) cur = kstep(ks, cur, std::true_type{}, par_any{});
+  for (; ks < ksteps; ks++) cur = kstep(ks, cur, std::false_type{}, par_any{});
 
   // ---- split-k: this block's partial sums go to plane z of the workspace, in
   // D's storage order, raw (alpha, beta and rounding are applied once, by the
