@@ -685,6 +685,17 @@ __device__ __forceinline__ void dma4(const uint8_t* g, uint8_t* lds_wave_base) {
   const uint32_t l = (uint32_t)(uintptr_t)(lds_ptr_t)lds_wave_base;
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off" : : "v"(g), "s"(l) : "memory");
 }
+// The same from a wave-uniform base (scalar registers) plus a 32-bit per-lane
+// byte offset, so that no per-lane 64-bit address is formed (the copy-ring
+// kernels run only on operands under 2 GiB).
+__device__ __forceinline__ void dma16s(const uint8_t* base, uint32_t off, uint8_t* lds_wave_base) {
+  const uint32_t l = (uint32_t)(uintptr_t)(lds_ptr_t)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(off), "s"(base), "s"(l) : "memory");
+}
+__device__ __forceinline__ void dma4s(const uint8_t* base, uint32_t off, uint8_t* lds_wave_base) {
+  const uint32_t l = (uint32_t)(uintptr_t)(lds_ptr_t)lds_wave_base;
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1" : : "v"(off), "s"(base), "s"(l) : "memory");
+}
 
 // op_b = N (B stored k x n): the B stage keeps the 64 k-rows as stored, rows of
 // BN * 2 bytes, with 16-byte slot s of row r holding chunk s ^ (4 * (r & 3)).
@@ -816,17 +827,17 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
     const uint8_t* mp = mbase + (size_t)st * MB;
 #pragma unroll
     for (int j = 0; j < NB; j++)
-      if (j % parts == part) dma16(bp + ob[j], base + A_VAL + A_META + (wave * NB + j) * 1024);
+      if (j % parts == part) dma16s(bp, ob[j], base + A_VAL + A_META + (wave * NB + j) * 1024);
 #pragma unroll
     for (int j = 0; j < NA; j++)
-      if ((NB + j) % parts == part) dma16(ap + oa[j], base + (wave * NA + j) * 1024);
+      if ((NB + j) % parts == part) dma16s(ap, oa[j], base + (wave * NA + j) * 1024);
 #pragma unroll
     for (int j = 0; j < NMT; j++) {
       if ((NB + NA + j) % parts != part) continue;
       if (HALF_META) {
-        if (lane < 32) dma4(mp + om[j], base + A_VAL + wave * 128);
+        if (lane < 32) dma4s(mp, om[j], base + A_VAL + wave * 128);
       } else {
-        dma4(mp + om[j], base + A_VAL + (wave * NMT + j) * 256);
+        dma4s(mp, om[j], base + A_VAL + (wave * NMT + j) * 256);
       }
     }
   };
@@ -851,7 +862,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
     for (int j = 0; j < NMG; j++) {
       int64_t o = (int64_t)mg * 32 + omc[j];
       if (o + 16 > A.mld) o = A.mld - 16;
-      dma16(A.meta + (size_t)r0 * A.mld + omr[j] + (size_t)o, base + (wave * NMG + j) * 1024);
+      dma16s(A.meta + (size_t)r0 * A.mld, omr[j] + (uint32_t)o, base + (wave * NMG + j) * 1024);
     }
   };
 
@@ -908,10 +919,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   b2_t bv[2];
   ab_t bw[2][FN];
   const int qshift = 16 * q;
-  // PAR: the parity of ks when the caller knows it statically (0 or 1), else -1
-  typedef std::integral_constant<int, -1> par_any;
-  auto load_group = [&](const uint8_t* st, int g, int ks, auto par_t) {
-    constexpr int PAR = decltype(par_t)::value;
+  // PH: ks % 4 when the caller knows it statically (0 .. 3), else -1
+  typedef std::integral_constant<int, -1> ph_any;
+  auto load_group = [&](const uint8_t* st, int g, int ks, auto ph_t) {
+    constexpr int PH = decltype(ph_t)::value;
     if constexpr (SP) {
       const uint8_t* la = st;
       const uint8_t* lm = st + A_VAL;
@@ -933,9 +944,10 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
                 // other step, whose 16-lane passes (32 rows, two 16-byte
                 // chunks apart by bit 3 of the row) fall on distinct banks;
                 // the odd step's words wait in registers
-                if (PAR >= 0 ? PAR == 0 : (ks & 1) == 0) {
+                const int k3 = PH >= 0 ? PH : (ks & 3);
+                if ((k3 & 1) == 0) {
                   const u32x4 mw = *(const u32x4*)(mslots + ((ks >> 2) & 1) * MSLOT + row * 32 +
-                                                   (((((ks & 3) >> 1) ^ (row >> 3)) & 1) << 4));
+                                                   ((((k3 >> 1) ^ (row >> 3)) & 1) << 4));
                   iv[0][fm] = (int)mw[0];
                   ivn[fm] = (int)mw[1];
                   ivo[fm][0] = (int)mw[2];
@@ -1059,16 +1071,18 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   // ks + 1 exists; the two kinds of step are separate copies of the body, so
   // the steady loop carries no per-group tests. cur = ks % S is kept in a
   // register rather than recomputed.
-  // NEXT_PAR: the parity of ks + 1 when known statically (else par_any)
-  auto kstep = [&](int ks, int cur, auto refill_t, auto next_par_t) {
+  // PH: ks % 4 when known statically (else -1)
+  auto kstep = [&](int ks, int cur, auto refill_t, auto ph_t) {
     constexpr bool REFILL = decltype(refill_t)::value;
+    constexpr int PH = decltype(ph_t)::value;
+    typedef std::integral_constant<int, PH < 0 ? -1 : (PH + 1) & 3> next_ph;
     const int nxt = cur + 1 == S ? 0 : cur + 1;          // (ks + 1) % S
     const int fil = cur == 0 ? S - 1 : cur - 1;          // (ks + S - 1) % S
     const uint8_t* st = ring + cur * STAGE;
     // batched metadata: the slot for k-steps ks + 4 .. ks + 7 is filled at the
     // start of every fourth step (the slot it overwrites was last read at the
     // start of step ks - 1), before that step's ring refill
-    const bool meta_fill = M4 && (ks & 3) == 0 && ks + 4 < ksteps;
+    const bool meta_fill = M4 && (PH >= 0 ? PH : (ks & 3)) == 0 && ks + 4 < ksteps;
 #pragma unroll
     for (int g = 0; g < G; g++) {
       if constexpr (M4) {
@@ -1076,7 +1090,7 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
       }
       if constexpr (REFILL) issue_part_at(ks + S - 1, fil, g, G);
       if (g + 1 < G) {
-        load_group(st, g + 1, ks, par_any{});
+        load_group(st, g + 1, ks, ph_t);
       } else if (REFILL || ks + 1 < ksteps) {
         // issued so far: stages up to min(ks+S-1, ksteps-1); stage ks+1 is
         // complete once at most stages ks+2 .. min(ks+S-1, ksteps-1) (and
@@ -1094,24 +1108,27 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
           wait_stages(min(S - 2, ksteps - ks - 2));
         }
         lds_barrier();                                   // every wave is done reading stage ks
-        load_group(ring + nxt * STAGE, 0, ks + 1, next_par_t);
+        load_group(ring + nxt * STAGE, 0, ks + 1, next_ph{});
       }
       compute_group(g);
     }
     return nxt;
   };
-  typedef std::integral_constant<int, 0> par_even;
-  typedef std::integral_constant<int, 1> par_odd;
-  int cur = kstep(0, 0, std::false_type{}, par_odd{});
+  typedef std::integral_constant<int, -1> phx;
+  int cur = kstep(0, 0, std::false_type{}, std::integral_constant<int, 0>{});
   int ks = 1;
-  // steady steps in pairs (odd, even), so that the parity the batched metadata
-  // reads depend on is static
-  for (; ks + S < ksteps; ks += 2) {
-    cur = kstep(ks, cur, std::true_type{}, par_even{});
-    cur = kstep(ks + 1, cur, std::true_type{}, par_odd{});
+  // steady steps four at a time from ks = 1, so that ks % 4 (which the batched
+  // metadata reads and fills depend on) is static in the loop body
+  if constexpr (M4) {
+    for (; ks + 3 + S - 1 < ksteps; ks += 4) {
+      cur = kstep(ks, cur, std::true_type{}, std::integral_constant<int, 1>{});
+      cur = kstep(ks + 1, cur, std::true_type{}, std::integral_constant<int, 2>{});
+      cur = kstep(ks + 2, cur, std::true_type{}, std::integral_constant<int, 3>{});
+      cur = kstep(ks + 3, cur, std::true_type{}, std::integral_constant<int, 0>{});
+    }
   }
-  for (; ks + S - 1 < ksteps; ks++) cur = kstep(ks, cur, std::true_type{}, par_any{});
-  for (; ks < ksteps; ks++) cur = kstep(ks, cur, std::false_type{}, par_any{});
+  for (; ks + S - 1 < ksteps; ks++) cur = kstep(ks, cur, std::true_type{}, phx{});
+  for (; ks < ksteps; ks++) cur = kstep(ks, cur, std::false_type{}, phx{});
 
   // ---- split-k: this block's partial sums go to plane z of the workspace, in
   // D's storage order, raw (alpha, beta and rounding are applied once, by the
