@@ -920,7 +920,6 @@ __global__ void __launch_bounds__(64 * WGM * WGN) gemm_dma_kernel(GemmArgs A) {
   ab_t bw[2][FN];
   const int qshift = 16 * q;
   // PH: ks % 4 when the caller knows it statically (0 .. 3), else -1
-  typedef std::integral_constant<int, -1> ph_any;
   auto load_group = [&](const uint8_t* st, int g, int ks, auto ph_t) {
     constexpr int PH = decltype(ph_t)::value;
     if constexpr (SP) {

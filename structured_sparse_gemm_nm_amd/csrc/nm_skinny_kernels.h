@@ -137,7 +137,8 @@ __global__ void __launch_bounds__(64 * SK2_WAVES) skinny2_kernel(GemmArgs A, int
     }
     // value word by word; lanes past the chunk use zero values, and their
     // offsets (whatever they are) select records past k, which are zero
-#pragma unroll(BIG ? 1 : PV)
+    constexpr int WUNROLL = BIG ? 1 : PV;
+#pragma unroll WUNROLL
     for (int wi = 0; wi < PV; wi++) {
       uint32_t word = pc.v[0];
 #pragma unroll
