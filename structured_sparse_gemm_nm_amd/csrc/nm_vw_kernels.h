@@ -120,13 +120,13 @@ __global__ void __launch_bounds__(64 * VW_WAVES) vw_gemm_kernel(GemmArgs A) {
     const uint8_t* bp = bbase + (size_t)st * bstep;
     const uint8_t* ap = abase + (size_t)st * A_ROW;
 #pragma unroll
-    for (int j = 0; j < NB; j++) dma16(bp + ob[j], base + (wave * NB + j) * 1024);
+    for (int j = 0; j < NB; j++) dma16s(bp, ob[j], base + (wave * NB + j) * 1024);
 #pragma unroll
-    for (int j = 0; j < NA; j++) dma16(ap + oa[j], base + B_ST + (wave * NA + j) * 1024);
+    for (int j = 0; j < NA; j++) dma16s(ap, oa[j], base + B_ST + (wave * NA + j) * 1024);
     // words from the one holding the step's first field; clamped into the row
     const int64_t w0 = ((int64_t)st * KP * b) >> 5;
     const int64_t w = w0 + mword < mwords ? w0 + mword : mwords - 1;
-    dma4((const uint8_t*)(mbase + w), base + B_ST + A_ST + wave * 256);
+    dma4((const uint8_t*)(mbase + w), base + B_ST + A_ST + wave * 256);   // (per-lane row: not a scalar base)
   };
 
   acc_t acc[FPW][FN];
@@ -190,13 +190,22 @@ __global__ void __launch_bounds__(64 * VW_WAVES) vw_gemm_kernel(GemmArgs A) {
 #pragma unroll
   for (int st = 0; st < S - 1; st++)
     if (st < ksteps) issue(st);
-  for (int ks = 0; ks < ksteps; ks++) {
-    if (ks + S - 1 < ksteps) issue(ks + S - 1);          // the slot freed at the end of step ks - 1
-    wait_stages(min(S - 1, ksteps - 1 - ks));             // stage ks has landed (this wave's copies)
+  // steps that refill the ring and the last S - 1 that do not, as separate
+  // loop bodies (no per-step tests in the steady loop)
+  auto vstep = [&](int ks, auto refill_t) {
+    if constexpr (decltype(refill_t)::value) {
+      issue(ks + S - 1);                                  // the slot freed at the end of step ks - 1
+      wait_stages(S - 1);                                 // stage ks has landed (this wave's copies)
+    } else {
+      wait_stages(min(S - 1, ksteps - 1 - ks));
+    }
     lds_barrier();                                        // ... and every wave's
     compute(ks);
     lds_barrier();                                        // every wave is done reading slot ks % S
-  }
+  };
+  int ks = 0;
+  for (; ks + S - 1 < ksteps; ks++) vstep(ks, std::true_type{});
+  for (; ks < ksteps; ks++) vstep(ks, std::false_type{});
 
   // ---- epilogue: D = alpha * acc + beta * C, accumulator element r of lane l
   // is D[4q + r][l % 16] of its 16 x 16 tile ----
