@@ -1649,6 +1649,16 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
           return launch_reduce<DT>(A, s);
         }
       }
+      if constexpr (AMODE == A_SPARSE24 && TM == 128 && TN == 128 && DT != DT_I8 && S1 == 3) {
+        // 2:4, 16-bit, 128 x 128 on four waves (the eight-wave kernel below
+        // cannot split a metadata fill evenly): metadata batched as for 256 x
+        // 256, 3 x 24 KB of ring + 8 KB of slots, still two blocks per CU
+        if (A.splits == 1 && (bkc || tiles > NUM_CU)) {
+          if (bkc) NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, 3, WGM, WGN, 5>), grid, dim3(64 * WGM * WGN), 0, s, A);
+          else NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, 3, WGM, WGN, 4>), grid, dim3(64 * WGM * WGN), 0, s, A);
+          return launch_reduce<DT>(A, s);
+        }
+      }
       if constexpr (AMODE == A_SPARSE24 && TM == 128 && TN == 128) {
         // eight waves (2 x 4 of 64 x 32) instead of four: measured faster for B
         // stored k x n when every CU has at most one tile (BERT FC2 NN 41.2 ->

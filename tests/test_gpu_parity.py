@@ -507,7 +507,10 @@ def test_spmm_kernel_names_the_launched_kernel():
     nn = plan_for("bf16", 1024, 4096, 4096, 2, 4, op_b="N").spmm_kernel
     assert nn.startswith("void nm::gemm_dma_kernel<1, 0, 128, 128,") and nn.endswith(", 2, 4, 0>(nm::GemmArgs)"), nn
     nt = plan_for("bf16", 1024, 4096, 4096, 2, 4, op_b="T").spmm_kernel
-    assert nt.startswith("void nm::gemm_dma_kernel<1, 0, 128, 128,") and nt.endswith(", 2, 2, 1>(nm::GemmArgs)"), nt
+    # four waves, op_b = T, batched metadata: layout bits 1 | 4
+    assert nt.startswith("void nm::gemm_dma_kernel<1, 0, 128, 128,") and nt.endswith(", 2, 2, 5>(nm::GemmArgs)"), nt
+    i8 = plan_for("i8", 1024, 4096, 4096, 2, 4, op_b="T").spmm_kernel
+    assert i8.startswith("void nm::gemm_dma_kernel<2, 0, 128, 128,") and i8.endswith(", 2, 2, 1>(nm::GemmArgs)"), i8
     ragged = plan_for("f16", 200, 144, 336, 2, 4).spmm_kernel
     assert ragged.startswith("void nm::gemm_kernel<0, 0,"), ragged
     assert "skinny2_kernel" in plan_for("f16", 100, 8, 1088, 2, 4).spmm_kernel
