@@ -1650,10 +1650,12 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
         }
       }
       if constexpr (AMODE == A_SPARSE24 && TM == 128 && TN == 128 && DT != DT_I8 && S1 == 3) {
-        // 2:4, 16-bit, 128 x 128 on four waves (the eight-wave kernel below
-        // cannot split a metadata fill evenly): metadata batched as for 256 x
-        // 256, 3 x 24 KB of ring + 8 KB of slots, still two blocks per CU
-        if (A.splits == 1 && (bkc || tiles > NUM_CU)) {
+        // 2:4, 16-bit, 128 x 128 on four waves: metadata batched as for 256 x
+        // 256, 3 x 24 KB of ring + 8 KB of slots, still two blocks per CU.
+        // Measured faster than the eight-wave kernel below (which cannot split
+        // a metadata fill evenly) also where that one had won: BERT FC2 NN
+        // 41-43 -> 33-34 us, PROJ NN 13.4 -> 11-13 us
+        if (A.splits == 1) {
           if (bkc) NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, 3, WGM, WGN, 5>), grid, dim3(64 * WGM * WGN), 0, s, A);
           else NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, 3, WGM, WGN, 4>), grid, dim3(64 * WGM * WGN), 0, s, A);
           return launch_reduce<DT>(A, s);
@@ -1663,7 +1665,8 @@ hipError_t launch_tiles_t(const nm_plan& pl, const GemmArgs& A, hipStream_t s) {
         // eight waves (2 x 4 of 64 x 32) instead of four: measured faster for B
         // stored k x n when every CU has at most one tile (BERT FC2 NN 41.2 ->
         // 38.4 us, PROJ NN 12.5 -> 11.7 us) and slower for B stored n x k
-        // (FC2 NT 37 -> 39.5 us)
+        // (FC2 NT 37 -> 39.5 us), before the batched metadata above; now int8
+        // and split-k only
         if (!bkc && tiles * A.splits <= NUM_CU) {
           NM_LAUNCH((gemm_dma_kernel<DT, AMODE, TM, TN, S1, 2, 4, 0>), grid, dim3(512), 0, s, A);
           return launch_reduce<DT>(A, s);

@@ -505,7 +505,9 @@ def test_spmm_kernel_names_the_launched_kernel():
     # op_b = T with metadata staged four k-steps at a time: layout bits 1 | 4
     assert big.startswith("void nm::gemm_dma_kernel<0, 0, 256, 256,") and big.endswith(", 5>(nm::GemmArgs)"), big
     nn = plan_for("bf16", 1024, 4096, 4096, 2, 4, op_b="N").spmm_kernel
-    assert nn.startswith("void nm::gemm_dma_kernel<1, 0, 128, 128,") and nn.endswith(", 2, 4, 0>(nm::GemmArgs)"), nn
+    assert nn.startswith("void nm::gemm_dma_kernel<1, 0, 128, 128,") and nn.endswith(", 2, 2, 4>(nm::GemmArgs)"), nn
+    nn8 = plan_for("i8", 1024, 4096, 4096, 2, 4, op_b="N").spmm_kernel   # int8: eight waves, one tile per CU
+    assert nn8.startswith("void nm::gemm_dma_kernel<2, 0, 128, 128,") and nn8.endswith(", 2, 4, 0>(nm::GemmArgs)"), nn8
     nt = plan_for("bf16", 1024, 4096, 4096, 2, 4, op_b="T").spmm_kernel
     # four waves, op_b = T, batched metadata: layout bits 1 | 4
     assert nt.startswith("void nm::gemm_dma_kernel<1, 0, 128, 128,") and nt.endswith(", 2, 2, 5>(nm::GemmArgs)"), nt
