@@ -866,6 +866,38 @@ def test_beta_epilogue_on_256_tiles(dtype, op_b, order):
     assert_close(dtype, logical(host(dc, raw)), ref, tol)
 
 
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("tile", ["128", "256"])
+@pytest.mark.parametrize("op_b", ["N", "T"])
+def test_batched_metadata_step_counts(dtype, tile, op_b):
+    """16-bit 2:4 kernels with the metadata staged four k-steps at a time, on
+    k-step counts that exercise the first step, the steady steps four at a
+    time, the remaining refill steps and the last steps (1, 2, 5, 6, 9 and 14
+    steps of 64), with beta != 0 and column-major D on some of them."""
+    m, n = (256, 384) if tile == "128" else (512, 512)
+    for i, steps in enumerate([1, 2, 5, 6, 9, 14]):
+        k = 64 * steps
+        a = rand(dtype, (m, k), 300 + steps)
+        v, meta = oracle.compress(a, dtype, 2, 4)
+        ahat, _ = oracle.prune_1d(a, dtype, 2, 4)
+        b_log = rand(dtype, (k, n), 400 + steps)
+        b_st = b_log if op_b == "N" else np.ascontiguousarray(b_log.T)
+        order = "col" if i % 2 else "row"
+        beta = -0.5 if i % 3 == 1 else 0.0
+        c = rand(dtype, (m, n), 500 + steps)
+        plan = plan_for(dtype, m, n, k, 2, 4, op_b=op_b, tile=tile, order_cd=order)
+        assert "%s, %s," % (tile, tile) in plan.spmm_kernel and plan.spmm_kernel.endswith(
+            ", %d>(nm::GemmArgs)" % (5 if op_b == "T" else 4)), plan.spmm_kernel
+        c_st = c if order == "row" else np.ascontiguousarray(c.T)
+        ref, tol = ref_product(dtype, ahat, b_log, 1.25, beta, c if beta else None)
+        d = Guarded(c_st.shape, torch.int16)
+        nm.nm_spmm(plan, 1.25, dev(v), dev(meta), dev(b_st), beta, dev(c_st) if beta else None, d.t)
+        sync()
+        d.check()
+        got = host(d.t, np.uint16)
+        assert_close(dtype, got if order == "row" else np.ascontiguousarray(got.T), ref, tol)
+
+
 def test_col_major_k_zero_and_alias():
     m, n = 40, 24
     c = rand("f16", (m, n), 11)
